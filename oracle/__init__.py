@@ -1,0 +1,7 @@
+"""CPU oracle of the RLT decoder transition.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.
+"""
+from .rlt_oracle import *  # noqa: F401,F403
+from .rlt_oracle import __all__  # noqa: F401
