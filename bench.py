@@ -1,0 +1,206 @@
+#!/usr/bin/env python
+"""Decoder tokens/s of the RLT recurrent decoder on one MI355X, and its roofline fraction.
+
+One benchmark step is one ``rlt_run_sequence`` call on a fresh state and empty memory: the
+token-parallel memory projection of all T tokens, then the T sequential decoder
+transitions for all B sequences, recording every s_t. The workload is the ~140M-scale
+configuration (d=768, 12 heads x 64, 12 blocks, FFN 3072, W=128, layer-specific memory,
+alpha=1, B=256, T=1024) with synthetic N(0,1) encoder outputs and N(0, 0.02) weights.
+
+Printed JSON (one line): value = B*T*steps / timed seconds; ``roofline`` for the dominant
+kernel (cross-attention; algorithmic bytes / HIP-event time of its launches over the timed
+region, against 8 TB/s HBM); ``step_roofline`` = ideal per-step roofline time over measured
+time; ``cpu_baseline`` = the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # MI355X HBM3E, bytes/s
+BF16_PEAK = 2.5e15       # MI355X dense bf16 MFMA, flop/s
+FP32_PEAK = 157.3e12
+METRIC = "RLT decoder tokens/sec (B seqs x T) on 1 MI355X; % of per-step roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cross_attn_traffic.json")
+
+
+def step_roofline_seconds(cfg, B: int, T: int) -> float:
+    """Ideal time of one run: memory projection + T steps, each at max(bytes / HBM peak,
+    flops / MFMA peak) with the algorithmic bytes of every step (weights once, the window and
+    the memory prefix of every layer once, s read and written)."""
+    d, L, F, W, G = cfg.d, cfg.n_layers, cfg.ffn, cfg.window, cfg.n_groups
+    es = 2 if cfg.dtype == "bf16" else 4
+    peak = BF16_PEAK if cfg.dtype == "bf16" else FP32_PEAK
+    p_step = 2 * d * d + L * (6 * d * d + 3 * d * F)
+    total = 0.0
+    for t in range(1, T + 1):
+        win = min(t, W)
+        by = es * (p_step + B * L * win * 2 * d + B * L * t * 2 * d) + B * d * (es + 8)
+        fl = 2 * B * p_step + 4 * B * L * d * (win + t)
+        total += max(by / HBM_PEAK, fl / peak)
+    mp_bytes = es * (B * T * d + G * B * T * 2 * d + 2 * G * d * d)
+    mp_flops = 2 * B * T * 2 * G * d * d
+    return total + max(mp_bytes / HBM_PEAK, mp_flops / peak)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(cfg, params, budget_s: float, n_seqs: int = 16) -> dict:
+    """The float64 oracle as it stands, on the first n_seqs sequences, token by token from
+    t = 1 until the time budget is used (memory projection of those tokens included)."""
+    import numpy as np
+
+    import oracle
+    from synth import make_encoder_outputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    T = cfg.seq_len
+    e = make_encoder_outputs(cfg, range(n_seqs)).astype(np.float64)
+    t0 = time.perf_counter()
+    p = oracle.prepare_params(params)
+    t_prep = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    km, vm = oracle.memory_projection(p, e)
+    t_mem = time.perf_counter() - t0
+    st = oracle.init_state(p, cfg, n_seqs)
+    t0 = time.perf_counter()
+    n = 0
+    while n < T and (n == 0 or time.perf_counter() - t0 + t_mem * (n + 1) / T < budget_s):
+        oracle.decoder_step(p, cfg, st, km, vm, e[:, n])
+        n += 1
+    wall = time.perf_counter() - t0 + t_mem * n / T  # projection of the n tokens used
+    return {"value": n_seqs * n / wall, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle, first {n_seqs} sequences, tokens 1..{n} of {T} "
+                      f"(memory projection pro rata), {wall:.1f} s; early tokens have short "
+                      "memory prefixes, so this overstates the oracle's whole-run rate",
+            "host_cpus": len(os.sched_getaffinity(0)), "param_prep_s": round(t_prep, 2)}
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from committed PMC counters, if taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="s140m_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): decoding shards over independent sequences with no exchange, so the "
+              "multi-GPU figure is N times the one-GPU figure at B/N sequences per GPU; it is "
+              "not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import stateful_decoding_amd as sd
+    from synth import CONFIGS, make_encoder_outputs, make_params
+
+    cfg = CONFIGS[args.workload]
+    B, T = cfg.batch, cfg.seq_len
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    print(f"[bench] workload {cfg.name}: B={B} T={T} d={cfg.d} L={cfg.n_layers} W={cfg.window} "
+          f"G={cfg.n_groups}", file=sys.stderr, flush=True)
+    params = make_params(cfg)
+    e_host = make_encoder_outputs(cfg, range(B))
+    c = sd.make_config(cfg)
+    model = sd.Model(c, sd.upload_weights(params, c, dev))
+    e = torch.from_numpy(e_host).to(dev, model.dtype).contiguous()
+    del e_host
+    state = sd.State(model, B)
+    mem = sd.Memory(model, B, T)
+    traj = torch.empty(B, T, cfg.d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        state.reset(stream)
+        mem.reset()
+        sd.rlt_run_sequence(model, state, mem, e, traj, stream)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    state.profile_begin(["cross_attn", "memproj"])
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        one_step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(stop)
+    prof = state.profile_end()
+    assert bool(torch.isfinite(traj).all()), "non-finite decoder output"
+    print(f"[bench] timed {args.steps} steps: {ms_total:.1f} ms (host wall {wall:.2f} s)",
+          file=sys.stderr, flush=True)
+
+    secs = ms_total / 1e3
+    value = B * T * args.steps / secs
+    ideal = step_roofline_seconds(cfg, B, T)
+    ca = prof["cross_attn"]
+    achieved = ca["bytes"] / (ca["total_ms"] / 1e3)
+    kernel_src = os.path.join(ROOT, "stateful_decoding_amd", "csrc", "attention.hip")
+    traffic = traffic_from_profile(kernel_src)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "seq_len": T, "d": cfg.d,
+                   "heads": cfg.n_heads, "head_dim": cfg.head_dim, "decoder_blocks": cfg.n_layers,
+                   "ffn": cfg.ffn, "window": cfg.window, "memory_groups": cfg.n_groups,
+                   "alpha": cfg.alpha, "inputs": "e_t ~ N(0,1), weights ~ N(0,0.02), seed 0"},
+        "roofline": {"bound": "hbm", "kernel": "cross_attn (k_attn_cross)",
+                     "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": traffic,
+                     "launches": ca["launches"],
+                     "avg_launch_us": round(ca["total_ms"] * 1e3 / ca["launches"], 2),
+                     "bytes_per_launch": round(ca["bytes"] / ca["launches"])},
+        "step_roofline": {"ideal_s": round(ideal, 4), "measured_s": round(secs / args.steps, 4),
+                          "frac": round(ideal / (secs / args.steps), 4),
+                          "peaks": "HBM 8.0 TB/s, bf16 MFMA 2.5 PFLOP/s"},
+        "kernel_share": {k: round(v["total_ms"] / ms_total, 4) for k, v in prof.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, params, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

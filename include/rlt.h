@@ -1,0 +1,233 @@
+/*
+ * rlt.h - C ABI of the MI355X (gfx950) Recurrent Looped Transformer decoder-step library.
+ *
+ * The library computes the per-token recurrent decoder transition H_{t-1} -> H_t of the
+ * Recurrent Looped Transformer for B independent sequences at once, plus the token-parallel
+ * projection of encoder outputs into the key/value memory that feeds it. Source of the
+ * method: "RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", section
+ * "Architecture: encoder memory meets recurrent decoder" (state H_t = (s_t, C_t^D), gated
+ * merge, per-block sliding-window self-attention + cross-attention to M_{<=t} + FFN, window W
+ * counting the current token, learned start state s*), and its section "Three design
+ * principles and their caveats" (memory projection runs token-parallel; transitions of
+ * independent sequences share one batched kernel; no parallel scan over tokens).
+ *
+ * Formulas (the pages state none; these are the readings the library implements):
+ *   u = alpha * s_{t-1};  g = sigmoid([e_t ; u] W_g + b_g);  h = g*e_t + (1-g)*u
+ *   for each block l:  h += SWA(RMSNorm(h; gamma_l0))      window: this token + W-1 past
+ *                      h += Cross(RMSNorm(h; gamma_l1))    memory entries 1..t of group g(l)
+ *                      h += (SiLU(f W1) * (f W3)) W2,  f = RMSNorm(h; gamma_l2)
+ *   s_t = h.   RMSNorm(x; gamma) = gamma * x / sqrt(mean(x^2) + eps).
+ *   Attention is multi-head (H heads of hd = d/H), softmax scale 1/sqrt(hd), no biases,
+ *   no positional encoding. Memory: K_j = e_j W_mK^(g), V_j = e_j W_mV^(g), g(l) = 0 when
+ *   G = 1 and g(l) = l when G = L.
+ *
+ * Conventions for every call:
+ *   - Device memory is allocated by the caller and borrowed by handles; the library never
+ *     allocates device memory. Handles are host objects owned by the library and freed by
+ *     the matching *_destroy (which never frees caller memory).
+ *   - "dtype" arrays hold float32 (RLT_F32) or bfloat16 (RLT_BF16) elements, row-major.
+ *     s, s*, b_g and the gains are always float32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is
+ *     enqueued on it and the call returns without waiting, except where stated.
+ *   - Every call validates all arguments before enqueuing anything; on error it returns a
+ *     non-zero rlt_status, mutates nothing, and rlt_last_error() describes the problem.
+ *     RLT_ERR_HIP reports a failed HIP call (launch or copy); state contents are then
+ *     undefined.
+ *   - Handles are not thread-safe. Distinct states on distinct streams may run concurrently.
+ */
+#ifndef RLT_H
+#define RLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rlt_status {
+  RLT_OK = 0,
+  RLT_ERR_ARG = 1,           /* NULL handle/pointer, non-finite alpha, bad count      */
+  RLT_ERR_SHAPE = 2,         /* sizes the library does not support or that disagree  */
+  RLT_ERR_DTYPE = 3,         /* unknown dtype                                        */
+  RLT_ERR_CAPACITY = 4,      /* caller buffer too small, or past the memory capacity */
+  RLT_ERR_NOT_PROJECTED = 5, /* a step needs memory entries that are not projected   */
+  RLT_ERR_HIP = 6,           /* a HIP runtime call failed                            */
+  RLT_ERR_VERSION = 7        /* snapshot from a model with another version tag       */
+} rlt_status;
+
+typedef enum rlt_dtype { RLT_F32 = 0, RLT_BF16 = 1 } rlt_dtype;
+
+/* Model shape. Supported: d = n_heads * head_dim, head_dim in {32, 64, 128}, d % 64 == 0,
+ * ffn % 64 == 0, 1 <= window <= 1024, n_groups in {1, n_layers}, eps >= 0, alpha finite.
+ * `version` is a caller-chosen tag of the weights, stored in snapshots and checked on import. */
+typedef struct rlt_config {
+  int32_t d;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t n_layers;   /* L_D */
+  int32_t ffn;        /* F   */
+  int32_t window;     /* W, counts the current token */
+  int32_t n_groups;   /* G   */
+  int32_t dtype;      /* rlt_dtype */
+  float alpha;        /* feedback scale */
+  float eps;          /* RMSNorm epsilon */
+  uint64_t version;
+} rlt_config;
+
+/* Device pointers to the weights, in the math convention y = x W (row-major [in][out]).
+ * Matrices are `dtype`; the rest float32. Only read during rlt_model_create. */
+typedef struct rlt_weights {
+  const float* s_star; /* [d]        learned start state s*                               */
+  const void* w_gate;  /* [2d][d]    rows 0..d-1 multiply e_t, rows d..2d-1 multiply u     */
+  const float* b_gate; /* [d]                                                              */
+  const float* gamma;  /* [L][3][d]  gains before self-attention, cross-attention, FFN    */
+  const void* wq;      /* [L][d][d]  */
+  const void* wk;      /* [L][d][d]  */
+  const void* wv;      /* [L][d][d]  */
+  const void* wo;      /* [L][d][d]  */
+  const void* wcq;     /* [L][d][d]  cross-attention query projection                     */
+  const void* wco;     /* [L][d][d]  cross-attention output projection                    */
+  const void* w1;      /* [L][d][F]  FFN gate branch (through SiLU)                       */
+  const void* w3;      /* [L][d][F]  FFN linear branch                                    */
+  const void* w2;      /* [L][F][d]  FFN down projection                                  */
+  const void* wmk;     /* [G][d][d]  memory key projection                                */
+  const void* wmv;     /* [G][d][d]  memory value projection                              */
+} rlt_weights;
+
+typedef struct rlt_model rlt_model;
+typedef struct rlt_state rlt_state;
+typedef struct rlt_memory rlt_memory;
+
+/* Thread-local description of the last error (empty string if none). Never NULL. */
+const char* rlt_last_error(void);
+
+/* Validates a configuration without touching the GPU. */
+rlt_status rlt_config_check(const rlt_config* cfg);
+
+/* --- model ------------------------------------------------------------------------------ */
+
+/* Bytes of device workspace rlt_model_create needs for the packed weights (0 if the
+ * configuration is invalid). */
+size_t rlt_model_ws_bytes(const rlt_config* cfg);
+
+/* Packs the weights into `ws` (device, >= rlt_model_ws_bytes, 256-byte aligned) in the
+ * layouts the kernels read, on `stream`, and waits for that stream: on return the caller may
+ * free the source weights. `ws` must stay alive until rlt_model_destroy. */
+rlt_status rlt_model_create(const rlt_config* cfg, const rlt_weights* w, void* ws,
+                            size_t ws_bytes, void* stream, rlt_model** out);
+void rlt_model_destroy(rlt_model* model);
+
+/* --- decoder state H_t = (s_t, C_t^D) ------------------------------------------------- */
+
+/* Bytes of device memory for the state of B sequences: s [B][d] float32, the per-layer
+ * self-attention caches, and the working buffers of one decoder step. */
+size_t rlt_state_bytes(const rlt_config* cfg, int32_t batch);
+
+/* Binds `buf` (device, >= rlt_state_bytes, 256-byte aligned) as the state of `batch`
+ * sequences and resets it on `stream` (see rlt_state_reset). */
+rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, size_t bytes,
+                            void* stream, rlt_state** out);
+
+/* s_0 = s* for every sequence, empty caches, position t = 0 (before the first token). */
+rlt_status rlt_state_reset(rlt_state* state, void* stream);
+
+/* Number of tokens the state has processed (t). */
+int64_t rlt_state_position(const rlt_state* state);
+void rlt_state_destroy(rlt_state* state);
+
+/* --- encoder memory M ----------------------------------------------------------------- */
+
+/* Bytes for the key and value memory of B sequences up to `capacity` tokens:
+ * K and V, each [G][B][H][capacity][hd] dtype. 1 <= capacity <= 65536. */
+size_t rlt_memory_bytes(const rlt_config* cfg, int32_t batch, int64_t capacity);
+
+/* Binds `buf` (device, >= rlt_memory_bytes, 256-byte aligned) as empty memory (length 0). */
+rlt_status rlt_memory_create(const rlt_model* model, int32_t batch, int64_t capacity, void* buf,
+                             size_t bytes, rlt_memory** out);
+
+/* Number of tokens whose keys/values have been projected (entries 0..length-1). */
+int64_t rlt_memory_length(const rlt_memory* mem);
+
+/* Marks the memory empty (length 0) so it can be projected again from token 0; host-only. */
+rlt_status rlt_memory_reset(rlt_memory* mem);
+void rlt_memory_destroy(rlt_memory* mem);
+
+/* Token-parallel memory projection of tokens t0 .. t0+n-1 (0-based) from encoder outputs
+ * e [B][n][d] dtype (device). Requires 0 <= t0 <= length (no holes), n >= 1 and
+ * t0 + n <= capacity; afterwards length = max(length, t0 + n). */
+rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, int64_t t0,
+                       int64_t n, void* stream);
+
+/* --- the recurrent transition --------------------------------------------------------- */
+
+/* One decoder step for every sequence: consumes e_t [B][d] dtype (device) for token
+ * t+1 (1-based), where t = rlt_state_position; needs memory length >= t+1 (else
+ * RLT_ERR_NOT_PROJECTED). Writes s_{t+1} to s_out [B][d] float32 (device) unless NULL, and
+ * advances the position. The state and the memory must belong to `model` and have the
+ * same batch. */
+rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
+                            const void* e_t, float* s_out, void* stream);
+
+/* n consecutive steps over e [B][n][d] dtype (device), the encoder outputs of tokens
+ * t+1 .. t+n. First projects every one of those tokens that the memory does not hold yet
+ * (same as rlt_memproj on the missing range; requires t <= length and t + n <= capacity),
+ * then runs n steps. s_traj [B][n][d] float32 (device) receives every s unless NULL. The
+ * result equals rlt_memproj followed by n calls of rlt_decoder_step. */
+rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                            const void* e, int64_t n, float* s_traj, void* stream);
+
+/* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
+
+/* Copies the state to caller buffers in canonical order and waits for the stream:
+ *   s [B][d] float32 (device); k, v [L][B][W-1][d] dtype (device), per layer and sequence
+ *   the retained entries oldest first, zero padded; *n_valid = min(t, W-1); *position = t;
+ *   *version = the model's version tag. Any output pointer may be NULL to skip it. */
+rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v,
+                            int32_t* n_valid, int64_t* position, uint64_t* version,
+                            void* stream);
+
+/* Loads a snapshot in the layout rlt_state_export writes (k/v rows beyond min(t, W-1) are
+ * ignored). Fails with RLT_ERR_VERSION, changing nothing, if `version` differs from the
+ * model's tag. Waits for the stream. */
+rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, const void* v,
+                            int64_t position, uint64_t version, void* stream);
+
+/* --- kernel timing --------------------------------------------------------------------- */
+
+/* Kernels of one decoder step (and the memory projection run by rlt_run_sequence). */
+typedef enum rlt_kernel {
+  RLT_K_GATE = 0,        /* gated merge: [e_t ; alpha s] W_g, sigmoid, merge            */
+  RLT_K_QKV = 1,         /* RMSNorm + q/k/v projection, k/v into the ring cache          */
+  RLT_K_SELF_ATTN = 2,   /* sliding-window attention over the ring cache                 */
+  RLT_K_SELF_OUT = 3,    /* self-attention output projection + residual                  */
+  RLT_K_CROSS_Q = 4,     /* RMSNorm + cross-attention query projection                   */
+  RLT_K_CROSS_ATTN = 5,  /* attention over memory entries 1..t                            */
+  RLT_K_CROSS_OUT = 6,   /* cross-attention output projection + residual                 */
+  RLT_K_FFN_UP = 7,      /* RMSNorm + W1/W3 projection + SiLU product                     */
+  RLT_K_FFN_DOWN = 8,    /* W2 projection + residual                                      */
+  RLT_K_MEMPROJ = 9,     /* memory projection                                             */
+  RLT_K_COUNT = 10
+} rlt_kernel;
+
+typedef struct rlt_kernel_stats {
+  int64_t launches;  /* launches timed                                                   */
+  double total_ms;   /* sum over launches of the HIP-event time around the launch        */
+  double bytes;      /* algorithmic bytes: each operand read once, each result written once */
+  double flops;      /* algorithmic floating-point operations                            */
+} rlt_kernel_stats;
+
+/* Starts timing, for this state, every launch of the kernels whose bit (1 << rlt_kernel) is
+ * set in `mask`: a HIP event is recorded on the launch stream before and after each one.
+ * Timing adds two event records per timed launch to the stream. */
+rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask);
+
+/* Stops timing, waits for the recorded events and writes RLT_K_COUNT entries to `out`
+ * (host array, indexed by rlt_kernel). */
+rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLT_H */

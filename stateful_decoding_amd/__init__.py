@@ -1,0 +1,10 @@
+"""MI355X (gfx950) Recurrent Looped Transformer decoder step.
+
+The product is the C-ABI library ``librlt.so`` (include/rlt.h); this package holds its HIP
+sources (``csrc/``), the build script and a thin ctypes binding with the same call names.
+"""
+from .binding import (  # noqa: F401
+    LIB_PATH, Memory, Model, RLTError, State, load_library, make_config, rlt_config,
+    rlt_decoder_step, rlt_memproj, rlt_run_sequence, rlt_state_export, rlt_state_import,
+    upload_weights,
+)

@@ -1,0 +1,313 @@
+"""ctypes binding of ``librlt.so`` (declared in include/rlt.h).
+
+Argument marshalling only: every step of the decoder runs in the library's HIP kernels. The
+functions carry the C names; small handle classes own the torch device buffers that the C
+handles borrow, so the memory stays alive as long as the handle. torch is used for device
+memory and streams, nothing else. There is no fallback: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librlt.so")
+
+RLT_F32, RLT_BF16 = 0, 1
+STATUS_NAMES = {0: "RLT_OK", 1: "RLT_ERR_ARG", 2: "RLT_ERR_SHAPE", 3: "RLT_ERR_DTYPE",
+                4: "RLT_ERR_CAPACITY", 5: "RLT_ERR_NOT_PROJECTED", 6: "RLT_ERR_HIP",
+                7: "RLT_ERR_VERSION"}
+
+WEIGHT_FIELDS = ("s_star", "w_gate", "b_gate", "gamma", "wq", "wk", "wv", "wo", "wcq", "wco",
+                 "w1", "w3", "w2", "wmk", "wmv")
+FP32_FIELDS = ("s_star", "b_gate", "gamma")
+
+
+class rlt_config(ctypes.Structure):
+    _fields_ = [("d", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
+                ("n_layers", c_int32), ("ffn", c_int32), ("window", c_int32),
+                ("n_groups", c_int32), ("dtype", c_int32), ("alpha", c_float), ("eps", c_float),
+                ("version", c_uint64)]
+
+
+class rlt_weights(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in WEIGHT_FIELDS]
+
+
+KERNEL_NAMES = ("gate", "qkv", "self_attn", "self_out", "cross_q", "cross_attn", "cross_out",
+                "ffn_up", "ffn_down", "memproj")
+
+
+class rlt_kernel_stats(ctypes.Structure):
+    _fields_ = [("launches", c_int64), ("total_ms", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("flops", ctypes.c_double)]
+
+
+class RLTError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librlt.so and declare its signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m stateful_decoding_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = c_void_p
+    sig = {
+        "rlt_last_error": (c_char_p, []),
+        "rlt_config_check": (c_int32, [POINTER(rlt_config)]),
+        "rlt_model_ws_bytes": (c_size_t, [POINTER(rlt_config)]),
+        "rlt_model_create": (c_int32, [POINTER(rlt_config), POINTER(rlt_weights), P, c_size_t, P,
+                                       POINTER(P)]),
+        "rlt_model_destroy": (None, [P]),
+        "rlt_state_bytes": (c_size_t, [POINTER(rlt_config), c_int32]),
+        "rlt_state_create": (c_int32, [P, c_int32, P, c_size_t, P, POINTER(P)]),
+        "rlt_state_reset": (c_int32, [P, P]),
+        "rlt_state_position": (c_int64, [P]),
+        "rlt_state_destroy": (None, [P]),
+        "rlt_memory_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
+        "rlt_memory_create": (c_int32, [P, c_int32, c_int64, P, c_size_t, POINTER(P)]),
+        "rlt_memory_length": (c_int64, [P]),
+        "rlt_memory_reset": (c_int32, [P]),
+        "rlt_profile_begin": (c_int32, [P, ctypes.c_uint32]),
+        "rlt_profile_end": (c_int32, [P, POINTER(rlt_kernel_stats)]),
+        "rlt_memory_destroy": (None, [P]),
+        "rlt_memproj": (c_int32, [P, P, P, c_int64, c_int64, P]),
+        "rlt_decoder_step": (c_int32, [P, P, P, P, P, P]),
+        "rlt_run_sequence": (c_int32, [P, P, P, P, c_int64, P, P]),
+        "rlt_state_export": (c_int32, [P, P, P, P, POINTER(c_int32), POINTER(c_int64),
+                                       POINTER(c_uint64), P]),
+        "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RLTError(status, load_library().rlt_last_error().decode())
+
+
+def make_config(cfg, version: int = 0) -> rlt_config:
+    """rlt_config from any object with the fields d, n_heads, head_dim, n_layers, ffn,
+    window, n_groups, alpha, eps and dtype ('fp32' | 'bf16')."""
+    g = (lambda k: cfg[k]) if isinstance(cfg, dict) else (lambda k: getattr(cfg, k))
+    dt = g("dtype")
+    return rlt_config(int(g("d")), int(g("n_heads")), int(g("head_dim")), int(g("n_layers")),
+                      int(g("ffn")), int(g("window")), int(g("n_groups")),
+                      RLT_BF16 if dt in ("bf16", RLT_BF16) else RLT_F32 if dt in ("fp32", RLT_F32) else int(dt),
+                      float(g("alpha")), float(g("eps")), int(version))
+
+
+def torch_dtype(c: rlt_config):
+    return torch.bfloat16 if c.dtype == RLT_BF16 else torch.float32
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _device_buffer(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte aligned blocks
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def upload_weights(params: dict, cfg: rlt_config, device="cuda") -> dict:
+    """Host arrays (numpy or torch) -> contiguous device tensors in the layouts of
+    rlt_weights: matrices in the config dtype, s*, b_g and the gains in float32."""
+    out = {}
+    dt = torch_dtype(cfg)
+    for name in WEIGHT_FIELDS:
+        x = params[name]
+        x = torch.as_tensor(x) if not isinstance(x, torch.Tensor) else x
+        out[name] = x.to(device=device, dtype=torch.float32 if name in FP32_FIELDS else dt).contiguous()
+    return out
+
+
+class Model:
+    """Packed weights on the device (rlt_model_create)."""
+
+    def __init__(self, cfg, weights: dict, version: int = 0, stream=None, device="cuda"):
+        self.lib = load_library()
+        self.cfg = cfg if isinstance(cfg, rlt_config) else make_config(cfg, version)
+        _check(self.lib.rlt_config_check(byref(self.cfg)))
+        self.dtype = torch_dtype(self.cfg)
+        w = rlt_weights(*[_ptr(weights[n]) for n in WEIGHT_FIELDS])
+        nbytes = self.lib.rlt_model_ws_bytes(byref(self.cfg))
+        self.ws = _device_buffer(nbytes, device)
+        h = c_void_p()
+        _check(self.lib.rlt_model_create(byref(self.cfg), byref(w), self.ws.data_ptr(), nbytes,
+                                         _stream(stream), byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self.lib.rlt_model_destroy(self.handle)
+            self.handle = None
+
+
+class State:
+    """Decoder state of `batch` sequences (rlt_state_create): s, caches, working buffers."""
+
+    def __init__(self, model: Model, batch: int, stream=None):
+        self.lib, self.model, self.batch = model.lib, model, int(batch)
+        nbytes = self.lib.rlt_state_bytes(byref(model.cfg), self.batch)
+        if nbytes == 0:
+            raise RLTError(2, f"invalid batch {batch}")
+        self.buf = _device_buffer(nbytes, model.ws.device)
+        h = c_void_p()
+        _check(self.lib.rlt_state_create(model.handle, self.batch, self.buf.data_ptr(), nbytes,
+                                         _stream(stream), byref(h)))
+        self.handle = h
+
+    @property
+    def position(self) -> int:
+        return self.lib.rlt_state_position(self.handle)
+
+    def reset(self, stream=None):
+        _check(self.lib.rlt_state_reset(self.handle, _stream(stream)))
+
+    def profile_begin(self, kernels=KERNEL_NAMES):
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_NAMES.index(k)
+        _check(self.lib.rlt_profile_begin(self.handle, mask))
+
+    def profile_end(self) -> dict:
+        """{kernel name: {launches, total_ms, bytes, flops}} for the timed kernels."""
+        out = (rlt_kernel_stats * len(KERNEL_NAMES))()
+        _check(self.lib.rlt_profile_end(self.handle, out))
+        return {n: {"launches": o.launches, "total_ms": o.total_ms, "bytes": o.bytes,
+                    "flops": o.flops} for n, o in zip(KERNEL_NAMES, out) if o.launches}
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self.lib.rlt_state_destroy(self.handle)
+            self.handle = None
+
+
+class Memory:
+    """Encoder key/value memory of `batch` sequences for up to `capacity` tokens."""
+
+    def __init__(self, model: Model, batch: int, capacity: int):
+        self.lib, self.model, self.batch, self.capacity = model.lib, model, int(batch), int(capacity)
+        nbytes = self.lib.rlt_memory_bytes(byref(model.cfg), self.batch, self.capacity)
+        if nbytes == 0:
+            raise RLTError(4, f"invalid batch {batch} or capacity {capacity}")
+        self.buf = _device_buffer(nbytes, model.ws.device)
+        h = c_void_p()
+        _check(self.lib.rlt_memory_create(model.handle, self.batch, self.capacity,
+                                          self.buf.data_ptr(), nbytes, byref(h)))
+        self.handle = h
+
+    @property
+    def length(self) -> int:
+        return self.lib.rlt_memory_length(self.handle)
+
+    def reset(self):
+        _check(self.lib.rlt_memory_reset(self.handle))
+
+    def views(self):
+        """(K, V) as tensors [G, B, H, capacity, hd] aliasing the memory buffer."""
+        c = self.model.cfg
+        n = c.n_groups * self.batch * c.n_heads * self.capacity * c.head_dim
+        es = 2 if c.dtype == RLT_BF16 else 4
+        half = (n * es + 255) // 256 * 256
+        shape = (c.n_groups, self.batch, c.n_heads, self.capacity, c.head_dim)
+        k = self.buf[: n * es].view(self.model.dtype).view(shape)
+        v = self.buf[half: half + n * es].view(self.model.dtype).view(shape)
+        return k, v
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self.lib.rlt_memory_destroy(self.handle)
+            self.handle = None
+
+
+def _need(t: torch.Tensor, shape, dtype, what):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)}")
+
+
+def rlt_memproj(model: Model, mem: Memory, e: torch.Tensor, t0: int, stream=None):
+    """Project e [B, n, d] into memory entries t0 .. t0+n-1."""
+    B, n, d = e.shape
+    _need(e, (mem.batch, n, model.cfg.d), model.dtype, "e")
+    _check(model.lib.rlt_memproj(model.handle, mem.handle, e.data_ptr(), int(t0), int(n),
+                                 _stream(stream)))
+
+
+def rlt_decoder_step(model: Model, state: State, mem: Memory, e_t: torch.Tensor,
+                     s_out: torch.Tensor | None = None, stream=None):
+    """One recurrent step; e_t [B, d]; optional s_out [B, d] float32."""
+    _need(e_t, (state.batch, model.cfg.d), model.dtype, "e_t")
+    if s_out is not None:
+        _need(s_out, (state.batch, model.cfg.d), torch.float32, "s_out")
+    _check(model.lib.rlt_decoder_step(model.handle, state.handle, mem.handle, e_t.data_ptr(),
+                                      _ptr(s_out), _stream(stream)))
+
+
+def rlt_run_sequence(model: Model, state: State, mem: Memory, e: torch.Tensor,
+                     s_traj: torch.Tensor | None = None, stream=None):
+    """Memory projection of the missing tokens, then e.shape[1] steps; optional s_traj
+    [B, n, d] float32."""
+    n = e.shape[1]
+    _need(e, (state.batch, n, model.cfg.d), model.dtype, "e")
+    if s_traj is not None:
+        _need(s_traj, (state.batch, n, model.cfg.d), torch.float32, "s_traj")
+    _check(model.lib.rlt_run_sequence(model.handle, state.handle, mem.handle, e.data_ptr(), int(n),
+                                      _ptr(s_traj), _stream(stream)))
+
+
+def rlt_state_export(state: State, stream=None):
+    """Snapshot (s [B, d] f32, k, v [L, B, W-1, d] dtype, n_valid, position, version)."""
+    c = state.model.cfg
+    dev = state.buf.device
+    s = torch.empty(state.batch, c.d, dtype=torch.float32, device=dev)
+    keep = c.window - 1
+    k = torch.empty(c.n_layers, state.batch, keep, c.d, dtype=state.model.dtype, device=dev)
+    v = torch.empty_like(k)
+    n_valid, pos, ver = c_int32(), c_int64(), c_uint64()
+    _check(state.lib.rlt_state_export(state.handle, s.data_ptr(), _ptr(k) if keep else None,
+                                      _ptr(v) if keep else None, byref(n_valid), byref(pos),
+                                      byref(ver), _stream(stream)))
+    return s, k, v, n_valid.value, pos.value, ver.value
+
+
+def rlt_state_import(state: State, s: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     position: int, version: int, stream=None):
+    c = state.model.cfg
+    _need(s, (state.batch, c.d), torch.float32, "s")
+    shape = (c.n_layers, state.batch, c.window - 1, c.d)
+    _need(k, shape, state.model.dtype, "k")
+    _need(v, shape, state.model.dtype, "v")
+    if c.window == 1:  # nothing retained; pass any valid pointer
+        k = v = s
+    _check(state.lib.rlt_state_import(state.handle, s.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      int(position), int(version), _stream(stream)))

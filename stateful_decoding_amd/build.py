@@ -1,0 +1,83 @@
+"""Build the gfx950 C-ABI library ``librlt.so`` in-tree with hipcc.
+
+Usage: ``python -m stateful_decoding_amd.build`` (or ``build()`` from Python). Every call
+compiles from source; nothing is cached.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "librlt.so")
+
+SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "misc.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # keep packed fp32 instructions out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build librlt.so")
+    return exe
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source to an object, then link ``librlt.so``. Returns the library path."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT, text=True)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), verbose)
+    for p in procs:
+        _wait(p, verbose)
+    tmp = LIB + ".tmp"
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item, verbose):
+    src, p = item
+    out, _ = p.communicate()
+    if p.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{out}")
+    if verbose and out.strip():
+        print(_filter(out), flush=True)
+
+
+def _filter(text: str) -> str:
+    # hipcc's host pass does not know the packed-fp32 target feature; that note is harmless.
+    return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,498 @@
+// Host side of the C ABI declared in include/rlt.h: argument validation, handle bookkeeping,
+// buffer layouts and the sequencing of kernel launches. Validation always completes before
+// anything is enqueued, so a rejected call leaves every handle and buffer untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+using namespace rlt;
+
+struct rlt_model {
+  rlt_config cfg;
+  Dims D;
+  Packed P;
+};
+
+struct rlt_state {
+  const rlt_model* model;
+  int B;
+  int64_t t;
+  StateBufs S;
+  Profiler prof;
+};
+
+struct rlt_memory {
+  const rlt_model* model;
+  int B;
+  int64_t len;
+  MemBufs M;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+rlt_status fail(rlt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+rlt_status ok() {
+  g_err.clear();
+  return RLT_OK;
+}
+
+rlt_status hip_fail(hipError_t e, const char* what) {
+  return fail(RLT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+
+rlt_status check_config(const rlt_config* c) {
+  if (!c) return fail(RLT_ERR_ARG, "config is NULL");
+  if (c->dtype != RLT_F32 && c->dtype != RLT_BF16)
+    return fail(RLT_ERR_DTYPE, "unknown dtype %d", c->dtype);
+  if (c->d <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->n_layers <= 0 || c->ffn <= 0 ||
+      c->window <= 0 || c->n_groups <= 0)
+    return fail(RLT_ERR_SHAPE, "all sizes must be positive");
+  if ((int64_t)c->n_heads * c->head_dim != c->d)
+    return fail(RLT_ERR_SHAPE, "d (%d) must equal n_heads (%d) * head_dim (%d)", c->d, c->n_heads,
+                c->head_dim);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(RLT_ERR_SHAPE, "head_dim %d unsupported (32, 64 or 128)", c->head_dim);
+  if (c->d % 64 != 0) return fail(RLT_ERR_SHAPE, "d (%d) must be a multiple of 64", c->d);
+  if (c->ffn % 64 != 0) return fail(RLT_ERR_SHAPE, "ffn (%d) must be a multiple of 64", c->ffn);
+  if (c->d > 16384 || c->ffn > 65536 || c->n_layers > 4096)
+    return fail(RLT_ERR_SHAPE, "sizes beyond the supported range");
+  if (c->window > kMaxWindow)
+    return fail(RLT_ERR_SHAPE, "window %d exceeds %d", c->window, kMaxWindow);
+  if (c->n_groups != 1 && c->n_groups != c->n_layers)
+    return fail(RLT_ERR_SHAPE, "n_groups must be 1 or n_layers (%d), got %d", c->n_layers,
+                c->n_groups);
+  if (!std::isfinite(c->alpha)) return fail(RLT_ERR_ARG, "alpha must be finite");
+  if (!std::isfinite(c->eps) || c->eps < 0.f) return fail(RLT_ERR_ARG, "eps must be >= 0");
+  return ok();
+}
+
+Dims dims_of(const rlt_config& c) {
+  Dims D;
+  D.d = c.d; D.H = c.n_heads; D.hd = c.head_dim; D.L = c.n_layers; D.F = c.ffn; D.W = c.window;
+  D.G = c.n_groups; D.dtype = c.dtype; D.alpha = c.alpha; D.eps = c.eps;
+  D.es = c.dtype == RLT_BF16 ? 2 : 4;
+  return D;
+}
+
+struct ModelLayout {
+  size_t w_gate_t, b_gate, s_star, gamma, wqkv_t, wo_t, wcq_t, wco_t, w13_t, w2_t, wm_t, total;
+};
+
+ModelLayout model_layout(const Dims& D) {
+  ModelLayout m;
+  size_t o = 0;
+  const size_t d = D.d, L = D.L, F = D.F, G = D.G, es = D.es;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  m.w_gate_t = take(2 * d * d * es);
+  m.b_gate = take(d * 4);
+  m.s_star = take(d * 4);
+  m.gamma = take(L * 3 * d * 4);
+  m.wqkv_t = take(L * 3 * d * d * es);
+  m.wo_t = take(L * d * d * es);
+  m.wcq_t = take(L * d * d * es);
+  m.wco_t = take(L * d * d * es);
+  m.w13_t = take(L * 2 * F * d * es);
+  m.w2_t = take(L * F * d * es);
+  m.wm_t = take(G * 2 * d * d * es);
+  m.total = o;
+  return m;
+}
+
+template <typename P>
+P* at(void* base, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+bool valid_batch(int B) { return B >= 1 && B <= (1 << 20); }
+
+}  // namespace
+
+namespace rlt {
+StateLayout state_layout(const Dims& D, int B) {
+  StateLayout s;
+  size_t o = 0;
+  const size_t b = B, d = D.d, es = D.es;
+  auto take = [&](size_t bytes) {
+    size_t a = o;
+    o = align_up(o + bytes);
+    return a;
+  };
+  const size_t ring = (size_t)D.L * b * D.H * D.W * D.hd * es;
+  s.s = take(b * d * 4);
+  s.ring_k = take(ring);
+  s.ring_v = take(ring);
+  s.h = take(b * d * 4);
+  s.q = take(b * d * 4);
+  s.qc = take(b * d * 4);
+  s.o = take(b * d * es);
+  s.act = take(b * D.F * es);
+  s.part = take(b * D.H * kMaxSplit * (D.hd + 2) * 4);
+  s.cnt = take(b * D.H * 4);
+  s.total = o;
+  return s;
+}
+}  // namespace rlt
+
+extern "C" {
+
+const char* rlt_last_error(void) { return g_err.c_str(); }
+
+rlt_status rlt_config_check(const rlt_config* cfg) { return check_config(cfg); }
+
+size_t rlt_model_ws_bytes(const rlt_config* cfg) {
+  if (check_config(cfg) != RLT_OK) return 0;
+  return model_layout(dims_of(*cfg)).total;
+}
+
+rlt_status rlt_model_create(const rlt_config* cfg, const rlt_weights* w, void* ws,
+                            size_t ws_bytes, void* stream, rlt_model** out) {
+  if (rlt_status s = check_config(cfg)) return s;
+  if (!w || !ws || !out) return fail(RLT_ERR_ARG, "weights, workspace and out must be non-NULL");
+  const void* ptrs[] = {w->s_star, w->w_gate, w->b_gate, w->gamma, w->wq, w->wk, w->wv, w->wo,
+                        w->wcq, w->wco, w->w1, w->w3, w->w2, w->wmk, w->wmv};
+  for (const void* p : ptrs)
+    if (!p) return fail(RLT_ERR_ARG, "a weight pointer is NULL");
+  const Dims D = dims_of(*cfg);
+  const ModelLayout m = model_layout(D);
+  if (ws_bytes < m.total)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, m.total);
+  if (!aligned(ws)) return fail(RLT_ERR_ARG, "workspace must be 256-byte aligned");
+
+  rlt_model* mdl = new (std::nothrow) rlt_model;
+  if (!mdl) return fail(RLT_ERR_ARG, "out of host memory");
+  mdl->cfg = *cfg;
+  mdl->D = D;
+  Packed& P = mdl->P;
+  P.w_gate_t = at<char>(ws, m.w_gate_t);
+  P.b_gate = at<float>(ws, m.b_gate);
+  P.s_star = at<float>(ws, m.s_star);
+  P.gamma = at<float>(ws, m.gamma);
+  P.wqkv_t = at<char>(ws, m.wqkv_t);
+  P.wo_t = at<char>(ws, m.wo_t);
+  P.wcq_t = at<char>(ws, m.wcq_t);
+  P.wco_t = at<char>(ws, m.wco_t);
+  P.w13_t = at<char>(ws, m.w13_t);
+  P.w2_t = at<char>(ws, m.w2_t);
+  P.wm_t = at<char>(ws, m.wm_t);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = D.d, F = D.F, dt = D.dtype;
+  const size_t es = D.es;
+  hipError_t e = hipSuccess;
+  auto src = [&](const void* base, size_t elems) {
+    return static_cast<const char*>(base) + elems * es;
+  };
+  auto dst = [&](void* base, size_t elems) { return static_cast<char*>(base) + elems * es; };
+#define RLT_PACK(call)                 \
+  if (e == hipSuccess) e = (call)
+  RLT_PACK(launch_pack_transpose(dt, w->w_gate, 2 * d, d, P.w_gate_t, 0, d, d, st));
+  RLT_PACK(hipMemcpyAsync(P.b_gate, w->b_gate, d * 4, hipMemcpyDeviceToDevice, st));
+  RLT_PACK(hipMemcpyAsync(P.s_star, w->s_star, d * 4, hipMemcpyDeviceToDevice, st));
+  RLT_PACK(hipMemcpyAsync(P.gamma, w->gamma, (size_t)D.L * 3 * d * 4, hipMemcpyDeviceToDevice, st));
+  for (int l = 0; l < D.L && e == hipSuccess; ++l) {
+    const size_t dd = (size_t)l * d * d, df = (size_t)l * d * F;
+    void* qkv = dst(P.wqkv_t, (size_t)l * 3 * d * d);
+    RLT_PACK(launch_pack_transpose(dt, src(w->wq, dd), d, d, qkv, 0, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wk, dd), d, d, qkv, d, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wv, dd), d, d, qkv, 2 * d, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wo, dd), d, d, dst(P.wo_t, dd), 0, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wcq, dd), d, d, dst(P.wcq_t, dd), 0, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wco, dd), d, d, dst(P.wco_t, dd), 0, d, d, st));
+    void* w13 = dst(P.w13_t, (size_t)l * 2 * F * d);
+    RLT_PACK(launch_pack_transpose(dt, src(w->w1, df), d, F, w13, 0, 16, 32, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->w3, df), d, F, w13, 16, 16, 32, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->w2, df), F, d, dst(P.w2_t, df), 0, d, d, st));
+  }
+  for (int g = 0; g < D.G && e == hipSuccess; ++g) {
+    const size_t dd = (size_t)g * d * d;
+    void* wm = dst(P.wm_t, (size_t)g * 2 * d * d);
+    RLT_PACK(launch_pack_transpose(dt, src(w->wmk, dd), d, d, wm, 0, d, d, st));
+    RLT_PACK(launch_pack_transpose(dt, src(w->wmv, dd), d, d, wm, d, d, d, st));
+  }
+#undef RLT_PACK
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    delete mdl;
+    return hip_fail(e, "packing weights");
+  }
+  *out = mdl;
+  return ok();
+}
+
+void rlt_model_destroy(rlt_model* model) { delete model; }
+
+size_t rlt_state_bytes(const rlt_config* cfg, int32_t batch) {
+  if (check_config(cfg) != RLT_OK || !valid_batch(batch)) return 0;
+  return state_layout(dims_of(*cfg), batch).total;
+}
+
+rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, size_t bytes,
+                            void* stream, rlt_state** out) {
+  if (!model || !buf || !out) return fail(RLT_ERR_ARG, "model, buffer and out must be non-NULL");
+  if (!valid_batch(batch)) return fail(RLT_ERR_SHAPE, "batch %d out of range", batch);
+  if (!aligned(buf)) return fail(RLT_ERR_ARG, "state buffer must be 256-byte aligned");
+  const StateLayout L = state_layout(model->D, batch);
+  if (bytes < L.total)
+    return fail(RLT_ERR_CAPACITY, "state buffer has %zu bytes, needs %zu", bytes, L.total);
+  rlt_state* s = new (std::nothrow) rlt_state;
+  if (!s) return fail(RLT_ERR_ARG, "out of host memory");
+  s->model = model;
+  s->B = batch;
+  s->t = 0;
+  s->S.s = at<float>(buf, L.s);
+  s->S.ring_k = at<char>(buf, L.ring_k);
+  s->S.ring_v = at<char>(buf, L.ring_v);
+  s->S.h = at<float>(buf, L.h);
+  s->S.q = at<float>(buf, L.q);
+  s->S.qc = at<float>(buf, L.qc);
+  s->S.o = at<char>(buf, L.o);
+  s->S.act = at<char>(buf, L.act);
+  s->S.part = at<float>(buf, L.part);
+  s->S.cnt = at<int>(buf, L.cnt);
+  hipError_t e = launch_reset(model->D, batch, model->P, s->S, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete s;
+    return hip_fail(e, "state reset");
+  }
+  *out = s;
+  return ok();
+}
+
+rlt_status rlt_state_reset(rlt_state* state, void* stream) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  hipError_t e = launch_reset(state->model->D, state->B, state->model->P, state->S,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "state reset");
+  state->t = 0;
+  return ok();
+}
+
+int64_t rlt_state_position(const rlt_state* state) { return state ? state->t : -1; }
+void rlt_state_destroy(rlt_state* state) {
+  if (!state) return;
+  state->prof.destroy();
+  delete state;
+}
+
+size_t rlt_memory_bytes(const rlt_config* cfg, int32_t batch, int64_t capacity) {
+  if (check_config(cfg) != RLT_OK || !valid_batch(batch) || capacity < 1 ||
+      capacity > kMaxCapacity)
+    return 0;
+  const Dims D = dims_of(*cfg);
+  return 2 * align_up((size_t)D.G * batch * D.H * capacity * D.hd * D.es);
+}
+
+rlt_status rlt_memory_create(const rlt_model* model, int32_t batch, int64_t capacity, void* buf,
+                             size_t bytes, rlt_memory** out) {
+  if (!model || !buf || !out) return fail(RLT_ERR_ARG, "model, buffer and out must be non-NULL");
+  if (!valid_batch(batch)) return fail(RLT_ERR_SHAPE, "batch %d out of range", batch);
+  if (capacity < 1 || capacity > kMaxCapacity)
+    return fail(RLT_ERR_CAPACITY, "capacity %lld outside [1, %lld]", (long long)capacity,
+                (long long)kMaxCapacity);
+  if (!aligned(buf)) return fail(RLT_ERR_ARG, "memory buffer must be 256-byte aligned");
+  const Dims& D = model->D;
+  const size_t half = align_up((size_t)D.G * batch * D.H * capacity * D.hd * D.es);
+  if (bytes < 2 * half)
+    return fail(RLT_ERR_CAPACITY, "memory buffer has %zu bytes, needs %zu", bytes, 2 * half);
+  rlt_memory* m = new (std::nothrow) rlt_memory;
+  if (!m) return fail(RLT_ERR_ARG, "out of host memory");
+  m->model = model;
+  m->B = batch;
+  m->len = 0;
+  m->M.k = buf;
+  m->M.v = at<char>(buf, half);
+  m->M.capacity = capacity;
+  *out = m;
+  return ok();
+}
+
+int64_t rlt_memory_length(const rlt_memory* mem) { return mem ? mem->len : -1; }
+
+rlt_status rlt_memory_reset(rlt_memory* mem) {
+  if (!mem) return fail(RLT_ERR_ARG, "memory is NULL");
+  mem->len = 0;
+  return ok();
+}
+void rlt_memory_destroy(rlt_memory* mem) { delete mem; }
+
+rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, int64_t t0,
+                       int64_t n, void* stream) {
+  if (!model || !mem || !e) return fail(RLT_ERR_ARG, "model, memory and e must be non-NULL");
+  if (mem->model != model) return fail(RLT_ERR_ARG, "memory belongs to another model");
+  if (!aligned16(e)) return fail(RLT_ERR_ARG, "e must be 16-byte aligned");
+  if (n < 1) return fail(RLT_ERR_ARG, "n must be >= 1");
+  if (t0 < 0 || t0 > mem->len)
+    return fail(RLT_ERR_NOT_PROJECTED, "t0 %lld leaves a hole (memory length %lld)",
+                (long long)t0, (long long)mem->len);
+  if (t0 + n > mem->M.capacity)
+    return fail(RLT_ERR_CAPACITY, "tokens up to %lld exceed capacity %lld", (long long)(t0 + n),
+                (long long)mem->M.capacity);
+  hipError_t err = launch_memproj(model->D, mem->B, model->P, mem->M, e, n, t0, n,
+                                  static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "memory projection");
+  if (t0 + n > mem->len) mem->len = t0 + n;
+  return ok();
+}
+
+static rlt_status check_step_args(const rlt_model* model, const rlt_state* state,
+                                  const rlt_memory* mem) {
+  if (!model || !state || !mem) return fail(RLT_ERR_ARG, "model, state and memory must be non-NULL");
+  if (state->model != model || mem->model != model)
+    return fail(RLT_ERR_ARG, "state or memory belongs to another model");
+  if (state->B != mem->B)
+    return fail(RLT_ERR_SHAPE, "state batch %d != memory batch %d", state->B, mem->B);
+  return ok();
+}
+
+rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
+                            const void* e_t, float* s_out, void* stream) {
+  if (rlt_status s = check_step_args(model, state, mem)) return s;
+  if (!e_t) return fail(RLT_ERR_ARG, "e_t is NULL");
+  if (!aligned16(e_t) || (s_out && !aligned16(s_out)))
+    return fail(RLT_ERR_ARG, "e_t and s_out must be 16-byte aligned");
+  if (mem->len < state->t + 1)
+    return fail(RLT_ERR_NOT_PROJECTED, "token %lld needs memory length %lld, have %lld",
+                (long long)(state->t + 1), (long long)(state->t + 1), (long long)mem->len);
+  const Dims& D = model->D;
+  hipError_t e = launch_step(D, state->B, model->P, state->S, mem->M, e_t, D.d, state->t, s_out,
+                             D.d, static_cast<hipStream_t>(stream), &state->prof);
+  if (e != hipSuccess) return hip_fail(e, "decoder step");
+  state->t += 1;
+  return ok();
+}
+
+rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                            const void* e, int64_t n, float* s_traj, void* stream) {
+  if (rlt_status s = check_step_args(model, state, mem)) return s;
+  if (!e) return fail(RLT_ERR_ARG, "e is NULL");
+  if (n < 1) return fail(RLT_ERR_ARG, "n must be >= 1");
+  if (!aligned16(e) || (s_traj && !aligned16(s_traj)))
+    return fail(RLT_ERR_ARG, "e and s_traj must be 16-byte aligned");
+  const int64_t t = state->t;
+  if (mem->len < t)
+    return fail(RLT_ERR_NOT_PROJECTED, "memory length %lld is behind position %lld",
+                (long long)mem->len, (long long)t);
+  if (t + n > mem->M.capacity)
+    return fail(RLT_ERR_CAPACITY, "tokens up to %lld exceed capacity %lld", (long long)(t + n),
+                (long long)mem->M.capacity);
+  const Dims& D = model->D;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int B = state->B;
+  hipError_t err = hipSuccess;
+  // project the tokens of [t, t+n) the memory does not hold yet
+  if (mem->len < t + n) {
+    const int64_t first = mem->len - t;  // index into e of the first missing token
+    const int64_t cnt = n - first;
+    const void* e_first = static_cast<const char*>(e) + (size_t)first * D.d * D.es;
+    int ev = -1;
+    const double rows = (double)B * cnt, d = D.d, es = (double)D.es;
+    err = state->prof.begin(RLT_K_MEMPROJ, st, ev);
+    if (err == hipSuccess) err = launch_memproj(D, B, model->P, mem->M, e_first, n, mem->len, cnt, st);
+    if (err == hipSuccess)
+      err = state->prof.end(RLT_K_MEMPROJ, ev,
+                            es * (rows * d + D.G * 2 * d * d + rows * D.G * 2 * d),
+                            2 * rows * d * D.G * 2 * d, st);
+    if (err != hipSuccess) return hip_fail(err, "memory projection");
+    mem->len = t + n;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const void* et = static_cast<const char*>(e) + (size_t)i * D.d * D.es;
+    float* out = s_traj ? s_traj + (size_t)i * D.d : nullptr;
+    err = launch_step(D, B, model->P, state->S, mem->M, et, n * D.d, state->t, out, n * D.d, st,
+                      &state->prof);
+    if (err != hipSuccess) return hip_fail(err, "decoder step");
+    state->t += 1;
+  }
+  return ok();
+}
+
+rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");
+  state->prof.mask = mask;
+  state->prof.recs.clear();
+  state->prof.used = 0;
+  return ok();
+}
+
+rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
+  if (!state || !out) return fail(RLT_ERR_ARG, "state and out must be non-NULL");
+  Profiler& P = state->prof;
+  for (int k = 0; k < RLT_K_COUNT; ++k) out[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
+  hipError_t e = hipSuccess;
+  if (P.used) e = hipEventSynchronize(P.events[P.used - 1]);
+  for (const Profiler::Rec& r : P.recs) {
+    if (e != hipSuccess) break;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, P.events[r.ev], P.events[r.ev + 1]);
+    rlt_kernel_stats& o = out[r.kind];
+    o.launches += 1;
+    o.total_ms += ms;
+    o.bytes += r.bytes;
+    o.flops += r.flops;
+  }
+  P.mask = 0;
+  P.recs.clear();
+  P.used = 0;
+  if (e != hipSuccess) return hip_fail(e, "reading kernel timers");
+  return ok();
+}
+
+rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v, int32_t* n_valid,
+                            int64_t* position, uint64_t* version, void* stream) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  const Dims& D = state->model->D;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_export(D, state->B, state->S, state->t, s, k, v, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "state export");
+  const int64_t keep = D.W - 1;
+  if (n_valid) *n_valid = (int32_t)(state->t < keep ? state->t : keep);
+  if (position) *position = state->t;
+  if (version) *version = state->model->cfg.version;
+  return ok();
+}
+
+rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, const void* v,
+                            int64_t position, uint64_t version, void* stream) {
+  if (!state || !s || !k || !v) return fail(RLT_ERR_ARG, "state, s, k and v must be non-NULL");
+  if (position < 0) return fail(RLT_ERR_ARG, "position must be >= 0");
+  if (version != state->model->cfg.version)
+    return fail(RLT_ERR_VERSION, "snapshot version %llu != model version %llu",
+                (unsigned long long)version, (unsigned long long)state->model->cfg.version);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_import(state->model->D, state->B, state->S, position, s, k, v, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "state import");
+  state->t = position;
+  return ok();
+}
+
+}  // extern "C"

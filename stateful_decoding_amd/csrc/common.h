@@ -1,0 +1,130 @@
+// Device-side building blocks shared by the gfx950 kernels: element types, 16-byte vector
+// loads, MFMA wrappers and wave/block reductions. Wavefronts are 64 lanes; every kernel in
+// this library runs 256-thread (4-wave) workgroups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlt {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+
+// Elements of T in one 16-byte vector.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> { static constexpr int N = 4; };
+template <> struct Vec16<bf16> { static constexpr int N = 8; };
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Widen one 16-byte vector of T to float.
+__device__ __forceinline__ void unpack(u32x4 raw, float (&out)[8]) {  // bf16 -> float
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(raw[i] << 16);
+    out[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack(u32x4 raw, float (&out)[4]) {  // float -> float
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(raw[i]);
+}
+
+template <typename T> __device__ __forceinline__ T to_elem(float x);
+template <> __device__ __forceinline__ float to_elem<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to_elem<bf16>(float x) { return (bf16)x; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+// ---- MFMA operand fragments -------------------------------------------------------------
+// One lane's share of a 16x32 (rows x k) operand tile: 8 consecutive k values of one row.
+// Lane l holds row (l % 16), k = 8 * (l / 16) + [0, 8). The A and B operands use the same
+// lane -> k assignment, so every product pairs matching k.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = __builtin_bit_cast(bf16x8, ld16(p)); }
+  __device__ __forceinline__ void zero() { v = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
+  __device__ __forceinline__ void from_f32(const float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+  }
+};
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p) {
+    u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  __device__ __forceinline__ void from_f32(const float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = x[i];
+  }
+};
+
+// acc(16x16, fp32) += A(16x32) * B(32x16). Output layout: lane l holds rows 4*(l/16)+i,
+// i = 0..3, of column l % 16.
+__device__ __forceinline__ void mfma_16x16x32(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+// fp32 operands: eight 16x16x4 steps; step i multiplies element i of every lane, i.e.
+// k = 8*(l/16) + i across the four lane groups, so the eight steps cover all 32 k.
+__device__ __forceinline__ void mfma_16x16x32(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// ---- reductions ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// Block-wide reductions over 256 threads; `red` is 4 floats of LDS. Every thread gets the
+// result. Contains two barriers.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+
+}  // namespace rlt

@@ -1,0 +1,143 @@
+// Internal interface between the C-ABI host code (api.cpp) and the HIP kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "rlt.h"
+
+namespace rlt {
+
+constexpr int kMaxSplit = 64;    // cross-attention partitions of the memory per (seq, head)
+constexpr int kMaxChunk = 1024;  // memory entries one workgroup attends over
+constexpr int kMaxWindow = 1024;
+constexpr int64_t kMaxCapacity = (int64_t)kMaxSplit * kMaxChunk;
+
+// Sizes derived from a validated rlt_config.
+struct Dims {
+  int d, H, hd, L, F, W, G, dtype;
+  float alpha, eps;
+  size_t es;  // element size of dtype
+};
+
+// Device pointers of the packed weights (all inside the model workspace).
+//   w_gate_t [d][2d]   gate weights, output-major (k contiguous)
+//   wqkv_t   [L][3d][d]
+//   wo_t, wcq_t, wco_t [L][d][d]
+//   w13_t    [L][2F][d]  rows in blocks of 32: 16 rows of W1^T then the same 16 of W3^T
+//   w2_t     [L][d][F]
+//   wm_t     [G][2d][d]  W_mK^T rows then W_mV^T rows
+struct Packed {
+  void* w_gate_t;
+  float* b_gate;
+  float* s_star;
+  float* gamma;
+  void* wqkv_t;
+  void* wo_t;
+  void* wcq_t;
+  void* wco_t;
+  void* w13_t;
+  void* w2_t;
+  void* wm_t;
+};
+
+// Device buffers of one decoder state (all inside the state buffer).
+//   s     [B][d] f32           decoder output s_t
+//   ring  [L][B][H][W][hd]     self-attention keys/values; token tau lives in slot tau % W.
+//                              W slots hold the W-1 retained entries plus the current one.
+//   h, q, qc [B][d] f32        residual stream, self-attention query, cross-attention query
+//   o     [B][d] dtype         attention output (operand of the output projections)
+//   act   [B][F] dtype         SiLU(f W1) * (f W3)
+//   part  [B][H][kMaxSplit][hd+2] f32  cross-attention partials (max, sum, hd outputs)
+//   cnt   [B][H] i32           arrival counters of the partial merge (kept at zero)
+struct StateBufs {
+  float* s;
+  void* ring_k;
+  void* ring_v;
+  float* h;
+  float* q;
+  float* qc;
+  void* o;
+  void* act;
+  float* part;
+  int* cnt;
+};
+
+struct MemBufs {
+  void* k;  // [G][B][H][capacity][hd]
+  void* v;
+  int64_t capacity;
+};
+
+// Byte layout of the state buffer; offsets are 256-byte aligned.
+struct StateLayout {
+  size_t s, ring_k, ring_v, h, q, qc, o, act, part, cnt, total;
+};
+StateLayout state_layout(const Dims& D, int B);
+
+// ---- launchers (return the first HIP error) -------------------------------------------
+
+// dst rows [row_base + (n / grp) * grp_stride + n % grp] of a [*][K] matrix receive column n
+// of src [K][N]; all in dtype.
+hipError_t launch_pack_transpose(int dtype, const void* src, int K, int N, void* dst,
+                                 int64_t row_base, int grp, int grp_stride, hipStream_t st);
+
+hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& S,
+                        hipStream_t st);
+
+// Projects n tokens per sequence into memory entries t0 .. t0+n-1; the encoder outputs of
+// sequence b, token i are at e + (b * e_seq + i) * d (elements).
+hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
+                          const void* e, int64_t e_seq, int64_t t0, int64_t n, hipStream_t st);
+
+// Event timing of selected kernels (owned by a state; see rlt_profile_begin).
+struct Profiler {
+  struct Rec {
+    int kind;
+    int ev;  // index of the start event in `events`; the end event follows it
+    double bytes, flops;
+  };
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> events;  // pool, reused across sessions
+  std::vector<Rec> recs;
+  size_t used = 0;
+  bool on(int kind) const { return (mask >> kind) & 1u; }
+  hipError_t begin(int kind, hipStream_t st, int& ev);
+  hipError_t end(int kind, int ev, double bytes, double flops, hipStream_t st);
+  void destroy();
+};
+
+// One decoder step at 0-based token index t0 (memory must hold entries 0..t0). e_t rows are
+// e_t + b * e_ld (elements). When out != NULL, s_t row b is also written to out + b * out_ld.
+hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S,
+                       const MemBufs& M, const void* e_t, int64_t e_ld, int64_t t0,
+                       float* out, int64_t out_ld, hipStream_t st, Profiler* prof);
+
+hipError_t launch_export(const Dims& D, int B, const StateBufs& S, int64_t t, float* s,
+                         void* k, void* v, hipStream_t st);
+hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
+                         const void* k, const void* v, hipStream_t st);
+
+// ---- kernel-level entry points used by launch_step -----------------------------------------
+hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, const void* e_t,
+                     int64_t e_ld, hipStream_t st);
+hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S, int slot,
+                    hipStream_t st);
+hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                   hipStream_t st);
+hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                    hipStream_t st);
+// h (+)= A W for the output projections: which = 0 (self-attn O), 1 (cross O), 2 (FFN down).
+// When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h.
+hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P,
+                         const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
+                         hipStream_t st);
+hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
+                     hipStream_t st);
+hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
+                      int64_t t, hipStream_t st);
+
+}  // namespace rlt

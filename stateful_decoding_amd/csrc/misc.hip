@@ -1,0 +1,211 @@
+// Support kernels: weight packing, state reset, snapshot export/import, and the decoder-step
+// sequencing (one launch per phase, all on the caller's stream).
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace rlt {
+
+// ---- weight packing: dst[row(n)][k] = src[k][n], 32x32 tiles through LDS -----------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_pack_transpose(const T* __restrict__ src, int K,
+                                                             int N, T* __restrict__ dst,
+                                                             int64_t row_base, int grp,
+                                                             int grp_stride) {
+  __shared__ T tile[32][33];
+  const int k0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int k = k0 + r, n = n0 + tx;
+    if (k < K && n < N) tile[r][tx] = src[(int64_t)k * N + n];
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int n = n0 + r, k = k0 + tx;
+    if (k < K && n < N) {
+      const int64_t row = row_base + (int64_t)(n / grp) * grp_stride + n % grp;
+      dst[row * K + k] = tile[tx][r];
+    }
+  }
+}
+
+hipError_t launch_pack_transpose(int dtype, const void* src, int K, int N, void* dst,
+                                 int64_t row_base, int grp, int grp_stride, hipStream_t st) {
+  const dim3 grid((N + 31) / 32, (K + 31) / 32);
+  if (dtype == RLT_BF16)
+    hipLaunchKernelGGL(k_pack_transpose<bf16>, grid, dim3(kThreads), 0, st,
+                       static_cast<const bf16*>(src), K, N, static_cast<bf16*>(dst), row_base,
+                       grp, grp_stride);
+  else
+    hipLaunchKernelGGL(k_pack_transpose<float>, grid, dim3(kThreads), 0, st,
+                       static_cast<const float*>(src), K, N, static_cast<float*>(dst), row_base,
+                       grp, grp_stride);
+  return hipGetLastError();
+}
+
+// ---- reset: s = s*, merge counters zero ---------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_reset(float* __restrict__ s,
+                                                    const float* __restrict__ s_star, int d,
+                                                    int64_t n_s, int* __restrict__ cnt,
+                                                    int64_t n_cnt) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n_s) s[i] = s_star[i % d];
+  if (i < n_cnt) cnt[i] = 0;
+}
+
+hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& S,
+                        hipStream_t st) {
+  const int64_t n_s = (int64_t)B * D.d, n_cnt = (int64_t)B * D.H;
+  const int64_t n = n_s > n_cnt ? n_s : n_cnt;
+  hipLaunchKernelGGL(k_reset, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, S.s, P.s_star, D.d, n_s, S.cnt, n_cnt);
+  return hipGetLastError();
+}
+
+// ---- snapshots: ring [L][B][H][W][hd] <-> canonical [L][B][W-1][d], oldest first ----------
+// Retained entries are the tokens t-n_valid .. t-1 (0-based), token tau in slot tau % W.
+template <typename T, bool EXPORT>
+__global__ __launch_bounds__(kThreads) void k_snapshot(T* __restrict__ ring_k,
+                                                       T* __restrict__ ring_v,
+                                                       T* __restrict__ can_k,
+                                                       T* __restrict__ can_v, int B, int H,
+                                                       int hd, int W, int64_t t, int n_valid,
+                                                       int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int d = H * hd, keep = W - 1;
+  const int c = (int)(i % d);
+  int64_t rest = i / d;
+  const int e = (int)(rest % keep);
+  rest /= keep;
+  const int b = (int)(rest % B);
+  const int l = (int)(rest / B);
+  const int hh = c / hd, dd = c % hd;
+  if (e >= n_valid) {
+    if (EXPORT) {
+      if (can_k) can_k[i] = to_elem<T>(0.f);
+      if (can_v) can_v[i] = to_elem<T>(0.f);
+    }
+    return;
+  }
+  const int64_t tau = t - n_valid + e;
+  const int64_t r = ((((int64_t)l * B + b) * H + hh) * W + (int)(tau % W)) * hd + dd;
+  if (EXPORT) {
+    if (can_k) can_k[i] = ring_k[r];
+    if (can_v) can_v[i] = ring_v[r];
+  } else {
+    ring_k[r] = can_k[i];
+    ring_v[r] = can_v[i];
+  }
+}
+
+template <typename T, bool EXPORT>
+static hipError_t snapshot_t(const Dims& D, int B, const StateBufs& S, int64_t t, void* k,
+                             void* v, hipStream_t st) {
+  const int keep = D.W - 1;
+  const int n_valid = (int)(t < keep ? t : keep);
+  const int64_t total = (int64_t)D.L * B * keep * D.d;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_snapshot<T, EXPORT>), dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, static_cast<T*>(S.ring_k), static_cast<T*>(S.ring_v),
+                     static_cast<T*>(k), static_cast<T*>(v), B, D.H, D.hd, D.W, t, n_valid, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const Dims& D, int B, const StateBufs& S, int64_t t, float* s, void* k,
+                         void* v, hipStream_t st) {
+  if (s) {
+    hipError_t e = hipMemcpyAsync(s, S.s, sizeof(float) * (size_t)B * D.d,
+                                  hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!k && !v) return hipSuccess;
+  return D.dtype == RLT_BF16 ? snapshot_t<bf16, true>(D, B, S, t, k, v, st)
+                             : snapshot_t<float, true>(D, B, S, t, k, v, st);
+}
+
+hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
+                         const void* k, const void* v, hipStream_t st) {
+  hipError_t e = hipMemcpyAsync(S.s, s, sizeof(float) * (size_t)B * D.d, hipMemcpyDeviceToDevice,
+                                st);
+  if (e != hipSuccess) return e;
+  return D.dtype == RLT_BF16
+             ? snapshot_t<bf16, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st)
+             : snapshot_t<float, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st);
+}
+
+// ---- kernel timing ---------------------------------------------------------------------------
+hipError_t Profiler::begin(int kind, hipStream_t st, int& ev) {
+  ev = -1;
+  if (!on(kind)) return hipSuccess;
+  while (events.size() < used + 2) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return err;
+    events.push_back(e);
+  }
+  ev = (int)used;
+  used += 2;
+  return hipEventRecord(events[ev], st);
+}
+
+hipError_t Profiler::end(int kind, int ev, double bytes, double flops, hipStream_t st) {
+  if (ev < 0) return hipSuccess;
+  recs.push_back(Rec{kind, ev, bytes, flops});
+  return hipEventRecord(events[ev + 1], st);
+}
+
+void Profiler::destroy() {
+  for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  events.clear();
+  recs.clear();
+  used = 0;
+  mask = 0;
+}
+
+// ---- one decoder step ------------------------------------------------------------------------
+// Algorithmic bytes and flops of each kernel: every operand read once, every result written
+// once (weights es bytes per element, fp32 activations 4, dtype activations es).
+hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S,
+                       const MemBufs& M, const void* e_t, int64_t e_ld, int64_t t0, float* out,
+                       int64_t out_ld, hipStream_t st, Profiler* prof) {
+  hipError_t e;
+  int ev = -1;
+  const double b = B, d = D.d, F = D.F, es = (double)D.es;
+  const double act32 = b * d * 4, actd = b * d * es;
+#define RLT_TIMED(kind, bytes, flops, call)                                   \
+  do {                                                                        \
+    if (prof && (e = prof->begin(kind, st, ev)) != hipSuccess) return e;      \
+    if ((e = (call)) != hipSuccess) return e;                                 \
+    if (prof && (e = prof->end(kind, ev, bytes, flops, st)) != hipSuccess) return e; \
+  } while (0)
+  RLT_TIMED(RLT_K_GATE, 2 * d * d * es + actd + 2 * act32, 4 * b * d * d,
+            gemm_gate(D, B, P, S, e_t, e_ld, st));
+  const int slot = (int)(t0 % D.W);
+  const int n_valid = (int)(t0 + 1 < D.W ? t0 + 1 : D.W);
+  const double t = (double)(t0 + 1);
+  for (int l = 0; l < D.L; ++l) {
+    const bool last = l == D.L - 1;
+    RLT_TIMED(RLT_K_QKV, 3 * d * d * es + 2 * act32 + 2 * actd, 6 * b * d * d,
+              gemm_qkv(D, B, l, P, S, slot, st));
+    RLT_TIMED(RLT_K_SELF_ATTN, n_valid * b * 2 * d * es + act32 + actd, 4 * b * d * n_valid,
+              attn_self(D, B, l, S, n_valid, st));
+    RLT_TIMED(RLT_K_SELF_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
+              gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, st));
+    RLT_TIMED(RLT_K_CROSS_Q, d * d * es + 2 * act32, 2 * b * d * d, gemm_cq(D, B, l, P, S, st));
+    RLT_TIMED(RLT_K_CROSS_ATTN, t * b * 2 * d * es + act32 + actd, 4 * b * d * t,
+              attn_cross(D, B, l, S, M, t0 + 1, st));
+    RLT_TIMED(RLT_K_CROSS_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
+              gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, st));
+    RLT_TIMED(RLT_K_FFN_UP, 2 * F * d * es + act32 + b * F * es, 4 * b * d * F,
+              gemm_w13(D, B, l, P, S, st));
+    RLT_TIMED(RLT_K_FFN_DOWN, F * d * es + b * F * es + 2 * act32 + (last && out ? act32 : 0),
+              2 * b * d * F,
+              gemm_residual(D, B, l, 2, P, S, last, last ? out : nullptr, out_ld, st));
+  }
+#undef RLT_TIMED
+  return hipSuccess;
+}
+
+}  // namespace rlt
