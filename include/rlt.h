@@ -139,7 +139,7 @@ void rlt_state_destroy(rlt_state* state);
 /* --- encoder memory M ----------------------------------------------------------------- */
 
 /* Bytes for the key and value memory of B sequences up to `capacity` tokens:
- * K and V, each [G][B][H][capacity][hd] dtype. 1 <= capacity <= 65536. */
+ * K and V, each [G][B][H][capacity][hd] dtype. 1 <= capacity <= 2^20. */
 size_t rlt_memory_bytes(const rlt_config* cfg, int32_t batch, int64_t capacity);
 
 /* Binds `buf` (device, >= rlt_memory_bytes, 256-byte aligned) as empty memory (length 0). */

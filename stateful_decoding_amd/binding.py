@@ -56,9 +56,11 @@ class RLTError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load librlt.so and declare its signatures. Raises if it has not been built."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load librlt.so (``LIB_PATH`` unless `path` is given) and declare its signatures.
+    Raises if it has not been built."""
     global _lib
+    path = LIB_PATH if path is None else path
     if _lib is not None and path == LIB_PATH:
         return _lib
     if not os.path.exists(path):

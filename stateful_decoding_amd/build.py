@@ -33,10 +33,15 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object, then link ``librlt.so``. Returns the library path."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, jobs: int = 4, out_dir: str | None = None,
+          defines: tuple = ()) -> str:
+    """Compile every source to an object, then link ``librlt.so`` (in the package, or in
+    ``out_dir``; ``defines`` are extra ``NAME=VALUE`` preprocessor definitions). Returns the
+    library path."""
+    objdir = os.path.join(out_dir or PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
+    lib = os.path.join(out_dir, "librlt.so") if out_dir else LIB
+    dflags = [f"-D{x}" for x in defines]
     cc = hipcc()
     procs = []
     objs = []
@@ -44,7 +49,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+        cmd = [cc, *HIPCC_FLAGS, *dflags, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -54,15 +59,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0), verbose)
     for p in procs:
         _wait(p, verbose)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _wait(item, verbose):

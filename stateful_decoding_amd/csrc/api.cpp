@@ -26,6 +26,12 @@ struct rlt_state {
   int64_t t;
   StateBufs S;
   Profiler prof;
+  // row groups: group g is rows [row0[g], row0[g + 1]); group 0 runs on the caller's stream,
+  // group g > 0 on aux[g], forked from and joined back to it with events
+  int ngroups;
+  int row0[kMaxGroups + 1];
+  hipStream_t aux[kMaxGroups];
+  hipEvent_t fork, join[kMaxGroups];
 };
 
 struct rlt_memory {
@@ -138,7 +144,7 @@ namespace rlt {
 StateLayout state_layout(const Dims& D, int B) {
   StateLayout s;
   size_t o = 0;
-  const size_t b = B, d = D.d, es = D.es;
+  const size_t b = B, d = D.d, es = D.es, b16 = (b + 15) / 16 * 16;
   auto take = [&](size_t bytes) {
     size_t a = o;
     o = align_up(o + bytes);
@@ -151,10 +157,10 @@ StateLayout state_layout(const Dims& D, int B) {
   s.h = take(b * d * 4);
   s.q = take(b * d * 4);
   s.qc = take(b * d * 4);
-  s.o = take(b * d * es);
-  s.act = take(b * D.F * es);
-  s.part = take(b * D.H * kMaxSplit * (D.hd + 2) * 4);
-  s.cnt = take(b * D.H * 4);
+  s.hg = take(b16 * d * es);
+  s.ssq = take(b * (d / 32) * 4);
+  s.o = take(b16 * d * es);
+  s.act = take(b16 * D.F * es);
   s.total = o;
   return s;
 }
@@ -272,11 +278,36 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
   s->S.h = at<float>(buf, L.h);
   s->S.q = at<float>(buf, L.q);
   s->S.qc = at<float>(buf, L.qc);
+  s->S.hg = at<char>(buf, L.hg);
+  s->S.ssq = at<float>(buf, L.ssq);
   s->S.o = at<char>(buf, L.o);
   s->S.act = at<char>(buf, L.act);
-  s->S.part = at<float>(buf, L.part);
-  s->S.cnt = at<int>(buf, L.cnt);
-  hipError_t e = launch_reset(model->D, batch, model->P, s->S, static_cast<hipStream_t>(stream));
+  s->S.Bt = batch;
+  s->fork = nullptr;
+  for (int g = 0; g < kMaxGroups; ++g) {
+    s->aux[g] = nullptr;
+    s->join[g] = nullptr;
+  }
+  int ng = batch / kGroupRows;
+  ng = ng < 1 ? 1 : ng > kMaxGroups ? kMaxGroups : ng;
+  const int per = ((batch + ng - 1) / ng + 15) / 16 * 16;
+  s->ngroups = 0;
+  for (int g = 0; g < ng && g * per < batch; ++g) {
+    s->row0[g] = g * per;
+    s->ngroups = g + 1;
+  }
+  s->row0[s->ngroups] = batch;
+  hipError_t e = hipSuccess;
+  if (s->ngroups > 1) e = hipEventCreateWithFlags(&s->fork, hipEventDisableTiming);
+  for (int g = 1; g < s->ngroups && e == hipSuccess; ++g) {
+    e = hipStreamCreateWithFlags(&s->aux[g], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s->join[g], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    rlt_state_destroy(s);
+    return hip_fail(e, "creating the row-group streams");
+  }
+  e = launch_reset(model->D, batch, model->P, s->S, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     delete s;
     return hip_fail(e, "state reset");
@@ -298,6 +329,11 @@ int64_t rlt_state_position(const rlt_state* state) { return state ? state->t : -
 void rlt_state_destroy(rlt_state* state) {
   if (!state) return;
   state->prof.destroy();
+  if (state->fork) (void)hipEventDestroy(state->fork);
+  for (int g = 0; g < kMaxGroups; ++g) {
+    if (state->join[g]) (void)hipEventDestroy(state->join[g]);
+    if (state->aux[g]) (void)hipStreamDestroy(state->aux[g]);
+  }
   delete state;
 }
 
@@ -329,6 +365,7 @@ rlt_status rlt_memory_create(const rlt_model* model, int32_t batch, int64_t capa
   m->M.k = buf;
   m->M.v = at<char>(buf, half);
   m->M.capacity = capacity;
+  m->M.Bt = batch;
   *out = m;
   return ok();
 }
@@ -361,6 +398,45 @@ rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, i
   return ok();
 }
 
+// n decoder steps over e rows (b, i) at e + (b * e_ld + i * d), s rows to out (+ b * out_ld
+// + i * d) when out != NULL; every row group on its own stream, all forked from and joined
+// back to `st`. Launches are issued step by step, alternating between the groups.
+static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
+                            const void* e, int64_t e_ld, int64_t n, float* out, int64_t out_ld,
+                            hipStream_t st) {
+  const Dims& D = model->D;
+  const int ng = state->ngroups;
+  hipError_t err = hipSuccess;
+  if (ng > 1) {
+    err = hipEventRecord(state->fork, st);
+    for (int g = 1; g < ng && err == hipSuccess; ++g)
+      err = hipStreamWaitEvent(state->aux[g], state->fork, 0);
+    if (err != hipSuccess) return err;
+  }
+  StateBufs Sg[kMaxGroups];
+  MemBufs Mg[kMaxGroups];
+  for (int g = 0; g < ng; ++g) {
+    Sg[g] = state_rows(D, state->S, state->row0[g]);
+    Mg[g] = memory_rows(D, mem->M, state->row0[g]);
+  }
+  const char* eb = static_cast<const char*>(e);
+  for (int64_t i = 0; i < n && err == hipSuccess; ++i) {
+    const int64_t t0 = state->t + i;
+    for (int g = 0; g < ng && err == hipSuccess; ++g) {
+      const int b0 = state->row0[g], rows = state->row0[g + 1] - b0;
+      const char* et = eb + ((size_t)b0 * e_ld + (size_t)i * D.d) * D.es;
+      float* o = out ? out + (size_t)b0 * out_ld + (size_t)i * D.d : nullptr;
+      err = launch_step(D, rows, model->P, Sg[g], Mg[g], et, e_ld, t0, o, out_ld,
+                        g == 0 ? st : state->aux[g], &state->prof);
+    }
+  }
+  for (int g = 1; g < ng && err == hipSuccess; ++g) {
+    err = hipEventRecord(state->join[g], state->aux[g]);
+    if (err == hipSuccess) err = hipStreamWaitEvent(st, state->join[g], 0);
+  }
+  return err;
+}
+
 static rlt_status check_step_args(const rlt_model* model, const rlt_state* state,
                                   const rlt_memory* mem) {
   if (!model || !state || !mem) return fail(RLT_ERR_ARG, "model, state and memory must be non-NULL");
@@ -381,8 +457,8 @@ rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_
     return fail(RLT_ERR_NOT_PROJECTED, "token %lld needs memory length %lld, have %lld",
                 (long long)(state->t + 1), (long long)(state->t + 1), (long long)mem->len);
   const Dims& D = model->D;
-  hipError_t e = launch_step(D, state->B, model->P, state->S, mem->M, e_t, D.d, state->t, s_out,
-                             D.d, static_cast<hipStream_t>(stream), &state->prof);
+  hipError_t e = run_steps(model, state, mem, e_t, D.d, 1, s_out, D.d,
+                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decoder step");
   state->t += 1;
   return ok();
@@ -422,14 +498,9 @@ rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory
     if (err != hipSuccess) return hip_fail(err, "memory projection");
     mem->len = t + n;
   }
-  for (int64_t i = 0; i < n; ++i) {
-    const void* et = static_cast<const char*>(e) + (size_t)i * D.d * D.es;
-    float* out = s_traj ? s_traj + (size_t)i * D.d : nullptr;
-    err = launch_step(D, B, model->P, state->S, mem->M, et, n * D.d, state->t, out, n * D.d, st,
-                      &state->prof);
-    if (err != hipSuccess) return hip_fail(err, "decoder step");
-    state->t += 1;
-  }
+  err = run_steps(model, state, mem, e, n * D.d, n, s_traj, n * D.d, st);
+  if (err != hipSuccess) return hip_fail(err, "decoder step");
+  state->t += n;
   return ok();
 }
 

@@ -2,15 +2,16 @@
 //
 // Both attentions of a decoder block are bandwidth work: one query per (sequence, head)
 // against n key/value rows that are read exactly once. One workgroup takes one (sequence,
-// head[, memory partition]) and streams its rows with 16-byte loads: hd/8 (bf16) or hd/4
-// (fp32) lanes share one row, so every wave load covers whole, contiguous rows. Scores go to
-// LDS, the softmax is max-subtracted, and values are accumulated in fp32.
+// head) and streams its key and value rows together with 16-byte loads: hd/8 (bf16) or
+// hd/4 (fp32) lanes share one row, so every wave load covers whole, contiguous rows. The
+// softmax is computed online in fp32 (running max, sum and output per row slot), so there is
+// no score buffer and no limit on n; partial states meet in registers and LDS, never in
+// global memory, so workgroups never wait on each other.
 //
 // Self-attention reads the per-layer ring cache (window = current token + W-1 past entries,
 // "RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", architecture section).
 // Cross-attention reads memory entries 1..t of the layer's group (prefix restriction, same
-// section); long prefixes are split over several workgroups whose partial (max, sum, output)
-// triples are merged by the last one to finish, so one launch does the whole attention.
+// section).
 #include <math.h>
 
 #include "common.h"
@@ -22,166 +23,115 @@ template <typename T, int HD>
 struct Geo {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte load
   static constexpr int LPR = HD / VEC;              // lanes per row
-  static constexpr int RPW = kWave / LPR;           // rows per wave load
-  static constexpr int RPB = RPW * (kThreads / kWave);
+  static constexpr int RPW = kWave / LPR;           // row slots per wave
   static_assert(LPR >= 1 && LPR <= kWave && HD % VEC == 0, "unsupported head size");
 };
 
-// Attention of one query over rows [0, n) of K/V (row stride HD). Leaves the unnormalised
-// output sum_j p_j v_j in o_lds[4*HD + i], and returns the running max and sum of p in
-// m_out / l_out (p_j = exp(s_j - max)). s_lds holds >= n floats. Every thread participates.
-template <typename T, int HD, int U>
-__device__ void attend_rows(const float* __restrict__ q, const T* __restrict__ K,
-                            const T* __restrict__ V, int n, float scale, float* s_lds,
-                            float* red, float* o_lds, float& m_out, float& l_out) {
-  using G = Geo<T, HD>;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int sub = lane % G::LPR, r = lane / G::LPR;
-  float qv[G::VEC];
-#pragma unroll
-  for (int i = 0; i < G::VEC; ++i) qv[i] = q[sub * G::VEC + i] * scale;
+// Running softmax state of one row slot: max m, sum l of exp(s - m), acc = sum exp(s - m) v.
+// Merging two states rescales both to the larger max; an empty state has m = -inf, l = 0.
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float mo, float lo,
+                                            const float* acco, int n) {
+  const float mn = fmaxf(m, mo);
+  const float a = m == -INFINITY ? 0.f : __expf(m - mn);
+  const float b = mo == -INFINITY ? 0.f : __expf(mo - mn);
+  l = l * a + lo * b;
+  for (int i = 0; i < n; ++i) acc[i] = acc[i] * a + acco[i] * b;
+  m = mn;
+}
 
-  float mloc = -INFINITY;
-  for (int base = 0; base < n; base += G::RPB * U) {
-    u32x4 raw[U];
+// One workgroup of NW waves per (sequence, head): softmax attention of one query over the
+// rows [0, n) of a contiguous [rows][HD] key block and value block, in a single pass. Each row
+// slot (LPR lanes) walks its rows with a running softmax state, U rows at a time with one
+// rescale per batch; slots merge through lane shuffles, waves through LDS. The query is q[b]
+// (fp32, head hh), K/V blocks start at K + bh * bh_stride; the output row o[b] (dtype) is
+// written in MFMA fragment order, as the output projection reads it.
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_attend(const float* __restrict__ q,
+                                                       const T* __restrict__ K,
+                                                       const T* __restrict__ V,
+                                                       int64_t bh_stride, int n, int H,
+                                                       float scale, T* __restrict__ out) {
+  using G = Geo<T, HD>;
+  constexpr int RPB = G::RPW * NW;  // rows per block per batch step
+  __shared__ float lds_m[NW], lds_l[NW];
+  __shared__ float lds_acc[NW][HD];
+  const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int sub = lane % G::LPR, slot = lane / G::LPR;
+  const T* Kb = K + (int64_t)bh * bh_stride + sub * G::VEC;
+  const T* Vb = V + (int64_t)bh * bh_stride + sub * G::VEC;
+  float qv[G::VEC];
+  const float* qp = q + (int64_t)b * d + hh * HD + sub * G::VEC;
+#pragma unroll
+  for (int i = 0; i < G::VEC; ++i) qv[i] = qp[i] * scale;
+
+  float m = -INFINITY, l = 0.f, acc[G::VEC];
+#pragma unroll
+  for (int i = 0; i < G::VEC; ++i) acc[i] = 0.f;
+  const int first = wave * G::RPW + slot;
+  for (int base = 0; base < n; base += RPB * U) {
+    u32x4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = base + u * G::RPB + wave * G::RPW + r;
-      raw[u] = row < n ? ld16(K + (int64_t)row * HD + sub * G::VEC) : u32x4{0, 0, 0, 0};
+      const int row = base + u * RPB + first;
+      const bool ok = row < n;
+      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
     }
+    float sc[U];
+    float mb = m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[G::VEC];
-      unpack(raw[u], kf);
+      unpack(kr[u], kf);
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < G::VEC; ++i) dot += qv[i] * kf[i];
 #pragma unroll
       for (int o = G::LPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-      const int row = base + u * G::RPB + wave * G::RPW + r;
-      if (row < n) {
-        if (sub == 0) s_lds[row] = dot;
-        mloc = fmaxf(mloc, dot);
-      }
+      const bool ok = base + u * RPB + first < n;
+      sc[u] = ok ? dot : -INFINITY;
+      mb = fmaxf(mb, sc[u]);
     }
-  }
-  const float m = block_max(mloc, red);
-  float lsum = 0.f;
-  for (int j = tid; j < n; j += kThreads) {
-    const float p = __expf(s_lds[j] - m);
-    s_lds[j] = p;
-    lsum += p;
-  }
-  const float l = block_sum(lsum, red);
-
-  float acc[G::VEC];
+    if (mb == -INFINITY) continue;  // this slot had no rows in the batch
+    const float c = m == -INFINITY ? 0.f : __expf(m - mb);
+    l *= c;
 #pragma unroll
-  for (int i = 0; i < G::VEC; ++i) acc[i] = 0.f;
-  for (int base = 0; base < n; base += G::RPB * U) {
-    u32x4 raw[U];
+    for (int i = 0; i < G::VEC; ++i) acc[i] *= c;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = base + u * G::RPB + wave * G::RPW + r;
-      raw[u] = row < n ? ld16(V + (int64_t)row * HD + sub * G::VEC) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = base + u * G::RPB + wave * G::RPW + r;
-      const float p = row < n ? s_lds[row] : 0.f;
+      const float p = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - mb);
       float vf[G::VEC];
-      unpack(raw[u], vf);
+      unpack(vr[u], vf);
+      l += p;
 #pragma unroll
       for (int i = 0; i < G::VEC; ++i) acc[i] += p * vf[i];
     }
+    m = mb;
   }
-  // sum over the row slots of the wave (lanes sharing `sub`), then over the four waves
+  // merge the row slots of the wave (lanes sharing `sub`)
 #pragma unroll
-  for (int o = G::LPR; o < kWave; o <<= 1)
+  for (int o = G::LPR; o < kWave; o <<= 1) {
+    const float mo = __shfl_xor(m, o, kWave), lo = __shfl_xor(l, o, kWave);
+    float ao[G::VEC];
 #pragma unroll
-    for (int i = 0; i < G::VEC; ++i) acc[i] += __shfl_xor(acc[i], o, kWave);
-  if (r == 0) {
-#pragma unroll
-    for (int i = 0; i < G::VEC; ++i) o_lds[wave * HD + sub * G::VEC + i] = acc[i];
+    for (int i = 0; i < G::VEC; ++i) ao[i] = __shfl_xor(acc[i], o, kWave);
+    merge_state(m, l, acc, mo, lo, ao, G::VEC);
   }
-  __syncthreads();
-  if (tid < HD) o_lds[4 * HD + tid] = (o_lds[tid] + o_lds[HD + tid]) + (o_lds[2 * HD + tid] + o_lds[3 * HD + tid]);
-  __syncthreads();
-  m_out = m;
-  l_out = l;
-}
-
-// Self-attention: one workgroup per (sequence, head). The ring slots [0, n_valid) hold the
-// window (the current token was written by the QKV projection).
-template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void k_attn_self(const float* __restrict__ q,
-                                                        const T* __restrict__ ring_k,
-                                                        const T* __restrict__ ring_v,
-                                                        T* __restrict__ out, int H, int W,
-                                                        int n_valid, float scale) {
-  __shared__ float s_lds[kMaxWindow];
-  __shared__ float red[4];
-  __shared__ float o_lds[5 * HD];
-  const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
-  const int64_t off = (int64_t)bh * W * HD;
-  float m, l;
-  attend_rows<T, HD, 4>(q + (int64_t)b * d + hh * HD, ring_k + off, ring_v + off, n_valid, scale,
-                        s_lds, red, o_lds, m, l);
-  if (threadIdx.x < HD) out[(int64_t)b * d + hh * HD + threadIdx.x] = to_elem<T>(o_lds[4 * HD + threadIdx.x] / l);
-}
-
-// Cross-attention over memory entries [0, t): item = ((b * H + h) * nsplit + split); split
-// covers entries [split * chunk, min(t, (split + 1) * chunk)).
-template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void k_attn_cross(
-    const float* __restrict__ qc, const T* __restrict__ mk, const T* __restrict__ mv,
-    int64_t cap, T* __restrict__ out, float* __restrict__ part, int* __restrict__ cnt, int H,
-    int t, int chunk, int nsplit, float scale) {
-  __shared__ float s_lds[kMaxChunk];
-  __shared__ float red[4];
-  __shared__ float o_lds[5 * HD];
-  __shared__ int last;
-  const int item = blockIdx.x;
-  const int bh = item / nsplit, split = item - bh * nsplit;
-  const int b = bh / H, hh = bh - b * H, d = H * HD;
-  const int j0 = split * chunk;
-  const int n = min(t - j0, chunk);
-  const int64_t off = ((int64_t)bh * cap + j0) * HD;
-  float m, l;
-  attend_rows<T, HD, 4>(qc + (int64_t)b * d + hh * HD, mk + off, mv + off, n, scale, s_lds, red,
-                        o_lds, m, l);
-  T* o = out + (int64_t)b * d + hh * HD;
-  if (nsplit == 1) {
-    if (threadIdx.x < HD) o[threadIdx.x] = to_elem<T>(o_lds[4 * HD + threadIdx.x] / l);
-    return;
-  }
-  constexpr int PS = HD + 2;
-  float* pb = part + (int64_t)bh * kMaxSplit * PS;
-  if (threadIdx.x == 0) {
-    pb[split * PS] = m;
-    pb[split * PS + 1] = l;
-  }
-  if (threadIdx.x < HD) pb[split * PS + 2 + threadIdx.x] = o_lds[4 * HD + threadIdx.x];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(cnt + bh, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = prev == nsplit - 1;
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (threadIdx.x < HD) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pb[s * PS]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = __expf(pb[s * PS] - M);
-      L += w * pb[s * PS + 1];
-      acc += w * pb[s * PS + 2 + threadIdx.x];
+  if (slot == 0) {
+    if (sub == 0) {
+      lds_m[wave] = m;
+      lds_l[wave] = l;
     }
-    o[threadIdx.x] = to_elem<T>(acc / L);
+#pragma unroll
+    for (int i = 0; i < G::VEC; ++i) lds_acc[wave][sub * G::VEC + i] = acc[i];
   }
-  if (threadIdx.x == 0) cnt[bh] = 0;
+  __syncthreads();
+  if (tid < HD) {
+    float M = lds_m[0], L = lds_l[0], A = lds_acc[0][tid];
+    for (int w = 1; w < NW; ++w) merge_state(M, L, &A, lds_m[w], lds_l[w], &lds_acc[w][tid], 1);
+    out[frag_off(b, hh * HD + tid, d / 32)] = to_elem<T>(A / L);
+  }
 }
 
 template <typename T>
@@ -189,40 +139,38 @@ static inline T* elem(void* base, int64_t off) {
   return static_cast<T*>(base) + off;
 }
 
+// Waves per workgroup: enough workgroups x waves to keep the chip streaming.
 template <typename T, int HD>
-static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                         hipStream_t st) {
-  const int64_t layer = (int64_t)B * D.H * D.W * HD;
-  hipLaunchKernelGGL((k_attn_self<T, HD>), dim3(B * D.H), dim3(kThreads), 0, st, S.q,
-                     elem<T>(S.ring_k, l * layer), elem<T>(S.ring_v, l * layer),
-                     static_cast<T*>(S.o), D.H, D.W, n_valid, 1.f / sqrtf((float)HD));
+static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
+                           int n, int H, T* out, hipStream_t st) {
+  const float scale = 1.f / sqrtf((float)HD);
+  if (BH >= 1024)
+    hipLaunchKernelGGL((k_attend<T, HD, 4, 4>), dim3(BH), dim3(4 * kWave), 0, st, q, K, V, bh_stride, n,
+                       H, scale, out);
+  else if (BH >= 512)
+    hipLaunchKernelGGL((k_attend<T, HD, 8, 4>), dim3(BH), dim3(8 * kWave), 0, st, q, K, V, bh_stride, n,
+                       H, scale, out);
+  else
+    hipLaunchKernelGGL((k_attend<T, HD, 16, 4>), dim3(BH), dim3(16 * kWave), 0, st, q, K, V, bh_stride,
+                       n, H, scale, out);
   return hipGetLastError();
 }
 
-// Partition of t memory entries: enough workgroups to fill the chip (about 2048), at least
-// 64 entries each, at most kMaxSplit partitions of at most kMaxChunk entries.
-static void cross_split(int64_t t, int bh, int& chunk, int& nsplit) {
-  const int want = (int)std::max<int64_t>(1, (2048 + bh - 1) / bh);
-  int64_t c = (t + want - 1) / want;
-  c = std::max<int64_t>(c, 64);
-  c = std::max<int64_t>(c, (t + kMaxSplit - 1) / kMaxSplit);
-  c = std::min<int64_t>(c, std::max<int64_t>(t, 1));
-  chunk = (int)c;
-  nsplit = (int)((t + c - 1) / c);
+template <typename T, int HD>
+static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
+                         hipStream_t st) {
+  const int64_t layer = (int64_t)S.Bt * D.H * D.W * HD;
+  return attend_t<T, HD>(B * D.H, S.q, elem<T>(S.ring_k, l * layer), elem<T>(S.ring_v, l * layer),
+                         (int64_t)D.W * HD, n_valid, D.H, static_cast<T*>(S.o), st);
 }
 
 template <typename T, int HD>
 static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
                           int64_t t, hipStream_t st) {
-  int chunk, nsplit;
-  cross_split(t, B * D.H, chunk, nsplit);
-  if (chunk > kMaxChunk || nsplit > kMaxSplit) return hipErrorInvalidValue;
   const int g = D.G == 1 ? 0 : l;
-  const int64_t grp = (int64_t)g * B * D.H * M.capacity * HD;
-  hipLaunchKernelGGL((k_attn_cross<T, HD>), dim3(B * D.H * nsplit), dim3(kThreads), 0, st, S.qc,
-                     elem<T>(M.k, grp), elem<T>(M.v, grp), M.capacity, static_cast<T*>(S.o),
-                     S.part, S.cnt, D.H, (int)t, chunk, nsplit, 1.f / sqrtf((float)HD));
-  return hipGetLastError();
+  const int64_t grp = (int64_t)g * M.Bt * D.H * M.capacity * HD;
+  return attend_t<T, HD>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
+                         M.capacity * HD, (int)t, D.H, static_cast<T*>(S.o), st);
 }
 
 #define RLT_HD_DISPATCH(fn, ...)                                              \

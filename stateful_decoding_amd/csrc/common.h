@@ -56,6 +56,7 @@ template <> struct Frag<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16* p) { v = __builtin_bit_cast(bf16x8, ld16(p)); }
   __device__ __forceinline__ void zero() { v = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
+  __device__ __forceinline__ void from_raw(const u32x4* r) { v = __builtin_bit_cast(bf16x8, r[0]); }
   __device__ __forceinline__ void from_f32(const float (&x)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
@@ -75,11 +76,27 @@ template <> struct Frag<float> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.f;
   }
+  __device__ __forceinline__ void from_raw(const u32x4* r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(r[0][i]);
+      v[4 + i] = __uint_as_float(r[1][i]);
+    }
+  }
   __device__ __forceinline__ void from_f32(const float (&x)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = x[i];
   }
 };
+
+// Element offset of (row, k) in a [rows][K] operand stored in MFMA fragment order: for every
+// 16-row tile and 32-wide k-step, the 64 lanes' 8 consecutive k values lie contiguously (1 KB
+// in bf16), so one wave load of a fragment reads whole cache lines. A row range that starts
+// on a multiple of 16 begins at the same offset as in row-major order (row * K).
+__host__ __device__ __forceinline__ int64_t frag_off(int64_t row, int k, int ksteps) {
+  return ((((row >> 4) * ksteps + (k >> 5)) << 6) + (row & 15) + (((k & 31) >> 3) << 4)) * 8 +
+         (k & 7);
+}
 
 // acc(16x16, fp32) += A(16x32) * B(32x16). Output layout: lane l holds rows 4*(l/16)+i,
 // i = 0..3, of column l % 16.

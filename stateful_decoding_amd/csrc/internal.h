@@ -11,10 +11,16 @@
 
 namespace rlt {
 
-constexpr int kMaxSplit = 64;    // cross-attention partitions of the memory per (seq, head)
-constexpr int kMaxChunk = 1024;  // memory entries one workgroup attends over
 constexpr int kMaxWindow = 1024;
-constexpr int64_t kMaxCapacity = (int64_t)kMaxSplit * kMaxChunk;
+constexpr int64_t kMaxCapacity = (int64_t)1 << 20;  // memory entries per sequence
+// Large batches run as row groups of about kGroupRows sequences (multiples of 16), each on its
+// own stream, at most kMaxGroups of them: one group's latency-bound projections then overlap
+// other groups' bandwidth-bound attention.
+#ifndef RLT_GROUP_ROWS
+#define RLT_GROUP_ROWS 128
+#endif
+constexpr int kGroupRows = RLT_GROUP_ROWS;
+constexpr int kMaxGroups = 4;
 
 // Sizes derived from a validated rlt_config.
 struct Dims {
@@ -23,8 +29,9 @@ struct Dims {
   size_t es;  // element size of dtype
 };
 
-// Device pointers of the packed weights (all inside the model workspace).
-//   w_gate_t [d][2d]   gate weights, output-major (k contiguous)
+// Device pointers of the packed weights (all inside the model workspace). Every matrix is
+// stored transposed (output-major) in MFMA fragment order (frag_off in common.h).
+//   w_gate_t [d][2d]   gate weights
 //   wqkv_t   [L][3d][d]
 //   wo_t, wcq_t, wco_t [L][d][d]
 //   w13_t    [L][2F][d]  rows in blocks of 32: 16 rows of W1^T then the same 16 of W3^T
@@ -49,32 +56,41 @@ struct Packed {
 //   ring  [L][B][H][W][hd]     self-attention keys/values; token tau lives in slot tau % W.
 //                              W slots hold the W-1 retained entries plus the current one.
 //   h, q, qc [B][d] f32        residual stream, self-attention query, cross-attention query
-//   o     [B][d] dtype         attention output (operand of the output projections)
-//   act   [B][F] dtype         SiLU(f W1) * (f W3)
-//   part  [B][H][kMaxSplit][hd+2] f32  cross-attention partials (max, sum, hd outputs)
-//   cnt   [B][H] i32           arrival counters of the partial merge (kept at zero)
+//   hg    [B16][d] dtype       h * gamma of the next RMSNorm (operand of the next projection)
+//   ssq   [B][d/32] f32        sums of h^2 over 32-column chunks (that norm's scale)
+//   o     [B16][d] dtype       attention output (operand of the output projections)
+//   act   [B16][F] dtype       SiLU(f W1) * (f W3)
+// hg, o and act are projection operands in MFMA fragment order, B16 = B rounded up to 16.
 struct StateBufs {
+  int Bt;  // batch of the whole state: row stride of the per-layer ring blocks
   float* s;
   void* ring_k;
   void* ring_v;
   float* h;
   float* q;
   float* qc;
+  void* hg;
+  float* ssq;
   void* o;
   void* act;
-  float* part;
-  int* cnt;
 };
 
 struct MemBufs {
   void* k;  // [G][B][H][capacity][hd]
   void* v;
   int64_t capacity;
+  int Bt;   // batch of the whole memory: row stride of the per-group blocks
 };
+
+// The rows [b0, b0 + n) of a state (and of its memory) as a state of n sequences: row-indexed
+// buffers are offset, ring/memory blocks keep the whole-batch strides. Sequences are
+// independent, so row groups can run on different streams.
+StateBufs state_rows(const Dims& D, const StateBufs& S, int b0);
+MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0);
 
 // Byte layout of the state buffer; offsets are 256-byte aligned.
 struct StateLayout {
-  size_t s, ring_k, ring_v, h, q, qc, o, act, part, cnt, total;
+  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, total;
 };
 StateLayout state_layout(const Dims& D, int B);
 

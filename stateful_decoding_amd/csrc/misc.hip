@@ -2,12 +2,14 @@
 // sequencing (one launch per phase, all on the caller's stream).
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace rlt {
 
-// ---- weight packing: dst[row(n)][k] = src[k][n], 32x32 tiles through LDS -----------------
+// ---- weight packing: dst row row(n) = column n of src [K][N], MFMA fragment order ----------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_pack_transpose(const T* __restrict__ src, int K,
                                                              int N, T* __restrict__ dst,
@@ -25,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_transpose(const T* __restrict
     const int n = n0 + r, k = k0 + tx;
     if (k < K && n < N) {
       const int64_t row = row_base + (int64_t)(n / grp) * grp_stride + n % grp;
-      dst[row * K + k] = tile[tx][r];
+      dst[frag_off(row, k, K / 32)] = tile[tx][r];
     }
   }
 }
@@ -44,22 +46,19 @@ hipError_t launch_pack_transpose(int dtype, const void* src, int K, int N, void*
   return hipGetLastError();
 }
 
-// ---- reset: s = s*, merge counters zero ---------------------------------------------------
+// ---- reset: s = s* ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_reset(float* __restrict__ s,
                                                     const float* __restrict__ s_star, int d,
-                                                    int64_t n_s, int* __restrict__ cnt,
-                                                    int64_t n_cnt) {
+                                                    int64_t n_s) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i < n_s) s[i] = s_star[i % d];
-  if (i < n_cnt) cnt[i] = 0;
 }
 
 hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& S,
                         hipStream_t st) {
-  const int64_t n_s = (int64_t)B * D.d, n_cnt = (int64_t)B * D.H;
-  const int64_t n = n_s > n_cnt ? n_s : n_cnt;
-  hipLaunchKernelGGL(k_reset, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     st, S.s, P.s_star, D.d, n_s, S.cnt, n_cnt);
+  const int64_t n_s = (int64_t)B * D.d;
+  hipLaunchKernelGGL(k_reset, dim3((unsigned)((n_s + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, S.s, P.s_star, D.d, n_s);
   return hipGetLastError();
 }
 
@@ -133,6 +132,32 @@ hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, co
   return D.dtype == RLT_BF16
              ? snapshot_t<bf16, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st)
              : snapshot_t<float, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st);
+}
+
+// ---- row groups -----------------------------------------------------------------------------
+StateBufs state_rows(const Dims& D, const StateBufs& S, int b0) {
+  StateBufs v = S;
+  const int64_t d = D.d;
+  v.s += b0 * d;
+  v.h += b0 * d;
+  v.q += b0 * d;
+  v.qc += b0 * d;
+  v.hg = static_cast<char*>(S.hg) + b0 * d * D.es;
+  v.ssq += b0 * (d / 32);
+  v.o = static_cast<char*>(S.o) + b0 * d * D.es;
+  v.act = static_cast<char*>(S.act) + (int64_t)b0 * D.F * D.es;
+  const int64_t ring_row = (int64_t)D.H * D.W * D.hd * D.es;
+  v.ring_k = static_cast<char*>(S.ring_k) + b0 * ring_row;
+  v.ring_v = static_cast<char*>(S.ring_v) + b0 * ring_row;
+  return v;
+}
+
+MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0) {
+  MemBufs v = M;
+  const int64_t row = (int64_t)D.H * M.capacity * D.hd * D.es;
+  v.k = static_cast<char*>(M.k) + b0 * row;
+  v.v = static_cast<char*>(M.v) + b0 * row;
+  return v;
 }
 
 // ---- kernel timing ---------------------------------------------------------------------------

@@ -52,6 +52,9 @@ def test_tiny_fp32_config():
          sigma=0.03),
     dict(dtype="bf16", head_dim=64, window=16, B=3, T=300),  # memory split over 5 workgroups
     dict(dtype="fp32", head_dim=64, window=33, B=2, T=200, n_layers=1),
+    # batches of >= 256 sequences run as row groups on separate streams
+    dict(dtype="bf16", head_dim=64, window=6, n_groups=2, B=300, T=40),
+    dict(dtype="fp32", head_dim=32, n_heads=4, window=3, B=256, T=12),
 ])
 def test_small_cases(case):
     case = dict(case)
@@ -75,9 +78,10 @@ def test_memory_projection_matches_oracle():
         assert max_rel_l2(got[:, :, :, :19], ref) < 1e-5
 
 
-def test_decoder_steps_equal_run_sequence_and_split():
+@pytest.mark.parametrize("B", [6, 280])
+def test_decoder_steps_equal_run_sequence_and_split(B):
     cfg = cfg_small(window=4, n_groups=2)
-    B, T = 6, 17
+    T = 17
     p, e = inputs(cfg, B, T, seed=11)
     a = GpuRun(cfg, p, B, T)
     full = a.run(e)
