@@ -88,13 +88,6 @@ struct ANormed {  // A = hg = h * gamma (dtype, fragment order); rows scaled by 
     f.from_raw(r);
     return f;
   }
-  // 1 / sqrt(mean(h^2) + eps) of a valid row; the chunks are added in order
-  __device__ float rinv(int row) const {
-    const float* p = ssq + (int64_t)row * nchunk;
-    float v = 0.f;
-    for (int j = 0; j < nchunk; ++j) v += p[j];
-    return rsqrtf(v / (float)K + eps);
-  }
 };
 
 template <typename T>
@@ -140,15 +133,25 @@ struct AGate {  // A = [e_t ; alpha * s] (K = 2d); a 32-wide k-step never stradd
 };
 
 // ---- epilogues ------------------------------------------------------------------------------
-// store() consumes a finished [bm][bn] fp32 tile held in LDS (row stride ld) whose element
-// (r, c) is output (r0 + r, c0 + c); consecutive threads take consecutive columns.
+// store() consumes a finished [BM][BN] fp32 tile held in LDS (row stride ld) whose element
+// (r, c) is output (r0 + r, c0 + c); thread tid takes elements tid, tid + NT, ... so
+// consecutive threads take consecutive columns. prefetch() runs before the main loop and loads
+// into registers (Pre) whatever store() will read from global memory, so those loads overlap
+// the operand loads instead of adding a round trip at the end.
+
+template <int E>
+struct Pre {
+  float a[E], b[E], c[E];
+};
 
 template <class D>
 struct EpiTile {
-  template <int NT>
-  __device__ void store(float* tile, int ld, int r0, int c0, int bm, int bn) const {
-    for (int i = threadIdx.x; i < bm * bn; i += NT) {
-      const int r = i / bn, c = i - r * bn;
+  template <int NT, int BM, int BN, int E>
+  __device__ void prefetch(Pre<E>&, int, int) const {}
+  template <int NT, int BM, int BN, int E>
+  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>&) const {
+    for (int i = threadIdx.x; i < BM * BN; i += NT) {
+      const int r = i / BN, c = i - r * BN;
       static_cast<const D*>(this)->op(r0 + r, c0 + c, tile[r * ld + c]);
     }
   }
@@ -197,24 +200,40 @@ struct EpiH {
   const float* gamma;
   float* ssq;
   int nchunk;
-  template <int NT>
-  __device__ void store(float* tile, int ld, int r0, int c0, int bm, int bn) const {
+  template <int NT, int BM, int BN, int E>
+  __device__ void prefetch(Pre<E>& pre, int r0, int c0) const {
     const D& self = static_cast<const D&>(*this);
-    for (int i = threadIdx.x; i < bm * bn; i += NT) {
-      const int r = i / bn, c = i - r * bn;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = threadIdx.x + j * NT;
+      if (i >= BM * BN) break;
+      const int r = i / BN, c = i - r * BN;
+      const int row = min(r0 + r, self.M - 1), col = c0 + c;
+      self.load_inputs(row, col, pre.a[j], pre.b[j]);
+      pre.c[j] = hg ? gamma[col] : 0.f;
+    }
+  }
+  template <int NT, int BM, int BN, int E>
+  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>& pre) const {
+    const D& self = static_cast<const D&>(*this);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = threadIdx.x + j * NT;
+      if (i >= BM * BN) break;
+      const int r = i / BN, c = i - r * BN;
       const int row = r0 + r, col = c0 + c;
       float sq = 0.f;
       if (row < self.M) {
-        const float v = self.value(row, col, tile[r * ld + c]);
-        if (hg) hg[frag_off(row, col, nchunk)] = to_elem<T>(v * gamma[col]);
+        const float v = self.value(row, col, tile[r * ld + c], pre.a[j], pre.b[j]);
+        if (hg) hg[frag_off(row, col, nchunk)] = to_elem<T>(v * pre.c[j]);
         sq = v * v;
       }
       tile[r * ld + c] = sq;
     }
     if (!hg) return;
     __syncthreads();
-    const int nch = bn / 32;
-    for (int j = threadIdx.x; j < bm * nch; j += NT) {
+    constexpr int nch = BN / 32;
+    for (int j = threadIdx.x; j < BM * nch; j += NT) {
       const int r = j / nch, ch = j - r * nch;
       if (r0 + r >= self.M) continue;
       const float* t = tile + r * ld + ch * 32;
@@ -232,10 +251,12 @@ struct EpiResidual : EpiH<T, EpiResidual<T>> {  // dst = h + v; optional copy to
   float* out;
   int64_t out_ld;
   int M, d;
-  __device__ float value(int row, int col, float v) const {
-    const int64_t i = (int64_t)row * d + col;
-    const float r = h[i] + v;
-    dst[i] = r;
+  __device__ void load_inputs(int row, int col, float& a, float&) const {
+    a = h[(int64_t)row * d + col];
+  }
+  __device__ float value(int row, int col, float v, float hv, float) const {
+    const float r = hv + v;
+    dst[(int64_t)row * d + col] = r;
     if (out) out[(int64_t)row * out_ld + col] = r;
     return r;
   }
@@ -250,11 +271,13 @@ struct EpiGate : EpiH<T, EpiGate<T>> {  // g = sigmoid(v + b); h = g e + (1 - g)
   const float* b;
   float alpha;
   int M, d;
-  __device__ float value(int row, int col, float v) const {
+  __device__ void load_inputs(int row, int col, float& ev, float& sv) const {
+    ev = to_f32<T>(e[(int64_t)row * lde + col]);
+    sv = s[(int64_t)row * d + col];
+  }
+  __device__ float value(int row, int col, float v, float ev, float sv) const {
     const float g = sigmoidf_(v + b[col]);
-    const float ev = to_f32<T>(e[(int64_t)row * lde + col]);
-    const float u = alpha * s[(int64_t)row * d + col];
-    const float r = g * ev + (1.f - g) * u;
+    const float r = g * ev + (1.f - g) * (alpha * sv);
     h[(int64_t)row * d + col] = r;
     return r;
   }
@@ -265,10 +288,12 @@ struct EpiSiluMul {  // packed columns come in blocks of 32: 16 of W1, then the 
                      // act is written in fragment order (the down projection's operand)
   T* act;
   int M, F;
-  template <int NT>
-  __device__ void store(float* tile, int ld, int r0, int c0, int bm, int bn) const {
-    const int half = bn / 2;
-    for (int i = threadIdx.x; i < bm * half; i += NT) {
+  template <int NT, int BM, int BN, int E>
+  __device__ void prefetch(Pre<E>&, int, int) const {}
+  template <int NT, int BM, int BN, int E>
+  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>&) const {
+    constexpr int half = BN / 2;
+    for (int i = threadIdx.x; i < BM * half; i += NT) {
       const int r = i / half, j = i - r * half;
       const int row = r0 + r;
       if (row >= M) continue;
@@ -330,9 +355,24 @@ __global__ __launch_bounds__(NW * kWave) void k_proj(int N, int K, const T* __re
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int r0 = tm * BM, c0 = tn * BN;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // 1/rms inputs: NT / BM lanes per row load that row's chunk sums now, add them at the end
+  constexpr int LPRR = NT / BM, QMAX = 8;
+  float sq[QMAX];
+  int nq = 0;
   if constexpr (AL::kNorm) {
-    if (tid < BM) rinv[tid] = al.rinv(min(r0 + tid, al.M - 1));
+    const int row = min(r0 + tid / LPRR, al.M - 1), part = tid % LPRR;
+    const int q = (al.nchunk + LPRR - 1) / LPRR;
+    nq = min(q, QMAX);
+    const float* p = al.ssq + (int64_t)row * al.nchunk;
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) {
+      const int ch = part + j * LPRR;
+      sq[j] = j < nq && ch < al.nchunk ? p[ch] : 0.f;
+    }
   }
+  constexpr int EPT = (BM * BN + NT - 1) / NT;
+  Pre<EPT> pre;
+  ep.template prefetch<NT, BM, BN>(pre, r0, c0);
 
   // k-steps (of 32) of this wave
   const int ksteps = K / 32;
@@ -394,6 +434,17 @@ __global__ __launch_bounds__(NW * kWave) void k_proj(int N, int K, const T* __re
       if (u < n) consume(st + u, raw[u]);
   }
 
+  if constexpr (AL::kNorm) {
+    // chunks beyond QMAX per lane (very wide rows) are added here, in the same lane order
+    const int row = min(r0 + tid / LPRR, al.M - 1), part = tid % LPRR;
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) v += sq[j];
+    for (int ch = part + QMAX * LPRR; ch < al.nchunk; ch += LPRR) v += al.ssq[(int64_t)row * al.nchunk + ch];
+#pragma unroll
+    for (int o = 1; o < LPRR; o <<= 1) v += __shfl_xor(v, o, kWave);
+    if (tid % LPRR == 0) rinv[tid / LPRR] = rsqrtf(v / (float)al.K + al.eps);
+  }
   // the wave partials -> LDS, summed into red[0 .. BM*LD) and scaled by 1/rms
   float* mine = red + wave * BM * LD;
 #pragma unroll
@@ -413,7 +464,7 @@ __global__ __launch_bounds__(NW * kWave) void k_proj(int N, int K, const T* __re
     red[o] = v;
   }
   __syncthreads();
-  ep.template store<NT>(red, LD, r0, c0, BM, BN);
+  ep.template store<NT, BM, BN>(red, LD, r0, c0, pre);
 }
 
 // ---- memory projection: register tiles, no split ------------------------------------------------
