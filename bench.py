@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--workload", default="s140m_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run 5 plain device copies of MIB MiB (fp32) and exit: the known-size "
+                         "kernel that scales the HBM byte counters of a profiler")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,8 +122,18 @@ def main():
               "not run here.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2**20 // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"launches": 5, "read_bytes": 4 * n,
+                                               "write_bytes": 4 * n}}), flush=True)
+        return
 
     import stateful_decoding_amd as sd
     from synth import CONFIGS, make_encoder_outputs, make_params
@@ -184,7 +197,7 @@ def main():
                    "heads": cfg.n_heads, "head_dim": cfg.head_dim, "decoder_blocks": cfg.n_layers,
                    "ffn": cfg.ffn, "window": cfg.window, "memory_groups": cfg.n_groups,
                    "alpha": cfg.alpha, "inputs": "e_t ~ N(0,1), weights ~ N(0,0.02), seed 0"},
-        "roofline": {"bound": "hbm", "kernel": "cross_attn (k_attn_cross)",
+        "roofline": {"bound": "hbm", "kernel": "k_attend_memory (cross-attention over memory 1..t)",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": traffic,

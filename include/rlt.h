@@ -212,14 +212,15 @@ typedef enum rlt_kernel {
 
 typedef struct rlt_kernel_stats {
   int64_t launches;  /* launches timed                                                   */
-  double total_ms;   /* sum over launches of the HIP-event time around the launch        */
+  double total_ms;   /* sum over launches of the kernel's duration (HIP events)           */
   double bytes;      /* algorithmic bytes: each operand read once, each result written once */
   double flops;      /* algorithmic floating-point operations                            */
 } rlt_kernel_stats;
 
 /* Starts timing, for this state, every launch of the kernels whose bit (1 << rlt_kernel) is
- * set in `mask`: a HIP event is recorded on the launch stream before and after each one.
- * Timing adds two event records per timed launch to the stream. */
+ * set in `mask`: each timed launch records a pair of HIP events at the start and at the end of
+ * its kernel (hipExtLaunchKernel), on the stream it runs on; no extra packets are queued.
+ * Events are pooled by the state and kept until rlt_state_destroy. */
 rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask);
 
 /* Stops timing, waits for the recorded events and writes RLT_K_COUNT entries to `out`

@@ -409,8 +409,8 @@ static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_
   hipError_t err = hipSuccess;
   if (ng > 1) {
     err = hipEventRecord(state->fork, st);
-    for (int g = 1; g < ng && err == hipSuccess; ++g)
-      err = hipStreamWaitEvent(state->aux[g], state->fork, 0);
+    for (int g = 0; g < ng && err == hipSuccess; ++g)
+      if (state->aux[g]) err = hipStreamWaitEvent(state->aux[g], state->fork, 0);
     if (err != hipSuccess) return err;
   }
   StateBufs Sg[kMaxGroups];
@@ -427,10 +427,11 @@ static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_
       const char* et = eb + ((size_t)b0 * e_ld + (size_t)i * D.d) * D.es;
       float* o = out ? out + (size_t)b0 * out_ld + (size_t)i * D.d : nullptr;
       err = launch_step(D, rows, model->P, Sg[g], Mg[g], et, e_ld, t0, o, out_ld,
-                        g == 0 ? st : state->aux[g], &state->prof);
+                        state->aux[g] ? state->aux[g] : st, &state->prof);
     }
   }
-  for (int g = 1; g < ng && err == hipSuccess; ++g) {
+  for (int g = 0; g < ng && err == hipSuccess; ++g) {
+    if (!state->aux[g]) continue;
     err = hipEventRecord(state->join[g], state->aux[g]);
     if (err == hipSuccess) err = hipStreamWaitEvent(st, state->join[g], 0);
   }
@@ -487,14 +488,11 @@ rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory
     const int64_t first = mem->len - t;  // index into e of the first missing token
     const int64_t cnt = n - first;
     const void* e_first = static_cast<const char*>(e) + (size_t)first * D.d * D.es;
-    int ev = -1;
     const double rows = (double)B * cnt, d = D.d, es = (double)D.es;
-    err = state->prof.begin(RLT_K_MEMPROJ, st, ev);
-    if (err == hipSuccess) err = launch_memproj(D, B, model->P, mem->M, e_first, n, mem->len, cnt, st);
-    if (err == hipSuccess)
-      err = state->prof.end(RLT_K_MEMPROJ, ev,
-                            es * (rows * d + D.G * 2 * d * d + rows * D.G * 2 * d),
-                            2 * rows * d * D.G * 2 * d, st);
+    Exec x(st);
+    err = state->prof.arm(RLT_K_MEMPROJ, es * (rows * d + D.G * 2 * d * d + rows * D.G * 2 * d),
+                          2 * rows * d * D.G * 2 * d, x);
+    if (err == hipSuccess) err = launch_memproj(D, B, model->P, mem->M, e_first, n, mem->len, cnt, x);
     if (err != hipSuccess) return hip_fail(err, "memory projection");
     mem->len = t + n;
   }
@@ -518,11 +516,12 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
   Profiler& P = state->prof;
   for (int k = 0; k < RLT_K_COUNT; ++k) out[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
   hipError_t e = hipSuccess;
-  if (P.used) e = hipEventSynchronize(P.events[P.used - 1]);
   for (const Profiler::Rec& r : P.recs) {
-    if (e != hipSuccess) break;
+    // launches of different row groups ran on different streams: wait for each one
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, P.events[r.ev], P.events[r.ev + 1]);
+    e = hipEventSynchronize(P.events[r.ev + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, P.events[r.ev], P.events[r.ev + 1]);
+    if (e != hipSuccess) break;
     rlt_kernel_stats& o = out[r.kind];
     o.launches += 1;
     o.total_ms += ms;

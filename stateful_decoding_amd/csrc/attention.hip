@@ -46,11 +46,9 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 // (fp32, head hh), K/V blocks start at K + bh * bh_stride; the output row o[b] (dtype) is
 // written in MFMA fragment order, as the output projection reads it.
 template <typename T, int HD, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_attend(const float* __restrict__ q,
-                                                       const T* __restrict__ K,
-                                                       const T* __restrict__ V,
-                                                       int64_t bh_stride, int n, int H,
-                                                       float scale, T* __restrict__ out) {
+__device__ __forceinline__ void attend(const float* __restrict__ q, const T* __restrict__ K,
+                                       const T* __restrict__ V, int64_t bh_stride, int n, int H,
+                                       float scale, T* __restrict__ out) {
   using G = Geo<T, HD>;
   constexpr int RPB = G::RPW * NW;  // rows per block per batch step
   __shared__ float lds_m[NW], lds_l[NW];
@@ -134,42 +132,54 @@ __global__ __launch_bounds__(NW * kWave) void k_attend(const float* __restrict__
   }
 }
 
+// The two uses get kernels of their own, so that traces tell them apart.
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_attend_window(const float* q, const T* K,
+                                                              const T* V, int64_t bh_stride,
+                                                              int n, int H, float scale, T* out) {
+  attend<T, HD, NW, U>(q, K, V, bh_stride, n, H, scale, out);
+}
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_attend_memory(const float* q, const T* K,
+                                                              const T* V, int64_t bh_stride,
+                                                              int n, int H, float scale, T* out) {
+  attend<T, HD, NW, U>(q, K, V, bh_stride, n, H, scale, out);
+}
+
 template <typename T>
 static inline T* elem(void* base, int64_t off) {
   return static_cast<T*>(base) + off;
 }
 
 // Waves per workgroup: enough workgroups x waves to keep the chip streaming.
-template <typename T, int HD>
+template <typename T, int HD, bool MEMORY>
 static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
-                           int n, int H, T* out, hipStream_t st) {
+                           int n, int H, T* out, const Exec& st) {
   const float scale = 1.f / sqrtf((float)HD);
-  if (BH >= 1024)
-    hipLaunchKernelGGL((k_attend<T, HD, 4, 4>), dim3(BH), dim3(4 * kWave), 0, st, q, K, V, bh_stride, n,
-                       H, scale, out);
-  else if (BH >= 512)
-    hipLaunchKernelGGL((k_attend<T, HD, 8, 4>), dim3(BH), dim3(8 * kWave), 0, st, q, K, V, bh_stride, n,
-                       H, scale, out);
-  else
-    hipLaunchKernelGGL((k_attend<T, HD, 16, 4>), dim3(BH), dim3(16 * kWave), 0, st, q, K, V, bh_stride,
-                       n, H, scale, out);
-  return hipGetLastError();
+  const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
+#define RLT_ATTEND(NW)                                                                        \
+  return launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,      \
+                dim3(BH), dim3(NW * kWave), st, q, K, V, bh_stride, n, H, scale, out)
+  if (nw == 4) RLT_ATTEND(4);
+  if (nw == 8) RLT_ATTEND(8);
+  RLT_ATTEND(16);
+#undef RLT_ATTEND
 }
 
 template <typename T, int HD>
 static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                         hipStream_t st) {
+                         const Exec& st) {
   const int64_t layer = (int64_t)S.Bt * D.H * D.W * HD;
-  return attend_t<T, HD>(B * D.H, S.q, elem<T>(S.ring_k, l * layer), elem<T>(S.ring_v, l * layer),
+  return attend_t<T, HD, false>(B * D.H, S.q, elem<T>(S.ring_k, l * layer), elem<T>(S.ring_v, l * layer),
                          (int64_t)D.W * HD, n_valid, D.H, static_cast<T*>(S.o), st);
 }
 
 template <typename T, int HD>
 static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                          int64_t t, hipStream_t st) {
+                          int64_t t, const Exec& st) {
   const int g = D.G == 1 ? 0 : l;
   const int64_t grp = (int64_t)g * M.Bt * D.H * M.capacity * HD;
-  return attend_t<T, HD>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
+  return attend_t<T, HD, true>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
                          M.capacity * HD, (int)t, D.H, static_cast<T*>(S.o), st);
 }
 
@@ -182,12 +192,12 @@ static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const
   }
 
 hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                     hipStream_t st) {
+                     const Exec& st) {
   RLT_HD_DISPATCH(self_t, D, B, l, S, n_valid, st)
 }
 
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      int64_t t, hipStream_t st) {
+                      int64_t t, const Exec& st) {
   RLT_HD_DISPATCH(cross_t, D, B, l, S, M, t, st)
 }
 

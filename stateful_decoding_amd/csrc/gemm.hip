@@ -515,29 +515,28 @@ constexpr Shape kBig{2, 2, 2, 2};  // 64 x 64
 
 template <typename T, int WM, int WN, int FM, int FN, class AL, class EP>
 static hipError_t run_gemm(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
-                           hipStream_t st) {
+                           const Exec& st) {
   constexpr int BM = 16 * FM * WM, BN = 16 * FN * WN;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
   if (N % BN != 0 || K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_tokens<T, WM, WN, FM, FN, AL, EP>), dim3((unsigned)blocks), dim3(kThreads),
-                     0, st, N, K, static_cast<const T*>(Wt), al, ep);
-  return hipGetLastError();
+  return launch(k_gemm_tokens<T, WM, WN, FM, FN, AL, EP>, dim3((unsigned)blocks), dim3(kThreads),
+                st, N, K, static_cast<const T*>(Wt), al, ep);
 }
 
 template <typename T, int FM, int FN, int NW, class AL, class EP>
 static void launch_proj(int64_t tiles, int N, int K, const T* W, const AL& al, const EP& ep,
-                        hipStream_t st) {
+                        const Exec& st) {
   constexpr int PS = FM * AL::kPer + AL::kShared + FN * (sizeof(T) == 2 ? 1 : 2);
   constexpr int U = 24 / PS < 1 ? 1 : 24 / PS > 6 ? 6 : 24 / PS;  // <= 96 VGPRs of raw loads
-  hipLaunchKernelGGL((k_proj<T, FM, FN, NW, U, AL, EP>), dim3((unsigned)tiles), dim3(NW * kWave),
-                     0, st, N, K, W, al, ep);
+  (void)launch(k_proj<T, FM, FN, NW, U, AL, EP>, dim3((unsigned)tiles), dim3(NW * kWave), st, N,
+               K, W, al, ep);
 }
 
 // Decoder-step projection with tile FM x FN: enough waves per block that each wave's share of K
 // fits one batch of loads, and more waves when there are few tiles.
 template <typename T, int FM, int FN, class AL, class EP>
 static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
-                           hipStream_t st) {
+                           const Exec& st) {
   constexpr int BM = 16 * FM, BN = 16 * FN;
   constexpr int PS = FM * AL::kPer + AL::kShared + FN * (sizeof(T) == 2 ? 1 : 2);
   constexpr int U = 24 / PS < 1 ? 1 : 24 / PS > 6 ? 6 : 24 / PS;
@@ -559,7 +558,7 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
 // Largest tile that still gives enough blocks to fill the chip.
 template <typename T, class AL, class EP>
 static hipError_t run_step_gemm(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
-                                hipStream_t st) {
+                                const Exec& st) {
   auto blocks = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * (N / bn); };
   if (N % 64 == 0 && blocks(32, 64) >= 320) return run_proj<T, 2, 4>(M, N, K, Wt, al, ep, st);
   if (blocks(32, 32) >= 320) return run_proj<T, 2, 2>(M, N, K, Wt, al, ep, st);
@@ -593,7 +592,7 @@ static ANormed<T> normed(const Dims& D, int B, const StateBufs& S) {
 
 template <typename T>
 static hipError_t gate_t(const Dims& D, int B, const Packed& P, const StateBufs& S,
-                         const void* e_t, int64_t e_ld, hipStream_t st) {
+                         const void* e_t, int64_t e_ld, const Exec& st) {
   AGate<T> al{static_cast<const T*>(e_t), e_ld, S.s, D.alpha, B, D.d};
   EpiGate<T> ep;
   ep.h = S.h; ep.e = static_cast<const T*>(e_t); ep.lde = e_ld; ep.s = S.s; ep.b = P.b_gate;
@@ -604,7 +603,7 @@ static hipError_t gate_t(const Dims& D, int B, const Packed& P, const StateBufs&
 
 template <typename T>
 static hipError_t qkv_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                        int slot, hipStream_t st) {
+                        int slot, const Exec& st) {
   EpiQKV<T> ep;
   const int64_t ring_layer = (int64_t)S.Bt * D.H * D.W * D.hd;
   ep.q = S.q; ep.ring_k = elem<T>(S.ring_k, l * ring_layer); ep.ring_v = elem<T>(S.ring_v, l * ring_layer);
@@ -615,7 +614,7 @@ static hipError_t qkv_t(const Dims& D, int B, int l, const Packed& P, const Stat
 
 template <typename T>
 static hipError_t cq_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                       hipStream_t st) {
+                       const Exec& st) {
   EpiStoreF32 ep;
   ep.out = S.qc; ep.ld = D.d; ep.M = B;
   return run_step_gemm<T>(B, D.d, D.d, elem<T>(P.wcq_t, (int64_t)l * D.d * D.d),
@@ -624,7 +623,7 @@ static hipError_t cq_t(const Dims& D, int B, int l, const Packed& P, const State
 
 template <typename T>
 static hipError_t w13_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                        hipStream_t st) {
+                        const Exec& st) {
   EpiSiluMul<T> ep{static_cast<T*>(S.act), B, D.F};
   return run_step_gemm<T>(B, 2 * D.F, D.d, elem<T>(P.w13_t, (int64_t)l * 2 * D.F * D.d),
                           normed<T>(D, B, S), ep, st);
@@ -636,7 +635,7 @@ static hipError_t w13_t(const Dims& D, int B, int l, const Packed& P, const Stat
 template <typename T>
 static hipError_t residual_t(const Dims& D, int B, int l, int which, const Packed& P,
                              const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
-                             hipStream_t st) {
+                             const Exec& st) {
   const void* A = which == 2 ? S.act : S.o;
   const int K = which == 2 ? D.F : D.d;
   const void* Wt = which == 0 ? elem<T>(P.wo_t, (int64_t)l * D.d * D.d)
@@ -653,7 +652,7 @@ static hipError_t residual_t(const Dims& D, int B, int l, int which, const Packe
 
 template <typename T>
 static hipError_t memproj_t(const Dims& D, int B, const Packed& P, const MemBufs& M,
-                            const void* e, int64_t e_seq, int64_t t0, int64_t n, hipStream_t st) {
+                            const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st) {
   const int64_t rows = (int64_t)B * n;
   if (rows > INT32_MAX / 2) return hipErrorInvalidValue;
   ATokens<T> al{static_cast<const T*>(e), e_seq, (int)rows, (int)n, D.d};
@@ -665,31 +664,31 @@ static hipError_t memproj_t(const Dims& D, int B, const Packed& P, const MemBufs
 }
 
 hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, const void* e_t,
-                     int64_t e_ld, hipStream_t st) {
+                     int64_t e_ld, const Exec& st) {
   return D.dtype == RLT_BF16 ? gate_t<bf16>(D, B, P, S, e_t, e_ld, st)
                              : gate_t<float>(D, B, P, S, e_t, e_ld, st);
 }
 hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S, int slot,
-                    hipStream_t st) {
+                    const Exec& st) {
   return D.dtype == RLT_BF16 ? qkv_t<bf16>(D, B, l, P, S, slot, st)
                              : qkv_t<float>(D, B, l, P, S, slot, st);
 }
 hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                   hipStream_t st) {
+                   const Exec& st) {
   return D.dtype == RLT_BF16 ? cq_t<bf16>(D, B, l, P, S, st) : cq_t<float>(D, B, l, P, S, st);
 }
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                    hipStream_t st) {
+                    const Exec& st) {
   return D.dtype == RLT_BF16 ? w13_t<bf16>(D, B, l, P, S, st) : w13_t<float>(D, B, l, P, S, st);
 }
 hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P,
                          const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
-                         hipStream_t st) {
+                         const Exec& st) {
   return D.dtype == RLT_BF16 ? residual_t<bf16>(D, B, l, which, P, S, dst_s, out, out_ld, st)
                              : residual_t<float>(D, B, l, which, P, S, dst_s, out, out_ld, st);
 }
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
-                          const void* e, int64_t e_seq, int64_t t0, int64_t n, hipStream_t st) {
+                          const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st) {
   return D.dtype == RLT_BF16 ? memproj_t<bf16>(D, B, P, M, e, e_seq, t0, n, st)
                              : memproj_t<float>(D, B, P, M, e, e_seq, t0, n, st);
 }

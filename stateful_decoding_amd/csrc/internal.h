@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI host code (api.cpp) and the HIP kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -21,6 +22,26 @@ constexpr int64_t kMaxCapacity = (int64_t)1 << 20;  // memory entries per sequen
 #endif
 constexpr int kGroupRows = RLT_GROUP_ROWS;
 constexpr int kMaxGroups = 4;
+
+// Where a kernel runs: its stream and, when it is being timed, a pair of events that the
+// launch itself records at the start and at the end of the kernel (hipExtLaunchKernel), so the
+// measured span is the kernel alone, without extra event packets around it.
+struct Exec {
+  hipStream_t st;
+  hipEvent_t start = nullptr, stop = nullptr;
+  Exec(hipStream_t s) : st(s) {}  // NOLINT: a plain stream is an untimed Exec
+  Exec(hipStream_t s, hipEvent_t a, hipEvent_t b) : st(s), start(a), stop(b) {}
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, const Exec& x,
+                         Args... args) {
+  if (x.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, x.st, x.start, x.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, x.st, args...);
+  return hipGetLastError();
+}
 
 // Sizes derived from a validated rlt_config.
 struct Dims {
@@ -107,7 +128,7 @@ hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& 
 // Projects n tokens per sequence into memory entries t0 .. t0+n-1; the encoder outputs of
 // sequence b, token i are at e + (b * e_seq + i) * d (elements).
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
-                          const void* e, int64_t e_seq, int64_t t0, int64_t n, hipStream_t st);
+                          const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st);
 
 // Event timing of selected kernels (owned by a state; see rlt_profile_begin).
 struct Profiler {
@@ -121,8 +142,9 @@ struct Profiler {
   std::vector<Rec> recs;
   size_t used = 0;
   bool on(int kind) const { return (mask >> kind) & 1u; }
-  hipError_t begin(int kind, hipStream_t st, int& ev);
-  hipError_t end(int kind, int ev, double bytes, double flops, hipStream_t st);
+  // If `kind` is profiled, gives x a fresh pair of timing events for its next launch and
+  // records that launch's algorithmic bytes and flops.
+  hipError_t arm(int kind, double bytes, double flops, Exec& x);
   void destroy();
 };
 
@@ -139,21 +161,21 @@ hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, co
 
 // ---- kernel-level entry points used by launch_step -----------------------------------------
 hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, const void* e_t,
-                     int64_t e_ld, hipStream_t st);
+                     int64_t e_ld, const Exec& st);
 hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S, int slot,
-                    hipStream_t st);
+                    const Exec& st);
 hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                   hipStream_t st);
+                   const Exec& st);
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                    hipStream_t st);
+                    const Exec& st);
 // h (+)= A W for the output projections: which = 0 (self-attn O), 1 (cross O), 2 (FFN down).
 // When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h.
 hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P,
                          const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
-                         hipStream_t st);
+                         const Exec& st);
 hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                     hipStream_t st);
+                     const Exec& st);
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      int64_t t, hipStream_t st);
+                      int64_t t, const Exec& st);
 
 }  // namespace rlt

@@ -161,8 +161,7 @@ MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0) {
 }
 
 // ---- kernel timing ---------------------------------------------------------------------------
-hipError_t Profiler::begin(int kind, hipStream_t st, int& ev) {
-  ev = -1;
+hipError_t Profiler::arm(int kind, double bytes, double flops, Exec& x) {
   if (!on(kind)) return hipSuccess;
   while (events.size() < used + 2) {
     hipEvent_t e;
@@ -170,15 +169,11 @@ hipError_t Profiler::begin(int kind, hipStream_t st, int& ev) {
     if (err != hipSuccess) return err;
     events.push_back(e);
   }
-  ev = (int)used;
+  x.start = events[used];
+  x.stop = events[used + 1];
+  recs.push_back(Rec{kind, (int)used, bytes, flops});
   used += 2;
-  return hipEventRecord(events[ev], st);
-}
-
-hipError_t Profiler::end(int kind, int ev, double bytes, double flops, hipStream_t st) {
-  if (ev < 0) return hipSuccess;
-  recs.push_back(Rec{kind, ev, bytes, flops});
-  return hipEventRecord(events[ev + 1], st);
+  return hipSuccess;
 }
 
 void Profiler::destroy() {
@@ -196,38 +191,38 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
                        const MemBufs& M, const void* e_t, int64_t e_ld, int64_t t0, float* out,
                        int64_t out_ld, hipStream_t st, Profiler* prof) {
   hipError_t e;
-  int ev = -1;
   const double b = B, d = D.d, F = D.F, es = (double)D.es;
   const double act32 = b * d * 4, actd = b * d * es;
-#define RLT_TIMED(kind, bytes, flops, call)                                   \
-  do {                                                                        \
-    if (prof && (e = prof->begin(kind, st, ev)) != hipSuccess) return e;      \
-    if ((e = (call)) != hipSuccess) return e;                                 \
-    if (prof && (e = prof->end(kind, ev, bytes, flops, st)) != hipSuccess) return e; \
+  // `call` launches one kernel on Exec x.
+#define RLT_TIMED(kind, bytes, flops, call)                                      \
+  do {                                                                           \
+    Exec x(st);                                                                  \
+    if (prof && (e = prof->arm(kind, bytes, flops, x)) != hipSuccess) return e;  \
+    if ((e = (call)) != hipSuccess) return e;                                    \
   } while (0)
   RLT_TIMED(RLT_K_GATE, 2 * d * d * es + actd + 2 * act32, 4 * b * d * d,
-            gemm_gate(D, B, P, S, e_t, e_ld, st));
+            gemm_gate(D, B, P, S, e_t, e_ld, x));
   const int slot = (int)(t0 % D.W);
   const int n_valid = (int)(t0 + 1 < D.W ? t0 + 1 : D.W);
   const double t = (double)(t0 + 1);
   for (int l = 0; l < D.L; ++l) {
     const bool last = l == D.L - 1;
     RLT_TIMED(RLT_K_QKV, 3 * d * d * es + 2 * act32 + 2 * actd, 6 * b * d * d,
-              gemm_qkv(D, B, l, P, S, slot, st));
+              gemm_qkv(D, B, l, P, S, slot, x));
     RLT_TIMED(RLT_K_SELF_ATTN, n_valid * b * 2 * d * es + act32 + actd, 4 * b * d * n_valid,
-              attn_self(D, B, l, S, n_valid, st));
+              attn_self(D, B, l, S, n_valid, x));
     RLT_TIMED(RLT_K_SELF_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
-              gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, st));
-    RLT_TIMED(RLT_K_CROSS_Q, d * d * es + 2 * act32, 2 * b * d * d, gemm_cq(D, B, l, P, S, st));
+              gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, x));
+    RLT_TIMED(RLT_K_CROSS_Q, d * d * es + 2 * act32, 2 * b * d * d, gemm_cq(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_CROSS_ATTN, t * b * 2 * d * es + act32 + actd, 4 * b * d * t,
-              attn_cross(D, B, l, S, M, t0 + 1, st));
+              attn_cross(D, B, l, S, M, t0 + 1, x));
     RLT_TIMED(RLT_K_CROSS_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
-              gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, st));
+              gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, x));
     RLT_TIMED(RLT_K_FFN_UP, 2 * F * d * es + act32 + b * F * es, 4 * b * d * F,
-              gemm_w13(D, B, l, P, S, st));
+              gemm_w13(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_FFN_DOWN, F * d * es + b * F * es + 2 * act32 + (last && out ? act32 : 0),
               2 * b * d * F,
-              gemm_residual(D, B, l, 2, P, S, last, last ? out : nullptr, out_ld, st));
+              gemm_residual(D, B, l, 2, P, S, last, last ? out : nullptr, out_ld, x));
   }
 #undef RLT_TIMED
   return hipSuccess;
