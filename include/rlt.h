@@ -217,11 +217,13 @@ typedef struct rlt_kernel_stats {
   double flops;      /* algorithmic floating-point operations                            */
 } rlt_kernel_stats;
 
-/* Starts timing, for this state, every launch of the kernels whose bit (1 << rlt_kernel) is
- * set in `mask`: each timed launch records a pair of HIP events at the start and at the end of
- * its kernel (hipExtLaunchKernel), on the stream it runs on; no extra packets are queued.
+/* Starts timing, for this state, launches of the kernels whose bit (1 << rlt_kernel) is set in
+ * `mask`: each timed launch records a pair of HIP events at the start and at the end of its
+ * kernel (hipExtLaunchKernel), on the stream it runs on; no extra packets are queued. Decoder
+ * launches are timed in the steps of tokens t (0-based position before the step) with
+ * t % token_stride == 0 (token_stride >= 1; 1 = every step), memory projections always.
  * Events are pooled by the state and kept until rlt_state_destroy. */
-rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask);
+rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride);
 
 /* Stops timing, waits for the recorded events and writes RLT_K_COUNT entries to `out`
  * (host array, indexed by rlt_kernel). */

@@ -83,7 +83,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_memory_create": (c_int32, [P, c_int32, c_int64, P, c_size_t, POINTER(P)]),
         "rlt_memory_length": (c_int64, [P]),
         "rlt_memory_reset": (c_int32, [P]),
-        "rlt_profile_begin": (c_int32, [P, ctypes.c_uint32]),
+        "rlt_profile_begin": (c_int32, [P, ctypes.c_uint32, c_int32]),
         "rlt_profile_end": (c_int32, [P, POINTER(rlt_kernel_stats)]),
         "rlt_memory_destroy": (None, [P]),
         "rlt_memproj": (c_int32, [P, P, P, c_int64, c_int64, P]),
@@ -192,11 +192,12 @@ class State:
     def reset(self, stream=None):
         _check(self.lib.rlt_state_reset(self.handle, _stream(stream)))
 
-    def profile_begin(self, kernels=KERNEL_NAMES):
+    def profile_begin(self, kernels=KERNEL_NAMES, token_stride: int = 1):
+        """Time launches of `kernels` in the steps of every token_stride-th token."""
         mask = 0
         for k in kernels:
             mask |= 1 << KERNEL_NAMES.index(k)
-        _check(self.lib.rlt_profile_begin(self.handle, mask))
+        _check(self.lib.rlt_profile_begin(self.handle, mask, int(token_stride)))
 
     def profile_end(self) -> dict:
         """{kernel name: {launches, total_ms, bytes, flops}} for the timed kernels."""

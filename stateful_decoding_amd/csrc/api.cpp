@@ -427,7 +427,8 @@ static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_
       const char* et = eb + ((size_t)b0 * e_ld + (size_t)i * D.d) * D.es;
       float* o = out ? out + (size_t)b0 * out_ld + (size_t)i * D.d : nullptr;
       err = launch_step(D, rows, model->P, Sg[g], Mg[g], et, e_ld, t0, o, out_ld,
-                        state->aux[g] ? state->aux[g] : st, &state->prof);
+                        state->aux[g] ? state->aux[g] : st,
+                        t0 % state->prof.stride == 0 ? &state->prof : nullptr);
     }
   }
   for (int g = 0; g < ng && err == hipSuccess; ++g) {
@@ -502,9 +503,11 @@ rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory
   return ok();
 }
 
-rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask) {
+rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride) {
   if (!state) return fail(RLT_ERR_ARG, "state is NULL");
   if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");
+  if (token_stride < 1) return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", token_stride);
+  state->prof.stride = token_stride;
   state->prof.mask = mask;
   state->prof.recs.clear();
   state->prof.used = 0;

@@ -138,6 +138,7 @@ struct Profiler {
     double bytes, flops;
   };
   uint32_t mask = 0;
+  int64_t stride = 1;  // decoder-step launches are timed for tokens t0 with t0 % stride == 0
   std::vector<hipEvent_t> events;  // pool, reused across sessions
   std::vector<Rec> recs;
   size_t used = 0;

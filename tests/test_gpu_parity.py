@@ -152,6 +152,32 @@ def test_errors_are_reported_before_any_work():
         sd.rlt_run_sequence(g.model, other, g.mem, torch.zeros(3, 1, cfg.d, dtype=torch.bfloat16,
                                                                  device="cuda"))
     assert ex.value.status_name == "RLT_ERR_SHAPE"
+    with pytest.raises(sd.RLTError) as ex:  # timing stride must be positive
+        g.state.profile_begin(["cross_attn"], token_stride=0)
+    assert ex.value.status_name == "RLT_ERR_ARG"
+
+
+def test_kernel_timing_counts_sampled_launches():
+    """Timed launches: every kind in the steps of tokens t % stride == 0, bytes as stated."""
+    cfg = cfg_small(n_layers=2, window=3)
+    B, T = 5, 11
+    p, e = inputs(cfg, B, T)
+    g = GpuRun(cfg, p, B, T)
+    g.state.profile_begin(token_stride=4)
+    g.run(e)
+    prof = g.state.profile_end()
+    steps = len(range(0, T, 4))  # tokens 0, 4, 8
+    assert prof["memproj"]["launches"] == 1
+    assert prof["gate"]["launches"] == steps
+    for k in ("qkv", "self_attn", "self_out", "cross_q", "cross_attn", "cross_out", "ffn_up",
+              "ffn_down"):
+        assert prof[k]["launches"] == steps * cfg.n_layers, k
+        assert prof[k]["total_ms"] > 0
+    es = 2 if cfg.dtype == "bf16" else 4
+    # memory attention reads t entries of K and V per sequence and layer at token t (1-based)
+    kv = sum(B * (t + 1) * 2 * cfg.d * es for t in range(0, T, 4)) * cfg.n_layers
+    act = steps * cfg.n_layers * B * cfg.d * (4 + es)
+    assert prof["cross_attn"]["bytes"] == pytest.approx(kv + act)
 
 
 # --- full-size workloads, sampled sequences ---------------------------------------------------
