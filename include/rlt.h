@@ -177,6 +177,32 @@ rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_
 rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory* mem,
                             const void* e, int64_t n, float* s_traj, void* stream);
 
+/* --- token-parallel pass for alpha = 0 -------------------------------------------------- */
+/* With feedback scale alpha = 0 the gated merge does not read s_{t-1} (h_t = g(e_t) * e_t),
+ * so the decoder blocks couple tokens only through causal attention - the window of W-1
+ * previous tokens of each layer and the memory prefix 1..t - and all n tokens can run layer by
+ * layer at once, as the feedback-off control of the independent evaluation did ("RLT Runs 96
+ * Blocks Per Token With Recurrent State, No Resets", "Three design principles and their
+ * caveats": a parallel decoder pass is not equivalent to the recurrence unless the feedback is
+ * off; "16 per-token recurrence, no quality gain": the feedback-off variant trained at 66.0K
+ * tokens/s against 8.4K for the recurrence). */
+
+/* Device workspace bytes of rlt_run_parallel for B sequences and n tokens (0 if invalid). */
+size_t rlt_parallel_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
+
+/* Same contract as rlt_run_sequence from a reset state (position 0): projects the memory of
+ * tokens 1..n it does not hold yet, writes every s_t to s_traj [B][n][d] float32 unless NULL,
+ * and leaves the state as n decoder steps would (s_n, the last W-1 keys/values per layer,
+ * position n), so decoding can continue with rlt_decoder_step. Results equal the recurrent
+ * path up to rounding (the projections run as large MFMA GEMMs on RMS-normalised bf16 rows and
+ * the attentions as causal flash attention with bf16 queries). Requires alpha == 0
+ * (RLT_ERR_ARG), dtype bf16 (RLT_ERR_DTYPE), position 0 (RLT_ERR_ARG), n <= memory capacity
+ * (RLT_ERR_CAPACITY) and `ws` (device, 256-byte aligned, >= rlt_parallel_ws_bytes; its contents
+ * are scratch, owned by the caller) (RLT_ERR_CAPACITY). */
+rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                            const void* e, int64_t n, float* s_traj, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
 
 /* Copies the state to caller buffers in canonical order and waits for the stream:
@@ -207,7 +233,11 @@ typedef enum rlt_kernel {
   RLT_K_FFN_UP = 7,      /* RMSNorm + W1/W3 projection + SiLU product                     */
   RLT_K_FFN_DOWN = 8,    /* W2 projection + residual                                      */
   RLT_K_MEMPROJ = 9,     /* memory projection                                             */
-  RLT_K_COUNT = 10
+  RLT_K_PAR_GEMM = 10,   /* token-parallel pass: every projection (all rows at once)      */
+  RLT_K_PAR_SELF = 11,   /* token-parallel pass: window attention                          */
+  RLT_K_PAR_CROSS = 12,  /* token-parallel pass: memory-prefix attention                   */
+  RLT_K_PAR_OTHER = 13,  /* token-parallel pass: RMSNorm rows, ring hand-off, final s      */
+  RLT_K_COUNT = 14
 } rlt_kernel;
 
 typedef struct rlt_kernel_stats {

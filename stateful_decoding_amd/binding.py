@@ -38,7 +38,8 @@ class rlt_weights(ctypes.Structure):
 
 
 KERNEL_NAMES = ("gate", "qkv", "self_attn", "self_out", "cross_q", "cross_attn", "cross_out",
-                "ffn_up", "ffn_down", "memproj")
+                "ffn_up", "ffn_down", "memproj", "par_gemm", "par_self_attn", "par_cross_attn",
+                "par_other")
 
 
 class rlt_kernel_stats(ctypes.Structure):
@@ -89,6 +90,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_memproj": (c_int32, [P, P, P, c_int64, c_int64, P]),
         "rlt_decoder_step": (c_int32, [P, P, P, P, P, P]),
         "rlt_run_sequence": (c_int32, [P, P, P, P, c_int64, P, P]),
+        "rlt_parallel_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
+        "rlt_run_parallel": (c_int32, [P, P, P, P, c_int64, P, P, c_size_t, P]),
         "rlt_state_export": (c_int32, [P, P, P, P, POINTER(c_int32), POINTER(c_int64),
                                        POINTER(c_uint64), P]),
         "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
@@ -286,6 +289,30 @@ def rlt_run_sequence(model: Model, state: State, mem: Memory, e: torch.Tensor,
         _need(s_traj, (state.batch, n, model.cfg.d), torch.float32, "s_traj")
     _check(model.lib.rlt_run_sequence(model.handle, state.handle, mem.handle, e.data_ptr(), int(n),
                                       _ptr(s_traj), _stream(stream)))
+
+
+def parallel_workspace(model: Model, batch: int, n: int) -> torch.Tensor:
+    """Device workspace for rlt_run_parallel over n tokens of `batch` sequences."""
+    nbytes = model.lib.rlt_parallel_ws_bytes(byref(model.cfg), int(batch), int(n))
+    if nbytes == 0:
+        raise RLTError(2, f"invalid batch {batch} or n {n} for the token-parallel pass")
+    return _device_buffer(nbytes, model.ws.device)
+
+
+def rlt_run_parallel(model: Model, state: State, mem: Memory, e: torch.Tensor,
+                     s_traj: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                     stream=None):
+    """Token-parallel pass over e [B, n, d] from a reset state (alpha = 0 models, bf16);
+    optional s_traj [B, n, d] float32; `ws` from parallel_workspace (allocated if None)."""
+    n = e.shape[1]
+    _need(e, (state.batch, n, model.cfg.d), model.dtype, "e")
+    if s_traj is not None:
+        _need(s_traj, (state.batch, n, model.cfg.d), torch.float32, "s_traj")
+    if ws is None:
+        ws = parallel_workspace(model, state.batch, n)
+    _check(model.lib.rlt_run_parallel(model.handle, state.handle, mem.handle, e.data_ptr(),
+                                      int(n), _ptr(s_traj), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def rlt_state_export(state: State, stream=None):

@@ -503,6 +503,57 @@ rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory
   return ok();
 }
 
+size_t rlt_parallel_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
+  if (check_config(cfg) != RLT_OK || !valid_batch(batch) || n < 1 || n > kMaxCapacity ||
+      (int64_t)batch * n > INT32_MAX / 2)
+    return 0;
+  return par_layout(dims_of(*cfg), batch, n).total;
+}
+
+rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                            const void* e, int64_t n, float* s_traj, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (rlt_status s = check_step_args(model, state, mem)) return s;
+  const Dims& D = model->D;
+  if (D.alpha != 0.f)
+    return fail(RLT_ERR_ARG, "the token-parallel pass needs alpha = 0 (the model has %g)",
+                (double)D.alpha);
+  if (D.dtype != RLT_BF16) return fail(RLT_ERR_DTYPE, "the token-parallel pass is bf16 only");
+  if (!e || !ws) return fail(RLT_ERR_ARG, "e and ws must be non-NULL");
+  if (n < 1) return fail(RLT_ERR_ARG, "n must be >= 1");
+  if (!aligned16(e) || (s_traj && !aligned16(s_traj)) || !aligned(ws))
+    return fail(RLT_ERR_ARG, "e and s_traj must be 16-byte aligned, ws 256-byte aligned");
+  if (state->t != 0)
+    return fail(RLT_ERR_ARG, "the token-parallel pass starts from a reset state (position %lld)",
+                (long long)state->t);
+  const int B = state->B;
+  if ((int64_t)B * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "B * n too large");
+  const size_t need = par_layout(D, B, n).total;
+  if (ws_bytes < need)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  if (n > mem->M.capacity)
+    return fail(RLT_ERR_CAPACITY, "n = %lld exceeds memory capacity %lld", (long long)n,
+                (long long)mem->M.capacity);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (mem->len < n) {
+    const int64_t first = mem->len, cnt = n - first;
+    const void* e_first = static_cast<const char*>(e) + (size_t)first * D.d * D.es;
+    const double rows = (double)B * cnt, d = D.d, es = (double)D.es;
+    Exec x(st);
+    err = state->prof.arm(RLT_K_MEMPROJ, es * (rows * d + D.G * 2 * d * d + rows * D.G * 2 * d),
+                          2 * rows * d * D.G * 2 * d, x);
+    if (err == hipSuccess) err = launch_memproj(D, B, model->P, mem->M, e_first, n, first, cnt, x);
+    if (err != hipSuccess) return hip_fail(err, "memory projection");
+    mem->len = n;
+  }
+  err = launch_parallel(D, B, model->P, state->S, mem->M, e, n, n, s_traj, n * D.d, ws, st,
+                        &state->prof);
+  if (err != hipSuccess) return hip_fail(err, "token-parallel pass");
+  state->t = n;
+  return ok();
+}
+
 rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride) {
   if (!state) return fail(RLT_ERR_ARG, "state is NULL");
   if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");

@@ -155,6 +155,22 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
                        const MemBufs& M, const void* e_t, int64_t e_ld, int64_t t0,
                        float* out, int64_t out_ld, hipStream_t st, Profiler* prof);
 
+// Workspace of the token-parallel pass (alpha = 0) over n tokens of B sequences; byte offsets.
+//   h [B n][d] f32 residual stream; a [R][d] bf16 normed operand (fragment order);
+//   q, k, v [B][H][n][hd] bf16; o [R][d], act [R][F] bf16 (fragment order); R = B n rounded up
+struct ParLayout {
+  size_t h, a, q, k, v, o, act, total;
+};
+ParLayout par_layout(const Dims& D, int B, int64_t n);
+
+// The token-parallel pass: memory entries 0..n-1 must be projected; the state must be at
+// position 0 (reset). Writes s rows of every token to out (when not NULL; row (b, i) at
+// out + b * out_seq + i * d), leaves s = s_n and the ring as n recurrent steps would. bf16 only.
+hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBufs& S,
+                           const MemBufs& M, const void* e, int64_t e_seq, int64_t n,
+                           float* out, int64_t out_seq, void* ws, hipStream_t st,
+                           Profiler* prof);
+
 hipError_t launch_export(const Dims& D, int B, const StateBufs& S, int64_t t, float* s,
                          void* k, void* v, hipStream_t st);
 hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,

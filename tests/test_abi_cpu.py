@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     raw = ctypes.CDLL(sd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -74,6 +74,12 @@ def test_buffer_sizes(lib):
     assert lib.rlt_memory_bytes(byref(c), 256, 0) == 0
     assert lib.rlt_memory_bytes(byref(c), 256, (1 << 20) + 1) == 0
     assert lib.rlt_state_bytes(byref(c), 0) == 0
+    # token-parallel workspace: f32 residual stream + bf16 operands per token (at least)
+    par = lib.rlt_parallel_ws_bytes(byref(c), 16, 8192)
+    rows = 16 * 8192
+    assert par >= rows * d * 4 + rows * (5 * d + F) * 2
+    assert lib.rlt_parallel_ws_bytes(byref(c), 16, 0) == 0
+    assert lib.rlt_parallel_ws_bytes(byref(c), 0, 8) == 0
 
 
 def test_null_arguments_rejected_without_gpu(lib):
@@ -85,6 +91,7 @@ def test_null_arguments_rejected_without_gpu(lib):
     assert lib.rlt_memproj(None, None, None, 0, 1, None) == 1
     assert lib.rlt_decoder_step(None, None, None, None, None, None) == 1
     assert lib.rlt_run_sequence(None, None, None, None, 1, None, None) == 1
+    assert lib.rlt_run_parallel(None, None, None, None, 1, None, None, 0, None) == 1
     assert lib.rlt_state_export(None, None, None, None, None, None, None, None) == 1
     assert lib.rlt_state_import(None, None, None, None, 0, 0, None) == 1
     assert lib.rlt_state_reset(None, None) == 1
