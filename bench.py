@@ -112,7 +112,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="s140m_bf16")
+    ap.add_argument("--mode", choices=("recurrent", "parallel"), default="recurrent",
+                    help="recurrent: rlt_run_sequence (the headline); parallel: the token-parallel "
+                         "pass for alpha = 0 (rlt_run_parallel)")
+    ap.add_argument("--workload", default=None,
+                    help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-stride", type=int, default=16,
@@ -146,6 +150,8 @@ def main():
     import stateful_decoding_amd as sd
     from synth import CONFIGS, make_encoder_outputs, make_params
 
+    if args.workload is None:
+        args.workload = "long_a0_bf16" if args.mode == "parallel" else "s140m_bf16"
     cfg = CONFIGS[args.workload]
     B, T = cfg.batch, cfg.seq_len
     torch.cuda.set_device(0)
@@ -162,6 +168,8 @@ def main():
     mem = sd.Memory(model, B, T)
     traj = torch.empty(B, T, cfg.d, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.mode == "parallel":
+        return bench_parallel(args, cfg, params, model, state, mem, e, traj, stream)
 
     def one_step():
         state.reset(stream)
@@ -222,6 +230,81 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, params, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+PAR_KINDS = ("par_gemm", "par_self_attn", "par_cross_attn", "par_other", "memproj")
+
+
+def bench_parallel(args, cfg, params, model, state, mem, e, traj, stream):
+    """The token-parallel pass for alpha = 0: one step is one rlt_run_parallel (memory
+    projection + all layers over all B x T tokens) on a reset state and emptied memory."""
+    import torch
+
+    import stateful_decoding_amd as sd
+
+    if cfg.alpha != 0.0:
+        sys.exit(f"--mode parallel needs an alpha = 0 workload ({cfg.name} has {cfg.alpha})")
+    B, T = cfg.batch, cfg.seq_len
+    ws = sd.parallel_workspace(model, B, T)
+
+    def one_step():
+        state.reset(stream)
+        mem.reset()
+        sd.rlt_run_parallel(model, state, mem, e, traj, ws, stream)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    state.profile_begin(list(PAR_KINDS))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    prof = state.profile_end()
+    assert bool(torch.isfinite(traj).all()), "non-finite decoder output"
+    secs = ms_total / 1e3
+    # per kind: ideal time at the HBM or MFMA peak, whichever binds
+    ideal = 0.0
+    for v in prof.values():
+        ideal += max(v["bytes"] / HBM_PEAK, v["flops"] / BF16_PEAK) / args.steps
+    dom_name, dom = max(prof.items(), key=lambda kv: kv[1]["total_ms"])
+    mfma = dom["flops"] / BF16_PEAK > dom["bytes"] / HBM_PEAK
+    rate = (dom["flops"] if mfma else dom["bytes"]) / (dom["total_ms"] / 1e3)
+    peak = BF16_PEAK if mfma else HBM_PEAK
+    kern = {"par_gemm": "k_gemm_rows (all projections)", "par_cross_attn": "k_flash (memory prefix)",
+            "par_self_attn": "k_flash (window)", "par_other": "k_norm_rows / hand-off",
+            "memproj": "k_gemm_tokens (memory projection)"}[dom_name]
+    out = {
+        "metric": "RLT token-parallel decoder pass at alpha = 0, tokens/sec (B seqs x T) on 1 "
+                  "MI355X; % of the pass roofline",
+        "value": round(B * T * args.steps / secs, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_total / args.steps, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "mode": "parallel", "batch": B, "seq_len": T, "d": cfg.d,
+                   "heads": cfg.n_heads, "head_dim": cfg.head_dim, "decoder_blocks": cfg.n_layers,
+                   "ffn": cfg.ffn, "window": cfg.window, "memory_groups": cfg.n_groups,
+                   "alpha": cfg.alpha, "inputs": "e_t ~ N(0,1), weights ~ N(0,0.02), seed 0"},
+        "roofline": {"bound": "mfma" if mfma else "hbm", "kernel": kern,
+                     "achieved": round(rate / 1e12, 1) if mfma else round(rate / 1e9, 1),
+                     "peak": (BF16_PEAK / 1e12) if mfma else (HBM_PEAK / 1e9),
+                     "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(rate / peak, 4),
+                     "traffic": None, "launches": dom["launches"],
+                     "avg_launch_us": round(dom["total_ms"] * 1e3 / dom["launches"], 2)},
+        "step_roofline": {"ideal_s": round(ideal, 5), "measured_s": round(secs / args.steps, 5),
+                          "frac": round(ideal / (secs / args.steps), 4),
+                          "peaks": "HBM 8.0 TB/s, bf16 MFMA 2.5 PFLOP/s, per kernel kind"},
+        "kernel_ms_per_step": {k: round(v["total_ms"] / args.steps, 2) for k, v in prof.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, params, args.cpu_seconds, n_seqs=4)
     print(json.dumps(out), flush=True)
 
 

@@ -216,12 +216,12 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
 
 // ---- causal flash attention, all queries of a (sequence, head) block at once ----------------------
 // A workgroup takes 64 consecutive queries of one (sequence, head); wave w owns queries
-// q0 + 16 w .. + 15. Key blocks of 32 are staged in LDS (K as rows, V transposed) and each wave
+// q0 + 16 w .. + 15. Key blocks of 64 are staged in LDS (K as rows, V transposed) and each wave
 // computes S^T = K Q^T with MFMA, so a lane holds the scores of one query (lane % 16) against
 // keys 4 (lane / 16) + i of each 16-key tile. The softmax is online (running max and sum per
 // query, in fp32). For O^T = V^T P^T the MFMA's k index is taken in the order the lane already
-// holds P (keys 4 g + [0, 4) of tile 0, then of tile 1, g = lane / 16), and V^T is read from
-// LDS in that same order, so P never moves between lanes.
+// holds P (per 32 keys: keys 4 g + [0, 4) of the first 16-key tile, then of the second,
+// g = lane / 16), and V^T is read from LDS in that same order, so P never moves between lanes.
 // Masks: the key j of query t is used when j <= t, and for the window also j > t - W.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
                                                     const bf16* __restrict__ V,
                                                     int64_t kv_bh_stride, int n, int H, int W,
                                                     int qblocks, float scale, bf16* __restrict__ o) {
-  constexpr int KB = 32, QB = 64, KS = HD / 32, VT = HD / 16;
+  constexpr int KB = 64, QB = 64, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
   __shared__ __attribute__((aligned(16))) bf16 ks[KB][HD + 8];
   __shared__ __attribute__((aligned(16))) bf16 vt[HD][KB + 8];
   // heavy blocks (late queries) first
@@ -254,61 +254,91 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
 
   const int kend = min(n, q0 + QB);                      // keys this block can use
   const int kbeg = W > 0 ? max(0, q0 - W + 1) / KB * KB : 0;
+  // staging: thread -> CH chunks of (key, 8 dims), consecutive threads on consecutive keys, so
+  // a wave's transposed V writes fill whole LDS rows without bank conflicts; the next block's
+  // chunks are loaded into registers while the current block is multiplied
+  constexpr int CH = KB * HD / 8 / kThreads;
+  static_assert(CH >= 1 && KB * HD / 8 == CH * kThreads, "staging split");
+  u32x4 kr[CH], vr[CH];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int c = tid + u * kThreads;
+      const int key = k0 + c % KB, dd = (c / KB) * 8;
+      kr[u] = vr[u] = u32x4{0, 0, 0, 0};
+      if (key < kend) {
+        kr[u] = ld16(Kb + (int64_t)key * HD + dd);
+        vr[u] = ld16(Vb + (int64_t)key * HD + dd);
+      }
+    }
+  };
+  // scores go through exp2: fold log2(e) into the scale
+  const float c2 = scale * 1.4426950408889634f;
+  if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += KB) {
     __syncthreads();  // the previous block's LDS reads are done
-    // stage 32 keys: thread -> (key, 8 dims)
-    for (int c = tid; c < KB * HD / 8; c += kThreads) {
-      const int kk = c / (HD / 8), dd = (c % (HD / 8)) * 8;
-      const int key = k0 + kk;
-      u32x4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
-      if (key < kend) {
-        kr = ld16(Kb + (int64_t)key * HD + dd);
-        vr = ld16(Vb + (int64_t)key * HD + dd);
-      }
-      *reinterpret_cast<u32x4*>(&ks[kk][dd]) = kr;
-      const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int c = tid + u * kThreads;
+      const int kk = c % KB, dd = (c / KB) * 8;
+      *reinterpret_cast<u32x4*>(&ks[kk][dd]) = kr[u];
+      const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[u]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) vt[dd + i][kk] = v8[i];
     }
     __syncthreads();
-    // S^T for the two 16-key tiles
-    f32x4 st[2];
+    if (k0 + KB < kend) fetch(k0 + KB);
+    // S^T for the NT 16-key tiles
+    f32x4 st[NT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NT; ++j) {
       st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        Frag<bf16> kf;
-        kf.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * j + (lane & 15)][32 * s + 8 * g]));
-        st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[s].v, st[j], 0, 0, 0);
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * j + (lane & 15)][32 * s + 8 * g]));
+        st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s].v, st[j], 0, 0, 0);
       }
     }
-    // mask, scale, block max of this lane's query
-    float p[8];
+    // scale (and mask, unless every key of the block is valid for every query of the wave:
+    // all keys exist, none is later than the wave's first query, none falls out of the window
+    // of its last)
+    const bool interior = k0 + KB <= kend && k0 + KB - 1 <= qw && (W <= 0 || k0 > qw + 15 - W);
+    float p[4 * NT];
     float mx = -INFINITY;
+    if (interior) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * j + 4 * g + i;
-        const bool ok = key <= tq && key < kend && (W <= 0 || key > tq - W);
-        const float sc = ok ? st[j][i] * scale : -INFINITY;
-        p[4 * j + i] = sc;
-        mx = fmaxf(mx, sc);
-      }
+        for (int i = 0; i < 4; ++i) {
+          p[4 * j + i] = st[j][i] * c2;
+          mx = fmaxf(mx, p[4 * j + i]);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * j + 4 * g + i;
+          const bool ok = key <= tq && key < kend && (W <= 0 || key > tq - W);
+          p[4 * j + i] = ok ? st[j][i] * c2 : -INFINITY;
+          mx = fmaxf(mx, p[4 * j + i]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     // a query with no key yet keeps m = -inf, l = 0 and adds zero weights (every wave runs the
-    // same MFMAs, so no lane leaves the loop early)
+    // same MFMAs, so no lane leaves the loop early); exp2(-inf) = 0
     const float mn = fmaxf(m, mx);
-    const float alpha = m == -INFINITY ? 0.f : __expf(m - mn);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - ms);
     float ps = 0.f;
-    bf16x8 pb;
+    bf16x8 pb[PK];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = p[e] == -INFINITY ? 0.f : __expf(p[e] - mn);
+    for (int e = 0; e < 4 * NT; ++e) {
+      const float x = __builtin_amdgcn_exp2f(p[e] - ms);
       ps += x;
-      pb[e] = (bf16)x;
+      pb[e / 8][e % 8] = (bf16)x;
     }
     ps += __shfl_xor(ps, 16, kWave);
     ps += __shfl_xor(ps, 32, kWave);
@@ -317,13 +347,17 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
 #pragma unroll
     for (int c = 0; c < VT; ++c) {
       acc[c] *= alpha;
-      // V^T rows 16 c + lane % 16, keys in the lane's P order
-      const bf16* vr = &vt[16 * c + (lane & 15)][0];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-      const u32x4 raw = {lo.x, lo.y, hi.x, hi.y};
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw), pb,
-                                                       acc[c], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < PK; ++h) {
+        // V^T row 16 c + lane % 16, the 8 keys of this lane's P order in k-step h: tile 2h
+        // keys 4g..4g+3, then tile 2h+1 keys 4g..4g+3
+        const bf16* vp = &vt[16 * c + (lane & 15)][32 * h];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 + 4 * g);
+        const u32x4 raw = {lo.x, lo.y, hi.x, hi.y};
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw), pb[h],
+                                                         acc[c], 0, 0, 0);
+      }
     }
   }
   if (tq >= n) return;
@@ -406,8 +440,8 @@ struct ParCtx {
 };
 
 template <int FM, int FN, class AL, class EP>
-static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
-                            const AL& al, const EP& ep, double out_bytes) {
+static hipError_t gemm_rows_t(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
+                              const AL& al, const EP& ep, double out_bytes) {
   constexpr int BM = 32 * FM, BN = 32 * FN;
   if (N % BN != 0 || K % 32 != 0) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)((R + BM - 1) / BM) * (N / BN);
@@ -418,6 +452,15 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
   if (e != hipSuccess) return e;
   return launch(k_gemm_rows<FM, FN, AL, EP>, dim3((unsigned)blocks), dim3(kThreads), x, N, K / 32,
                 wks, static_cast<const bf16*>(Wt), al, ep);
+}
+
+// Largest register tile the shape allows: 64 x 64 per wave (128 x 128 per block) when N is a
+// multiple of 128, else 32 x 32 per wave.
+template <class AL, class EP>
+static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
+                            const AL& al, const EP& ep, double out_bytes) {
+  if (N % 128 == 0) return gemm_rows_t<4, 4>(c, R, N, K, wks, Wt, al, ep, out_bytes);
+  return gemm_rows_t<2, 2>(c, R, N, K, wks, Wt, al, ep, out_bytes);
 }
 
 // W > 0: window attention (keys t-W+1..t of this layer); W = 0: memory prefix 0..t.
@@ -488,7 +531,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     PTokens al{eb, e_seq, n, d, R};
     PGate ep;
     ep.h = h; ep.e = eb; ep.e_seq = e_seq; ep.b = P.b_gate; ep.n = n; ep.d = d; ep.R = R;
-    if ((err = gemm_rows<2, 2>(c, R, d, d, 2 * d / 32, P.w_gate_t, al, ep, Rd * 6)) != hipSuccess)
+    if ((err = gemm_rows(c, R, d, d, 2 * d / 32, P.w_gate_t, al, ep, Rd * 6)) != hipSuccess)
       return err;
   }
   const int keep = n < D.W - 1 ? n : D.W - 1;
@@ -501,7 +544,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       PHeads ep{{}, q, kk, vv, n, d, H, hd, R};
       const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
-      if ((err = gemm_rows<2, 2>(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
+      if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
           hipSuccess)
         return err;
     }
@@ -520,7 +563,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       PResidual ep{{}, h, nullptr, 0, n, d, R};
       const bf16* Wo = static_cast<const bf16*>(P.wo_t) + wdd;
-      if ((err = gemm_rows<2, 2>(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8)) !=
           hipSuccess)
         return err;
     }
@@ -529,7 +572,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       PHeads ep{{}, q, nullptr, nullptr, n, d, H, hd, R};
       const bf16* Wc = static_cast<const bf16*>(P.wcq_t) + wdd;
-      if ((err = gemm_rows<2, 2>(c, R, d, d, d / 32, Wc, PA{a, d / 32, R}, ep, Rd * 2)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wc, PA{a, d / 32, R}, ep, Rd * 2)) !=
           hipSuccess)
         return err;
     }
@@ -544,7 +587,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       PResidual ep{{}, h, nullptr, 0, n, d, R};
       const bf16* Wco = static_cast<const bf16*>(P.wco_t) + wdd;
-      if ((err = gemm_rows<2, 2>(c, R, d, d, d / 32, Wco, PA{o, d / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wco, PA{o, d / 32, R}, ep, Rd * 8)) !=
           hipSuccess)
         return err;
     }
@@ -553,14 +596,14 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       PSilu ep{act, F, R};
       const bf16* W13 = static_cast<const bf16*>(P.w13_t) + (int64_t)l * 2 * F * d;
-      if ((err = gemm_rows<2, 2>(c, R, 2 * F, d, d / 32, W13, PA{a, d / 32, R}, ep,
+      if ((err = gemm_rows(c, R, 2 * F, d, d / 32, W13, PA{a, d / 32, R}, ep,
                                  (double)R * F * 2)) != hipSuccess)
         return err;
     }
     {
       PResidual ep{{}, h, last ? out : nullptr, out_seq, n, d, R};
       const bf16* W2 = static_cast<const bf16*>(P.w2_t) + (int64_t)l * d * F;
-      if ((err = gemm_rows<2, 2>(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep,
+      if ((err = gemm_rows(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep,
                                  Rd * (last && out ? 12 : 8))) != hipSuccess)
         return err;
     }
