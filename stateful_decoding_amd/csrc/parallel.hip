@@ -16,6 +16,8 @@
 // pairs, so they are large MFMA contractions rather than weight-streaming ones. bf16 only.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -86,6 +88,78 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rows(int N, int ksteps, int w
       for (int j = 0; j < FN; ++j) mfma_16x16x32(acc[i][j], a[i], b[j]);
   }
   ep.template tile<FM, FN>(acc, rw + (lane >> 4) * 4, cw, lane);
+}
+
+// The same product staged through LDS for operands in fragment order: a 128 x 128 block of 4
+// waves (64 x 64 each) fetches every k-step's 8 A and 8 B fragments once (16 KB, one 16-byte
+// load per thread and operand pair), into one of two LDS buffers while the other is multiplied;
+// waves then read their 4 + 4 fragments from LDS. One barrier per k-step.
+template <class EP>
+__global__ __launch_bounds__(kThreads) void k_gemm_lds(int N, int ksteps, const bf16* __restrict__ A,
+                                                     int R, const bf16* __restrict__ Wt, EP ep) {
+  constexpr int FM = 4, FN = 4, BM = 128, BN = 128;
+  __shared__ __attribute__((aligned(16))) u32x4 as[2][8][kWave];
+  __shared__ __attribute__((aligned(16))) u32x4 bs[2][8][kWave];
+  const int tiles_n = N / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  // this thread stages fragments f and f + 4 of A and of B (f = tid / 64, its lane = tid % 64)
+  const int f = tid / kWave;
+  const int last_rt = (R - 1) >> 4;
+  const bf16* ap[2];
+  const bf16* bp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rt = min(tm * 8 + f + 4 * u, last_rt);
+    ap[u] = A + ((((int64_t)rt * ksteps) << 6) + lane) * 8;
+    bp[u] = Wt + ((((int64_t)(tn * 8 + f + 4 * u) * ksteps) << 6) + lane) * 8;
+  }
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ra[2], rb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    ra[u] = ld16(ap[u]);
+    rb[u] = ld16(bp[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    as[0][f + 4 * u][lane] = ra[u];
+    bs[0][f + 4 * u][lane] = rb[u];
+  }
+  __syncthreads();
+  for (int s = 0; s < ksteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < ksteps) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ra[u] = ld16(ap[u] + (s + 1) * 512);
+        rb[u] = ld16(bp[u] + (s + 1) * 512);
+      }
+    }
+    Frag<bf16> a[FM], b[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i].from_raw(&as[cur][wm * 4 + i][lane]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j].from_raw(&bs[cur][wn * 4 + j][lane]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_16x16x32(acc[i][j], a[i], b[j]);
+    if (s + 1 < ksteps) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        as[cur ^ 1][f + 4 * u][lane] = ra[u];
+        bs[cur ^ 1][f + 4 * u][lane] = rb[u];
+      }
+    }
+    __syncthreads();
+  }
+  ep.template tile<FM, FN>(acc, tm * BM + wm * 64 + (lane >> 4) * 4, tn * BN + wn * 64, lane);
 }
 
 // Epilogues. Lane l of a wave holds acc[fm][fn][i] = C[rbase + 16 fm + i][cwave + 16 fn + l % 16]
@@ -455,10 +529,22 @@ static hipError_t gemm_rows_t(const ParCtx& c, int R, int N, int K, int wks, con
 }
 
 // Largest register tile the shape allows: 64 x 64 per wave (128 x 128 per block) when N is a
-// multiple of 128, else 32 x 32 per wave.
+// multiple of 128, else 32 x 32 per wave. Fragment-ordered operands with such N go through LDS.
 template <class AL, class EP>
 static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
                             const AL& al, const EP& ep, double out_bytes) {
+  if constexpr (std::is_same<AL, PA>::value) {
+    if (N % 128 == 0 && wks == K / 32) {
+      const int64_t blocks = (int64_t)((R + 127) / 128) * (N / 128);
+      if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+      Exec x(c.st);
+      hipError_t e = c.arm(RLT_K_PAR_GEMM, 2.0 * ((double)R * K + (double)K * N) + out_bytes,
+                           2.0 * R * N * K, x);
+      if (e != hipSuccess) return e;
+      return launch(k_gemm_lds<EP>, dim3((unsigned)blocks), dim3(kThreads), x, N, K / 32, al.a,
+                    R, static_cast<const bf16*>(Wt), ep);
+    }
+  }
   if (N % 128 == 0) return gemm_rows_t<4, 4>(c, R, N, K, wks, Wt, al, ep, out_bytes);
   return gemm_rows_t<2, 2>(c, R, N, K, wks, Wt, al, ep, out_bytes);
 }
