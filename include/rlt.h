@@ -132,8 +132,13 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
 /* s_0 = s* for every sequence, empty caches, position t = 0 (before the first token). */
 rlt_status rlt_state_reset(rlt_state* state, void* stream);
 
-/* Number of tokens the state has processed (t). */
+/* Number of tokens every sequence of the state has processed (t), or -1 once a step with an
+ * active mask has run (rlt_decoder_step_ragged): then the sequences may be at different
+ * positions, which rlt_state_positions reads. */
 int64_t rlt_state_position(const rlt_state* state);
+
+/* Waits for `stream` and copies the B per-sequence positions (int64, host array `out`). */
+rlt_status rlt_state_positions(const rlt_state* state, int64_t* out, void* stream);
 void rlt_state_destroy(rlt_state* state);
 
 /* --- encoder memory M ----------------------------------------------------------------- */
@@ -168,6 +173,19 @@ rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, i
  * same batch. */
 rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
                             const void* e_t, float* s_out, void* stream);
+
+/* Ragged "ready updates": one decoder step for the sequences whose byte in `active` (device,
+ * [B] uint8, non-zero = active; NULL = all) is set, each at its own position: sequence b
+ * consumes e_t row b as its token pos_b + 1 and advances; the others keep s, their window and
+ * their position, and their s_out row receives their unchanged s. Sequences that are ready
+ * share one batched launch per kernel ("RLT Runs 96 Blocks Per Token With Recurrent State, No
+ * Resets", "Three design principles and their caveats": ready updates of independent
+ * sequences share one batched kernel). The memory must hold entries up to the largest
+ * position any sequence can have (the number of steps run since reset), else
+ * RLT_ERR_NOT_PROJECTED. After such a step rlt_state_position returns -1. */
+rlt_status rlt_decoder_step_ragged(const rlt_model* model, rlt_state* state,
+                                   const rlt_memory* mem, const void* e_t, const uint8_t* active,
+                                   float* s_out, void* stream);
 
 /* n consecutive steps over e [B][n][d] dtype (device), the encoder outputs of tokens
  * t+1 .. t+n. First projects every one of those tokens that the memory does not hold yet
@@ -207,8 +225,10 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
 
 /* Copies the state to caller buffers in canonical order and waits for the stream:
  *   s [B][d] float32 (device); k, v [L][B][W-1][d] dtype (device), per layer and sequence
- *   the retained entries oldest first, zero padded; *n_valid = min(t, W-1); *position = t;
- *   *version = the model's version tag. Any output pointer may be NULL to skip it. */
+ *   the retained entries oldest first (sequence b keeps min(t_b, W-1) of them, t_b its own
+ *   position), zero padded; *n_valid = min(t, W-1) and *position = t when every sequence is
+ *   at the same position t, else both -1 (see rlt_state_positions); *version = the model's
+ *   version tag. Any output pointer may be NULL to skip it. */
 rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v,
                             int32_t* n_valid, int64_t* position, uint64_t* version,
                             void* stream);

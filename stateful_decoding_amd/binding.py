@@ -79,6 +79,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_state_create": (c_int32, [P, c_int32, P, c_size_t, P, POINTER(P)]),
         "rlt_state_reset": (c_int32, [P, P]),
         "rlt_state_position": (c_int64, [P]),
+        "rlt_state_positions": (c_int32, [P, P, P]),
+        "rlt_decoder_step_ragged": (c_int32, [P, P, P, P, P, P, P]),
         "rlt_state_destroy": (None, [P]),
         "rlt_memory_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
         "rlt_memory_create": (c_int32, [P, c_int32, c_int64, P, c_size_t, POINTER(P)]),
@@ -195,6 +197,12 @@ class State:
     def reset(self, stream=None):
         _check(self.lib.rlt_state_reset(self.handle, _stream(stream)))
 
+    def positions(self, stream=None):
+        """Per-sequence positions (waits for the stream), as a list of ints."""
+        out = (c_int64 * self.batch)()
+        _check(self.lib.rlt_state_positions(self.handle, out, _stream(stream)))
+        return list(out)
+
     def profile_begin(self, kernels=KERNEL_NAMES, token_stride: int = 1):
         """Time launches of `kernels` in the steps of every token_stride-th token."""
         mask = 0
@@ -277,6 +285,21 @@ def rlt_decoder_step(model: Model, state: State, mem: Memory, e_t: torch.Tensor,
         _need(s_out, (state.batch, model.cfg.d), torch.float32, "s_out")
     _check(model.lib.rlt_decoder_step(model.handle, state.handle, mem.handle, e_t.data_ptr(),
                                       _ptr(s_out), _stream(stream)))
+
+
+def rlt_decoder_step_ragged(model: Model, state: State, mem: Memory, e_t: torch.Tensor,
+                            active: torch.Tensor | None = None,
+                            s_out: torch.Tensor | None = None, stream=None):
+    """One step for the sequences with active[b] != 0 (device uint8 [B]; None = all), each at
+    its own position; e_t [B, d]; optional s_out [B, d] float32."""
+    _need(e_t, (state.batch, model.cfg.d), model.dtype, "e_t")
+    if active is not None:
+        _need(active, (state.batch,), torch.uint8, "active")
+    if s_out is not None:
+        _need(s_out, (state.batch, model.cfg.d), torch.float32, "s_out")
+    _check(model.lib.rlt_decoder_step_ragged(model.handle, state.handle, mem.handle,
+                                             e_t.data_ptr(), _ptr(active), _ptr(s_out),
+                                             _stream(stream)))
 
 
 def rlt_run_sequence(model: Model, state: State, mem: Memory, e: torch.Tensor,

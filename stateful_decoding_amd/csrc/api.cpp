@@ -23,7 +23,10 @@ struct rlt_model {
 struct rlt_state {
   const rlt_model* model;
   int B;
+  // tokens processed: every row's position while `ragged` is false; once a step ran with an
+  // active mask, the largest position any row can have (an upper bound)
   int64_t t;
+  bool ragged;
   StateBufs S;
   Profiler prof;
   // row groups: group g is rows [row0[g], row0[g + 1]); group 0 runs on the caller's stream,
@@ -161,6 +164,7 @@ StateLayout state_layout(const Dims& D, int B) {
   s.ssq = take(b * (d / 32) * 4);
   s.o = take(b16 * d * es);
   s.act = take(b16 * D.F * es);
+  s.pos = take(b * 8);
   s.total = o;
   return s;
 }
@@ -282,7 +286,11 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
   s->S.ssq = at<float>(buf, L.ssq);
   s->S.o = at<char>(buf, L.o);
   s->S.act = at<char>(buf, L.act);
+  s->S.pos = at<int64_t>(buf, L.pos);
+  s->S.active = nullptr;
+  s->S.t_uniform = -1;
   s->S.Bt = batch;
+  s->ragged = false;
   s->fork = nullptr;
   for (int g = 0; g < kMaxGroups; ++g) {
     s->aux[g] = nullptr;
@@ -322,10 +330,23 @@ rlt_status rlt_state_reset(rlt_state* state, void* stream) {
                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "state reset");
   state->t = 0;
+  state->ragged = false;
   return ok();
 }
 
-int64_t rlt_state_position(const rlt_state* state) { return state ? state->t : -1; }
+rlt_status rlt_state_positions(const rlt_state* state, int64_t* out, void* stream) {
+  if (!state || !out) return fail(RLT_ERR_ARG, "state and out must be non-NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out, state->S.pos, sizeof(int64_t) * (size_t)state->B,
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "reading positions");
+  return ok();
+}
+
+int64_t rlt_state_position(const rlt_state* state) {
+  return state && !state->ragged ? state->t : -1;
+}
 void rlt_state_destroy(rlt_state* state) {
   if (!state) return;
   state->prof.destroy();
@@ -403,7 +424,7 @@ rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, i
 // back to `st`. Launches are issued step by step, alternating between the groups.
 static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
                             const void* e, int64_t e_ld, int64_t n, float* out, int64_t out_ld,
-                            hipStream_t st) {
+                            hipStream_t st, const uint8_t* active = nullptr) {
   const Dims& D = model->D;
   const int ng = state->ngroups;
   hipError_t err = hipSuccess;
@@ -415,13 +436,16 @@ static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_
   }
   StateBufs Sg[kMaxGroups];
   MemBufs Mg[kMaxGroups];
+  StateBufs S = state->S;
+  S.active = active;
   for (int g = 0; g < ng; ++g) {
-    Sg[g] = state_rows(D, state->S, state->row0[g]);
+    Sg[g] = state_rows(D, S, state->row0[g]);
     Mg[g] = memory_rows(D, mem->M, state->row0[g]);
   }
   const char* eb = static_cast<const char*>(e);
   for (int64_t i = 0; i < n && err == hipSuccess; ++i) {
     const int64_t t0 = state->t + i;
+    for (int g = 0; g < ng; ++g) Sg[g].t_uniform = state->ragged ? -1 : t0;
     for (int g = 0; g < ng && err == hipSuccess; ++g) {
       const int b0 = state->row0[g], rows = state->row0[g + 1] - b0;
       const char* et = eb + ((size_t)b0 * e_ld + (size_t)i * D.d) * D.es;
@@ -466,6 +490,25 @@ rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_
   return ok();
 }
 
+rlt_status rlt_decoder_step_ragged(const rlt_model* model, rlt_state* state,
+                                   const rlt_memory* mem, const void* e_t, const uint8_t* active,
+                                   float* s_out, void* stream) {
+  if (rlt_status s = check_step_args(model, state, mem)) return s;
+  if (!e_t) return fail(RLT_ERR_ARG, "e_t is NULL");
+  if (!aligned16(e_t) || (s_out && !aligned16(s_out)))
+    return fail(RLT_ERR_ARG, "e_t and s_out must be 16-byte aligned");
+  if (mem->len < state->t + 1)
+    return fail(RLT_ERR_NOT_PROJECTED, "positions up to %lld need memory length %lld, have %lld",
+                (long long)state->t, (long long)(state->t + 1), (long long)mem->len);
+  const Dims& D = model->D;
+  hipError_t e = run_steps(model, state, mem, e_t, D.d, 1, s_out, D.d,
+                           static_cast<hipStream_t>(stream), active);
+  if (e != hipSuccess) return hip_fail(e, "decoder step");
+  state->t += 1;
+  if (active) state->ragged = true;
+  return ok();
+}
+
 rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory* mem,
                             const void* e, int64_t n, float* s_traj, void* stream) {
   if (rlt_status s = check_step_args(model, state, mem)) return s;
@@ -480,6 +523,9 @@ rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory
   if (t + n > mem->M.capacity)
     return fail(RLT_ERR_CAPACITY, "tokens up to %lld exceed capacity %lld", (long long)(t + n),
                 (long long)mem->M.capacity);
+  if (state->ragged && mem->len < t + n)
+    return fail(RLT_ERR_NOT_PROJECTED, "sequences at different positions: the memory must hold "
+                "entries up to %lld already", (long long)(t + n));
   const Dims& D = model->D;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int B = state->B;
@@ -523,7 +569,7 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
   if (n < 1) return fail(RLT_ERR_ARG, "n must be >= 1");
   if (!aligned16(e) || (s_traj && !aligned16(s_traj)) || !aligned(ws))
     return fail(RLT_ERR_ARG, "e and s_traj must be 16-byte aligned, ws 256-byte aligned");
-  if (state->t != 0)
+  if (state->t != 0 || state->ragged)
     return fail(RLT_ERR_ARG, "the token-parallel pass starts from a reset state (position %lld)",
                 (long long)state->t);
   const int B = state->B;
@@ -594,12 +640,12 @@ rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v, 
   if (!state) return fail(RLT_ERR_ARG, "state is NULL");
   const Dims& D = state->model->D;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_export(D, state->B, state->S, state->t, s, k, v, st);
+  hipError_t e = launch_export(D, state->B, state->S, s, k, v, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "state export");
   const int64_t keep = D.W - 1;
-  if (n_valid) *n_valid = (int32_t)(state->t < keep ? state->t : keep);
-  if (position) *position = state->t;
+  if (n_valid) *n_valid = state->ragged ? -1 : (int32_t)(state->t < keep ? state->t : keep);
+  if (position) *position = state->ragged ? -1 : state->t;
   if (version) *version = state->model->cfg.version;
   return ok();
 }
@@ -616,6 +662,7 @@ rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, con
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "state import");
   state->t = position;
+  state->ragged = false;
   return ok();
 }
 

@@ -40,20 +40,26 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 }
 
 // One workgroup of NW waves per (sequence, head): softmax attention of one query over the
-// rows [0, n) of a contiguous [rows][HD] key block and value block, in a single pass. Each row
+// rows [0, n) of a contiguous [rows][HD] key block and value block, in a single pass; n comes
+// from the sequence's own position, so sequences of one batch may be at different tokens. Each row
 // slot (LPR lanes) walks its rows with a running softmax state, U rows at a time with one
 // rescale per batch; slots merge through lane shuffles, waves through LDS. The query is q[b]
 // (fp32, head hh), K/V blocks start at K + bh * bh_stride; the output row o[b] (dtype) is
 // written in MFMA fragment order, as the output projection reads it.
 template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __restrict__ K,
-                                       const T* __restrict__ V, int64_t bh_stride, int n, int H,
-                                       float scale, T* __restrict__ out) {
+                                       const T* __restrict__ V, int64_t bh_stride,
+                                       const int64_t* __restrict__ pos, int64_t t_uniform,
+                                       int window, int H, float scale, T* __restrict__ out) {
   using G = Geo<T, HD>;
   constexpr int RPB = G::RPW * NW;  // rows per block per batch step
   __shared__ float lds_m[NW], lds_l[NW];
   __shared__ float lds_acc[NW][HD];
   const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
+  // rows attended: the memory prefix 1..t+1 of this sequence, or its window of
+  // min(t + 1, W) ring slots (t = tokens the sequence has processed before this step)
+  const int64_t tb = (t_uniform >= 0 ? t_uniform : pos[b]) + 1;
+  const int n = window > 0 ? (int)(tb < window ? tb : window) : (int)tb;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int sub = lane % G::LPR, slot = lane / G::LPR;
   const T* Kb = K + (int64_t)bh * bh_stride + sub * G::VEC;
@@ -136,14 +142,18 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_window(const float* q, const T* K,
                                                               const T* V, int64_t bh_stride,
-                                                              int n, int H, float scale, T* out) {
-  attend<T, HD, NW, U>(q, K, V, bh_stride, n, H, scale, out);
+                                                              const int64_t* pos,
+                                                              int64_t t_uniform, int window,
+                                                              int H, float scale, T* out) {
+  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_memory(const float* q, const T* K,
                                                               const T* V, int64_t bh_stride,
-                                                              int n, int H, float scale, T* out) {
-  attend<T, HD, NW, U>(q, K, V, bh_stride, n, H, scale, out);
+                                                              const int64_t* pos,
+                                                              int64_t t_uniform, int window,
+                                                              int H, float scale, T* out) {
+  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
 }
 
 template <typename T>
@@ -154,12 +164,14 @@ static inline T* elem(void* base, int64_t off) {
 // Waves per workgroup: enough workgroups x waves to keep the chip streaming.
 template <typename T, int HD, bool MEMORY>
 static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
-                           int n, int H, T* out, const Exec& st) {
+                           const int64_t* pos, int64_t t_uniform, int window, int H, T* out,
+                           const Exec& st) {
   const float scale = 1.f / sqrtf((float)HD);
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
-#define RLT_ATTEND(NW)                                                                        \
-  return launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,      \
-                dim3(BH), dim3(NW * kWave), st, q, K, V, bh_stride, n, H, scale, out)
+#define RLT_ATTEND(NW)                                                                     \
+  return launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,   \
+                dim3(BH), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, window, \
+                H, scale, out)
   if (nw == 4) RLT_ATTEND(4);
   if (nw == 8) RLT_ATTEND(8);
   RLT_ATTEND(16);
@@ -167,20 +179,21 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
 }
 
 template <typename T, int HD>
-static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                         const Exec& st) {
+static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, const Exec& st) {
   const int64_t layer = (int64_t)S.Bt * D.H * D.W * HD;
-  return attend_t<T, HD, false>(B * D.H, S.q, elem<T>(S.ring_k, l * layer), elem<T>(S.ring_v, l * layer),
-                         (int64_t)D.W * HD, n_valid, D.H, static_cast<T*>(S.o), st);
+  return attend_t<T, HD, false>(B * D.H, S.q, elem<T>(S.ring_k, l * layer),
+                                elem<T>(S.ring_v, l * layer), (int64_t)D.W * HD, S.pos, S.t_uniform, D.W, D.H,
+                                static_cast<T*>(S.o), st);
 }
 
 template <typename T, int HD>
 static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                          int64_t t, const Exec& st) {
+                          const Exec& st) {
   const int g = D.G == 1 ? 0 : l;
   const int64_t grp = (int64_t)g * M.Bt * D.H * M.capacity * HD;
   return attend_t<T, HD, true>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
-                         M.capacity * HD, (int)t, D.H, static_cast<T*>(S.o), st);
+                               M.capacity * HD, S.pos, S.t_uniform, 0, D.H,
+                               static_cast<T*>(S.o), st);
 }
 
 #define RLT_HD_DISPATCH(fn, ...)                                              \
@@ -191,14 +204,13 @@ static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const
     default: return hipErrorInvalidValue;                                      \
   }
 
-hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                     const Exec& st) {
-  RLT_HD_DISPATCH(self_t, D, B, l, S, n_valid, st)
+hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec& st) {
+  RLT_HD_DISPATCH(self_t, D, B, l, S, st)
 }
 
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      int64_t t, const Exec& st) {
-  RLT_HD_DISPATCH(cross_t, D, B, l, S, M, t, st)
+                      const Exec& st) {
+  RLT_HD_DISPATCH(cross_t, D, B, l, S, M, st)
 }
 
 }  // namespace rlt

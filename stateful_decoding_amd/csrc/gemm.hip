@@ -157,17 +157,26 @@ struct EpiTile {
   }
 };
 
-template <typename T>
-struct EpiQKV : EpiTile<EpiQKV<T>> {  // q -> fp32 buffer; k, v -> ring slot
+// ROWS = false: every row writes ring slot `slot`; ROWS = true: row r writes slot pos[r] % W and
+// rows outside `active` keep their ring (ragged steps).
+template <typename T, bool ROWS>
+struct EpiQKV : EpiTile<EpiQKV<T, ROWS>> {  // q -> fp32 buffer; k, v -> the row's ring slot
   float* q;
   T* ring_k;
   T* ring_v;
+  const int64_t* pos;
+  const uint8_t* active;  // NULL: every row
   int M, d, H, hd, W, slot;
   __device__ void op(int row, int col, float v) const {
     if (row >= M) return;
     if (col < d) {
       q[(int64_t)row * d + col] = v;
       return;
+    }
+    int sl = slot;
+    if constexpr (ROWS) {
+      if (active && !active[row]) return;
+      sl = (int)pos[row] % W;  // positions stay below the memory capacity (2^20)
     }
     int c = col - d;
     T* dst = ring_k;
@@ -176,7 +185,7 @@ struct EpiQKV : EpiTile<EpiQKV<T>> {  // q -> fp32 buffer; k, v -> ring slot
       dst = ring_v;
     }
     const int hh = c / hd, dd = c - hh * hd;
-    dst[(((int64_t)row * H + hh) * W + slot) * hd + dd] = to_elem<T>(v);
+    dst[(((int64_t)row * H + hh) * W + sl) * hd + dd] = to_elem<T>(v);
   }
 };
 
@@ -230,6 +239,7 @@ struct EpiH {
       }
       tile[r * ld + c] = sq;
     }
+    self.finish(r0, c0, BM);
     if (!hg) return;
     __syncthreads();
     constexpr int nch = BN / 32;
@@ -244,21 +254,42 @@ struct EpiH {
   }
 };
 
-template <typename T>
-struct EpiResidual : EpiH<T, EpiResidual<T>> {  // dst = h + v; optional copy to out
+// dst = h + v; optional copy to out. FINAL: the last launch of a step (dst = s): rows outside
+// `active` keep s (and copy it to out), and the positions of the other rows advance.
+template <typename T, bool FINAL>
+struct EpiResidual : EpiH<T, EpiResidual<T, FINAL>> {
   const float* h;
   float* dst;
   float* out;
   int64_t out_ld;
+  const uint8_t* active;  // FINAL only; NULL: every row
+  int64_t* pos;           // FINAL only
   int M, d;
-  __device__ void load_inputs(int row, int col, float& a, float&) const {
-    a = h[(int64_t)row * d + col];
+  __device__ bool kept(int row) const {
+    if constexpr (FINAL) return active && !active[row];
+    return false;
   }
-  __device__ float value(int row, int col, float v, float hv, float) const {
+  __device__ void load_inputs(int row, int col, float& a, float& b) const {
+    a = h[(int64_t)row * d + col];
+    b = kept(row) ? dst[(int64_t)row * d + col] : 0.f;
+  }
+  __device__ float value(int row, int col, float v, float hv, float old) const {
+    if (kept(row)) {
+      if (out) out[(int64_t)row * out_ld + col] = old;
+      return old;
+    }
     const float r = hv + v;
     dst[(int64_t)row * d + col] = r;
     if (out) out[(int64_t)row * out_ld + col] = r;
     return r;
+  }
+  // once per row: the column-0 tile advances the position
+  __device__ void finish(int r0, int c0, int BM) const {
+    if constexpr (FINAL) {
+      if (c0 != 0) return;
+      const int row = r0 + (int)threadIdx.x;
+      if ((int)threadIdx.x < BM && row < M && !kept(row)) pos[row] += 1;
+    }
   }
 };
 
@@ -275,6 +306,7 @@ struct EpiGate : EpiH<T, EpiGate<T>> {  // g = sigmoid(v + b); h = g e + (1 - g)
     ev = to_f32<T>(e[(int64_t)row * lde + col]);
     sv = s[(int64_t)row * d + col];
   }
+  __device__ void finish(int, int, int) const {}
   __device__ float value(int row, int col, float v, float ev, float sv) const {
     const float g = sigmoidf_(v + b[col]);
     const float r = g * ev + (1.f - g) * (alpha * sv);
@@ -601,15 +633,25 @@ static hipError_t gate_t(const Dims& D, int B, const Packed& P, const StateBufs&
   return run_step_gemm<T>(B, D.d, 2 * D.d, P.w_gate_t, al, ep, st);
 }
 
-template <typename T>
-static hipError_t qkv_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                        int slot, const Exec& st) {
-  EpiQKV<T> ep;
+template <typename T, bool ROWS>
+static hipError_t qkv_rows_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                             const Exec& st) {
+  EpiQKV<T, ROWS> ep;
   const int64_t ring_layer = (int64_t)S.Bt * D.H * D.W * D.hd;
   ep.q = S.q; ep.ring_k = elem<T>(S.ring_k, l * ring_layer); ep.ring_v = elem<T>(S.ring_v, l * ring_layer);
-  ep.M = B; ep.d = D.d; ep.H = D.H; ep.hd = D.hd; ep.W = D.W; ep.slot = slot;
+  ep.pos = S.pos; ep.active = S.active;
+  ep.M = B; ep.d = D.d; ep.H = D.H; ep.hd = D.hd; ep.W = D.W;
+  ep.slot = S.t_uniform >= 0 ? (int)(S.t_uniform % D.W) : -1;
   return run_step_gemm<T>(B, 3 * D.d, D.d, elem<T>(P.wqkv_t, (int64_t)l * 3 * D.d * D.d),
                           normed<T>(D, B, S), ep, st);
+}
+
+// every row at the same position and all of them active: one ring slot for the launch
+template <typename T>
+static hipError_t qkv_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                        const Exec& st) {
+  if (S.t_uniform >= 0 && !S.active) return qkv_rows_t<T, false>(D, B, l, P, S, st);
+  return qkv_rows_t<T, true>(D, B, l, P, S, st);
 }
 
 template <typename T>
@@ -632,22 +674,35 @@ static hipError_t w13_t(const Dims& D, int B, int l, const Packed& P, const Stat
 // h (+)= A W for the output projections; the result feeds the next RMSNorm: after the
 // self-attention output the cross-attention norm of layer l, after the cross-attention output
 // the FFN norm, after the FFN the next layer's first norm (none after the last layer).
-template <typename T>
-static hipError_t residual_t(const Dims& D, int B, int l, int which, const Packed& P,
-                             const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
-                             const Exec& st) {
+template <typename T, bool FINAL>
+static hipError_t residual_kind_t(const Dims& D, int B, int l, int which, const Packed& P,
+                                  const StateBufs& S, float* out, int64_t out_ld,
+                                  const Exec& st) {
   const void* A = which == 2 ? S.act : S.o;
   const int K = which == 2 ? D.F : D.d;
   const void* Wt = which == 0 ? elem<T>(P.wo_t, (int64_t)l * D.d * D.d)
                  : which == 1 ? elem<T>(P.wco_t, (int64_t)l * D.d * D.d)
                               : elem<T>(P.w2_t, (int64_t)l * D.d * D.F);
   AFrag<T> al{static_cast<const T*>(A), K / 32, B};
-  EpiResidual<T> ep;
-  ep.h = S.h; ep.dst = dst_s ? S.s : S.h; ep.out = out; ep.out_ld = out_ld; ep.M = B; ep.d = D.d;
+  EpiResidual<T, FINAL> ep;
+  ep.h = S.h; ep.dst = FINAL ? S.s : S.h; ep.out = out; ep.out_ld = out_ld; ep.M = B; ep.d = D.d;
+  ep.active = FINAL ? S.active : nullptr;
+  ep.pos = FINAL ? S.pos : nullptr;
   const float* g = which < 2 ? P.gamma + ((int64_t)l * 3 + which + 1) * D.d
                  : l + 1 < D.L ? P.gamma + (int64_t)(l + 1) * 3 * D.d : nullptr;
-  next_norm<T>(ep, D, S, dst_s ? nullptr : g);
+  next_norm<T>(ep, D, S, FINAL ? nullptr : g);
   return run_step_gemm<T>(B, D.d, K, Wt, al, ep, st);
+}
+
+// h (+)= A W for the output projections; the result feeds the next RMSNorm: after the
+// self-attention output the cross-attention norm of layer l, after the cross-attention output
+// the FFN norm, after the FFN the next layer's first norm (none after the last layer).
+template <typename T>
+static hipError_t residual_t(const Dims& D, int B, int l, int which, const Packed& P,
+                             const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
+                             const Exec& st) {
+  if (dst_s) return residual_kind_t<T, true>(D, B, l, which, P, S, out, out_ld, st);
+  return residual_kind_t<T, false>(D, B, l, which, P, S, out, out_ld, st);
 }
 
 template <typename T>
@@ -668,10 +723,9 @@ hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, 
   return D.dtype == RLT_BF16 ? gate_t<bf16>(D, B, P, S, e_t, e_ld, st)
                              : gate_t<float>(D, B, P, S, e_t, e_ld, st);
 }
-hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S, int slot,
+hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                     const Exec& st) {
-  return D.dtype == RLT_BF16 ? qkv_t<bf16>(D, B, l, P, S, slot, st)
-                             : qkv_t<float>(D, B, l, P, S, slot, st);
+  return D.dtype == RLT_BF16 ? qkv_t<bf16>(D, B, l, P, S, st) : qkv_t<float>(D, B, l, P, S, st);
 }
 hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                    const Exec& st) {

@@ -81,6 +81,7 @@ struct Packed {
 //   ssq   [B][d/32] f32        sums of h^2 over 32-column chunks (that norm's scale)
 //   o     [B16][d] dtype       attention output (operand of the output projections)
 //   act   [B16][F] dtype       SiLU(f W1) * (f W3)
+//   pos   [B] int64            tokens each sequence has processed (its position t)
 // hg, o and act are projection operands in MFMA fragment order, B16 = B rounded up to 16.
 struct StateBufs {
   int Bt;  // batch of the whole state: row stride of the per-layer ring blocks
@@ -94,6 +95,13 @@ struct StateBufs {
   float* ssq;
   void* o;
   void* act;
+  int64_t* pos;
+  // rows that take part in the current step (device, one byte per row; NULL: all of them).
+  // Other rows compute along but store nothing: their s, ring and position stay as they are.
+  const uint8_t* active;
+  // the position of every row when the host knows they are all equal, else -1 (kernels then
+  // read pos per row); saves a dependent load at the start of each attention block
+  int64_t t_uniform;
 };
 
 struct MemBufs {
@@ -111,7 +119,7 @@ MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0);
 
 // Byte layout of the state buffer; offsets are 256-byte aligned.
 struct StateLayout {
-  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, total;
+  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, pos, total;
 };
 StateLayout state_layout(const Dims& D, int B);
 
@@ -122,8 +130,11 @@ StateLayout state_layout(const Dims& D, int B);
 hipError_t launch_pack_transpose(int dtype, const void* src, int K, int N, void* dst,
                                  int64_t row_base, int grp, int grp_stride, hipStream_t st);
 
+// s = s*, positions 0.
 hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& S,
                         hipStream_t st);
+// Every one of the B positions = t.
+hipError_t launch_set_positions(int64_t* pos, int B, int64_t t, hipStream_t st);
 
 // Projects n tokens per sequence into memory entries t0 .. t0+n-1; the encoder outputs of
 // sequence b, token i are at e + (b * e_seq + i) * d (elements).
@@ -149,8 +160,10 @@ struct Profiler {
   void destroy();
 };
 
-// One decoder step at 0-based token index t0 (memory must hold entries 0..t0). e_t rows are
-// e_t + b * e_ld (elements). When out != NULL, s_t row b is also written to out + b * out_ld.
+// One decoder step of every row of S that is active: row b consumes e_t + b * e_ld (elements)
+// at its own position pos[b] (memory must hold entries 0..pos[b]), and its position advances.
+// When out != NULL, row b of s is also written to out + b * out_ld (inactive rows: their
+// unchanged s). t0 is the largest position, used only to count algorithmic bytes for `prof`.
 hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S,
                        const MemBufs& M, const void* e_t, int64_t e_ld, int64_t t0,
                        float* out, int64_t out_ld, hipStream_t st, Profiler* prof);
@@ -171,28 +184,32 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
                            float* out, int64_t out_seq, void* ws, hipStream_t st,
                            Profiler* prof);
 
-hipError_t launch_export(const Dims& D, int B, const StateBufs& S, int64_t t, float* s,
-                         void* k, void* v, hipStream_t st);
+// Canonical snapshot: row b's retained entries are its tokens pos[b]-n_b .. pos[b]-1 with
+// n_b = min(pos[b], W-1), oldest first, zero-padded to W-1. Import sets every position to t.
+hipError_t launch_export(const Dims& D, int B, const StateBufs& S, float* s, void* k, void* v,
+                         hipStream_t st);
 hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
                          const void* k, const void* v, hipStream_t st);
 
 // ---- kernel-level entry points used by launch_step -----------------------------------------
 hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, const void* e_t,
                      int64_t e_ld, const Exec& st);
-hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S, int slot,
+hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                     const Exec& st);
 hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                    const Exec& st);
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                     const Exec& st);
 // h (+)= A W for the output projections: which = 0 (self-attn O), 1 (cross O), 2 (FFN down).
-// When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h.
+// When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h, and
+// the positions of the active rows advance: this is the last launch of the step.
 hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P,
                          const StateBufs& S, bool dst_s, float* out, int64_t out_ld,
                          const Exec& st);
-hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, int n_valid,
-                     const Exec& st);
+// Window attention over the min(t + 1, W) ring slots of each row, memory attention over its
+// entries 0..t (t = the row's position).
+hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec& st);
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      int64_t t, const Exec& st);
+                      const Exec& st);
 
 }  // namespace rlt

@@ -46,30 +46,45 @@ hipError_t launch_pack_transpose(int dtype, const void* src, int K, int N, void*
   return hipGetLastError();
 }
 
-// ---- reset: s = s* ----------------------------------------------------------------------------
+// ---- reset: s = s*, positions 0 ----------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_reset(float* __restrict__ s,
                                                     const float* __restrict__ s_star, int d,
-                                                    int64_t n_s) {
+                                                    int64_t n_s, int64_t* __restrict__ pos,
+                                                    int B) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i < n_s) s[i] = s_star[i % d];
+  if (i < B) pos[i] = 0;
 }
 
 hipError_t launch_reset(const Dims& D, int B, const Packed& P, const StateBufs& S,
                         hipStream_t st) {
   const int64_t n_s = (int64_t)B * D.d;
   hipLaunchKernelGGL(k_reset, dim3((unsigned)((n_s + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     st, S.s, P.s_star, D.d, n_s);
+                     st, S.s, P.s_star, D.d, n_s, S.pos, B);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kThreads) void k_set_pos(int64_t* __restrict__ pos, int B, int64_t t) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < B) pos[i] = t;
+}
+
+hipError_t launch_set_positions(int64_t* pos, int B, int64_t t, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_pos, dim3((unsigned)((B + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, pos, B, t);
   return hipGetLastError();
 }
 
 // ---- snapshots: ring [L][B][H][W][hd] <-> canonical [L][B][W-1][d], oldest first ----------
-// Retained entries are the tokens t-n_valid .. t-1 (0-based), token tau in slot tau % W.
+// Row b retains its tokens t-n .. t-1 (0-based), t = pos[b], n = min(t, W-1), token tau in slot
+// tau % W; canonical entries beyond n are zero on export.
 template <typename T, bool EXPORT>
 __global__ __launch_bounds__(kThreads) void k_snapshot(T* __restrict__ ring_k,
                                                        T* __restrict__ ring_v,
                                                        T* __restrict__ can_k,
                                                        T* __restrict__ can_v, int B, int H,
-                                                       int hd, int W, int64_t t, int n_valid,
+                                                       int hd, int W,
+                                                       const int64_t* __restrict__ pos,
                                                        int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= total) return;
@@ -81,6 +96,8 @@ __global__ __launch_bounds__(kThreads) void k_snapshot(T* __restrict__ ring_k,
   const int b = (int)(rest % B);
   const int l = (int)(rest / B);
   const int hh = c / hd, dd = c % hd;
+  const int64_t t = pos[b];
+  const int n_valid = (int)(t < keep ? t : keep);
   if (e >= n_valid) {
     if (EXPORT) {
       if (can_k) can_k[i] = to_elem<T>(0.f);
@@ -100,28 +117,28 @@ __global__ __launch_bounds__(kThreads) void k_snapshot(T* __restrict__ ring_k,
 }
 
 template <typename T, bool EXPORT>
-static hipError_t snapshot_t(const Dims& D, int B, const StateBufs& S, int64_t t, void* k,
-                             void* v, hipStream_t st) {
+static hipError_t snapshot_t(const Dims& D, int B, const StateBufs& S, void* k, void* v,
+                             hipStream_t st) {
   const int keep = D.W - 1;
-  const int n_valid = (int)(t < keep ? t : keep);
   const int64_t total = (int64_t)D.L * B * keep * D.d;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL((k_snapshot<T, EXPORT>), dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, st, static_cast<T*>(S.ring_k), static_cast<T*>(S.ring_v),
-                     static_cast<T*>(k), static_cast<T*>(v), B, D.H, D.hd, D.W, t, n_valid, total);
+                     static_cast<T*>(k), static_cast<T*>(v), B, D.H, D.hd, D.W,
+                     (const int64_t*)S.pos, total);
   return hipGetLastError();
 }
 
-hipError_t launch_export(const Dims& D, int B, const StateBufs& S, int64_t t, float* s, void* k,
-                         void* v, hipStream_t st) {
+hipError_t launch_export(const Dims& D, int B, const StateBufs& S, float* s, void* k, void* v,
+                         hipStream_t st) {
   if (s) {
     hipError_t e = hipMemcpyAsync(s, S.s, sizeof(float) * (size_t)B * D.d,
                                   hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return e;
   }
   if (!k && !v) return hipSuccess;
-  return D.dtype == RLT_BF16 ? snapshot_t<bf16, true>(D, B, S, t, k, v, st)
-                             : snapshot_t<float, true>(D, B, S, t, k, v, st);
+  return D.dtype == RLT_BF16 ? snapshot_t<bf16, true>(D, B, S, k, v, st)
+                             : snapshot_t<float, true>(D, B, S, k, v, st);
 }
 
 hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
@@ -129,9 +146,10 @@ hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, co
   hipError_t e = hipMemcpyAsync(S.s, s, sizeof(float) * (size_t)B * D.d, hipMemcpyDeviceToDevice,
                                 st);
   if (e != hipSuccess) return e;
+  if ((e = launch_set_positions(S.pos, B, t, st)) != hipSuccess) return e;
   return D.dtype == RLT_BF16
-             ? snapshot_t<bf16, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st)
-             : snapshot_t<float, false>(D, B, S, t, const_cast<void*>(k), const_cast<void*>(v), st);
+             ? snapshot_t<bf16, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st)
+             : snapshot_t<float, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st);
 }
 
 // ---- row groups -----------------------------------------------------------------------------
@@ -146,6 +164,8 @@ StateBufs state_rows(const Dims& D, const StateBufs& S, int b0) {
   v.ssq += b0 * (d / 32);
   v.o = static_cast<char*>(S.o) + b0 * d * D.es;
   v.act = static_cast<char*>(S.act) + (int64_t)b0 * D.F * D.es;
+  v.pos += b0;
+  if (S.active) v.active += b0;
   const int64_t ring_row = (int64_t)D.H * D.W * D.hd * D.es;
   v.ring_k = static_cast<char*>(S.ring_k) + b0 * ring_row;
   v.ring_v = static_cast<char*>(S.ring_v) + b0 * ring_row;
@@ -202,20 +222,19 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
   } while (0)
   RLT_TIMED(RLT_K_GATE, 2 * d * d * es + actd + 2 * act32, 4 * b * d * d,
             gemm_gate(D, B, P, S, e_t, e_ld, x));
-  const int slot = (int)(t0 % D.W);
   const int n_valid = (int)(t0 + 1 < D.W ? t0 + 1 : D.W);
   const double t = (double)(t0 + 1);
   for (int l = 0; l < D.L; ++l) {
     const bool last = l == D.L - 1;
     RLT_TIMED(RLT_K_QKV, 3 * d * d * es + 2 * act32 + 2 * actd, 6 * b * d * d,
-              gemm_qkv(D, B, l, P, S, slot, x));
+              gemm_qkv(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_SELF_ATTN, n_valid * b * 2 * d * es + act32 + actd, 4 * b * d * n_valid,
-              attn_self(D, B, l, S, n_valid, x));
+              attn_self(D, B, l, S, x));
     RLT_TIMED(RLT_K_SELF_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
               gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, x));
     RLT_TIMED(RLT_K_CROSS_Q, d * d * es + 2 * act32, 2 * b * d * d, gemm_cq(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_CROSS_ATTN, t * b * 2 * d * es + act32 + actd, 4 * b * d * t,
-              attn_cross(D, B, l, S, M, t0 + 1, x));
+              attn_cross(D, B, l, S, M, x));
     RLT_TIMED(RLT_K_CROSS_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
               gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, x));
     RLT_TIMED(RLT_K_FFN_UP, 2 * F * d * es + act32 + b * F * es, 4 * b * d * F,

@@ -697,8 +697,10 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
   const int64_t total = (int64_t)B * d;
   Exec x(st);
   if ((err = c.arm(RLT_K_PAR_OTHER, (double)total * 8, 0, x)) != hipSuccess) return err;
-  return launch(k_copy_last, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads),
-                x, (const float*)h, n, d, total, S.s);
+  err = launch(k_copy_last, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads),
+               x, (const float*)h, n, d, total, S.s);
+  if (err != hipSuccess) return err;
+  return launch_set_positions(S.pos, B, n, st);
 }
 
 }  // namespace rlt
