@@ -239,6 +239,15 @@ rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v,
 rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, const void* v,
                             int64_t position, uint64_t version, void* stream);
 
+/* The same for a snapshot whose sequences are at different positions: `positions` is a host
+ * array of B positions (as rlt_state_positions reads them, each in [0, 2^20]); sequence b's
+ * canonical k/v rows hold its min(positions[b], W-1) retained entries. Waits for the stream.
+ * Together with rlt_state_export and rlt_state_positions this splits and resumes a batch of
+ * ragged sequences ("exact prefix snapshot"). */
+rlt_status rlt_state_import_ragged(rlt_state* state, const float* s, const void* k,
+                                   const void* v, const int64_t* positions, uint64_t version,
+                                   void* stream);
+
 /* --- kernel timing --------------------------------------------------------------------- */
 
 /* Kernels of one decoder step (and the memory projection run by rlt_run_sequence). */

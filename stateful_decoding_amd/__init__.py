@@ -6,5 +6,6 @@ sources (``csrc/``), the build script and a thin ctypes binding with the same ca
 from .binding import (  # noqa: F401
     LIB_PATH, Memory, Model, RLTError, State, load_library, make_config, parallel_workspace,
     rlt_config, rlt_decoder_step, rlt_decoder_step_ragged, rlt_memproj, rlt_run_parallel,
-    rlt_run_sequence, rlt_state_export, rlt_state_import, upload_weights,
+    rlt_run_sequence, rlt_state_export, rlt_state_import, rlt_state_import_ragged,
+    upload_weights,
 )

@@ -97,6 +97,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_state_export": (c_int32, [P, P, P, P, POINTER(c_int32), POINTER(c_int64),
                                        POINTER(c_uint64), P]),
         "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
+        "rlt_state_import_ragged": (c_int32, [P, P, P, P, P, c_uint64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -364,3 +365,20 @@ def rlt_state_import(state: State, s: torch.Tensor, k: torch.Tensor, v: torch.Te
         k = v = s
     _check(state.lib.rlt_state_import(state.handle, s.data_ptr(), k.data_ptr(), v.data_ptr(),
                                       int(position), int(version), _stream(stream)))
+
+
+def rlt_state_import_ragged(state: State, s: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            positions, version: int, stream=None):
+    """rlt_state_import for sequences at different positions (a list of B ints)."""
+    c = state.model.cfg
+    _need(s, (state.batch, c.d), torch.float32, "s")
+    shape = (c.n_layers, state.batch, c.window - 1, c.d)
+    _need(k, shape, state.model.dtype, "k")
+    _need(v, shape, state.model.dtype, "v")
+    if len(positions) != state.batch:
+        raise ValueError(f"positions must have {state.batch} entries")
+    if c.window == 1:
+        k = v = s
+    pos = (c_int64 * state.batch)(*[int(x) for x in positions])
+    _check(state.lib.rlt_state_import_ragged(state.handle, s.data_ptr(), k.data_ptr(),
+                                             v.data_ptr(), pos, int(version), _stream(stream)))

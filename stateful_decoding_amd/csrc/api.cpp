@@ -666,4 +666,34 @@ rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, con
   return ok();
 }
 
+rlt_status rlt_state_import_ragged(rlt_state* state, const float* s, const void* k,
+                                   const void* v, const int64_t* positions, uint64_t version,
+                                   void* stream) {
+  if (!state || !s || !k || !v || !positions)
+    return fail(RLT_ERR_ARG, "state, s, k, v and positions must be non-NULL");
+  if (version != state->model->cfg.version)
+    return fail(RLT_ERR_VERSION, "snapshot version %llu != model version %llu",
+                (unsigned long long)version, (unsigned long long)state->model->cfg.version);
+  int64_t lo = positions[0], hi = positions[0];
+  for (int b = 1; b < state->B; ++b) {
+    lo = positions[b] < lo ? positions[b] : lo;
+    hi = positions[b] > hi ? positions[b] : hi;
+  }
+  if (lo < 0 || hi > kMaxCapacity)
+    return fail(RLT_ERR_ARG, "positions must lie in [0, %lld]", (long long)kMaxCapacity);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Dims& D = state->model->D;
+  hipError_t e = hipMemcpyAsync(state->S.s, s, sizeof(float) * (size_t)state->B * D.d,
+                                hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(state->S.pos, positions, sizeof(int64_t) * (size_t)state->B,
+                       hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = launch_import_caches(D, state->B, state->S, k, v, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "state import");
+  state->t = hi;
+  state->ragged = lo != hi;
+  return ok();
+}
+
 }  // extern "C"

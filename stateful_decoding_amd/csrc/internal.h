@@ -190,6 +190,9 @@ hipError_t launch_export(const Dims& D, int B, const StateBufs& S, float* s, voi
                          hipStream_t st);
 hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
                          const void* k, const void* v, hipStream_t st);
+// Ring slots from canonical k, v at the positions S.pos already holds.
+hipError_t launch_import_caches(const Dims& D, int B, const StateBufs& S, const void* k,
+                                const void* v, hipStream_t st);
 
 // ---- kernel-level entry points used by launch_step -----------------------------------------
 hipError_t gemm_gate(const Dims& D, int B, const Packed& P, const StateBufs& S, const void* e_t,

@@ -141,15 +141,20 @@ hipError_t launch_export(const Dims& D, int B, const StateBufs& S, float* s, voi
                              : snapshot_t<float, true>(D, B, S, k, v, st);
 }
 
+hipError_t launch_import_caches(const Dims& D, int B, const StateBufs& S, const void* k,
+                                const void* v, hipStream_t st) {
+  return D.dtype == RLT_BF16
+             ? snapshot_t<bf16, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st)
+             : snapshot_t<float, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st);
+}
+
 hipError_t launch_import(const Dims& D, int B, const StateBufs& S, int64_t t, const float* s,
                          const void* k, const void* v, hipStream_t st) {
   hipError_t e = hipMemcpyAsync(S.s, s, sizeof(float) * (size_t)B * D.d, hipMemcpyDeviceToDevice,
                                 st);
   if (e != hipSuccess) return e;
   if ((e = launch_set_positions(S.pos, B, t, st)) != hipSuccess) return e;
-  return D.dtype == RLT_BF16
-             ? snapshot_t<bf16, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st)
-             : snapshot_t<float, false>(D, B, S, const_cast<void*>(k), const_cast<void*>(v), st);
+  return launch_import_caches(D, B, S, k, v, st);
 }
 
 // ---- row groups -----------------------------------------------------------------------------
