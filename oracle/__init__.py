@@ -1,7 +1,11 @@
-"""CPU oracle of the RLT decoder transition.
+"""CPU oracle of the RLT decoder transition and of its backward pass.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and by the
 benchmark's CPU-baseline leg, never by the product path.
 """
 from .rlt_oracle import *  # noqa: F401,F403
-from .rlt_oracle import __all__  # noqa: F401
+from .rlt_oracle import __all__ as _fwd
+from .rlt_backward import *  # noqa: F401,F403
+from .rlt_backward import __all__ as _bwd
+
+__all__ = list(_fwd) + list(_bwd)
