@@ -221,6 +221,52 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
                             const void* e, int64_t n, float* s_traj, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* --- backward pass ("RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", section
+ * "Training and serving implications": training backpropagates through the whole sequence,
+ * and the gradient between consecutive states also runs through the decoder's self-attention
+ * keys/values; "16 per-token recurrence, no quality gain": a backward pass that walks the
+ * tokens in reverse) ------------------------------------------------------------------------ */
+
+/* Gradient outputs of rlt_bptt: device float32 buffers (caller-owned), one per parameter, each
+ * laid out like the matching rlt_weights field. */
+typedef struct rlt_grads {
+  float* s_star; /* [d]        */
+  float* w_gate; /* [2d][d]    */
+  float* b_gate; /* [d]        */
+  float* gamma;  /* [L][3][d]  */
+  float* wq;     /* [L][d][d]  */
+  float* wk;
+  float* wv;
+  float* wo;
+  float* wcq;
+  float* wco;
+  float* w1;     /* [L][d][F]  */
+  float* w3;     /* [L][d][F]  */
+  float* w2;     /* [L][F][d]  */
+  float* wmk;    /* [G][d][d]  */
+  float* wmv;    /* [G][d][d]  */
+} rlt_grads;
+
+/* Device workspace bytes of rlt_bptt for B sequences of n tokens (0 if invalid). The workspace
+ * holds what the reverse walk needs from the forward pass (about
+ * n * B * L * d * (20 + 5 * element size) bytes), the memory, and backward copies of the
+ * weights. */
+size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
+
+/* Backpropagation through time over whole sequences. Runs the decoder from the start state
+ * (s*, empty caches) over e [B][n][d] (dtype, device, 16-byte aligned), projecting the memory
+ * of all n tokens itself, then walks the tokens in reverse for the upstream gradients
+ * ds [B][n][d] float32 (device): ds[b][t] = dLoss/ds_t of sequence b. Every buffer of `grads`
+ * is overwritten with dLoss/dparameter (float32, summed over the batch); de [B][n][d] float32
+ * (device, or NULL to skip) receives dLoss/de through the gated merge and the memory
+ * projection; s_traj [B][n][d] float32 (device, or NULL) receives the forward trajectory.
+ * Gradients through the self-attention keys/values of later tokens are included. Independent
+ * of any rlt_state or rlt_memory. `ws`: device, 256-byte aligned, >= rlt_bptt_ws_bytes bytes,
+ * scratch owned by the caller (RLT_ERR_CAPACITY if smaller). Asynchronous on `stream`. */
+rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
+                    const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
+                    size_t ws_bytes, void* stream);
+
 /* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
 
 /* Copies the state to caller buffers in canonical order and waits for the stream:

@@ -42,6 +42,10 @@ KERNEL_NAMES = ("gate", "qkv", "self_attn", "self_out", "cross_q", "cross_attn",
                 "par_other")
 
 
+class rlt_grads(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in WEIGHT_FIELDS]
+
+
 class rlt_kernel_stats(ctypes.Structure):
     _fields_ = [("launches", c_int64), ("total_ms", ctypes.c_double), ("bytes", ctypes.c_double),
                 ("flops", ctypes.c_double)]
@@ -98,6 +102,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                        POINTER(c_uint64), P]),
         "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
         "rlt_state_import_ragged": (c_int32, [P, P, P, P, P, c_uint64, P]),
+        "rlt_bptt_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
+        "rlt_bptt": (c_int32, [P, P, c_int32, c_int64, P, P, POINTER(rlt_grads), P, P, c_size_t,
+                               P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -337,6 +344,53 @@ def rlt_run_parallel(model: Model, state: State, mem: Memory, e: torch.Tensor,
     _check(model.lib.rlt_run_parallel(model.handle, state.handle, mem.handle, e.data_ptr(),
                                       int(n), _ptr(s_traj), ws.data_ptr(),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bptt_workspace(model: Model, batch: int, n: int) -> torch.Tensor:
+    """Device workspace for rlt_bptt over n tokens of `batch` sequences."""
+    nbytes = model.lib.rlt_bptt_ws_bytes(byref(model.cfg), int(batch), int(n))
+    if nbytes == 0:
+        raise RLTError(2, f"invalid batch {batch} or n {n} for the backward pass")
+    return _device_buffer(nbytes, model.ws.device)
+
+
+def grad_buffers(model: Model) -> dict:
+    """Zero-initialised float32 device buffers shaped like the weights, one per rlt_grads
+    field."""
+    c = model.cfg
+    d, F, L, G = c.d, c.ffn, c.n_layers, c.n_groups
+    shapes = {"s_star": (d,), "w_gate": (2 * d, d), "b_gate": (d,), "gamma": (L, 3, d),
+              "wq": (L, d, d), "wk": (L, d, d), "wv": (L, d, d), "wo": (L, d, d),
+              "wcq": (L, d, d), "wco": (L, d, d), "w1": (L, d, F), "w3": (L, d, F),
+              "w2": (L, F, d), "wmk": (G, d, d), "wmv": (G, d, d)}
+    return {k: torch.zeros(shapes[k], dtype=torch.float32, device=model.ws.device)
+            for k in WEIGHT_FIELDS}
+
+
+def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
+             de: torch.Tensor | None = None, s_traj: torch.Tensor | None = None,
+             ws: torch.Tensor | None = None, stream=None):
+    """Forward from s* over e [B, n, d] and backpropagation through time of the upstream
+    gradients ds [B, n, d] float32 into `grads` (from grad_buffers; overwritten), de [B, n, d]
+    float32 and s_traj [B, n, d] float32 (both optional); `ws` from bptt_workspace."""
+    B, n = int(e.shape[0]), int(e.shape[1])
+    d = model.cfg.d
+    _need(e, (B, n, d), model.dtype, "e")
+    _need(ds, (B, n, d), torch.float32, "ds")
+    if de is not None:
+        _need(de, (B, n, d), torch.float32, "de")
+    if s_traj is not None:
+        _need(s_traj, (B, n, d), torch.float32, "s_traj")
+    for k in WEIGHT_FIELDS:
+        if not isinstance(grads.get(k), torch.Tensor) or grads[k].dtype != torch.float32 \
+                or not grads[k].is_contiguous() or not grads[k].is_cuda:
+            raise ValueError(f"grads[{k!r}] must be a contiguous float32 CUDA tensor")
+    if ws is None:
+        ws = bptt_workspace(model, B, n)
+    g = rlt_grads(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    _check(model.lib.rlt_bptt(model.handle, e.data_ptr(), B, n, ds.data_ptr(), _ptr(s_traj),
+                              byref(g), _ptr(de), ws.data_ptr(), ws.numel() * ws.element_size(),
+                              _stream(stream)))
 
 
 def rlt_state_export(state: State, stream=None):

@@ -696,4 +696,42 @@ rlt_status rlt_state_import_ragged(rlt_state* state, const float* s, const void*
   return ok();
 }
 
+// ---- backward pass ---------------------------------------------------------------------------
+
+size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
+  if (check_config(cfg) != RLT_OK || !valid_batch(batch) || n < 1 || n > kMaxCapacity ||
+      (int64_t)batch * n > INT32_MAX / 2)
+    return 0;
+  return train_layout(dims_of(*cfg), batch, n).total;
+}
+
+rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
+                    const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!model) return fail(RLT_ERR_ARG, "model is NULL");
+  if (!e || !ds || !grads || !ws) return fail(RLT_ERR_ARG, "e, ds, grads and ws must be non-NULL");
+  float* const gp[] = {grads->s_star, grads->w_gate, grads->b_gate, grads->gamma, grads->wq,
+                       grads->wk,     grads->wv,     grads->wo,     grads->wcq,   grads->wco,
+                       grads->w1,     grads->w3,     grads->w2,     grads->wmk,   grads->wmv};
+  for (float* p : gp)
+    if (!p) return fail(RLT_ERR_ARG, "a gradient pointer is NULL");
+  if (!valid_batch(batch)) return fail(RLT_ERR_SHAPE, "batch %d out of range", batch);
+  if (n < 1 || n > kMaxCapacity)
+    return fail(RLT_ERR_SHAPE, "n = %lld must be in [1, %lld]", (long long)n,
+                (long long)kMaxCapacity);
+  if ((int64_t)batch * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "batch * n too large");
+  if (!aligned16(e) || !aligned(ws)) return fail(RLT_ERR_ARG, "e must be 16-byte aligned, ws 256-byte aligned");
+  const Dims& D = model->D;
+  const size_t need = train_layout(D, batch, n).total;
+  if (ws_bytes < need)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  GradPtrs g{grads->s_star, grads->w_gate, grads->b_gate, grads->gamma, grads->wq, grads->wk,
+             grads->wv,     grads->wo,     grads->wcq,    grads->wco,   grads->w1, grads->w3,
+             grads->w2,     grads->wmk,    grads->wmv};
+  hipError_t err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws,
+                               static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "backward pass");
+  return ok();
+}
+
 }  // extern "C"

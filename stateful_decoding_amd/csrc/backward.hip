@@ -1,0 +1,1298 @@
+// Backpropagation through time of the decoder on gfx950: a forward pass over the whole sequence
+// that keeps what the reverse walk needs, then the reverse walk over the tokens.
+//
+// "RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", section "Training and serving
+// implications": pretraining backpropagates through the full sequence, and the gradient of one
+// state with respect to the previous one also runs through the self-attention keys and values
+// of the window, not only through s_t. The walk below therefore carries two kinds of gradient
+// from token t+1 back to token t: dLoss/ds_t through the next gated merge, and, per layer, the
+// gradients of every key/value still inside a later token's window (fp32 accumulators in a
+// ring of W slots). Memory keys/values collect gradients from every later token; those sums are
+// formed after the walk by a token-parallel pass over each memory entry.
+//
+// Per token and layer the walk runs, newest layer first (dres = gradient of the residual stream):
+//   FFN      recompute u = f [W1 W3] (f = RMSNorm(z)), dm = dres W2^T, du from the SiLU product,
+//            df = du [W1 W3]^T, dres += RMSNorm'(z) df
+//   cross    doc = dres Wco^T, dqc from one online pass over memory 0..t, dc = dqc Wcq^T,
+//            dres += RMSNorm'(y) dc
+//   self     do = dres Wo^T, dq and the window's key/value gradients from two passes over the
+//            window, da = [dq dk dv] [Wq Wk Wv]^T, dres += RMSNorm'(x) da
+// and then the gated merge (dLoss/de_t and the gradient carried to s_{t-1}). The per-token
+// GEMMs are the decoder step's split-K projections (k_proj) against transposed copies of the
+// packed weights. Weight gradients are sums over all (token, sequence) rows of x^T dy; the walk
+// stores both operands for Tc tokens at a time and adds them in large MFMA GEMMs per chunk.
+#include <math.h>
+
+#include "proj.h"
+
+namespace rlt {
+
+// ---- workspace -------------------------------------------------------------------------------
+namespace {
+constexpr size_t kAlignWs = 256;
+constexpr int kRowSplits = 32;  // row splits of the deterministic column sums
+constexpr int kChunkRows = 4096;
+size_t up(size_t x) { return (x + kAlignWs - 1) / kAlignWs * kAlignWs; }
+
+// Backward copies of the packed weights, in elements from the start of the bw region:
+// every matrix stored input-major (rows = input features of the forward map) in fragment order.
+struct BwOff {
+  size_t wg, wqkv, wo, wcq, wco, w13, w2, wm, total;
+};
+BwOff bw_off(const Dims& D) {
+  const size_t d = D.d, F = D.F, L = D.L, G = D.G;
+  BwOff o;
+  o.wg = 0;                        // [2d][d]   rows: e then u features; k: gate outputs
+  o.wqkv = o.wg + 2 * d * d;       // [L][d][3d] k: q, k, v outputs
+  o.wo = o.wqkv + L * 3 * d * d;   // [L][d][d]
+  o.wcq = o.wo + L * d * d;
+  o.wco = o.wcq + L * d * d;
+  o.w13 = o.wco + L * d * d;       // [L][d][2F] k: W1 outputs, then W3 outputs
+  o.w2 = o.w13 + L * 2 * F * d;    // [L][F][d]
+  o.wm = o.w2 + L * F * d;         // [G][d][2d] k: memory key outputs, then value outputs
+  o.total = o.wm + G * 2 * d * d;
+  return o;
+}
+}  // namespace
+
+TrainLayout train_layout(const Dims& D, int B, int64_t n) {
+  TrainLayout t;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t a = o;
+    o = up(o + bytes);
+    return a;
+  };
+  const size_t b = B, d = D.d, F = D.F, L = D.L, H = D.H, es = D.es, N = (size_t)n;
+  t.Tc = std::max<int64_t>(1, std::min<int64_t>(n, (kChunkRows + B - 1) / B));
+  t.Mc = t.Tc * B;
+  const size_t Mc = (size_t)t.Mc;
+  t.state = take(state_layout(D, B).total);
+  t.mem_k = take((size_t)D.G * b * N * d * es);
+  t.mem_v = take((size_t)D.G * b * N * d * es);
+  t.bw = take(bw_off(D).total * es);
+  t.s_hist = take((N + 1) * b * d * 4);
+  const size_t act = L * N * b * d;
+  t.xs = take(act * 4);
+  t.ys = take(act * 4);
+  t.zs = take(act * 4);
+  t.qs = take(act * 4);
+  t.qcs = take(act * 4);
+  t.os = take(act * es);
+  t.ocs = take(act * es);
+  t.docs = take(act * es);
+  t.khist = take(act * es);
+  t.vhist = take(act * es);
+  t.lse = take(L * N * b * H * 4);
+  t.dlt = take(L * N * b * H * 4);
+  t.dres = take(b * d * 4);
+  t.dn = take(b * d * 4);
+  t.dattn = take(b * d * 4);
+  t.u13 = take(b * 2 * F * 4);
+  t.gsave = take(b * d * 4);
+  t.carry = take(b * d * 4);
+  t.rinv = take(b * 3 * 4);
+  t.dkacc = take(L * b * D.W * d * 4);
+  t.dvacc = take(L * b * D.W * d * 4);
+  t.ca = take(L * Mc * d * es);
+  t.cc = take(L * Mc * d * es);
+  t.cf = take(L * Mc * d * es);
+  t.cm = take(L * Mc * F * es);
+  t.yqkv = take(L * Mc * 3 * d * es);
+  t.yo = take(L * Mc * d * es);
+  t.ycq = take(L * Mc * d * es);
+  t.yco = take(L * Mc * d * es);
+  t.y13 = take(L * Mc * 2 * F * es);
+  t.y2 = take(L * Mc * d * es);
+  t.pg = take((3 * L + 1) * Mc * d * 4);
+  t.xg = take(Mc * 2 * d * es);
+  t.yg = take(Mc * d * es);
+  t.part = take((3 * L + 1) * kRowSplits * d * 4);
+  t.dkv = take(b * N * 2 * d * es);
+  t.total = o;
+  return t;
+}
+
+// ---- small kernels ---------------------------------------------------------------------------
+
+// Transposes a packed forward matrix (rows = N outputs, k = K inputs, fragment order) into the
+// backward layout (rows = K inputs, k = N outputs). With w13 set the source rows interleave W1
+// and W3 in blocks of 16 and the destination k runs over all W1 outputs, then all W3 outputs.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_repack(const T* __restrict__ src, int N, int K,
+                                                     T* __restrict__ dst, int w13, int F,
+                                                     int64_t mats) {
+  const int64_t per = (int64_t)N * K;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= per * mats) return;
+  const int64_t mi = i / per;
+  const int64_t r = i - mi * per;
+  const int k = (int)(r / N), c = (int)(r - (int64_t)k * N);  // dst row k (input), column c
+  int row = c;                                                  // source row (output)
+  if (w13) {
+    const int which = c / F, f = c - which * F;
+    row = 32 * (f / 16) + 16 * which + f % 16;
+  }
+  dst[mi * per + frag_off(k, c, N / 32)] = src[mi * per + frag_off(row, k, K / 32)];
+}
+
+// dst rows [B][d] = s* (the state before the first token).
+__global__ __launch_bounds__(kThreads) void k_fill_start(float* __restrict__ dst,
+                                                         const float* __restrict__ s_star, int d,
+                                                         int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < total) dst[i] = s_star[i % d];
+}
+
+// Copies of the forward's working buffers at three points of each layer of token i.
+//   stage 0 (after the q/k/v projection): x = h, q, and this token's key/value ring slot
+//   stage 1 (after the cross-attention query): y = h, qc, o (self-attention output)
+//   stage 2 (after the cross-attention output projection): z = h, oc (cross output)
+struct SaveArgs {
+  int stage, B, d, H, hd, W;
+  int64_t n, i;
+  const float* h;
+  const float* q;
+  const void* o;  // fragment order [B16][d]
+  const void* ring_k;  // this layer's ring block [B][H][W][hd]
+  const void* ring_v;
+  float* h_dst;  // [B][d] rows of token i
+  float* q_dst;
+  void* o_dst;   // row-major [B][d]
+  void* k_dst;   // this layer's history block [B][H][n][hd]
+  void* v_dst;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_save(SaveArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)a.B * a.d) return;
+  const int b = (int)(idx / a.d), c = (int)(idx - (int64_t)b * a.d);
+  a.h_dst[idx] = a.h[idx];
+  if (a.stage < 2) a.q_dst[idx] = a.q[idx];
+  if (a.stage == 0) {
+    const int hh = c / a.hd, dd = c - hh * a.hd;
+    const int64_t ring = (((int64_t)b * a.H + hh) * a.W + (int)(a.i % a.W)) * a.hd + dd;
+    const int64_t hist = (((int64_t)b * a.H + hh) * a.n + a.i) * a.hd + dd;
+    static_cast<T*>(a.k_dst)[hist] = static_cast<const T*>(a.ring_k)[ring];
+    static_cast<T*>(a.v_dst)[hist] = static_cast<const T*>(a.ring_v)[ring];
+  } else {
+    static_cast<T*>(a.o_dst)[idx] = static_cast<const T*>(a.o)[frag_off(b, c, a.d / 32)];
+  }
+}
+
+// s_traj[b][i] = s_hist[i + 1][b]
+__global__ __launch_bounds__(kThreads) void k_traj(const float* __restrict__ s_hist,
+                                                   float* __restrict__ out, int B, int64_t n,
+                                                   int d) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)B * n * d) return;
+  const int c = (int)(idx % d);
+  const int64_t rest = idx / d;
+  const int64_t i = rest % n;
+  const int b = (int)(rest / n);
+  out[idx] = s_hist[((i + 1) * B + b) * d + c];
+}
+
+// Start of token i's walk: dres = G[:, i] + carry (carry = dLoss/ds_i through token i+1), and
+// its dtype copy (the operand of the FFN down-projection's backward).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_walk_begin(const float* __restrict__ G,
+                                                         const float* __restrict__ carry,
+                                                         float* __restrict__ dres,
+                                                         T* __restrict__ dres_t, int B, int d,
+                                                         int64_t n, int64_t i) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)B * d) return;
+  const int b = (int)(idx / d), c = (int)(idx - (int64_t)b * d);
+  const float v = G[((int64_t)b * n + i) * d + c] + carry[idx];
+  dres[idx] = v;
+  dres_t[idx] = to_elem<T>(v);
+}
+
+// The three RMSNorm operands of one layer of one token, from the saved residual streams:
+// a = gain0 x r_x, c = gain1 y r_y, f = gain2 z r_z (dtype rows), and the scales r. One
+// workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_norm_rows3(const float* __restrict__ x,
+                                                         const float* __restrict__ y,
+                                                         const float* __restrict__ z,
+                                                         const float* __restrict__ gamma, int d,
+                                                         float eps, T* __restrict__ a,
+                                                         T* __restrict__ c, T* __restrict__ f,
+                                                         float* __restrict__ rinv) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const float* src[3] = {x + (int64_t)b * d, y + (int64_t)b * d, z + (int64_t)b * d};
+  T* dst[3] = {a + (int64_t)b * d, c + (int64_t)b * d, f + (int64_t)b * d};
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d; j += kThreads) ss += src[w][j] * src[w][j];
+    const float r = rsqrtf(block_sum(ss, red) / (float)d + eps);
+    for (int j = threadIdx.x; j < d; j += kThreads)
+      dst[w][j] = to_elem<T>(gamma[w * d + j] * src[w][j] * r);
+    if (threadIdx.x == 0) rinv[b * 3 + w] = r;
+  }
+}
+
+// Backward of an RMSNorm y = gain * x * r at one row per workgroup, added to the residual
+// gradient: dres += gain * dn * r - x * r^3 * sum(gain * dn * x) / d. Also writes dres in the
+// working dtype (the next GEMM operand, when res_t != NULL) and the row's gain-gradient terms
+// dn * x * r (fp32, summed over rows later).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_norm_back(const float* __restrict__ dn,
+                                                        const float* __restrict__ x,
+                                                        const float* __restrict__ gain,
+                                                        const float* __restrict__ rinv, int which,
+                                                        int d, float* __restrict__ dres,
+                                                        T* __restrict__ res_t,
+                                                        float* __restrict__ pgain) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int64_t o = (int64_t)b * d;
+  const float r = rinv[b * 3 + which];
+  float s = 0.f;
+  for (int j = threadIdx.x; j < d; j += kThreads) s += gain[j] * dn[o + j] * x[o + j];
+  const float inner = block_sum(s, red);
+  const float k = r * r * r * inner / (float)d;
+  for (int j = threadIdx.x; j < d; j += kThreads) {
+    const float g = dn[o + j], xv = x[o + j];
+    const float v = dres[o + j] + gain[j] * g * r - xv * k;
+    dres[o + j] = v;
+    if (res_t) res_t[o + j] = to_elem<T>(v);
+    pgain[o + j] = g * xv * r;
+  }
+}
+
+// Column sums of nmat row-major [rows][d] fp32 matrices (matrix m at P + m * stride * d),
+// deterministic: k_colsum_part sums kRowSplits row ranges, k_colsum_final adds the splits in
+// order to the matrix's output.
+__global__ __launch_bounds__(kThreads) void k_colsum_part(const float* __restrict__ P, int64_t rows,
+                                                          int64_t stride, int d,
+                                                          float* __restrict__ part) {
+  const int m = blockIdx.z, split = blockIdx.y;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= d) return;
+  const int64_t per = (rows + kRowSplits - 1) / kRowSplits;
+  const int64_t r0 = split * per, r1 = std::min<int64_t>(rows, r0 + per);
+  const float* p = P + (int64_t)m * stride * d + c;
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += p[r * d];
+  part[((int64_t)m * kRowSplits + split) * d + c] = s;
+}
+
+struct ColOut {
+  float* gamma;   // matrices 0 .. 3L-1 add into gamma + m * d
+  float* extra;   // matrix 3L (if present) adds into extra
+  int n_gamma;
+};
+
+__global__ __launch_bounds__(kThreads) void k_colsum_final(const float* __restrict__ part, int d,
+                                                           ColOut out) {
+  const int m = blockIdx.y;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= d) return;
+  float s = 0.f;
+  for (int k = 0; k < kRowSplits; ++k) s += part[((int64_t)m * kRowSplits + k) * d + c];
+  float* dst = m < out.n_gamma ? out.gamma + (int64_t)m * d : out.extra;
+  dst[c] += s;
+}
+
+// ---- per-token GEMM operands and epilogues -----------------------------------------------------
+
+template <typename T>
+struct ARows {  // A = row-major [M][ld] dtype rows
+  static constexpr bool kNorm = false;
+  static constexpr int kPer = sizeof(T) == 2 ? 1 : 2, kShared = 0;
+  const T* a;
+  int64_t ld;
+  int M;
+  __device__ void issue(int, int row, int step, int lane, u32x4* r) const {
+    const T* p = a + (int64_t)row * ld + step * 32 + (lane >> 4) * 8;
+    r[0] = ld16(p);
+    if constexpr (kPer == 2) r[1] = ld16(p + 4);
+  }
+  __device__ void issue_shared(int, u32x4*) const {}
+  __device__ Frag<T> make(const u32x4* r, const u32x4*) const {
+    Frag<T> f;
+    f.from_raw(r);
+    return f;
+  }
+  // token-GEMM interface
+  __device__ Frag<T> load(int row, int k, float&) const {
+    Frag<T> f;
+    if (row < M) f.load(a + (int64_t)row * ld + k);
+    else f.zero();
+    return f;
+  }
+};
+
+// FFN recompute: u1 = f W1, u3 = f W3 (packed columns interleave 16 of each per 32); keeps u1
+// and u3 (fp32, [M][2F]: u1 then u3) and writes m = silu(u1) u3 (dtype rows [M][F]).
+template <typename T>
+struct EpiU13 {
+  float* u;
+  T* m;
+  int M, F;
+  template <int NT, int BM, int BN, int E>
+  __device__ void prefetch(Pre<E>&, int, int) const {}
+  template <int NT, int BM, int BN, int E>
+  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>&) const {
+    constexpr int half = BN / 2;
+    for (int i = threadIdx.x; i < BM * half; i += NT) {
+      const int r = i / half, j = i - r * half;
+      const int row = r0 + r;
+      if (row >= M) continue;
+      const int cp = (j / 16) * 32 + (j % 16);
+      const float z1 = tile[r * ld + cp], z3 = tile[r * ld + cp + 16];
+      const int f = c0 / 2 + j;
+      u[(int64_t)row * 2 * F + f] = z1;
+      u[(int64_t)row * 2 * F + F + f] = z3;
+      m[(int64_t)row * F + f] = to_elem<T>(z1 * sigmoidf_(z1) * z3);
+    }
+  }
+};
+
+// dm -> du1 = dm u3 sigma(u1) (1 + u1 (1 - sigma(u1))), du3 = dm silu(u1), dtype rows [M][2F].
+template <typename T>
+struct EpiSiluBack : EpiTile<EpiSiluBack<T>> {
+  const float* u;
+  T* du;
+  int M, F;
+  __device__ void op(int row, int col, float dm) const {
+    if (row >= M) return;
+    const float u1 = u[(int64_t)row * 2 * F + col], u3 = u[(int64_t)row * 2 * F + F + col];
+    const float sg = sigmoidf_(u1);
+    du[(int64_t)row * 2 * F + col] = to_elem<T>(dm * u3 * sg * (1.f + u1 * (1.f - sg)));
+    du[(int64_t)row * 2 * F + F + col] = to_elem<T>(dm * u1 * sg);
+  }
+};
+
+// Gate recompute: v = [e ; u] W_g, g = sigmoid(v + b); dz = dres (e - u) g (1 - g). Writes dz
+// (dtype and fp32 rows), g, and the gate operand [e ; u] (dtype rows [M][2d]).
+template <typename T>
+struct EpiGateBack : EpiTile<EpiGateBack<T>> {
+  const T* e;
+  int64_t lde;
+  const float* s;  // s_{t-1} rows
+  const float* b;
+  const float* dres;
+  float alpha;
+  T* dz;
+  float* dz32;
+  float* g;
+  T* xg;
+  int M, d;
+  __device__ void op(int row, int col, float v) const {
+    if (row >= M) return;
+    const int64_t o = (int64_t)row * d + col;
+    const float gv = sigmoidf_(v + b[col]);
+    const float ev = to_f32<T>(e[(int64_t)row * lde + col]), uv = alpha * s[o];
+    const float z = dres[o] * (ev - uv) * gv * (1.f - gv);
+    dz[o] = to_elem<T>(z);
+    dz32[o] = z;
+    g[o] = gv;
+    xg[(int64_t)row * 2 * d + col] = to_elem<T>(ev);
+    xg[(int64_t)row * 2 * d + d + col] = to_elem<T>(uv);
+  }
+};
+
+// [de_gate | du_gate] = dz W_g^T: de_t = dres g + de_gate, carry = alpha (dres (1 - g) + du_gate)
+struct EpiGateOut : EpiTile<EpiGateOut> {
+  const float* dres;
+  const float* g;
+  float* de;  // row b of token t (NULL: not wanted)
+  int64_t de_ld;
+  float* carry;
+  float alpha;
+  int M, d;
+  __device__ void op(int row, int col, float v) const {
+    if (row >= M) return;
+    if (col < d) {
+      const int64_t o = (int64_t)row * d + col;
+      if (de) de[(int64_t)row * de_ld + col] = dres[o] * g[o] + v;
+    } else {
+      const int64_t o = (int64_t)row * d + (col - d);
+      carry[o] = alpha * (dres[o] * (1.f - g[o]) + v);
+    }
+  }
+};
+
+// de += [dKm | dVm] [WmK | WmV]^T (token GEMM, register tiles)
+struct EpiAddF32 {
+  float* out;
+  int64_t ld;
+  int M;
+  template <int FM, int FN>
+  __device__ void tile(const f32x4 (&acc)[FM][FN], int rbase, int cwave, int lane) const {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rbase + 16 * fm + i;
+          if (row < M) out[(int64_t)row * ld + cwave + 16 * fn + (lane & 15)] += acc[fm][fn][i];
+        }
+  }
+};
+
+// ---- attention backward of one token ----------------------------------------------------------
+
+template <typename T, int HD>
+struct AGeo {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int LPR = HD / VEC;
+  static constexpr int RPW = kWave / LPR;
+};
+
+// Online state of one row slot for the backward of o = softmax(s) v with s_j = scale q.k_j:
+// m = running max, l = sum e_j, c = sum e_j dp_j (dp_j = do.v_j), A = sum e_j dp_j k_j,
+// Bk = sum e_j k_j, with e_j = exp(s_j - m). Then D = c / l = sum p_j dp_j and
+// dq = scale (A - D Bk) / l.
+template <int V>
+struct BwdState {
+  float m, l, c, A[V], Bk[V];
+  __device__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+    c = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) A[i] = Bk[i] = 0.f;
+  }
+  __device__ void merge(float mo, float lo, float co, const float* Ao, const float* Bo) {
+    const float mn = fmaxf(m, mo);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mn);
+    const float b = mo == -INFINITY ? 0.f : __expf(mo - mn);
+    l = l * a + lo * b;
+    c = c * a + co * b;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      A[i] = A[i] * a + Ao[i] * b;
+      Bk[i] = Bk[i] * a + Bo[i] * b;
+    }
+    m = mn;
+  }
+};
+
+// Cross-attention backward of token t (0-based) for one (sequence, head) per workgroup: keys
+// and values are memory entries 0..t of the layer's group. Writes dq (dtype row-major, the
+// query-projection backward's operand), lse = m + log l and D (for the memory gradients formed
+// after the walk), and a dtype copy of do (same use).
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_xattn_back(
+    const float* __restrict__ q, const float* __restrict__ dout, const T* __restrict__ K,
+    const T* __restrict__ V, int64_t bh_stride, int ntok, int H, float scale,
+    T* __restrict__ dq, float* __restrict__ lse, float* __restrict__ dlt, T* __restrict__ do_t) {
+  using G = AGeo<T, HD>;
+  constexpr int VEC = G::VEC, RPB = G::RPW * NW;
+  __shared__ float s_m[NW], s_l[NW], s_c[NW];
+  __shared__ float s_A[NW][HD], s_B[NW][HD];
+  const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int sub = lane % G::LPR, slot = lane / G::LPR;
+  const T* Kb = K + (int64_t)bh * bh_stride + sub * VEC;
+  const T* Vb = V + (int64_t)bh * bh_stride + sub * VEC;
+  const int64_t qo = (int64_t)b * d + hh * HD + sub * VEC;
+  float qv[VEC], dv[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    qv[i] = q[qo + i] * scale;
+    dv[i] = dout[qo + i];
+  }
+  BwdState<VEC> S;
+  S.init();
+  const int first = wave * G::RPW + slot;
+  for (int base = 0; base < ntok; base += RPB * U) {
+    u32x4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = base + u * RPB + first;
+      const bool ok = row < ntok;
+      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+    }
+    float sc[U], dp[U];
+    float mb = S.m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VEC], vf[VEC];
+      unpack(kr[u], kf);
+      unpack(vr[u], vf);
+      float s = 0.f, p = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        s += qv[i] * kf[i];
+        p += dv[i] * vf[i];
+      }
+#pragma unroll
+      for (int o = G::LPR / 2; o >= 1; o >>= 1) {
+        s += __shfl_xor(s, o, kWave);
+        p += __shfl_xor(p, o, kWave);
+      }
+      const bool ok = base + u * RPB + first < ntok;
+      sc[u] = ok ? s : -INFINITY;
+      dp[u] = p;
+      mb = fmaxf(mb, sc[u]);
+    }
+    if (mb == -INFINITY) continue;
+    const float cs = S.m == -INFINITY ? 0.f : __expf(S.m - mb);
+    S.l *= cs;
+    S.c *= cs;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      S.A[i] *= cs;
+      S.Bk[i] *= cs;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - mb);
+      float kf[VEC];
+      unpack(kr[u], kf);
+      S.l += e;
+      S.c += e * dp[u];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        S.A[i] += e * dp[u] * kf[i];
+        S.Bk[i] += e * kf[i];
+      }
+    }
+    S.m = mb;
+  }
+#pragma unroll
+  for (int o = G::LPR; o < kWave; o <<= 1) {
+    const float mo = __shfl_xor(S.m, o, kWave), lo = __shfl_xor(S.l, o, kWave),
+                co = __shfl_xor(S.c, o, kWave);
+    float Ao[VEC], Bo[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      Ao[i] = __shfl_xor(S.A[i], o, kWave);
+      Bo[i] = __shfl_xor(S.Bk[i], o, kWave);
+    }
+    S.merge(mo, lo, co, Ao, Bo);
+  }
+  if (slot == 0) {
+    if (sub == 0) {
+      s_m[wave] = S.m;
+      s_l[wave] = S.l;
+      s_c[wave] = S.c;
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      s_A[wave][sub * VEC + i] = S.A[i];
+      s_B[wave][sub * VEC + i] = S.Bk[i];
+    }
+  }
+  __syncthreads();
+  if (tid < HD) {
+    BwdState<1> R;
+    R.m = s_m[0];
+    R.l = s_l[0];
+    R.c = s_c[0];
+    R.A[0] = s_A[0][tid];
+    R.Bk[0] = s_B[0][tid];
+    for (int w = 1; w < NW; ++w) R.merge(s_m[w], s_l[w], s_c[w], &s_A[w][tid], &s_B[w][tid]);
+    const float D = R.c / R.l;
+    const int64_t o = (int64_t)b * d + hh * HD + tid;
+    dq[o] = to_elem<T>(scale * (R.A[0] - D * R.Bk[0]) / R.l);
+    do_t[o] = to_elem<T>(dout[o]);
+    if (tid == 0) {
+      lse[bh] = R.m + __logf(R.l);
+      dlt[bh] = D;
+    }
+  }
+}
+
+// Self-attention backward of token t for one (sequence, head) per workgroup over the window
+// keys j = lo..t (lo = max(0, t - W + 1)) of the layer's key/value history. Pass 1 forms the
+// softmax normaliser and D; pass 2 adds every key's gradient scale dz_j q and value gradient
+// p_j do into the fp32 accumulators (slot j % W), and for j = t, whose gradient is then
+// complete, writes dk, dv (with dq) to out [M][3d] and clears the slot.
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_swa_back(
+    const float* __restrict__ q, const float* __restrict__ dout, const T* __restrict__ K,
+    const T* __restrict__ V, int64_t n, int64_t t, int W, int H, float scale,
+    float* __restrict__ dkacc, float* __restrict__ dvacc, T* __restrict__ out) {
+  using G = AGeo<T, HD>;
+  constexpr int VEC = G::VEC, RPB = G::RPW * NW;
+  __shared__ float s_m[NW], s_l[NW], s_c[NW];
+  __shared__ float s_q[NW][HD];
+  __shared__ float s_stat[2];
+  const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int sub = lane % G::LPR, slot = lane / G::LPR;
+  const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int nk = (int)(t - lo + 1);
+  const T* Kb = K + ((int64_t)bh * n + lo) * HD + sub * VEC;
+  const T* Vb = V + ((int64_t)bh * n + lo) * HD + sub * VEC;
+  const int64_t qo = (int64_t)b * d + hh * HD + sub * VEC;
+  float qv[VEC], dv[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    qv[i] = q[qo + i];
+    dv[i] = dout[qo + i];
+  }
+  const int first = wave * G::RPW + slot;
+  auto scores = [&](int row, float& s, float& p) {
+    float kf[VEC], vf[VEC];
+    unpack(ld16(Kb + (int64_t)row * HD), kf);
+    unpack(ld16(Vb + (int64_t)row * HD), vf);
+    s = 0.f;
+    p = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      s += qv[i] * kf[i];
+      p += dv[i] * vf[i];
+    }
+#pragma unroll
+    for (int o = G::LPR / 2; o >= 1; o >>= 1) {
+      s += __shfl_xor(s, o, kWave);
+      p += __shfl_xor(p, o, kWave);
+    }
+    s *= scale;
+  };
+  // pass 1: m, l, c over the window (every lane of a slot walks the same rows)
+  float m = -INFINITY, l = 0.f, c = 0.f;
+  for (int row = first; row - first < nk; row += RPB) {
+    if (row >= nk) break;
+    float s, p;
+    scores(row, s, p);
+    const float mn = fmaxf(m, s);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mn), e = __expf(s - mn);
+    l = l * a + e;
+    c = c * a + e * p;
+    m = mn;
+  }
+#pragma unroll
+  for (int o = G::LPR; o < kWave; o <<= 1) {
+    const float mo = __shfl_xor(m, o, kWave), lo2 = __shfl_xor(l, o, kWave),
+                co = __shfl_xor(c, o, kWave);
+    const float mn = fmaxf(m, mo);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mn);
+    const float bb = mo == -INFINITY ? 0.f : __expf(mo - mn);
+    l = l * a + lo2 * bb;
+    c = c * a + co * bb;
+    m = mn;
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+    s_c[wave] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = s_m[0], Lx = s_l[0], C = s_c[0];
+    for (int w = 1; w < NW; ++w) {
+      const float mn = fmaxf(M, s_m[w]);
+      const float a = M == -INFINITY ? 0.f : __expf(M - mn);
+      const float bb = s_m[w] == -INFINITY ? 0.f : __expf(s_m[w] - mn);
+      Lx = Lx * a + s_l[w] * bb;
+      C = C * a + s_c[w] * bb;
+      M = mn;
+    }
+    s_stat[0] = M + __logf(Lx);  // log-sum-exp
+    s_stat[1] = C / Lx;          // D = sum_j p_j dp_j
+  }
+  __syncthreads();
+  const float lse = s_stat[0], D = s_stat[1];
+  // pass 2: key/value gradients into the accumulators, dq in registers
+  float dqa[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) dqa[i] = 0.f;
+  float* ak = dkacc + (int64_t)bh * W * HD + sub * VEC;
+  float* av = dvacc + (int64_t)bh * W * HD + sub * VEC;
+  for (int row = first; row < nk; row += RPB) {
+    float s, p;
+    scores(row, s, p);
+    const float pj = __expf(s - lse);
+    const float dz = pj * (p - D);
+    float kf[VEC];
+    unpack(ld16(Kb + (int64_t)row * HD), kf);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) dqa[i] += dz * kf[i];
+    const int64_t j = lo + row;
+    const int64_t so = (int64_t)(j % W) * HD;
+    float gk[VEC], gv[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      gk[i] = ak[so + i] + scale * dz * qv[i];
+      gv[i] = av[so + i] + pj * dv[i];
+    }
+    if (j == t) {  // every later token that saw this key has been walked
+      const int64_t oo = (int64_t)b * 3 * d + hh * HD + sub * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        out[oo + d + i] = to_elem<T>(gk[i]);
+        out[oo + 2 * d + i] = to_elem<T>(gv[i]);
+        ak[so + i] = 0.f;
+        av[so + i] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        ak[so + i] = gk[i];
+        av[so + i] = gv[i];
+      }
+    }
+  }
+  // dq: sum over the slots of the wave, then over the waves
+#pragma unroll
+  for (int o = G::LPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) dqa[i] += __shfl_xor(dqa[i], o, kWave);
+  if (slot == 0)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) s_q[wave][sub * VEC + i] = dqa[i];
+  __syncthreads();
+  if (tid < HD) {
+    float v = 0.f;
+    for (int w = 0; w < NW; ++w) v += s_q[w][tid];
+    out[(int64_t)b * 3 * d + hh * HD + tid] = to_elem<T>(scale * v);
+  }
+}
+
+// ---- memory gradients after the walk ------------------------------------------------------------
+// For memory entry j of one (sequence, head) and each layer using the group:
+//   dV_j = sum_{t >= j} p_tj do_t,  dK_j = scale sum_{t >= j} p_tj (do_t . V_j - D_t) qc_t
+// with p_tj = exp(scale qc_t . K_j - lse_t). One workgroup takes 64 entries (4 lanes each, a
+// quarter of the head dims per lane) and walks the later tokens in tiles staged in LDS. Writes
+// [dK | dV] rows (b * n + j) in dtype.
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void k_mem_back(
+    const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ qcs,
+    const T* __restrict__ docs, const float* __restrict__ lse, const float* __restrict__ dlt,
+    int l0, int l1, int B, int64_t n, int H, float scale, T* __restrict__ dkv) {
+  constexpr int KB = 64, TQ = 16, Q4 = HD / 4;
+  __shared__ float s_q[TQ][HD], s_do[TQ][HD], s_lse[TQ], s_D[TQ];
+  const int bh = blockIdx.y, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int64_t j0 = (int64_t)blockIdx.x * KB;
+  const int tid = threadIdx.x, key = tid / 4, part = tid % 4;
+  const int64_t j = j0 + key;
+  const bool valid = j < n;
+  float kf[Q4], vf[Q4], gk[Q4], gv[Q4];
+  const T* kp = K + ((int64_t)bh * n + (valid ? j : 0)) * HD + part * Q4;
+  const T* vp = V + ((int64_t)bh * n + (valid ? j : 0)) * HD + part * Q4;
+#pragma unroll
+  for (int i = 0; i < Q4; ++i) {
+    kf[i] = to_f32<T>(kp[i]);
+    vf[i] = to_f32<T>(vp[i]);
+    gk[i] = 0.f;
+    gv[i] = 0.f;
+  }
+  const int64_t layer = n * B * d;  // elements per layer of qcs / docs
+  for (int l = l0; l < l1; ++l) {
+    for (int64_t t0 = j0; t0 < n; t0 += TQ) {
+      __syncthreads();
+      for (int x = tid; x < TQ * HD; x += kThreads) {
+        const int r = x / HD, c = x - r * HD;
+        const int64_t t = t0 + r;
+        const int64_t o = l * layer + (t * B + b) * d + hh * HD + c;
+        s_q[r][c] = t < n ? qcs[o] : 0.f;
+        s_do[r][c] = t < n ? to_f32<T>(docs[o]) : 0.f;
+      }
+      if (tid < TQ) {
+        const int64_t t = t0 + tid;
+        const int64_t o = ((int64_t)l * n + t) * B * H + bh;
+        s_lse[tid] = t < n ? lse[o] : INFINITY;
+        s_D[tid] = t < n ? dlt[o] : 0.f;
+      }
+      __syncthreads();
+      for (int r = 0; r < TQ; ++r) {
+        float s = 0.f, p = 0.f;
+#pragma unroll
+        for (int i = 0; i < Q4; ++i) {
+          s += s_q[r][part * Q4 + i] * kf[i];
+          p += s_do[r][part * Q4 + i] * vf[i];
+        }
+        s += __shfl_xor(s, 1, kWave);
+        s += __shfl_xor(s, 2, kWave);
+        p += __shfl_xor(p, 1, kWave);
+        p += __shfl_xor(p, 2, kWave);
+        const int64_t t = t0 + r;
+        const float pj = (valid && t >= j && t < n) ? __expf(scale * s - s_lse[r]) : 0.f;
+        const float dz = pj * (p - s_D[r]);
+#pragma unroll
+        for (int i = 0; i < Q4; ++i) {
+          gv[i] += pj * s_do[r][part * Q4 + i];
+          gk[i] += scale * dz * s_q[r][part * Q4 + i];
+        }
+      }
+    }
+  }
+  if (!valid) return;
+  T* o = dkv + ((int64_t)b * n + j) * 2 * d + hh * HD + part * Q4;
+#pragma unroll
+  for (int i = 0; i < Q4; ++i) {
+    o[i] = to_elem<T>(gk[i]);
+    o[d + i] = to_elem<T>(gv[i]);
+  }
+}
+
+// ---- weight gradients: C[K][N] += X[M][K]^T Y[M][N] ----------------------------------------------
+// 64 x 64 output tile per workgroup (2 x 2 waves of 32 x 32), contraction over rows in steps of
+// 64. Both operand tiles are staged transposed in LDS ([k][m]), so one lane's MFMA fragment
+// (8 consecutive rows) is one 16-byte LDS read. Output column c goes to dst.p[c / split] at
+// (k, c % split) of a [K][split] fp32 matrix, added to what is there.
+struct WDst {
+  float* p[3];
+  int split;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_wgrad(const T* __restrict__ X, int64_t ldx,
+                                                    const T* __restrict__ Y, int64_t ldy,
+                                                    int64_t M, int K, int N, WDst dst) {
+  constexpr int BT = 64, MT = 64, PAD = 8, LDT = MT + PAD;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  __shared__ __align__(16) T xs[BT][LDT];
+  __shared__ __align__(16) T ys[BT][LDT];
+  const int tiles_n = N / BT;
+  const int k0 = (blockIdx.x / tiles_n) * BT, n0 = (blockIdx.x % tiles_n) * BT;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wk = wave / 2, wn = wave % 2;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int LOADS = BT * MT / VEC / kThreads;  // 16-byte loads per operand per thread
+  for (int64_t m0 = 0; m0 < M; m0 += MT) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int x = tid + u * kThreads;
+      const int mr = x / (BT / VEC), kc = (x % (BT / VEC)) * VEC;
+      const int64_t m = m0 + mr;
+      u32x4 rx = u32x4{0, 0, 0, 0}, ry = u32x4{0, 0, 0, 0};
+      if (m < M) {
+        rx = ld16(X + m * ldx + k0 + kc);
+        ry = ld16(Y + m * ldy + n0 + kc);
+      }
+      const T* px = reinterpret_cast<const T*>(&rx);
+      const T* py = reinterpret_cast<const T*>(&ry);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        xs[kc + e][mr] = px[e];
+        ys[kc + e][mr] = py[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < MT; ks += 32) {
+      Frag<T> a[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i].load(&xs[wk * 32 + i * 16 + (lane & 15)][ks + (lane >> 4) * 8]);
+        bf[i].load(&ys[wn * 32 + i * 16 + (lane & 15)][ks + (lane >> 4) * 8]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mfma_16x16x32(acc[i][j], a[i], bf[j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = k0 + wk * 32 + i * 16 + (lane >> 4) * 4 + e;
+        const int c = n0 + wn * 32 + j * 16 + (lane & 15);
+        const int which = c / dst.split, cc = c - which * dst.split;
+        dst.p[which][(int64_t)k * dst.split + cc] += acc[i][j][e];
+      }
+}
+
+// ---- host side ---------------------------------------------------------------------------------
+
+template <typename T>
+static inline T* el(void* base, int64_t off) {
+  return static_cast<T*>(base) + off;
+}
+template <typename T>
+static inline const T* el(const void* base, int64_t off) {
+  return static_cast<const T*>(base) + off;
+}
+static inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+#define RLT_TRY(...)                       \
+  do {                                     \
+    hipError_t err_ = (__VA_ARGS__);       \
+    if (err_ != hipSuccess) return err_;   \
+  } while (0)
+
+template <typename T>
+static hipError_t wgrad(const T* X, int64_t ldx, const T* Y, int64_t ldy, int64_t M, int K, int N,
+                        WDst dst, hipStream_t st) {
+  if (K % 64 || N % 64 || M <= 0) return hipErrorInvalidValue;
+  return launch(k_wgrad<T>, dim3((unsigned)((K / 64) * (N / 64))), dim3(kThreads), Exec(st), X,
+                ldx, Y, ldy, M, K, N, dst);
+}
+
+template <typename T, int HD>
+static hipError_t xattn_back(int BH, const float* q, const float* dout, const T* K, const T* V,
+                             int64_t bh_stride, int ntok, int H, T* dq, float* lse, float* dlt,
+                             T* do_t, hipStream_t st) {
+  const float scale = 1.f / sqrtf((float)HD);
+  const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
+#define RLT_XB(NW)                                                                             \
+  return launch(k_xattn_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), Exec(st), q, dout, K, V, \
+                bh_stride, ntok, H, scale, dq, lse, dlt, do_t)
+  if (nw == 4) RLT_XB(4);
+  if (nw == 8) RLT_XB(8);
+  RLT_XB(16);
+#undef RLT_XB
+}
+
+template <typename T, int HD>
+static hipError_t swa_back(int BH, const float* q, const float* dout, const T* K, const T* V,
+                           int64_t n, int64_t t, int W, int H, float* dkacc, float* dvacc, T* out,
+                           hipStream_t st) {
+  const float scale = 1.f / sqrtf((float)HD);
+  const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
+#define RLT_SB(NW)                                                                             \
+  return launch(k_swa_back<T, HD, NW>, dim3(BH), dim3(NW * kWave), Exec(st), q, dout, K, V, n, \
+                t, W, H, scale, dkacc, dvacc, out)
+  if (nw == 4) RLT_SB(4);
+  if (nw == 8) RLT_SB(8);
+  RLT_SB(16);
+#undef RLT_SB
+}
+
+// Column sums of `nmat` fp32 matrices of `rows` valid rows (matrix m at P + m * stride * d)
+// added to out (matrices below out.n_gamma into out.gamma + m * d, the next into out.extra).
+static hipError_t colsums(const float* P, int nmat, int64_t rows, int64_t stride, int d,
+                          float* part, ColOut out, hipStream_t st) {
+  RLT_TRY(launch(k_colsum_part, dim3(blocks_for(d), kRowSplits, nmat), dim3(kThreads), Exec(st), P,
+                 rows, stride, d, part));
+  return launch(k_colsum_final, dim3(blocks_for(d), nmat), dim3(kThreads), Exec(st),
+                (const float*)part, d, out);
+}
+
+template <typename T>
+struct Walk {  // pointers into the workspace of one call
+  const Dims& D;
+  int B;
+  int64_t n;
+  const TrainLayout& TL;
+  void* ws;
+  template <typename P>
+  P* at(size_t off) const {
+    return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+  }
+  // rows of chunk-local token li in a per-layer chunk buffer of `width` columns
+  T* chunk(size_t base, int l, int64_t width, int64_t li) const {
+    return at<T>(base) + ((int64_t)l * TL.Mc + li * B) * width;
+  }
+  // fp32 gain/bias-gradient rows: matrix m (3 l + which, or 3 L for the gate bias)
+  float* pg(int m, int64_t li) const {
+    return at<float>(TL.pg) + ((int64_t)m * TL.Mc + li * B) * D.d;
+  }
+  // [L][n][B][d] saved rows of layer l, token i
+  template <typename P>
+  P* saved(size_t base, int l, int64_t i) const {
+    return at<P>(base) + (((int64_t)l * n + i) * B) * D.d;
+  }
+};
+
+// The reverse walk over token i (chunk-local index li).
+template <typename T, int HD>
+static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M, const T* e,
+                             const float* G, float* de, int64_t i, int64_t li, hipStream_t st) {
+  const Dims& D = w.D;
+  const TrainLayout& TL = w.TL;
+  const int B = w.B, d = D.d, F = D.F, L = D.L, H = D.H, BH = B * D.H;
+  const int64_t n = w.n;
+  const BwOff bo = bw_off(D);
+  const T* bw = w.template at<T>(TL.bw);
+  float* dres = w.template at<float>(TL.dres);
+  float* dn = w.template at<float>(TL.dn);
+  float* dattn = w.template at<float>(TL.dattn);
+  float* rinv = w.template at<float>(TL.rinv);
+  float* u13 = w.template at<float>(TL.u13);
+  float* gsave = w.template at<float>(TL.gsave);
+  float* carry = w.template at<float>(TL.carry);
+  const Exec x(st);
+  const int64_t dd = (int64_t)d * d;
+
+  RLT_TRY(launch(k_walk_begin<T>, dim3(blocks_for((int64_t)B * d)), dim3(kThreads), x, G,
+                 (const float*)carry, dres, w.chunk(TL.y2, L - 1, d, li), B, d, n, i));
+  for (int l = L - 1; l >= 0; --l) {
+    const float* gam = P.gamma + (int64_t)l * 3 * d;
+    const float* xs = w.template saved<float>(TL.xs, l, i);
+    const float* ys = w.template saved<float>(TL.ys, l, i);
+    const float* zs = w.template saved<float>(TL.zs, l, i);
+    T* ca = w.chunk(TL.ca, l, d, li);
+    T* cc = w.chunk(TL.cc, l, d, li);
+    T* cf = w.chunk(TL.cf, l, d, li);
+    RLT_TRY(launch(k_norm_rows3<T>, dim3(B), dim3(kThreads), x, xs, ys, zs, gam, d, D.eps, ca,
+                   cc, cf, rinv));
+    // feed-forward: recompute u, then dm -> du -> df -> dres
+    {
+      EpiU13<T> ep{u13, w.chunk(TL.cm, l, F, li), B, F};
+      RLT_TRY(run_step_gemm<T>(B, 2 * F, d, el<T>(P.w13_t, (int64_t)l * 2 * F * d),
+                               ARows<T>{cf, d, B}, ep, x));
+    }
+    T* y13 = w.chunk(TL.y13, l, 2 * F, li);
+    {
+      EpiSiluBack<T> ep;
+      ep.u = u13; ep.du = y13; ep.M = B; ep.F = F;
+      RLT_TRY(run_step_gemm<T>(B, F, d, bw + bo.w2 + (int64_t)l * F * d,
+                               ARows<T>{w.chunk(TL.y2, l, d, li), d, B}, ep, x));
+    }
+    EpiStoreF32 to_dn;
+    to_dn.out = dn; to_dn.ld = d; to_dn.M = B;
+    EpiStoreF32 to_dattn;
+    to_dattn.out = dattn; to_dattn.ld = d; to_dattn.M = B;
+    RLT_TRY(run_step_gemm<T>(B, d, 2 * F, bw + bo.w13 + (int64_t)l * d * 2 * F,
+                             ARows<T>{y13, 2 * F, B}, to_dn, x));
+    T* yco = w.chunk(TL.yco, l, d, li);
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, zs, gam + 2 * d,
+                   (const float*)rinv, 2, d, dres, yco, w.pg(3 * l + 2, li)));
+    // cross-attention
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wco + l * dd, ARows<T>{yco, d, B}, to_dattn, x));
+    const int g = D.G == 1 ? 0 : l;
+    const int64_t grp = (int64_t)g * B * n * d;
+    T* ycq = w.chunk(TL.ycq, l, d, li);
+    const int64_t stat = ((int64_t)l * n + i) * BH;
+    RLT_TRY(xattn_back<T, HD>(BH, w.template saved<float>(TL.qcs, l, i), dattn,
+                              el<T>(M.k, grp), el<T>(M.v, grp), n * HD, (int)(i + 1), H, ycq,
+                              w.template at<float>(TL.lse) + stat,
+                              w.template at<float>(TL.dlt) + stat,
+                              w.template saved<T>(TL.docs, l, i), st));
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wcq + l * dd, ARows<T>{ycq, d, B}, to_dn, x));
+    T* yo = w.chunk(TL.yo, l, d, li);
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, ys, gam + d,
+                   (const float*)rinv, 1, d, dres, yo, w.pg(3 * l + 1, li)));
+    // self-attention
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn, x));
+    T* yqkv = w.chunk(TL.yqkv, l, 3 * d, li);
+    const int64_t hist = (int64_t)l * B * n * d, acc = (int64_t)l * B * D.W * d;
+    RLT_TRY(swa_back<T, HD>(BH, w.template saved<float>(TL.qs, l, i), dattn,
+                            w.template at<T>(TL.khist) + hist, w.template at<T>(TL.vhist) + hist,
+                            n, i, D.W, H, w.template at<float>(TL.dkacc) + acc,
+                            w.template at<float>(TL.dvacc) + acc, yqkv, st));
+    RLT_TRY(run_step_gemm<T>(B, d, 3 * d, bw + bo.wqkv + (int64_t)l * 3 * dd,
+                             ARows<T>{yqkv, 3 * d, B}, to_dn, x));
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, xs, gam,
+                   (const float*)rinv, 0, d, dres, l > 0 ? w.chunk(TL.y2, l - 1, d, li) : (T*)nullptr,
+                   w.pg(3 * l, li)));
+  }
+  // gated merge: recompute g, then dz, then de_t and the carry to s_{t-1}
+  const T* et = e + i * d;
+  const float* s_prev = w.template at<float>(TL.s_hist) + i * B * d;
+  T* yg = w.template at<T>(TL.yg) + li * B * d;
+  {
+    AGate<T> al{et, n * d, s_prev, D.alpha, B, d};
+    EpiGateBack<T> ep;
+    ep.e = et; ep.lde = n * d; ep.s = s_prev; ep.b = P.b_gate; ep.dres = dres; ep.alpha = D.alpha;
+    ep.dz = yg; ep.dz32 = w.pg(3 * L, li); ep.g = gsave;
+    ep.xg = w.template at<T>(TL.xg) + li * B * 2 * d; ep.M = B; ep.d = d;
+    RLT_TRY(run_step_gemm<T>(B, d, 2 * d, P.w_gate_t, al, ep, x));
+  }
+  {
+    EpiGateOut ep;
+    ep.dres = dres; ep.g = gsave; ep.de = de ? de + i * d : nullptr; ep.de_ld = n * d;
+    ep.carry = carry; ep.alpha = D.alpha; ep.M = B; ep.d = d;
+    RLT_TRY(run_step_gemm<T>(B, 2 * d, d, bw + bo.wg, ARows<T>{yg, d, B}, ep, x));
+  }
+  return hipSuccess;
+}
+
+// Weight and gain gradients of the chunk of tokens [i0, i1).
+template <typename T>
+static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, int64_t i1,
+                              hipStream_t st) {
+  const Dims& D = w.D;
+  const TrainLayout& TL = w.TL;
+  const int B = w.B, d = D.d, F = D.F, L = D.L;
+  const int64_t rows = (i1 - i0) * B, dd = (int64_t)d * d, dF = (int64_t)d * F;
+  for (int l = 0; l < L; ++l) {
+    RLT_TRY(wgrad<T>(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, rows, d,
+                     3 * d, WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}, st));
+    RLT_TRY(wgrad<T>(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, rows, d,
+                     d, WDst{{g.wo + l * dd, nullptr, nullptr}, d}, st));
+    RLT_TRY(wgrad<T>(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, rows, d, d,
+                     WDst{{g.wcq + l * dd, nullptr, nullptr}, d}, st));
+    RLT_TRY(wgrad<T>(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, rows, d,
+                     d, WDst{{g.wco + l * dd, nullptr, nullptr}, d}, st));
+    RLT_TRY(wgrad<T>(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, rows, d,
+                     2 * F, WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}, st));
+    RLT_TRY(wgrad<T>(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, rows, F, d,
+                     WDst{{g.w2 + l * dF, nullptr, nullptr}, d}, st));
+  }
+  RLT_TRY(wgrad<T>(w.template at<T>(TL.xg), 2 * d, w.template at<T>(TL.yg), d, rows, 2 * d, d,
+                   WDst{{g.w_gate, nullptr, nullptr}, d}, st));
+  return colsums(w.pg(0, 0), 3 * L + 1, rows, TL.Mc, d, w.template at<float>(TL.part),
+                 ColOut{g.gamma, g.b_gate, 3 * L}, st);
+}
+
+template <typename T, int HD>
+static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const void* e_v,
+                         const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
+                         hipStream_t st) {
+  const TrainLayout TL = train_layout(D, B, n);
+  const Walk<T> w{D, B, n, TL, ws};
+  const int d = D.d, F = D.F, L = D.L, H = D.H;
+  const T* e = static_cast<const T*>(e_v);
+  const Exec x(st);
+  // backward copies of the weights
+  {
+    const BwOff bo = bw_off(D);
+    T* bw = w.template at<T>(TL.bw);
+    auto repack = [&](const void* src, int N, int K, T* dst, int w13, int64_t mats) {
+      return launch(k_repack<T>, dim3(blocks_for((int64_t)N * K * mats)), dim3(kThreads), x,
+                    static_cast<const T*>(src), N, K, dst, w13, F, mats);
+    };
+    RLT_TRY(repack(P.w_gate_t, d, 2 * d, bw + bo.wg, 0, 1));
+    RLT_TRY(repack(P.wqkv_t, 3 * d, d, bw + bo.wqkv, 0, L));
+    RLT_TRY(repack(P.wo_t, d, d, bw + bo.wo, 0, L));
+    RLT_TRY(repack(P.wcq_t, d, d, bw + bo.wcq, 0, L));
+    RLT_TRY(repack(P.wco_t, d, d, bw + bo.wco, 0, L));
+    RLT_TRY(repack(P.w13_t, 2 * F, d, bw + bo.w13, 1, L));
+    RLT_TRY(repack(P.w2_t, d, F, bw + bo.w2, 0, L));
+    RLT_TRY(repack(P.wm_t, 2 * d, d, bw + bo.wm, 0, D.G));
+  }
+  // state, memory, s_0 = s*
+  StateBufs S;
+  {
+    const StateLayout SL = state_layout(D, B);
+    char* base = w.template at<char>(TL.state);
+    S.Bt = B;
+    S.s = reinterpret_cast<float*>(base + SL.s);
+    S.ring_k = base + SL.ring_k;
+    S.ring_v = base + SL.ring_v;
+    S.h = reinterpret_cast<float*>(base + SL.h);
+    S.q = reinterpret_cast<float*>(base + SL.q);
+    S.qc = reinterpret_cast<float*>(base + SL.qc);
+    S.hg = base + SL.hg;
+    S.ssq = reinterpret_cast<float*>(base + SL.ssq);
+    S.o = base + SL.o;
+    S.act = base + SL.act;
+    S.pos = reinterpret_cast<int64_t*>(base + SL.pos);
+    S.active = nullptr;
+    S.t_uniform = 0;
+  }
+  MemBufs M{w.template at<void>(TL.mem_k), w.template at<void>(TL.mem_v), n, B};
+  float* s_hist = w.template at<float>(TL.s_hist);
+  RLT_TRY(launch_reset(D, B, P, S, st));
+  RLT_TRY(launch_memproj(D, B, P, M, e, n, 0, n, x));
+  RLT_TRY(launch(k_fill_start, dim3(blocks_for((int64_t)B * d)), dim3(kThreads), x, s_hist,
+                 (const float*)P.s_star, d, (int64_t)B * d));
+  // forward, saving x, y, z, q, qc, o, oc and every key/value
+  const int64_t ring_layer = (int64_t)B * H * D.W * D.hd;
+  for (int64_t i = 0; i < n; ++i) {
+    S.t_uniform = i;
+    RLT_TRY(gemm_gate(D, B, P, S, e + i * d, n * d, x));
+    for (int l = 0; l < L; ++l) {
+      const bool last = l == L - 1;
+      SaveArgs a;
+      a.B = B; a.d = d; a.H = H; a.hd = D.hd; a.W = D.W; a.n = n; a.i = i;
+      a.h = S.h;
+      a.ring_k = el<T>(S.ring_k, l * ring_layer);
+      a.ring_v = el<T>(S.ring_v, l * ring_layer);
+      a.k_dst = w.template at<T>(TL.khist) + (int64_t)l * B * n * d;
+      a.v_dst = w.template at<T>(TL.vhist) + (int64_t)l * B * n * d;
+      const dim3 grid(blocks_for((int64_t)B * d));
+      RLT_TRY(gemm_qkv(D, B, l, P, S, x));
+      a.stage = 0; a.q = S.q; a.o = nullptr; a.o_dst = nullptr;
+      a.h_dst = w.template saved<float>(TL.xs, l, i);
+      a.q_dst = w.template saved<float>(TL.qs, l, i);
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
+      RLT_TRY(attn_self(D, B, l, S, x));
+      RLT_TRY(gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, x));
+      RLT_TRY(gemm_cq(D, B, l, P, S, x));
+      a.stage = 1; a.q = S.qc; a.o = S.o;
+      a.h_dst = w.template saved<float>(TL.ys, l, i);
+      a.q_dst = w.template saved<float>(TL.qcs, l, i);
+      a.o_dst = w.template saved<T>(TL.os, l, i);
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
+      RLT_TRY(attn_cross(D, B, l, S, M, x));
+      RLT_TRY(gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, x));
+      a.stage = 2; a.q = nullptr; a.q_dst = nullptr;
+      a.h_dst = w.template saved<float>(TL.zs, l, i);
+      a.o_dst = w.template saved<T>(TL.ocs, l, i);
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
+      RLT_TRY(gemm_w13(D, B, l, P, S, x));
+      RLT_TRY(gemm_residual(D, B, l, 2, P, S, last, last ? s_hist + (i + 1) * B * d : nullptr, d,
+                            x));
+    }
+  }
+  if (s_traj)
+    RLT_TRY(launch(k_traj, dim3(blocks_for((int64_t)B * n * d)), dim3(kThreads), x,
+                   (const float*)s_hist, s_traj, B, n, d));
+  // gradients start at zero
+  {
+    const int64_t dd = (int64_t)d * d, dF = (int64_t)d * F;
+    struct Z {
+      float* p;
+      int64_t n;
+    } zs[] = {{g.s_star, d},     {g.w_gate, 2 * dd}, {g.b_gate, d},     {g.gamma, 3LL * L * d},
+              {g.wq, L * dd},    {g.wk, L * dd},     {g.wv, L * dd},    {g.wo, L * dd},
+              {g.wcq, L * dd},   {g.wco, L * dd},    {g.w1, L * dF},    {g.w3, L * dF},
+              {g.w2, L * dF},    {g.wmk, D.G * dd},  {g.wmv, D.G * dd}};
+    for (const Z& z : zs) RLT_TRY(hipMemsetAsync(z.p, 0, sizeof(float) * z.n, st));
+    if (de) RLT_TRY(hipMemsetAsync(de, 0, sizeof(float) * B * n * d, st));
+    RLT_TRY(hipMemsetAsync(w.template at<float>(TL.carry), 0, sizeof(float) * B * d, st));
+    const size_t accb = sizeof(float) * (size_t)L * B * D.W * d;
+    RLT_TRY(hipMemsetAsync(w.template at<float>(TL.dkacc), 0, accb, st));
+    RLT_TRY(hipMemsetAsync(w.template at<float>(TL.dvacc), 0, accb, st));
+  }
+  // the reverse walk, one chunk of Tc tokens at a time (newest chunk first)
+  for (int64_t i1 = n; i1 > 0;) {
+    const int64_t i0 = std::max<int64_t>(0, i1 - TL.Tc);
+    for (int64_t i = i1 - 1; i >= i0; --i) RLT_TRY((walk_token<T, HD>(w, P, M, e, G, de, i, i - i0, st)));
+    RLT_TRY(chunk_grads<T>(w, g, i0, i1, st));
+    i1 = i0;
+  }
+  // s_0 = s* for every sequence
+  RLT_TRY(colsums(w.template at<float>(TL.carry), 1, B, B, d, w.template at<float>(TL.part),
+                  ColOut{nullptr, g.s_star, 0}, st));
+  // memory entries: gradients from every later token, then the memory projection's backward
+  const BwOff bo = bw_off(D);
+  const float scale = 1.f / sqrtf((float)HD);
+  T* dkv = w.template at<T>(TL.dkv);
+  for (int gi = 0; gi < D.G; ++gi) {
+    const int l0 = D.G == 1 ? 0 : gi, l1 = D.G == 1 ? L : gi + 1;
+    const int64_t grp = (int64_t)gi * B * n * d;
+    RLT_TRY(launch(k_mem_back<T, HD>, dim3((unsigned)((n + 63) / 64), B * H), dim3(kThreads), x,
+                   el<T>(M.k, grp), el<T>(M.v, grp),
+                   (const float*)w.template at<float>(TL.qcs), (const T*)w.template at<T>(TL.docs),
+                   (const float*)w.template at<float>(TL.lse),
+                   (const float*)w.template at<float>(TL.dlt), l0, l1, B, n, H, scale, dkv));
+    RLT_TRY(wgrad<T>(e, d, dkv, 2 * d, (int64_t)B * n, d, 2 * d,
+                     WDst{{g.wmk + (int64_t)gi * d * d, g.wmv + (int64_t)gi * d * d, nullptr}, d},
+                     st));
+    if (de) {
+      const T* wm = w.template at<T>(TL.bw) + bo.wm + (int64_t)gi * 2 * d * d;
+      RLT_TRY((run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(
+          (int)((int64_t)B * n), d, 2 * d, wm, ARows<T>{dkv, 2 * d, (int)((int64_t)B * n)},
+          EpiAddF32{de, d, (int)((int64_t)B * n)}, x)));
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
+                       const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
+                       hipStream_t st) {
+  switch (D.hd) {
+    case 32:
+      return D.dtype == RLT_BF16 ? bptt_t<bf16, 32>(D, B, n, P, e, G, s_traj, g, de, ws, st)
+                                 : bptt_t<float, 32>(D, B, n, P, e, G, s_traj, g, de, ws, st);
+    case 64:
+      return D.dtype == RLT_BF16 ? bptt_t<bf16, 64>(D, B, n, P, e, G, s_traj, g, de, ws, st)
+                                 : bptt_t<float, 64>(D, B, n, P, e, G, s_traj, g, de, ws, st);
+    case 128:
+      return D.dtype == RLT_BF16 ? bptt_t<bf16, 128>(D, B, n, P, e, G, s_traj, g, de, ws, st)
+                                 : bptt_t<float, 128>(D, B, n, P, e, G, s_traj, g, de, ws, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+#undef RLT_TRY
+
+}  // namespace rlt

@@ -215,4 +215,30 @@ hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
                       const Exec& st);
 
+// ---- backward pass (backpropagation through time) ----------------------------------------------
+
+// Gradient outputs (device, float32), laid out like the matching rlt_weights fields.
+struct GradPtrs {
+  float *s_star, *w_gate, *b_gate, *gamma, *wq, *wk, *wv, *wo, *wcq, *wco, *w1, *w3, *w2, *wmk,
+      *wmv;
+};
+
+// Byte offsets in the workspace of one backward pass over n tokens of B sequences (all 256-byte
+// aligned). Tc tokens form one chunk of weight-gradient rows (Mc = Tc * B rows).
+struct TrainLayout {
+  int64_t Tc, Mc;
+  size_t state, mem_k, mem_v, bw, s_hist, xs, ys, zs, qs, qcs, os, ocs, docs, khist, vhist, lse,
+      dlt, dres, dn, dattn, u13, gsave, carry, rinv, dkacc, dvacc, ca, cc, cf, cm, yqkv, yo, ycq,
+      yco, y13, y2, pg, xg, yg, part, dkv, total;
+};
+TrainLayout train_layout(const Dims& D, int B, int64_t n);
+
+// Forward over the n tokens of e [B][n][d] from s* (memory projected inside), keeping what the
+// reverse walk needs, then the reverse walk for upstream gradients G [B][n][d]: every field of
+// `g` is overwritten with dLoss/dparam for Loss = sum_{b,t} G[b][t] . s_t(b); de [B][n][d]
+// (optional) receives dLoss/de; s_traj [B][n][d] (optional) the forward trajectory.
+hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
+                       const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
+                       hipStream_t st);
+
 }  // namespace rlt

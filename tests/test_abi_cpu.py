@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     raw = ctypes.CDLL(sd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -80,6 +80,11 @@ def test_buffer_sizes(lib):
     assert par >= rows * d * 4 + rows * (5 * d + F) * 2
     assert lib.rlt_parallel_ws_bytes(byref(c), 16, 0) == 0
     assert lib.rlt_parallel_ws_bytes(byref(c), 0, 8) == 0
+    # backward workspace: five fp32 and five dtype rows per (token, sequence, layer) at least
+    bw = lib.rlt_bptt_ws_bytes(byref(c), 4, 64)
+    assert bw >= 4 * 64 * c.n_layers * d * (5 * 4 + 5 * 2)
+    assert lib.rlt_bptt_ws_bytes(byref(c), 4, 0) == 0
+    assert lib.rlt_bptt_ws_bytes(byref(c), 0, 8) == 0
 
 
 def test_null_arguments_rejected_without_gpu(lib):
@@ -92,6 +97,7 @@ def test_null_arguments_rejected_without_gpu(lib):
     assert lib.rlt_decoder_step(None, None, None, None, None, None) == 1
     assert lib.rlt_run_sequence(None, None, None, None, 1, None, None) == 1
     assert lib.rlt_run_parallel(None, None, None, None, 1, None, None, 0, None) == 1
+    assert lib.rlt_bptt(None, None, 1, 1, None, None, None, None, None, 0, None) == 1
     assert lib.rlt_state_export(None, None, None, None, None, None, None, None) == 1
     assert lib.rlt_state_import(None, None, None, None, 0, 0, None) == 1
     assert lib.rlt_state_reset(None, None) == 1

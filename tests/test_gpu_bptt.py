@@ -1,0 +1,98 @@
+"""Backpropagation through time on the GPU (rlt_bptt) against the float64 oracle's reverse
+traversal (oracle.bptt), for the loss sum_{b,t} G[b, t] . s_t(b) with seeded random G.
+
+Every gradient tensor is compared as a whole: relative L2 error ||gpu - oracle|| / ||oracle||,
+bounded by the same figure as the forward parity (1e-4 fp32, 3e-2 bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stateful_decoding_amd as sd
+from synth import RLTConfig
+from tests.gpu_helpers import TOL, inputs, max_rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg_small(**kw):
+    base = dict(name="bptt", d=64, n_heads=2, head_dim=32, n_layers=2, ffn=128, window=3,
+                n_groups=2, alpha=0.7, batch=3, seq_len=10, dtype="fp32", sigma=0.05)
+    base.update(kw)
+    return RLTConfig(**base)
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def run_case(cfg, B, T, seed):
+    p, e = inputs(cfg, B, T, seed=seed, random_gains=True, random_gate_bias=True)
+    G = np.random.default_rng(seed + 1000).standard_normal((B, T, cfg.d)).astype(np.float32)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    Gd = torch.from_numpy(G).cuda()
+    grads = sd.grad_buffers(model)
+    de = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+    traj = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+    print(f"case d={cfg.d} hd={cfg.head_dim} L={cfg.n_layers} F={cfg.ffn} W={cfg.window} "
+          f"G={cfg.n_groups} alpha={cfg.alpha} {cfg.dtype} B={B} T={T}", flush=True)
+    sd.rlt_bptt(model, ed, Gd, grads, de=de, s_traj=traj)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in grads.items()}
+    ref_traj, ref, ref_de = oracle.bptt(p, cfg, e, G)
+    errs = {k: rel_l2(got[k], ref[k]) for k in oracle.GRAD_NAMES}
+    errs["de"] = rel_l2(de.cpu().numpy(), ref_de)
+    errs["s_traj"] = max_rel_l2(traj.cpu().numpy(), ref_traj)
+    worst = max(errs, key=errs.get)
+    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    return errs, worst
+
+
+CASES = [
+    dict(dtype="fp32", B=3, T=10),                                               # G = L
+    dict(dtype="fp32", B=2, T=9, n_groups=1, alpha=1.0, window=4, head_dim=64, n_heads=1),
+    dict(dtype="fp32", B=4, T=7, window=1, n_layers=1, n_groups=1),             # W = 1
+    dict(dtype="bf16", B=5, T=24, d=128, n_heads=2, head_dim=64, ffn=256, window=5),
+    dict(dtype="bf16", B=3, T=12, d=256, n_heads=2, head_dim=128, ffn=512, window=20,
+         n_groups=1),                                                            # W > T
+    dict(dtype="bf16", B=300, T=40, d=128, n_heads=4, head_dim=32, ffn=192, window=6),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bptt_matches_oracle(case):
+    case = dict(case)
+    B, T = case.pop("B"), case.pop("T")
+    cfg = cfg_small(**case)
+    errs, worst = run_case(cfg, B, T, seed=B + T)
+    assert errs[worst] <= TOL[cfg.dtype], (worst, errs[worst])
+
+
+def test_bptt_chunked_rows_span_several_weight_gradient_chunks():
+    """B = 300 sequences make 14-token weight-gradient chunks, so 40 tokens take three
+    chunks, the first one short; fp32 holds that bookkeeping to the tight bound."""
+    cfg = cfg_small(dtype="fp32", d=64, ffn=128, window=5)
+    errs, worst = run_case(cfg, 300, 40, seed=3)
+    assert errs[worst] <= TOL["fp32"], (worst, errs[worst])
+
+
+def test_bptt_argument_errors():
+    cfg = cfg_small()
+    p, e = inputs(cfg, 2, 4)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    Gd = torch.zeros(2, 4, cfg.d, device="cuda")
+    grads = sd.grad_buffers(model)
+    ws = sd.bptt_workspace(model, 2, 4)
+    with pytest.raises(sd.RLTError) as ex:
+        sd.rlt_bptt(model, ed, Gd, grads, ws=ws[: ws.numel() // 2])
+    assert ex.value.status_name == "RLT_ERR_CAPACITY"
+    lib = model.lib
+    g = sd.binding.rlt_grads(*[grads[k].data_ptr() for k in sd.binding.WEIGHT_FIELDS])
+    g.w2 = None
+    st = lib.rlt_bptt(model.handle, ed.data_ptr(), 2, 4, Gd.data_ptr(), None,
+                      sd.binding.byref(g), None, ws.data_ptr(), ws.numel(), None)
+    assert sd.binding.STATUS_NAMES[st] == "RLT_ERR_ARG"
