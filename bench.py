@@ -112,9 +112,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--mode", choices=("recurrent", "parallel"), default="recurrent",
+    ap.add_argument("--mode", choices=("recurrent", "parallel", "train"), default="recurrent",
                     help="recurrent: rlt_run_sequence (the headline); parallel: the token-parallel "
-                         "pass for alpha = 0 (rlt_run_parallel)")
+                         "pass for alpha = 0 (rlt_run_parallel); train: forward + "
+                         "backpropagation through time (rlt_bptt)")
     ap.add_argument("--workload", default=None,
                     help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -170,6 +171,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.mode == "parallel":
         return bench_parallel(args, cfg, params, model, state, mem, e, traj, stream)
+    if args.mode == "train":
+        del state, mem
+        return bench_train(args, cfg, params, model, e, traj, stream)
 
     def one_step():
         state.reset(stream)
@@ -305,6 +309,136 @@ def bench_parallel(args, cfg, params, model, state, mem, e, traj, stream):
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, params, args.cpu_seconds, n_seqs=4)
+    print(json.dumps(out), flush=True)
+
+
+LOSS_SCALE = 2.0 ** -100
+TRAIN_KINDS = ("gate", "qkv", "self_attn", "self_out", "cross_q", "cross_attn", "cross_out",
+               "ffn_up", "ffn_down", "memproj", "bwd_proj", "bwd_self_attn", "bwd_cross_attn",
+               "bwd_memory", "bwd_wgrad", "bwd_other")
+TRAIN_KERNELS = {"bwd_cross_attn": "k_xattn_back (memory-prefix attention backward)",
+                 "bwd_self_attn": "k_swa_back (window attention backward)",
+                 "bwd_memory": "k_mem_back (memory key/value gradients)",
+                 "bwd_wgrad": "k_wgrad (weight gradients)",
+                 "bwd_proj": "k_proj (backward projections)",
+                 "cross_attn": "k_attend_memory (forward cross-attention)"}
+
+
+def cpu_baseline_train(cfg, params, budget_s: float, n_seqs: int = 2) -> dict:
+    """The float64 oracle's forward + backward (oracle.bptt) as it stands, on the first n_seqs
+    sequences and the first n tokens, n doubling from 8 while a run stays within the budget."""
+    import numpy as np
+
+    import oracle
+    from synth import make_encoder_outputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    p = oracle.prepare_params(params)
+    e = make_encoder_outputs(cfg, range(n_seqs)).astype(np.float64)
+    G = np.random.default_rng(0).standard_normal(e.shape)
+    n, wall = 8, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.bptt(p, cfg, e[:, :n], G[:, :n])
+        wall = time.perf_counter() - t0
+        if n >= cfg.seq_len or wall * 2.5 > budget_s:
+            break
+        n = min(cfg.seq_len, 2 * n)
+    return {"value": n_seqs * n / wall, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle.bptt (forward + reverse walk), first {n_seqs} "
+                      f"sequences, tokens 1..{n} of {cfg.seq_len}, {wall:.1f} s; short prefixes "
+                      "overstate the whole-run rate",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_train(args, cfg, params, model, e, traj, stream):
+    """Forward + backpropagation through time: one step is one rlt_bptt over all B x T tokens
+    (memory projection, the recurrent forward keeping what the walk needs, the reverse walk,
+    weight and memory gradients) for seeded N(0, 1) upstream gradients of every s_t."""
+    import torch
+
+    import stateful_decoding_amd as sd
+
+    B, T, d = cfg.batch, cfg.seq_len, cfg.d
+    ws = sd.bptt_workspace(model, B, T)
+    grads = sd.grad_buffers(model)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    # Loss scaling: this random-init model's backward grows about 1.1x per token, beyond fp32
+    # over 1024 tokens at unit scale; the walk is linear in ds, so the scale changes no work.
+    ds = torch.randn(B, T, d, device="cuda", generator=gen, dtype=torch.float32) * LOSS_SCALE
+    de = torch.empty(B, T, d, device="cuda", dtype=torch.float32)
+    print(f"[bench] train workspace {ws.numel() / 2**30:.1f} GiB", file=sys.stderr, flush=True)
+
+    def one_step(kernels=None):
+        return sd.rlt_bptt(model, e, ds, grads, de=de, s_traj=traj, ws=ws, stream=stream,
+                           time_kernels=kernels, token_stride=1)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        one_step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    secs = ms_total / 1e3
+    print(f"[bench] timed {args.steps} steps: {ms_total:.1f} ms", file=sys.stderr, flush=True)
+    # one more step with every launch timed: per-kind breakdown and the roofline
+    prof = one_step(list(TRAIN_KINDS))
+    ok = all(bool(torch.isfinite(g).all()) for g in grads.values())
+    assert ok and bool(torch.isfinite(de).all()), "non-finite gradients"
+    ideal = 0.0
+    for k, v in prof.items():
+        peak = FP32_PEAK if k == "bwd_memory" else BF16_PEAK
+        ideal += max(v["bytes"] / HBM_PEAK, v["flops"] / peak)
+    timed = {k: v for k, v in prof.items() if v["launches"]}
+    dom_name, dom = max(timed.items(), key=lambda kv: kv[1]["total_ms"])
+    if dom_name == "bwd_memory":
+        bound, peak, rate = "alu", FP32_PEAK, dom["flops"] / (dom["total_ms"] / 1e3)
+    elif dom["flops"] / BF16_PEAK > dom["bytes"] / HBM_PEAK:
+        bound, peak, rate = "mfma", BF16_PEAK, dom["flops"] / (dom["total_ms"] / 1e3)
+    else:
+        bound, peak, rate = "hbm", HBM_PEAK, dom["bytes"] / (dom["total_ms"] / 1e3)
+    gbs = bound == "hbm"
+    kernel_ms = sum(v["total_ms"] for v in timed.values())
+    out = {
+        "metric": "RLT decoder training tokens/sec (forward + backpropagation through time, "
+                  "B seqs x T) on 1 MI355X; % of the pass roofline",
+        "value": round(B * T * args.steps / secs, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_total / args.steps, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "mode": "train", "batch": B, "seq_len": T, "d": d,
+                   "heads": cfg.n_heads, "head_dim": cfg.head_dim, "decoder_blocks": cfg.n_layers,
+                   "ffn": cfg.ffn, "window": cfg.window, "memory_groups": cfg.n_groups,
+                   "alpha": cfg.alpha,
+                   "inputs": "e_t ~ N(0,1), weights ~ N(0,0.02), upstream dL/ds_t ~ N(0,1) x 2^-100 "
+                             "(loss scaling), seed 0"},
+        "roofline": {"bound": bound, "kernel": TRAIN_KERNELS.get(dom_name, dom_name),
+                     "achieved": round(rate / (1e9 if gbs else 1e12), 1),
+                     "peak": peak / (1e9 if gbs else 1e12), "unit": "GB/s" if gbs else "TFLOP/s",
+                     "frac": round(rate / peak, 4), "traffic": None,
+                     "launches": dom["launches"],
+                     "avg_launch_us": round(dom["total_ms"] * 1e3 / dom["launches"], 2),
+                     "timed": "every launch of one extra step after the timed steps"},
+        "pass_roofline": {"ideal_s": round(ideal, 4), "measured_s": round(secs / args.steps, 4),
+                          "frac": round(ideal / (secs / args.steps), 4),
+                          "peaks": "HBM 8.0 TB/s, bf16 MFMA 2.5 PFLOP/s (fp32 vector 157.3 "
+                                   "TFLOP/s for the memory-gradient kernel), per kernel kind",
+                          "kernel_sum_s": round(kernel_ms / 1e3, 4)},
+        "kernel_ms_per_step": {k: round(v["total_ms"], 1) for k, v in timed.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_train(cfg, params, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

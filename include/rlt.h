@@ -227,6 +227,13 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
  * keys/values; "16 per-token recurrence, no quality gain": a backward pass that walks the
  * tokens in reverse) ------------------------------------------------------------------------ */
 
+/* Optional kernel timing of rlt_bptt (see rlt_kernel and rlt_kernel_stats below). */
+typedef struct rlt_timing {
+  uint32_t kernels;     /* bit (1 << rlt_kernel) per kernel to time */
+  int32_t token_stride; /* >= 1 */
+} rlt_timing;
+struct rlt_kernel_stats;
+
 /* Gradient outputs of rlt_bptt: device float32 buffers (caller-owned), one per parameter, each
  * laid out like the matching rlt_weights field. */
 typedef struct rlt_grads {
@@ -262,10 +269,15 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
  * projection; s_traj [B][n][d] float32 (device, or NULL) receives the forward trajectory.
  * Gradients through the self-attention keys/values of later tokens are included. Independent
  * of any rlt_state or rlt_memory. `ws`: device, 256-byte aligned, >= rlt_bptt_ws_bytes bytes,
- * scratch owned by the caller (RLT_ERR_CAPACITY if smaller). Asynchronous on `stream`. */
+ * scratch owned by the caller (RLT_ERR_CAPACITY if smaller). Asynchronous on `stream`, unless
+ * `timing` is non-NULL with kernels != 0: then the launches of those kernels (rlt_kernel bits)
+ * are timed with events, in the forward and reverse steps of tokens t with
+ * t % token_stride == 0 and in every launch outside the token loops, and the call waits for the
+ * stream and writes RLT_K_COUNT entries to `stats` (host array, required then). */
 rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
                     const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
-                    size_t ws_bytes, void* stream);
+                    size_t ws_bytes, const struct rlt_timing* timing, struct rlt_kernel_stats* stats,
+                    void* stream);
 
 /* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
 
@@ -312,7 +324,13 @@ typedef enum rlt_kernel {
   RLT_K_PAR_SELF = 11,   /* token-parallel pass: window attention                          */
   RLT_K_PAR_CROSS = 12,  /* token-parallel pass: memory-prefix attention                   */
   RLT_K_PAR_OTHER = 13,  /* token-parallel pass: RMSNorm rows, ring hand-off, final s      */
-  RLT_K_COUNT = 14
+  RLT_K_BWD_PROJ = 14,   /* backward pass: per-token projections against transposed weights */
+  RLT_K_BWD_SELF = 15,   /* backward pass: window attention backward, key/value gradients    */
+  RLT_K_BWD_CROSS = 16,  /* backward pass: memory-prefix attention backward (query gradient) */
+  RLT_K_BWD_MEM = 17,    /* backward pass: memory key/value gradients after the walk         */
+  RLT_K_BWD_WGRAD = 18,  /* backward pass: weight-gradient GEMMs over chunks of rows         */
+  RLT_K_BWD_OTHER = 19,  /* backward pass: RMSNorm rows and backward, saves, sums, repacking */
+  RLT_K_COUNT = 20
 } rlt_kernel;
 
 typedef struct rlt_kernel_stats {

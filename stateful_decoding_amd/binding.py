@@ -39,11 +39,16 @@ class rlt_weights(ctypes.Structure):
 
 KERNEL_NAMES = ("gate", "qkv", "self_attn", "self_out", "cross_q", "cross_attn", "cross_out",
                 "ffn_up", "ffn_down", "memproj", "par_gemm", "par_self_attn", "par_cross_attn",
-                "par_other")
+                "par_other", "bwd_proj", "bwd_self_attn", "bwd_cross_attn", "bwd_memory",
+                "bwd_wgrad", "bwd_other")
 
 
 class rlt_grads(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in WEIGHT_FIELDS]
+
+
+class rlt_timing(ctypes.Structure):
+    _fields_ = [("kernels", ctypes.c_uint32), ("token_stride", c_int32)]
 
 
 class rlt_kernel_stats(ctypes.Structure):
@@ -104,7 +109,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_state_import_ragged": (c_int32, [P, P, P, P, P, c_uint64, P]),
         "rlt_bptt_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
         "rlt_bptt": (c_int32, [P, P, c_int32, c_int64, P, P, POINTER(rlt_grads), P, P, c_size_t,
-                               P]),
+                               POINTER(rlt_timing), P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -369,10 +374,13 @@ def grad_buffers(model: Model) -> dict:
 
 def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
              de: torch.Tensor | None = None, s_traj: torch.Tensor | None = None,
-             ws: torch.Tensor | None = None, stream=None):
+             ws: torch.Tensor | None = None, stream=None, time_kernels=None,
+             token_stride: int = 1):
     """Forward from s* over e [B, n, d] and backpropagation through time of the upstream
     gradients ds [B, n, d] float32 into `grads` (from grad_buffers; overwritten), de [B, n, d]
-    float32 and s_traj [B, n, d] float32 (both optional); `ws` from bptt_workspace."""
+    float32 and s_traj [B, n, d] float32 (both optional); `ws` from bptt_workspace. With
+    `time_kernels` (names from KERNEL_NAMES) the call waits for the stream and returns
+    {name: {launches, total_ms, bytes, flops}} of those kernels' sampled launches."""
     B, n = int(e.shape[0]), int(e.shape[1])
     d = model.cfg.d
     _need(e, (B, n, d), model.dtype, "e")
@@ -388,9 +396,22 @@ def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
     if ws is None:
         ws = bptt_workspace(model, B, n)
     g = rlt_grads(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    timing = None
+    stats = None
+    if time_kernels:
+        mask = 0
+        for k in time_kernels:
+            mask |= 1 << KERNEL_NAMES.index(k)
+        timing = rlt_timing(mask, int(token_stride))
+        stats = (rlt_kernel_stats * len(KERNEL_NAMES))()
     _check(model.lib.rlt_bptt(model.handle, e.data_ptr(), B, n, ds.data_ptr(), _ptr(s_traj),
                               byref(g), _ptr(de), ws.data_ptr(), ws.numel() * ws.element_size(),
-                              _stream(stream)))
+                              None if timing is None else byref(timing), stats, _stream(stream)))
+    if stats is None:
+        return None
+    return {KERNEL_NAMES[i]: {"launches": stats[i].launches, "total_ms": stats[i].total_ms,
+                              "bytes": stats[i].bytes, "flops": stats[i].flops}
+            for i in range(len(KERNEL_NAMES)) if (timing.kernels >> i) & 1}
 
 
 def rlt_state_export(state: State, stream=None):

@@ -707,7 +707,8 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
 
 rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
                     const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, const rlt_timing* timing, rlt_kernel_stats* stats,
+                    void* stream) {
   if (!model) return fail(RLT_ERR_ARG, "model is NULL");
   if (!e || !ds || !grads || !ws) return fail(RLT_ERR_ARG, "e, ds, grads and ws must be non-NULL");
   float* const gp[] = {grads->s_star, grads->w_gate, grads->b_gate, grads->gamma, grads->wq,
@@ -720,7 +721,16 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
     return fail(RLT_ERR_SHAPE, "n = %lld must be in [1, %lld]", (long long)n,
                 (long long)kMaxCapacity);
   if ((int64_t)batch * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "batch * n too large");
-  if (!aligned16(e) || !aligned(ws)) return fail(RLT_ERR_ARG, "e must be 16-byte aligned, ws 256-byte aligned");
+  if (!aligned16(e) || !aligned(ws))
+    return fail(RLT_ERR_ARG, "e must be 16-byte aligned, ws 256-byte aligned");
+  const bool timed = timing && timing->kernels;
+  if (timed) {
+    if (!stats) return fail(RLT_ERR_ARG, "stats must be non-NULL when timing kernels");
+    if (timing->kernels >> RLT_K_COUNT)
+      return fail(RLT_ERR_ARG, "timing has kernel bits beyond RLT_K_COUNT");
+    if (timing->token_stride < 1)
+      return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", timing->token_stride);
+  }
   const Dims& D = model->D;
   const size_t need = train_layout(D, batch, n).total;
   if (ws_bytes < need)
@@ -728,8 +738,29 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
   GradPtrs g{grads->s_star, grads->w_gate, grads->b_gate, grads->gamma, grads->wq, grads->wk,
              grads->wv,     grads->wo,     grads->wcq,    grads->wco,   grads->w1, grads->w3,
              grads->w2,     grads->wmk,    grads->wmv};
-  hipError_t err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws,
-                               static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Profiler prof;
+  if (timed) {
+    prof.mask = timing->kernels;
+    prof.stride = timing->token_stride;
+  }
+  hipError_t err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, st,
+                               timed ? &prof : nullptr);
+  if (timed) {
+    for (int k = 0; k < RLT_K_COUNT; ++k) stats[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
+    if (err == hipSuccess) err = hipStreamSynchronize(st);
+    for (const Profiler::Rec& r : prof.recs) {
+      if (err != hipSuccess) break;
+      float ms = 0.f;
+      err = hipEventElapsedTime(&ms, prof.events[r.ev], prof.events[r.ev + 1]);
+      rlt_kernel_stats& o = stats[r.kind];
+      o.launches += 1;
+      o.total_ms += ms;
+      o.bytes += r.bytes;
+      o.flops += r.flops;
+    }
+    prof.destroy();
+  }
   if (err != hipSuccess) return hip_fail(err, "backward pass");
   return ok();
 }

@@ -925,20 +925,20 @@ static inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads -
 
 template <typename T>
 static hipError_t wgrad(const T* X, int64_t ldx, const T* Y, int64_t ldy, int64_t M, int K, int N,
-                        WDst dst, hipStream_t st) {
+                        WDst dst, const Exec& x) {
   if (K % 64 || N % 64 || M <= 0) return hipErrorInvalidValue;
-  return launch(k_wgrad<T>, dim3((unsigned)((K / 64) * (N / 64))), dim3(kThreads), Exec(st), X,
+  return launch(k_wgrad<T>, dim3((unsigned)((K / 64) * (N / 64))), dim3(kThreads), x, X,
                 ldx, Y, ldy, M, K, N, dst);
 }
 
 template <typename T, int HD>
 static hipError_t xattn_back(int BH, const float* q, const float* dout, const T* K, const T* V,
                              int64_t bh_stride, int ntok, int H, T* dq, float* lse, float* dlt,
-                             T* do_t, hipStream_t st) {
+                             T* do_t, const Exec& x) {
   const float scale = 1.f / sqrtf((float)HD);
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
 #define RLT_XB(NW)                                                                             \
-  return launch(k_xattn_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), Exec(st), q, dout, K, V, \
+  return launch(k_xattn_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, q, dout, K, V,        \
                 bh_stride, ntok, H, scale, dq, lse, dlt, do_t)
   if (nw == 4) RLT_XB(4);
   if (nw == 8) RLT_XB(8);
@@ -949,11 +949,11 @@ static hipError_t xattn_back(int BH, const float* q, const float* dout, const T*
 template <typename T, int HD>
 static hipError_t swa_back(int BH, const float* q, const float* dout, const T* K, const T* V,
                            int64_t n, int64_t t, int W, int H, float* dkacc, float* dvacc, T* out,
-                           hipStream_t st) {
+                           const Exec& x) {
   const float scale = 1.f / sqrtf((float)HD);
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
 #define RLT_SB(NW)                                                                             \
-  return launch(k_swa_back<T, HD, NW>, dim3(BH), dim3(NW * kWave), Exec(st), q, dout, K, V, n, \
+  return launch(k_swa_back<T, HD, NW>, dim3(BH), dim3(NW * kWave), x, q, dout, K, V, n,        \
                 t, W, H, scale, dkacc, dvacc, out)
   if (nw == 4) RLT_SB(4);
   if (nw == 8) RLT_SB(8);
@@ -964,10 +964,10 @@ static hipError_t swa_back(int BH, const float* q, const float* dout, const T* K
 // Column sums of `nmat` fp32 matrices of `rows` valid rows (matrix m at P + m * stride * d)
 // added to out (matrices below out.n_gamma into out.gamma + m * d, the next into out.extra).
 static hipError_t colsums(const float* P, int nmat, int64_t rows, int64_t stride, int d,
-                          float* part, ColOut out, hipStream_t st) {
-  RLT_TRY(launch(k_colsum_part, dim3(blocks_for(d), kRowSplits, nmat), dim3(kThreads), Exec(st), P,
-                 rows, stride, d, part));
-  return launch(k_colsum_final, dim3(blocks_for(d), nmat), dim3(kThreads), Exec(st),
+                          float* part, ColOut out, const Exec& x, const Exec& x2) {
+  RLT_TRY(launch(k_colsum_part, dim3(blocks_for(d), kRowSplits, nmat), dim3(kThreads), x, P, rows,
+                 stride, d, part));
+  return launch(k_colsum_final, dim3(blocks_for(d), nmat), dim3(kThreads), x2,
                 (const float*)part, d, out);
 }
 
@@ -997,10 +997,25 @@ struct Walk {  // pointers into the workspace of one call
   }
 };
 
-// The reverse walk over token i (chunk-local index li).
+// Exec of one launch: armed with timing events when `prof` times `kind` and the launch is
+// sampled; the first arming error is kept and reported at the end.
+struct Timer {
+  Profiler* prof;
+  hipStream_t st;
+  hipError_t err = hipSuccess;
+  Exec at(int kind, double bytes, double flops, bool sampled = true) {
+    Exec x(st);
+    if (prof && sampled && err == hipSuccess) err = prof->arm(kind, bytes, flops, x);
+    return x;
+  }
+};
+
+// The reverse walk over token i (chunk-local index li). Algorithmic bytes: weights, operands
+// and results once each (es per dtype element, 4 per fp32 one).
 template <typename T, int HD>
 static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M, const T* e,
-                             const float* G, float* de, int64_t i, int64_t li, hipStream_t st) {
+                             const float* G, float* de, int64_t i, int64_t li, Timer& tm,
+                             bool sampled) {
   const Dims& D = w.D;
   const TrainLayout& TL = w.TL;
   const int B = w.B, d = D.d, F = D.F, L = D.L, H = D.H, BH = B * D.H;
@@ -1014,11 +1029,17 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
   float* u13 = w.template at<float>(TL.u13);
   float* gsave = w.template at<float>(TL.gsave);
   float* carry = w.template at<float>(TL.carry);
-  const Exec x(st);
   const int64_t dd = (int64_t)d * d;
+  const double b = B, es = (double)D.es, rows32 = b * d * 4, rowsT = b * d * es;
+  // a per-token projection: N x K weights, A rows of K, `out` bytes of results
+  auto proj = [&](double N, double K, double out) {
+    return tm.at(RLT_K_BWD_PROJ, N * K * es + b * K * es + out, 2 * b * N * K, sampled);
+  };
+  auto other = [&](double bytes) { return tm.at(RLT_K_BWD_OTHER, bytes, 0, sampled); };
 
-  RLT_TRY(launch(k_walk_begin<T>, dim3(blocks_for((int64_t)B * d)), dim3(kThreads), x, G,
-                 (const float*)carry, dres, w.chunk(TL.y2, L - 1, d, li), B, d, n, i));
+  RLT_TRY(launch(k_walk_begin<T>, dim3(blocks_for((int64_t)B * d)), dim3(kThreads),
+                 other(3 * rows32 + rowsT), G, (const float*)carry, dres,
+                 w.chunk(TL.y2, L - 1, d, li), B, d, n, i));
   for (int l = L - 1; l >= 0; --l) {
     const float* gam = P.gamma + (int64_t)l * 3 * d;
     const float* xs = w.template saved<float>(TL.xs, l, i);
@@ -1027,58 +1048,69 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     T* ca = w.chunk(TL.ca, l, d, li);
     T* cc = w.chunk(TL.cc, l, d, li);
     T* cf = w.chunk(TL.cf, l, d, li);
-    RLT_TRY(launch(k_norm_rows3<T>, dim3(B), dim3(kThreads), x, xs, ys, zs, gam, d, D.eps, ca,
-                   cc, cf, rinv));
+    RLT_TRY(launch(k_norm_rows3<T>, dim3(B), dim3(kThreads), other(3 * rows32 + 3 * rowsT), xs, ys,
+                   zs, gam, d, D.eps, ca, cc, cf, rinv));
     // feed-forward: recompute u, then dm -> du -> df -> dres
     {
       EpiU13<T> ep{u13, w.chunk(TL.cm, l, F, li), B, F};
       RLT_TRY(run_step_gemm<T>(B, 2 * F, d, el<T>(P.w13_t, (int64_t)l * 2 * F * d),
-                               ARows<T>{cf, d, B}, ep, x));
+                               ARows<T>{cf, d, B}, ep, proj(2 * F, d, b * F * (8 + es))));
     }
     T* y13 = w.chunk(TL.y13, l, 2 * F, li);
     {
       EpiSiluBack<T> ep;
       ep.u = u13; ep.du = y13; ep.M = B; ep.F = F;
       RLT_TRY(run_step_gemm<T>(B, F, d, bw + bo.w2 + (int64_t)l * F * d,
-                               ARows<T>{w.chunk(TL.y2, l, d, li), d, B}, ep, x));
+                               ARows<T>{w.chunk(TL.y2, l, d, li), d, B}, ep,
+                               proj(F, d, b * 2 * F * (4 + es))));
     }
     EpiStoreF32 to_dn;
     to_dn.out = dn; to_dn.ld = d; to_dn.M = B;
     EpiStoreF32 to_dattn;
     to_dattn.out = dattn; to_dattn.ld = d; to_dattn.M = B;
     RLT_TRY(run_step_gemm<T>(B, d, 2 * F, bw + bo.w13 + (int64_t)l * d * 2 * F,
-                             ARows<T>{y13, 2 * F, B}, to_dn, x));
+                             ARows<T>{y13, 2 * F, B}, to_dn, proj(d, 2 * F, rows32)));
     T* yco = w.chunk(TL.yco, l, d, li);
-    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, zs, gam + 2 * d,
-                   (const float*)rinv, 2, d, dres, yco, w.pg(3 * l + 2, li)));
+    const double nb = 5 * rows32 + rowsT;  // dn, x, dres in, dres out, gain terms; dtype copy
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, zs,
+                   gam + 2 * d, (const float*)rinv, 2, d, dres, yco, w.pg(3 * l + 2, li)));
     // cross-attention
-    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wco + l * dd, ARows<T>{yco, d, B}, to_dattn, x));
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wco + l * dd, ARows<T>{yco, d, B}, to_dattn,
+                             proj(d, d, rows32)));
     const int g = D.G == 1 ? 0 : l;
     const int64_t grp = (int64_t)g * B * n * d;
     T* ycq = w.chunk(TL.ycq, l, d, li);
     const int64_t stat = ((int64_t)l * n + i) * BH;
+    const double ntok = (double)(i + 1);
     RLT_TRY(xattn_back<T, HD>(BH, w.template saved<float>(TL.qcs, l, i), dattn,
                               el<T>(M.k, grp), el<T>(M.v, grp), n * HD, (int)(i + 1), H, ycq,
                               w.template at<float>(TL.lse) + stat,
                               w.template at<float>(TL.dlt) + stat,
-                              w.template saved<T>(TL.docs, l, i), st));
-    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wcq + l * dd, ARows<T>{ycq, d, B}, to_dn, x));
+                              w.template saved<T>(TL.docs, l, i),
+                              tm.at(RLT_K_BWD_CROSS, ntok * b * 2 * d * es + 2 * rows32 +
+                                        2 * rowsT + 8 * b * H, 8 * b * d * ntok, sampled)));
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wcq + l * dd, ARows<T>{ycq, d, B}, to_dn,
+                             proj(d, d, rows32)));
     T* yo = w.chunk(TL.yo, l, d, li);
-    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, ys, gam + d,
-                   (const float*)rinv, 1, d, dres, yo, w.pg(3 * l + 1, li)));
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, ys,
+                   gam + d, (const float*)rinv, 1, d, dres, yo, w.pg(3 * l + 1, li)));
     // self-attention
-    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn, x));
+    RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn,
+                             proj(d, d, rows32)));
     T* yqkv = w.chunk(TL.yqkv, l, 3 * d, li);
     const int64_t hist = (int64_t)l * B * n * d, acc = (int64_t)l * B * D.W * d;
+    const double nk = (double)std::min<int64_t>(i + 1, D.W);
     RLT_TRY(swa_back<T, HD>(BH, w.template saved<float>(TL.qs, l, i), dattn,
                             w.template at<T>(TL.khist) + hist, w.template at<T>(TL.vhist) + hist,
                             n, i, D.W, H, w.template at<float>(TL.dkacc) + acc,
-                            w.template at<float>(TL.dvacc) + acc, yqkv, st));
+                            w.template at<float>(TL.dvacc) + acc, yqkv,
+                            tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * (es + 8) + 2 * rows32 +
+                                      3 * rowsT, 14 * b * d * nk, sampled)));
     RLT_TRY(run_step_gemm<T>(B, d, 3 * d, bw + bo.wqkv + (int64_t)l * 3 * dd,
-                             ARows<T>{yqkv, 3 * d, B}, to_dn, x));
-    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), x, (const float*)dn, xs, gam,
-                   (const float*)rinv, 0, d, dres, l > 0 ? w.chunk(TL.y2, l - 1, d, li) : (T*)nullptr,
-                   w.pg(3 * l, li)));
+                             ARows<T>{yqkv, 3 * d, B}, to_dn, proj(d, 3 * d, rows32)));
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, xs, gam,
+                   (const float*)rinv, 0, d, dres,
+                   l > 0 ? w.chunk(TL.y2, l - 1, d, li) : (T*)nullptr, w.pg(3 * l, li)));
   }
   // gated merge: recompute g, then dz, then de_t and the carry to s_{t-1}
   const T* et = e + i * d;
@@ -1090,13 +1122,15 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     ep.e = et; ep.lde = n * d; ep.s = s_prev; ep.b = P.b_gate; ep.dres = dres; ep.alpha = D.alpha;
     ep.dz = yg; ep.dz32 = w.pg(3 * L, li); ep.g = gsave;
     ep.xg = w.template at<T>(TL.xg) + li * B * 2 * d; ep.M = B; ep.d = d;
-    RLT_TRY(run_step_gemm<T>(B, d, 2 * d, P.w_gate_t, al, ep, x));
+    RLT_TRY(run_step_gemm<T>(B, d, 2 * d, P.w_gate_t, al, ep,
+                             proj(d, 2 * d, 3 * rows32 + rowsT + b * 2 * d * es)));
   }
   {
     EpiGateOut ep;
     ep.dres = dres; ep.g = gsave; ep.de = de ? de + i * d : nullptr; ep.de_ld = n * d;
     ep.carry = carry; ep.alpha = D.alpha; ep.M = B; ep.d = d;
-    RLT_TRY(run_step_gemm<T>(B, 2 * d, d, bw + bo.wg, ARows<T>{yg, d, B}, ep, x));
+    RLT_TRY(run_step_gemm<T>(B, 2 * d, d, bw + bo.wg, ARows<T>{yg, d, B}, ep,
+                             proj(2 * d, d, 4 * rows32)));
   }
   return hipSuccess;
 }
@@ -1104,47 +1138,59 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
 // Weight and gain gradients of the chunk of tokens [i0, i1).
 template <typename T>
 static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, int64_t i1,
-                              hipStream_t st) {
+                              Timer& tm) {
   const Dims& D = w.D;
   const TrainLayout& TL = w.TL;
   const int B = w.B, d = D.d, F = D.F, L = D.L;
   const int64_t rows = (i1 - i0) * B, dd = (int64_t)d * d, dF = (int64_t)d * F;
+  const double es = (double)D.es;
+  auto gx = [&](double K, double N) {
+    return tm.at(RLT_K_BWD_WGRAD, rows * (K + N) * es + K * N * 8, 2.0 * rows * K * N);
+  };
   for (int l = 0; l < L; ++l) {
     RLT_TRY(wgrad<T>(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, rows, d,
-                     3 * d, WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}, st));
+                     3 * d, WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}, gx(d, 3 * d)));
     RLT_TRY(wgrad<T>(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, rows, d,
-                     d, WDst{{g.wo + l * dd, nullptr, nullptr}, d}, st));
+                     d, WDst{{g.wo + l * dd, nullptr, nullptr}, d}, gx(d, d)));
     RLT_TRY(wgrad<T>(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, rows, d, d,
-                     WDst{{g.wcq + l * dd, nullptr, nullptr}, d}, st));
+                     WDst{{g.wcq + l * dd, nullptr, nullptr}, d}, gx(d, d)));
     RLT_TRY(wgrad<T>(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, rows, d,
-                     d, WDst{{g.wco + l * dd, nullptr, nullptr}, d}, st));
+                     d, WDst{{g.wco + l * dd, nullptr, nullptr}, d}, gx(d, d)));
     RLT_TRY(wgrad<T>(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, rows, d,
-                     2 * F, WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}, st));
+                     2 * F, WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}, gx(d, 2 * F)));
     RLT_TRY(wgrad<T>(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, rows, F, d,
-                     WDst{{g.w2 + l * dF, nullptr, nullptr}, d}, st));
+                     WDst{{g.w2 + l * dF, nullptr, nullptr}, d}, gx(F, d)));
   }
   RLT_TRY(wgrad<T>(w.template at<T>(TL.xg), 2 * d, w.template at<T>(TL.yg), d, rows, 2 * d, d,
-                   WDst{{g.w_gate, nullptr, nullptr}, d}, st));
+                   WDst{{g.w_gate, nullptr, nullptr}, d}, gx(2 * d, d)));
+  const double cs = (3.0 * L + 1) * rows * d * 4;
   return colsums(w.pg(0, 0), 3 * L + 1, rows, TL.Mc, d, w.template at<float>(TL.part),
-                 ColOut{g.gamma, g.b_gate, 3 * L}, st);
+                 ColOut{g.gamma, g.b_gate, 3 * L}, tm.at(RLT_K_BWD_OTHER, cs, cs / 4),
+                 tm.at(RLT_K_BWD_OTHER, 0, 0));
 }
 
 template <typename T, int HD>
 static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const void* e_v,
                          const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, Profiler* prof) {
   const TrainLayout TL = train_layout(D, B, n);
   const Walk<T> w{D, B, n, TL, ws};
   const int d = D.d, F = D.F, L = D.L, H = D.H;
   const T* e = static_cast<const T*>(e_v);
   const Exec x(st);
+  Timer tm{prof, st};
+  const int64_t stride = prof ? prof->stride : 1;
+  const double b = B, es = (double)D.es, dsz = d, Fd = F;
+  const double act32 = b * d * 4, actd = b * d * es;
   // backward copies of the weights
   {
     const BwOff bo = bw_off(D);
     T* bw = w.template at<T>(TL.bw);
     auto repack = [&](const void* src, int N, int K, T* dst, int w13, int64_t mats) {
-      return launch(k_repack<T>, dim3(blocks_for((int64_t)N * K * mats)), dim3(kThreads), x,
-                    static_cast<const T*>(src), N, K, dst, w13, F, mats);
+      const double bytes = 2.0 * N * K * mats * es;
+      return launch(k_repack<T>, dim3(blocks_for((int64_t)N * K * mats)), dim3(kThreads),
+                    tm.at(RLT_K_BWD_OTHER, bytes, 0), static_cast<const T*>(src), N, K, dst, w13,
+                    F, mats);
     };
     RLT_TRY(repack(P.w_gate_t, d, 2 * d, bw + bo.wg, 0, 1));
     RLT_TRY(repack(P.wqkv_t, 3 * d, d, bw + bo.wqkv, 0, L));
@@ -1178,14 +1224,25 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
   MemBufs M{w.template at<void>(TL.mem_k), w.template at<void>(TL.mem_v), n, B};
   float* s_hist = w.template at<float>(TL.s_hist);
   RLT_TRY(launch_reset(D, B, P, S, st));
-  RLT_TRY(launch_memproj(D, B, P, M, e, n, 0, n, x));
+  {
+    const double rows = b * n;
+    RLT_TRY(launch_memproj(D, B, P, M, e, n, 0, n,
+                           tm.at(RLT_K_MEMPROJ, es * (rows * dsz + D.G * 2 * dsz * dsz +
+                                                      rows * D.G * 2 * dsz),
+                                 2 * rows * dsz * D.G * 2 * dsz)));
+  }
   RLT_TRY(launch(k_fill_start, dim3(blocks_for((int64_t)B * d)), dim3(kThreads), x, s_hist,
                  (const float*)P.s_star, d, (int64_t)B * d));
-  // forward, saving x, y, z, q, qc, o, oc and every key/value
+  // forward, saving x, y, z, q, qc, o, oc and every key/value (bytes counted as in the decoder
+  // step)
   const int64_t ring_layer = (int64_t)B * H * D.W * D.hd;
   for (int64_t i = 0; i < n; ++i) {
     S.t_uniform = i;
-    RLT_TRY(gemm_gate(D, B, P, S, e + i * d, n * d, x));
+    const bool smp = i % stride == 0;
+    const double nv = (double)std::min<int64_t>(i + 1, D.W), t = (double)(i + 1);
+    RLT_TRY(gemm_gate(D, B, P, S, e + i * d, n * d,
+                      tm.at(RLT_K_GATE, 2 * dsz * dsz * es + actd + 2 * act32, 4 * b * dsz * dsz,
+                            smp)));
     for (int l = 0; l < L; ++l) {
       const bool last = l == L - 1;
       SaveArgs a;
@@ -1196,28 +1253,46 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
       a.k_dst = w.template at<T>(TL.khist) + (int64_t)l * B * n * d;
       a.v_dst = w.template at<T>(TL.vhist) + (int64_t)l * B * n * d;
       const dim3 grid(blocks_for((int64_t)B * d));
-      RLT_TRY(gemm_qkv(D, B, l, P, S, x));
+      RLT_TRY(gemm_qkv(D, B, l, P, S,
+                       tm.at(RLT_K_QKV, 3 * dsz * dsz * es + 2 * act32 + 2 * actd,
+                             6 * b * dsz * dsz, smp)));
       a.stage = 0; a.q = S.q; a.o = nullptr; a.o_dst = nullptr;
       a.h_dst = w.template saved<float>(TL.xs, l, i);
       a.q_dst = w.template saved<float>(TL.qs, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
-      RLT_TRY(attn_self(D, B, l, S, x));
-      RLT_TRY(gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, x));
-      RLT_TRY(gemm_cq(D, B, l, P, S, x));
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
+                     tm.at(RLT_K_BWD_OTHER, 4 * act32 + 4 * actd, 0, smp), a));
+      RLT_TRY(attn_self(D, B, l, S,
+                        tm.at(RLT_K_SELF_ATTN, nv * b * 2 * dsz * es + act32 + actd,
+                              4 * b * dsz * nv, smp)));
+      RLT_TRY(gemm_residual(D, B, l, 0, P, S, false, nullptr, 0,
+                            tm.at(RLT_K_SELF_OUT, dsz * dsz * es + actd + 2 * act32,
+                                  2 * b * dsz * dsz, smp)));
+      RLT_TRY(gemm_cq(D, B, l, P, S,
+                      tm.at(RLT_K_CROSS_Q, dsz * dsz * es + 2 * act32, 2 * b * dsz * dsz, smp)));
       a.stage = 1; a.q = S.qc; a.o = S.o;
       a.h_dst = w.template saved<float>(TL.ys, l, i);
       a.q_dst = w.template saved<float>(TL.qcs, l, i);
       a.o_dst = w.template saved<T>(TL.os, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
-      RLT_TRY(attn_cross(D, B, l, S, M, x));
-      RLT_TRY(gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, x));
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
+                     tm.at(RLT_K_BWD_OTHER, 4 * act32 + 2 * actd, 0, smp), a));
+      RLT_TRY(attn_cross(D, B, l, S, M,
+                         tm.at(RLT_K_CROSS_ATTN, t * b * 2 * dsz * es + act32 + actd,
+                               4 * b * dsz * t, smp)));
+      RLT_TRY(gemm_residual(D, B, l, 1, P, S, false, nullptr, 0,
+                            tm.at(RLT_K_CROSS_OUT, dsz * dsz * es + actd + 2 * act32,
+                                  2 * b * dsz * dsz, smp)));
       a.stage = 2; a.q = nullptr; a.q_dst = nullptr;
       a.h_dst = w.template saved<float>(TL.zs, l, i);
       a.o_dst = w.template saved<T>(TL.ocs, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), x, a));
-      RLT_TRY(gemm_w13(D, B, l, P, S, x));
+      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
+                     tm.at(RLT_K_BWD_OTHER, 2 * act32 + 2 * actd, 0, smp), a));
+      RLT_TRY(gemm_w13(D, B, l, P, S,
+                       tm.at(RLT_K_FFN_UP, 2 * Fd * dsz * es + act32 + b * Fd * es,
+                             4 * b * dsz * Fd, smp)));
       RLT_TRY(gemm_residual(D, B, l, 2, P, S, last, last ? s_hist + (i + 1) * B * d : nullptr, d,
-                            x));
+                            tm.at(RLT_K_FFN_DOWN, Fd * dsz * es + b * Fd * es + 2 * act32 +
+                                                      (last ? act32 : 0),
+                                  2 * b * dsz * Fd, smp)));
     }
   }
   if (s_traj)
@@ -1243,54 +1318,60 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
   // the reverse walk, one chunk of Tc tokens at a time (newest chunk first)
   for (int64_t i1 = n; i1 > 0;) {
     const int64_t i0 = std::max<int64_t>(0, i1 - TL.Tc);
-    for (int64_t i = i1 - 1; i >= i0; --i) RLT_TRY((walk_token<T, HD>(w, P, M, e, G, de, i, i - i0, st)));
-    RLT_TRY(chunk_grads<T>(w, g, i0, i1, st));
+    for (int64_t i = i1 - 1; i >= i0; --i)
+      RLT_TRY(walk_token<T, HD>(w, P, M, e, G, de, i, i - i0, tm, i % stride == 0));
+    RLT_TRY(chunk_grads<T>(w, g, i0, i1, tm));
     i1 = i0;
   }
   // s_0 = s* for every sequence
   RLT_TRY(colsums(w.template at<float>(TL.carry), 1, B, B, d, w.template at<float>(TL.part),
-                  ColOut{nullptr, g.s_star, 0}, st));
+                  ColOut{nullptr, g.s_star, 0}, x, x));
   // memory entries: gradients from every later token, then the memory projection's backward
   const BwOff bo = bw_off(D);
   const float scale = 1.f / sqrtf((float)HD);
   T* dkv = w.template at<T>(TL.dkv);
+  const double rows = b * n;
   for (int gi = 0; gi < D.G; ++gi) {
     const int l0 = D.G == 1 ? 0 : gi, l1 = D.G == 1 ? L : gi + 1;
     const int64_t grp = (int64_t)gi * B * n * d;
-    RLT_TRY(launch(k_mem_back<T, HD>, dim3((unsigned)((n + 63) / 64), B * H), dim3(kThreads), x,
+    const double nl = l1 - l0;
+    RLT_TRY(launch(k_mem_back<T, HD>, dim3((unsigned)((n + 63) / 64), B * H), dim3(kThreads),
+                   tm.at(RLT_K_BWD_MEM,
+                         rows * dsz * (4 * es + nl * (4 + es)) + nl * rows * H * 8,
+                         nl * 4.0 * b * dsz * (double)n * (double)(n + 1)),
                    el<T>(M.k, grp), el<T>(M.v, grp),
                    (const float*)w.template at<float>(TL.qcs), (const T*)w.template at<T>(TL.docs),
                    (const float*)w.template at<float>(TL.lse),
                    (const float*)w.template at<float>(TL.dlt), l0, l1, B, n, H, scale, dkv));
     RLT_TRY(wgrad<T>(e, d, dkv, 2 * d, (int64_t)B * n, d, 2 * d,
                      WDst{{g.wmk + (int64_t)gi * d * d, g.wmv + (int64_t)gi * d * d, nullptr}, d},
-                     st));
+                     tm.at(RLT_K_BWD_WGRAD, rows * 3 * dsz * es + 2 * dsz * dsz * 8,
+                           2 * rows * dsz * 2 * dsz)));
     if (de) {
       const T* wm = w.template at<T>(TL.bw) + bo.wm + (int64_t)gi * 2 * d * d;
-      RLT_TRY((run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(
+      RLT_TRY(run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(
           (int)((int64_t)B * n), d, 2 * d, wm, ARows<T>{dkv, 2 * d, (int)((int64_t)B * n)},
-          EpiAddF32{de, d, (int)((int64_t)B * n)}, x)));
+          EpiAddF32{de, d, (int)((int64_t)B * n)},
+          tm.at(RLT_K_BWD_PROJ, 2 * dsz * dsz * es + rows * 2 * dsz * es + rows * dsz * 8,
+                2 * rows * dsz * 2 * dsz)));
     }
   }
-  return hipSuccess;
+  return tm.err;
 }
 
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st) {
+                       hipStream_t st, Profiler* prof) {
+#define RLT_BPTT(HDV)                                                                           \
+  return D.dtype == RLT_BF16 ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, prof) \
+                             : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, prof)
   switch (D.hd) {
-    case 32:
-      return D.dtype == RLT_BF16 ? bptt_t<bf16, 32>(D, B, n, P, e, G, s_traj, g, de, ws, st)
-                                 : bptt_t<float, 32>(D, B, n, P, e, G, s_traj, g, de, ws, st);
-    case 64:
-      return D.dtype == RLT_BF16 ? bptt_t<bf16, 64>(D, B, n, P, e, G, s_traj, g, de, ws, st)
-                                 : bptt_t<float, 64>(D, B, n, P, e, G, s_traj, g, de, ws, st);
-    case 128:
-      return D.dtype == RLT_BF16 ? bptt_t<bf16, 128>(D, B, n, P, e, G, s_traj, g, de, ws, st)
-                                 : bptt_t<float, 128>(D, B, n, P, e, G, s_traj, g, de, ws, st);
-    default:
-      return hipErrorInvalidValue;
+    case 32: RLT_BPTT(32);
+    case 64: RLT_BPTT(64);
+    case 128: RLT_BPTT(128);
+    default: return hipErrorInvalidValue;
   }
+#undef RLT_BPTT
 }
 
 #undef RLT_TRY

@@ -237,8 +237,10 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n);
 // reverse walk needs, then the reverse walk for upstream gradients G [B][n][d]: every field of
 // `g` is overwritten with dLoss/dparam for Loss = sum_{b,t} G[b][t] . s_t(b); de [B][n][d]
 // (optional) receives dLoss/de; s_traj [B][n][d] (optional) the forward trajectory.
+// With `prof`, launches of the kernels it times are timed in the steps of tokens
+// i % prof->stride == 0 and everywhere outside the token loops.
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st);
+                       hipStream_t st, Profiler* prof);
 
 }  // namespace rlt

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import stateful_decoding_amd as sd
-from synth import RLTConfig
+from synth import CONFIGS, RLTConfig
 from tests.gpu_helpers import TOL, inputs, max_rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -94,5 +94,39 @@ def test_bptt_argument_errors():
     g = sd.binding.rlt_grads(*[grads[k].data_ptr() for k in sd.binding.WEIGHT_FIELDS])
     g.w2 = None
     st = lib.rlt_bptt(model.handle, ed.data_ptr(), 2, 4, Gd.data_ptr(), None,
-                      sd.binding.byref(g), None, ws.data_ptr(), ws.numel(), None)
+                      sd.binding.byref(g), None, ws.data_ptr(), ws.numel(), None, None, None)
     assert sd.binding.STATUS_NAMES[st] == "RLT_ERR_ARG"
+
+
+def test_full_size_bptt_early_tokens_match_oracle():
+    """The benchmark's launch configuration (the 140M-scale workload, B = 256, T = 1024): the
+    whole forward and the whole reverse walk run, with the loss restricted to sequences 0 and
+    255 at tokens 1..16. Every gradient then equals the oracle's for those two sequences over
+    those 16 tokens, and dLoss/de is exactly zero for every other sequence and later token."""
+    cfg = CONFIGS["s140m_bf16"]
+    B, T, n_or = cfg.batch, cfg.seq_len, 16
+    seqs = [0, B - 1]
+    p, e = inputs(cfg, B, T)
+    G = np.zeros((B, T, cfg.d), np.float32)
+    G[seqs, :n_or] = np.random.default_rng(7).standard_normal((2, n_or, cfg.d))
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(e).to("cuda", model.dtype).contiguous()
+    Gd = torch.from_numpy(G).cuda()
+    del e
+    grads = sd.grad_buffers(model)
+    de = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+    print(f"full size {cfg.name}: B={B} T={T}, loss on sequences {seqs} tokens 1..{n_or}",
+          flush=True)
+    sd.rlt_bptt(model, ed, Gd, grads, de=de)
+    torch.cuda.synchronize()
+    e_or = ed[seqs, :n_or].float().cpu().numpy()
+    _, ref, ref_de = oracle.bptt(p, cfg, e_or, G[seqs, :n_or])
+    errs = {k: rel_l2(grads[k].cpu().numpy(), ref[k]) for k in oracle.GRAD_NAMES}
+    de_h = de.cpu().numpy()
+    errs["de"] = rel_l2(de_h[seqs, :n_or], ref_de)
+    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    mask = np.ones(B, bool)
+    mask[seqs] = False
+    assert not np.any(de_h[mask]) and not np.any(de_h[seqs, n_or:])
+    worst = max(errs, key=errs.get)
+    assert errs[worst] <= TOL["bf16"], (worst, errs[worst])
