@@ -92,8 +92,8 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.gsave = take(b * d * 4);
   t.carry = take(b * d * 4);
   t.rinv = take(b * 3 * 4);
-  t.dkacc = take(L * b * D.W * d * 4);
-  t.dvacc = take(L * b * D.W * d * 4);
+  t.dkacc = take(L * D.W * b * d * es);      // window-backward rings: do of the last W tokens
+  t.dvacc = take(2 * L * D.W * b * H * 4);  // and their lse, D
   t.ca = take(L * Mc * d * es);
   t.cc = take(L * Mc * d * es);
   t.cf = take(L * Mc * d * es);
@@ -109,6 +109,10 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.yg = take(Mc * d * es);
   t.part = take((3 * L + 1) * kRowSplits * d * 4);
   t.dkv = take(b * N * 2 * d * es);
+  // weight-gradient operands transposed to [features][rows] (rows padded to 32)
+  const size_t Mp = (Mc + 31) / 32 * 32;
+  t.tx = take(Mp * std::max(2 * d, F) * es);
+  t.ty = take(Mp * std::max(3 * d, 2 * F) * es);
   t.total = o;
   return t;
 }
@@ -604,20 +608,24 @@ __global__ __launch_bounds__(NW * kWave) void k_xattn_back(
   }
 }
 
-// Self-attention backward of token t for one (sequence, head) per workgroup over the window
-// keys j = lo..t (lo = max(0, t - W + 1)) of the layer's key/value history. Pass 1 forms the
-// softmax normaliser and D; pass 2 adds every key's gradient scale dz_j q and value gradient
-// p_j do into the fp32 accumulators (slot j % W), and for j = t, whose gradient is then
-// complete, writes dk, dv (with dq) to out [M][3d] and clears the slot.
-template <typename T, int HD, int NW>
+// Self-attention backward of token t for one (sequence, head) per workgroup.
+//   dq_t: one online pass over the window keys j = lo..t (lo = max(0, t - W + 1)) of the layer's
+//         key/value history, as for the memory prefix; it also yields lse_t and D_t, which go
+//         with do_t to rings of W slots (slot t % W) for the tokens walked after this one.
+//   dk_t, dv_t: token t's key/value is seen by the later tokens t' = t..min(t + W - 1, n - 1),
+//         all walked already: dk_t = scale sum_t' dz_t't q_t', dv_t = sum_t' p_t't do_t' with
+//         p_t't = exp(scale q_t'.k_t - lse_t') and dz = p (do_t'.v_t - D_t'), from the saved
+//         queries and the rings. Writes [dq | dk | dv] (dtype) to out [M][3d].
+template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_swa_back(
-    const float* __restrict__ q, const float* __restrict__ dout, const T* __restrict__ K,
-    const T* __restrict__ V, int64_t n, int64_t t, int W, int H, float scale,
-    float* __restrict__ dkacc, float* __restrict__ dvacc, T* __restrict__ out) {
+    const float* __restrict__ qs, const float* __restrict__ dout, const T* __restrict__ K,
+    const T* __restrict__ V, int64_t n, int64_t t, int W, int B, int H, float scale,
+    T* __restrict__ ring_do, float* __restrict__ ring_lse, float* __restrict__ ring_dlt,
+    T* __restrict__ out) {
   using G = AGeo<T, HD>;
   constexpr int VEC = G::VEC, RPB = G::RPW * NW;
   __shared__ float s_m[NW], s_l[NW], s_c[NW];
-  __shared__ float s_q[NW][HD];
+  __shared__ float s_A[NW][HD], s_B[NW][HD];
   __shared__ float s_stat[2];
   const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -626,129 +634,204 @@ __global__ __launch_bounds__(NW * kWave) void k_swa_back(
   const int nk = (int)(t - lo + 1);
   const T* Kb = K + ((int64_t)bh * n + lo) * HD + sub * VEC;
   const T* Vb = V + ((int64_t)bh * n + lo) * HD + sub * VEC;
-  const int64_t qo = (int64_t)b * d + hh * HD + sub * VEC;
+  const int64_t ho = hh * HD + sub * VEC;  // this lane's dims within a row of d
+  const float* q_t = qs + t * B * d + (int64_t)b * d;
   float qv[VEC], dv[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
-    qv[i] = q[qo + i];
-    dv[i] = dout[qo + i];
+    qv[i] = q_t[ho + i] * scale;
+    dv[i] = dout[(int64_t)b * d + ho + i];
   }
+  // ---- dq_t, lse_t, D_t: online pass over the window keys
+  BwdState<VEC> S;
+  S.init();
   const int first = wave * G::RPW + slot;
-  auto scores = [&](int row, float& s, float& p) {
-    float kf[VEC], vf[VEC];
-    unpack(ld16(Kb + (int64_t)row * HD), kf);
-    unpack(ld16(Vb + (int64_t)row * HD), vf);
-    s = 0.f;
-    p = 0.f;
+  for (int base = 0; base < nk; base += RPB * U) {
+    u32x4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = base + u * RPB + first;
+      const bool ok = row < nk;
+      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+    }
+    float sc[U], dp[U];
+    float mb = S.m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VEC], vf[VEC];
+      unpack(kr[u], kf);
+      unpack(vr[u], vf);
+      float sv = 0.f, pv = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        sv += qv[i] * kf[i];
+        pv += dv[i] * vf[i];
+      }
+#pragma unroll
+      for (int o = G::LPR / 2; o >= 1; o >>= 1) {
+        sv += __shfl_xor(sv, o, kWave);
+        pv += __shfl_xor(pv, o, kWave);
+      }
+      const bool ok = base + u * RPB + first < nk;
+      sc[u] = ok ? sv : -INFINITY;
+      dp[u] = pv;
+      mb = fmaxf(mb, sc[u]);
+    }
+    if (mb == -INFINITY) continue;
+    const float cs = S.m == -INFINITY ? 0.f : __expf(S.m - mb);
+    S.l *= cs;
+    S.c *= cs;
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      s += qv[i] * kf[i];
-      p += dv[i] * vf[i];
+      S.A[i] *= cs;
+      S.Bk[i] *= cs;
     }
 #pragma unroll
-    for (int o = G::LPR / 2; o >= 1; o >>= 1) {
-      s += __shfl_xor(s, o, kWave);
-      p += __shfl_xor(p, o, kWave);
+    for (int u = 0; u < U; ++u) {
+      const float e = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - mb);
+      float kf[VEC];
+      unpack(kr[u], kf);
+      S.l += e;
+      S.c += e * dp[u];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        S.A[i] += e * dp[u] * kf[i];
+        S.Bk[i] += e * kf[i];
+      }
     }
-    s *= scale;
-  };
-  // pass 1: m, l, c over the window (every lane of a slot walks the same rows)
-  float m = -INFINITY, l = 0.f, c = 0.f;
-  for (int row = first; row - first < nk; row += RPB) {
-    if (row >= nk) break;
-    float s, p;
-    scores(row, s, p);
-    const float mn = fmaxf(m, s);
-    const float a = m == -INFINITY ? 0.f : __expf(m - mn), e = __expf(s - mn);
-    l = l * a + e;
-    c = c * a + e * p;
-    m = mn;
+    S.m = mb;
   }
 #pragma unroll
   for (int o = G::LPR; o < kWave; o <<= 1) {
-    const float mo = __shfl_xor(m, o, kWave), lo2 = __shfl_xor(l, o, kWave),
-                co = __shfl_xor(c, o, kWave);
-    const float mn = fmaxf(m, mo);
-    const float a = m == -INFINITY ? 0.f : __expf(m - mn);
-    const float bb = mo == -INFINITY ? 0.f : __expf(mo - mn);
-    l = l * a + lo2 * bb;
-    c = c * a + co * bb;
-    m = mn;
-  }
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = l;
-    s_c[wave] = c;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float M = s_m[0], Lx = s_l[0], C = s_c[0];
-    for (int w = 1; w < NW; ++w) {
-      const float mn = fmaxf(M, s_m[w]);
-      const float a = M == -INFINITY ? 0.f : __expf(M - mn);
-      const float bb = s_m[w] == -INFINITY ? 0.f : __expf(s_m[w] - mn);
-      Lx = Lx * a + s_l[w] * bb;
-      C = C * a + s_c[w] * bb;
-      M = mn;
-    }
-    s_stat[0] = M + __logf(Lx);  // log-sum-exp
-    s_stat[1] = C / Lx;          // D = sum_j p_j dp_j
-  }
-  __syncthreads();
-  const float lse = s_stat[0], D = s_stat[1];
-  // pass 2: key/value gradients into the accumulators, dq in registers
-  float dqa[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) dqa[i] = 0.f;
-  float* ak = dkacc + (int64_t)bh * W * HD + sub * VEC;
-  float* av = dvacc + (int64_t)bh * W * HD + sub * VEC;
-  for (int row = first; row < nk; row += RPB) {
-    float s, p;
-    scores(row, s, p);
-    const float pj = __expf(s - lse);
-    const float dz = pj * (p - D);
-    float kf[VEC];
-    unpack(ld16(Kb + (int64_t)row * HD), kf);
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) dqa[i] += dz * kf[i];
-    const int64_t j = lo + row;
-    const int64_t so = (int64_t)(j % W) * HD;
-    float gk[VEC], gv[VEC];
+    const float mo = __shfl_xor(S.m, o, kWave), lo2 = __shfl_xor(S.l, o, kWave),
+                co = __shfl_xor(S.c, o, kWave);
+    float Ao[VEC], Bo[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      gk[i] = ak[so + i] + scale * dz * qv[i];
-      gv[i] = av[so + i] + pj * dv[i];
+      Ao[i] = __shfl_xor(S.A[i], o, kWave);
+      Bo[i] = __shfl_xor(S.Bk[i], o, kWave);
     }
-    if (j == t) {  // every later token that saw this key has been walked
-      const int64_t oo = (int64_t)b * 3 * d + hh * HD + sub * VEC;
+    S.merge(mo, lo2, co, Ao, Bo);
+  }
+  if (slot == 0) {
+    if (sub == 0) {
+      s_m[wave] = S.m;
+      s_l[wave] = S.l;
+      s_c[wave] = S.c;
+    }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        out[oo + d + i] = to_elem<T>(gk[i]);
-        out[oo + 2 * d + i] = to_elem<T>(gv[i]);
-        ak[so + i] = 0.f;
-        av[so + i] = 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        ak[so + i] = gk[i];
-        av[so + i] = gv[i];
-      }
+    for (int i = 0; i < VEC; ++i) {
+      s_A[wave][sub * VEC + i] = S.A[i];
+      s_B[wave][sub * VEC + i] = S.Bk[i];
     }
   }
-  // dq: sum over the slots of the wave, then over the waves
+  __syncthreads();
+  const int64_t ro = (int64_t)b * 3 * d + hh * HD;  // this head's columns of out row b
+  const int64_t rslot = t % W;
+  if (tid < HD) {
+    BwdState<1> R;
+    R.m = s_m[0];
+    R.l = s_l[0];
+    R.c = s_c[0];
+    R.A[0] = s_A[0][tid];
+    R.Bk[0] = s_B[0][tid];
+    for (int w = 1; w < NW; ++w) R.merge(s_m[w], s_l[w], s_c[w], &s_A[w][tid], &s_B[w][tid]);
+    const float D = R.c / R.l;
+    out[ro + tid] = to_elem<T>(scale * (R.A[0] - D * R.Bk[0]) / R.l);
+    ring_do[(rslot * B + b) * d + hh * HD + tid] = to_elem<T>(dout[(int64_t)b * d + hh * HD + tid]);
+    if (tid == 0) {
+      const float lse = R.m + __logf(R.l);
+      s_stat[0] = lse;
+      s_stat[1] = D;
+      ring_lse[rslot * B * H + bh] = lse;
+      ring_dlt[rslot * B * H + bh] = D;
+    }
+  }
+  __syncthreads();
+  // ---- dk_t, dv_t: token t itself (from registers and LDS), then the later tokens
+  float kt[VEC], vt[VEC], gk[VEC], gv[VEC];
+  {
+    float kf[VEC], vf[VEC];
+    unpack(ld16(Kb + (int64_t)(nk - 1) * HD), kf);  // row t of the history
+    unpack(ld16(Vb + (int64_t)(nk - 1) * HD), vf);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      kt[i] = kf[i];
+      vt[i] = vf[i];
+      gk[i] = 0.f;
+      gv[i] = 0.f;
+    }
+  }
+  const int64_t hi = t + W - 1 < n - 1 ? t + W - 1 : n - 1;  // last token whose window holds t
+  const int nq = (int)(hi - t + 1);
+  for (int r = first; r < nq; r += RPB) {
+    const int64_t tp = t + r;
+    float qf[VEC], df[VEC], lse, D;
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        qf[i] = qv[i] / scale;
+        df[i] = dv[i];
+      }
+      lse = s_stat[0];
+      D = s_stat[1];
+    } else {
+      const float* qp = qs + tp * B * d + (int64_t)b * d + ho;
+      const int64_t sl = tp % W;
+      u32x4 raw = ld16(ring_do + (sl * B + b) * d + ho);
+      float tmp[VEC];
+      unpack(raw, tmp);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        qf[i] = qp[i];
+        df[i] = tmp[i];
+      }
+      lse = ring_lse[sl * B * H + bh];
+      D = ring_dlt[sl * B * H + bh];
+    }
+    float sv = 0.f, pv = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      sv += qf[i] * kt[i];
+      pv += df[i] * vt[i];
+    }
+#pragma unroll
+    for (int o = G::LPR / 2; o >= 1; o >>= 1) {
+      sv += __shfl_xor(sv, o, kWave);
+      pv += __shfl_xor(pv, o, kWave);
+    }
+    const float pj = __expf(scale * sv - lse);
+    const float dz = pj * (pv - D);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      gk[i] += scale * dz * qf[i];
+      gv[i] += pj * df[i];
+    }
+  }
+  // sum over the slots of the wave, then over the waves
 #pragma unroll
   for (int o = G::LPR; o < kWave; o <<= 1)
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) dqa[i] += __shfl_xor(dqa[i], o, kWave);
+    for (int i = 0; i < VEC; ++i) {
+      gk[i] += __shfl_xor(gk[i], o, kWave);
+      gv[i] += __shfl_xor(gv[i], o, kWave);
+    }
   if (slot == 0)
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) s_q[wave][sub * VEC + i] = dqa[i];
+    for (int i = 0; i < VEC; ++i) {
+      s_A[wave][sub * VEC + i] = gk[i];
+      s_B[wave][sub * VEC + i] = gv[i];
+    }
   __syncthreads();
   if (tid < HD) {
-    float v = 0.f;
-    for (int w = 0; w < NW; ++w) v += s_q[w][tid];
-    out[(int64_t)b * 3 * d + hh * HD + tid] = to_elem<T>(scale * v);
+    float k = 0.f, v = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      k += s_A[w][tid];
+      v += s_B[w][tid];
+    }
+    out[ro + d + tid] = to_elem<T>(k);
+    out[ro + 2 * d + tid] = to_elem<T>(v);
   }
 }
 
@@ -830,80 +913,73 @@ __global__ __launch_bounds__(kThreads) void k_mem_back(
 }
 
 // ---- weight gradients: C[K][N] += X[M][K]^T Y[M][N] ----------------------------------------------
-// 64 x 64 output tile per workgroup (2 x 2 waves of 32 x 32), contraction over rows in steps of
-// 64. Both operand tiles are staged transposed in LDS ([k][m]), so one lane's MFMA fragment
-// (8 consecutive rows) is one 16-byte LDS read. Output column c goes to dst.p[c / split] at
-// (k, c % split) of a [K][split] fp32 matrix, added to what is there.
+// Both operands are first transposed to [features][rows] in MFMA fragment order (rows padded with
+// zeros to a multiple of 32), which makes the contraction over rows the fragments' k dimension;
+// the product is then the register-tiled token GEMM (k_gemm_tokens) with the transposed X as
+// operand A and the transposed Y in the place of the packed weights.
+
+// dst[frag_off(c, m, Mp / 32)] = src[m][c] for m < M, zero for M <= m < Mp. One workgroup per
+// 32 x 32 tile, staged in LDS; each store is 8 consecutive rows of one column (16 bytes bf16).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_mfrag(const T* __restrict__ src, int64_t ld,
+                                                    int64_t M, int64_t Mp, T* __restrict__ dst) {
+  __shared__ T tile[32][33];
+  const int64_t m0 = (int64_t)blockIdx.y * 32;
+  const int c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t m = m0 + r;
+    tile[r][tx] = m < M ? src[m * ld + c0 + tx] : to_elem<T>(0.f);
+  }
+  __syncthreads();
+  if (threadIdx.x >= 128) return;
+  const int c = threadIdx.x / 4, g = threadIdx.x % 4;
+  T v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = tile[g * 8 + e][c];
+  T* o = dst + frag_off(c0 + c, (int)(m0 + g * 8), (int)(Mp / 32));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = v[e];
+}
+
+template <typename T>
+struct AMfrag {  // A = [rows][K] in fragment order (ksteps = K / 32); token-GEMM interface
+  const T* a;
+  int ksteps;
+  int M;
+  __device__ Frag<T> load(int row, int k, float&) const {
+    Frag<T> f;
+    if (row < M) f.load(a + frag_off(row, k, ksteps));
+    else f.zero();
+    return f;
+  }
+};
+
+// Output column c goes to p[c / split] at (row, c % split) of a [rows][split] fp32 matrix,
+// added to what is there.
 struct WDst {
   float* p[3];
   int split;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_wgrad(const T* __restrict__ X, int64_t ldx,
-                                                    const T* __restrict__ Y, int64_t ldy,
-                                                    int64_t M, int K, int N, WDst dst) {
-  constexpr int BT = 64, MT = 64, PAD = 8, LDT = MT + PAD;
-  constexpr int VEC = 16 / (int)sizeof(T);
-  __shared__ __align__(16) T xs[BT][LDT];
-  __shared__ __align__(16) T ys[BT][LDT];
-  const int tiles_n = N / BT;
-  const int k0 = (blockIdx.x / tiles_n) * BT, n0 = (blockIdx.x % tiles_n) * BT;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int wk = wave / 2, wn = wave % 2;
-  f32x4 acc[2][2];
+struct EpiAddSplit {
+  WDst dst;
+  int M;
+  template <int FM, int FN>
+  __device__ void tile(const f32x4 (&acc)[FM][FN], int rbase, int cwave, int lane) const {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int LOADS = BT * MT / VEC / kThreads;  // 16-byte loads per operand per thread
-  for (int64_t m0 = 0; m0 < M; m0 += MT) {
-    __syncthreads();
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int x = tid + u * kThreads;
-      const int mr = x / (BT / VEC), kc = (x % (BT / VEC)) * VEC;
-      const int64_t m = m0 + mr;
-      u32x4 rx = u32x4{0, 0, 0, 0}, ry = u32x4{0, 0, 0, 0};
-      if (m < M) {
-        rx = ld16(X + m * ldx + k0 + kc);
-        ry = ld16(Y + m * ldy + n0 + kc);
-      }
-      const T* px = reinterpret_cast<const T*>(&rx);
-      const T* py = reinterpret_cast<const T*>(&ry);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        xs[kc + e][mr] = px[e];
-        ys[kc + e][mr] = py[e];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < MT; ks += 32) {
-      Frag<T> a[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i].load(&xs[wk * 32 + i * 16 + (lane & 15)][ks + (lane >> 4) * 8]);
-        bf[i].load(&ys[wn * 32 + i * 16 + (lane & 15)][ks + (lane >> 4) * 8]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mfma_16x16x32(acc[i][j], a[i], bf[j]);
-    }
+        for (int i = 0; i < 4; ++i) {
+          const int row = rbase + 16 * fm + i;
+          const int c = cwave + 16 * fn + (lane & 15);
+          const int which = c / dst.split, cc = c - which * dst.split;
+          if (row < M) dst.p[which][(int64_t)row * dst.split + cc] += acc[fm][fn][i];
+        }
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = k0 + wk * 32 + i * 16 + (lane >> 4) * 4 + e;
-        const int c = n0 + wn * 32 + j * 16 + (lane & 15);
-        const int which = c / dst.split, cc = c - which * dst.split;
-        dst.p[which][(int64_t)k * dst.split + cc] += acc[i][j][e];
-      }
-}
+};
 
 // ---- host side ---------------------------------------------------------------------------------
 
@@ -923,12 +999,19 @@ static inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads -
     if (err_ != hipSuccess) return err_;   \
   } while (0)
 
+// C[K][N] += X[M][K]^T Y[M][N] through the transposition scratch tx, ty (>= Mp * K and
+// Mp * N elements, Mp = M rounded up to 32).
 template <typename T>
 static hipError_t wgrad(const T* X, int64_t ldx, const T* Y, int64_t ldy, int64_t M, int K, int N,
-                        WDst dst, const Exec& x) {
-  if (K % 64 || N % 64 || M <= 0) return hipErrorInvalidValue;
-  return launch(k_wgrad<T>, dim3((unsigned)((K / 64) * (N / 64))), dim3(kThreads), x, X,
-                ldx, Y, ldy, M, K, N, dst);
+                        WDst dst, T* tx, T* ty, const Exec& xt, const Exec& x) {
+  if (K % 64 || N % 64 || M <= 0 || M > INT32_MAX / 2) return hipErrorInvalidValue;
+  const int64_t Mp = (M + 31) / 32 * 32;
+  RLT_TRY(launch(k_mfrag<T>, dim3(K / 32, (unsigned)(Mp / 32)), dim3(kThreads), xt, X, ldx, M, Mp,
+                 tx));
+  RLT_TRY(launch(k_mfrag<T>, dim3(N / 32, (unsigned)(Mp / 32)), dim3(kThreads), Exec(xt.st), Y,
+                 ldy, M, Mp, ty));
+  return run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(
+      K, N, (int)Mp, ty, AMfrag<T>{tx, (int)(Mp / 32), K}, EpiAddSplit{dst, K}, x);
 }
 
 template <typename T, int HD>
@@ -947,14 +1030,14 @@ static hipError_t xattn_back(int BH, const float* q, const float* dout, const T*
 }
 
 template <typename T, int HD>
-static hipError_t swa_back(int BH, const float* q, const float* dout, const T* K, const T* V,
-                           int64_t n, int64_t t, int W, int H, float* dkacc, float* dvacc, T* out,
-                           const Exec& x) {
+static hipError_t swa_back(int BH, int B, const float* qs, const float* dout, const T* K,
+                           const T* V, int64_t n, int64_t t, int W, int H, T* ring_do,
+                           float* ring_lse, float* ring_dlt, T* out, const Exec& x) {
   const float scale = 1.f / sqrtf((float)HD);
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
-#define RLT_SB(NW)                                                                             \
-  return launch(k_swa_back<T, HD, NW>, dim3(BH), dim3(NW * kWave), x, q, dout, K, V, n,        \
-                t, W, H, scale, dkacc, dvacc, out)
+#define RLT_SB(NW)                                                                              \
+  return launch(k_swa_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, qs, dout, K, V, n, t, W, \
+                B, H, scale, ring_do, ring_lse, ring_dlt, out)
   if (nw == 4) RLT_SB(4);
   if (nw == 8) RLT_SB(8);
   RLT_SB(16);
@@ -1098,14 +1181,18 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn,
                              proj(d, d, rows32)));
     T* yqkv = w.chunk(TL.yqkv, l, 3 * d, li);
-    const int64_t hist = (int64_t)l * B * n * d, acc = (int64_t)l * B * D.W * d;
+    const int64_t hist = (int64_t)l * B * n * d;
+    const int64_t rd = (int64_t)l * D.W * B * d, rs = (int64_t)l * D.W * BH;
     const double nk = (double)std::min<int64_t>(i + 1, D.W);
-    RLT_TRY(swa_back<T, HD>(BH, w.template saved<float>(TL.qs, l, i), dattn,
+    const double nq = (double)std::min<int64_t>(n - i, D.W);
+    RLT_TRY(swa_back<T, HD>(BH, B, w.template at<float>(TL.qs) + (int64_t)l * n * B * d, dattn,
                             w.template at<T>(TL.khist) + hist, w.template at<T>(TL.vhist) + hist,
-                            n, i, D.W, H, w.template at<float>(TL.dkacc) + acc,
-                            w.template at<float>(TL.dvacc) + acc, yqkv,
-                            tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * (es + 8) + 2 * rows32 +
-                                      3 * rowsT, 14 * b * d * nk, sampled)));
+                            n, i, D.W, H, w.template at<T>(TL.dkacc) + rd,
+                            w.template at<float>(TL.dvacc) + rs,
+                            w.template at<float>(TL.dvacc) + (int64_t)L * D.W * BH + rs, yqkv,
+                            tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * es + nq * b * d * (4 + es) +
+                                      2 * rows32 + 4 * rowsT, (10 * nk + 8 * nq) * b * d,
+                                  sampled)));
     RLT_TRY(run_step_gemm<T>(B, d, 3 * d, bw + bo.wqkv + (int64_t)l * 3 * dd,
                              ARows<T>{yqkv, 3 * d, B}, to_dn, proj(d, 3 * d, rows32)));
     RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, xs, gam,
@@ -1144,25 +1231,31 @@ static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, i
   const int B = w.B, d = D.d, F = D.F, L = D.L;
   const int64_t rows = (i1 - i0) * B, dd = (int64_t)d * d, dF = (int64_t)d * F;
   const double es = (double)D.es;
-  auto gx = [&](double K, double N) {
-    return tm.at(RLT_K_BWD_WGRAD, rows * (K + N) * es + K * N * 8, 2.0 * rows * K * N);
+  T* tx = w.template at<T>(TL.tx);
+  T* ty = w.template at<T>(TL.ty);
+  // operands transposed once (read + write), then the GEMM (reads both, adds into fp32 C)
+  auto gw = [&](const T* X, int64_t ldx, const T* Y, int64_t ldy, int K, int N, WDst dst) {
+    return wgrad<T>(X, ldx, Y, ldy, rows, K, N, dst, tx, ty,
+                    tm.at(RLT_K_BWD_OTHER, 2.0 * rows * (K + N) * es, 0),
+                    tm.at(RLT_K_BWD_WGRAD, rows * (K + N) * es + (double)K * N * 8,
+                          2.0 * rows * K * N));
   };
   for (int l = 0; l < L; ++l) {
-    RLT_TRY(wgrad<T>(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, rows, d,
-                     3 * d, WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}, gx(d, 3 * d)));
-    RLT_TRY(wgrad<T>(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, rows, d,
-                     d, WDst{{g.wo + l * dd, nullptr, nullptr}, d}, gx(d, d)));
-    RLT_TRY(wgrad<T>(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, rows, d, d,
-                     WDst{{g.wcq + l * dd, nullptr, nullptr}, d}, gx(d, d)));
-    RLT_TRY(wgrad<T>(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, rows, d,
-                     d, WDst{{g.wco + l * dd, nullptr, nullptr}, d}, gx(d, d)));
-    RLT_TRY(wgrad<T>(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, rows, d,
-                     2 * F, WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}, gx(d, 2 * F)));
-    RLT_TRY(wgrad<T>(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, rows, F, d,
-                     WDst{{g.w2 + l * dF, nullptr, nullptr}, d}, gx(F, d)));
+    RLT_TRY(gw(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, d, 3 * d,
+               WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}));
+    RLT_TRY(gw(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, d, d,
+               WDst{{g.wo + l * dd, nullptr, nullptr}, d}));
+    RLT_TRY(gw(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, d, d,
+               WDst{{g.wcq + l * dd, nullptr, nullptr}, d}));
+    RLT_TRY(gw(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, d, d,
+               WDst{{g.wco + l * dd, nullptr, nullptr}, d}));
+    RLT_TRY(gw(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, d, 2 * F,
+               WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}));
+    RLT_TRY(gw(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, F, d,
+               WDst{{g.w2 + l * dF, nullptr, nullptr}, d}));
   }
-  RLT_TRY(wgrad<T>(w.template at<T>(TL.xg), 2 * d, w.template at<T>(TL.yg), d, rows, 2 * d, d,
-                   WDst{{g.w_gate, nullptr, nullptr}, d}, gx(2 * d, d)));
+  RLT_TRY(gw(w.template at<T>(TL.xg), 2 * d, w.template at<T>(TL.yg), d, 2 * d, d,
+             WDst{{g.w_gate, nullptr, nullptr}, d}));
   const double cs = (3.0 * L + 1) * rows * d * 4;
   return colsums(w.pg(0, 0), 3 * L + 1, rows, TL.Mc, d, w.template at<float>(TL.part),
                  ColOut{g.gamma, g.b_gate, 3 * L}, tm.at(RLT_K_BWD_OTHER, cs, cs / 4),
@@ -1311,9 +1404,6 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     for (const Z& z : zs) RLT_TRY(hipMemsetAsync(z.p, 0, sizeof(float) * z.n, st));
     if (de) RLT_TRY(hipMemsetAsync(de, 0, sizeof(float) * B * n * d, st));
     RLT_TRY(hipMemsetAsync(w.template at<float>(TL.carry), 0, sizeof(float) * B * d, st));
-    const size_t accb = sizeof(float) * (size_t)L * B * D.W * d;
-    RLT_TRY(hipMemsetAsync(w.template at<float>(TL.dkacc), 0, accb, st));
-    RLT_TRY(hipMemsetAsync(w.template at<float>(TL.dvacc), 0, accb, st));
   }
   // the reverse walk, one chunk of Tc tokens at a time (newest chunk first)
   for (int64_t i1 = n; i1 > 0;) {
@@ -1343,10 +1433,16 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
                    (const float*)w.template at<float>(TL.qcs), (const T*)w.template at<T>(TL.docs),
                    (const float*)w.template at<float>(TL.lse),
                    (const float*)w.template at<float>(TL.dlt), l0, l1, B, n, H, scale, dkv));
-    RLT_TRY(wgrad<T>(e, d, dkv, 2 * d, (int64_t)B * n, d, 2 * d,
-                     WDst{{g.wmk + (int64_t)gi * d * d, g.wmv + (int64_t)gi * d * d, nullptr}, d},
-                     tm.at(RLT_K_BWD_WGRAD, rows * 3 * dsz * es + 2 * dsz * dsz * 8,
-                           2 * rows * dsz * 2 * dsz)));
+    for (int64_t r0 = 0; r0 < (int64_t)B * n; r0 += TL.Mc) {  // in chunks of rows
+      const int64_t rc = std::min<int64_t>(TL.Mc, (int64_t)B * n - r0);
+      RLT_TRY(wgrad<T>(e + r0 * d, d, dkv + r0 * 2 * d, 2 * d, rc, d, 2 * d,
+                       WDst{{g.wmk + (int64_t)gi * d * d, g.wmv + (int64_t)gi * d * d, nullptr},
+                            d},
+                       w.template at<T>(TL.tx), w.template at<T>(TL.ty),
+                       tm.at(RLT_K_BWD_OTHER, 2.0 * rc * 3 * dsz * es, 0),
+                       tm.at(RLT_K_BWD_WGRAD, rc * 3 * dsz * es + 2 * dsz * dsz * 8,
+                             2.0 * rc * dsz * 2 * dsz)));
+    }
     if (de) {
       const T* wm = w.template at<T>(TL.bw) + bo.wm + (int64_t)gi * 2 * d * d;
       RLT_TRY(run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(

@@ -229,7 +229,7 @@ struct TrainLayout {
   int64_t Tc, Mc;
   size_t state, mem_k, mem_v, bw, s_hist, xs, ys, zs, qs, qcs, os, ocs, docs, khist, vhist, lse,
       dlt, dres, dn, dattn, u13, gsave, carry, rinv, dkacc, dvacc, ca, cc, cf, cm, yqkv, yo, ycq,
-      yco, y13, y2, pg, xg, yg, part, dkv, total;
+      yco, y13, y2, pg, xg, yg, part, dkv, tx, ty, total;
 };
 TrainLayout train_layout(const Dims& D, int B, int64_t n);
 

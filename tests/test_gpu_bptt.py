@@ -28,6 +28,20 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
 
 
+def grad_errors(got: dict, ref: dict) -> dict:
+    """Relative L2 error per gradient tensor. A tensor whose exact gradient is zero (e.g. the
+    query and key weights when the window holds one token) is judged on the scale of the
+    loss's other gradients: ||got|| over their mean norm, so a rounding residue passes and a
+    real leak does not."""
+    norms = [float(np.linalg.norm(np.asarray(ref[k], np.float64))) for k in oracle.GRAD_NAMES]
+    scale = float(np.mean([x for x in norms if x > 0]))
+    out = {}
+    for k, nr in zip(oracle.GRAD_NAMES, norms):
+        diff = np.linalg.norm(np.asarray(got[k], np.float64) - np.asarray(ref[k], np.float64))
+        out[k] = float(diff / (nr if nr > 0 else scale))
+    return out
+
+
 def run_case(cfg, B, T, seed):
     p, e = inputs(cfg, B, T, seed=seed, random_gains=True, random_gate_bias=True)
     G = np.random.default_rng(seed + 1000).standard_normal((B, T, cfg.d)).astype(np.float32)
@@ -43,7 +57,7 @@ def run_case(cfg, B, T, seed):
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in grads.items()}
     ref_traj, ref, ref_de = oracle.bptt(p, cfg, e, G)
-    errs = {k: rel_l2(got[k], ref[k]) for k in oracle.GRAD_NAMES}
+    errs = grad_errors(got, ref)
     errs["de"] = rel_l2(de.cpu().numpy(), ref_de)
     errs["s_traj"] = max_rel_l2(traj.cpu().numpy(), ref_traj)
     worst = max(errs, key=errs.get)
@@ -121,7 +135,7 @@ def test_full_size_bptt_early_tokens_match_oracle():
     torch.cuda.synchronize()
     e_or = ed[seqs, :n_or].float().cpu().numpy()
     _, ref, ref_de = oracle.bptt(p, cfg, e_or, G[seqs, :n_or])
-    errs = {k: rel_l2(grads[k].cpu().numpy(), ref[k]) for k in oracle.GRAD_NAMES}
+    errs = grad_errors({k: v.cpu().numpy() for k, v in grads.items()}, ref)
     de_h = de.cpu().numpy()
     errs["de"] = rel_l2(de_h[seqs, :n_or], ref_de)
     print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
