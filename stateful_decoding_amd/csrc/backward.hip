@@ -912,6 +912,140 @@ __global__ __launch_bounds__(kThreads) void k_mem_back(
   }
 }
 
+// The same memory gradients on MFMA (bf16 models). One workgroup takes 64 entries of one
+// (sequence, head), 16 per wave, and walks the later tokens in tiles of 32 staged in LDS (queries
+// converted to bf16, row-major for the score products and transposed for the gradient products).
+// Per tile and wave: S = Q K^T and dP = dO V^T (the wave's keys and values stay in registers as
+// the B operands), p = exp(scale S - lse), dz = p (dP - D), then dV += p^T dO and dK += dz^T Q.
+// The score tiles leave each lane holding one entry's values for tokens 4g..4g+3 and 16+4g..
+// 16+4g+3 (g = lane / 16), which is taken as the contraction order of the gradient products, so
+// p and dz never move; the staged transposes are read in that order.
+template <int HD>
+__global__ __launch_bounds__(kThreads) void k_mem_back_mfma(
+    const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ qcs,
+    const bf16* __restrict__ docs, const float* __restrict__ lse, const float* __restrict__ dlt,
+    int l0, int l1, int B, int n, int H, float scale, bf16* __restrict__ dkv) {
+  constexpr int KB = 64, TQ = 32, KS = HD / 32, CT = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16 q_r[TQ][HD + 8];
+  __shared__ __attribute__((aligned(16))) bf16 o_r[TQ][HD + 8];
+  __shared__ __attribute__((aligned(16))) bf16 q_t[HD][TQ + 8];
+  __shared__ __attribute__((aligned(16))) bf16 o_t[HD][TQ + 8];
+  __shared__ float s_lse[TQ], s_D[TQ];
+  const int bh = blockIdx.y, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int j0 = blockIdx.x * KB;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4;
+  const int jw = j0 + 16 * wave;
+  const int jl = jw + (lane & 15);  // this lane's entry as an operand / score column
+  const bf16* Kb = K + (int64_t)bh * n * HD;
+  const bf16* Vb = V + (int64_t)bh * n * HD;
+  Frag<bf16> kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (jl < n) {
+      kf[s].load(Kb + (int64_t)jl * HD + 32 * s + 8 * g);
+      vf[s].load(Vb + (int64_t)jl * HD + 32 * s + 8 * g);
+    } else {
+      kf[s].zero();
+      vf[s].zero();
+    }
+  }
+  f32x4 gk[CT], gv[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) gk[c] = gv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c2 = scale * 1.4426950408889634f, l2e = 1.4426950408889634f;
+  const int64_t layer = (int64_t)n * B * d;
+  for (int l = l0; l < l1; ++l) {
+    for (int t0 = j0 / TQ * TQ; t0 < n; t0 += TQ) {
+      __syncthreads();  // the previous tile's LDS reads are done
+      for (int x = tid; x < TQ * HD / 4; x += kThreads) {  // 4 dims per item
+        const int r = x / (HD / 4), c = (x % (HD / 4)) * 4;
+        const int t = t0 + r;
+        float qv[4] = {0.f, 0.f, 0.f, 0.f}, ov[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < n) {
+          const int64_t o = l * layer + ((int64_t)t * B + b) * d + hh * HD + c;
+          const u32x4 raw = ld16(qcs + o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qv[i] = __uint_as_float(raw[i]);
+            ov[i] = (float)docs[o + i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16 qb = (bf16)qv[i], ob = (bf16)ov[i];
+          q_r[r][c + i] = qb;
+          o_r[r][c + i] = ob;
+          q_t[c + i][r] = qb;
+          o_t[c + i][r] = ob;
+        }
+      }
+      if (tid < TQ) {
+        const int t = t0 + tid;
+        const int64_t o = ((int64_t)l * n + t) * B * H + bh;
+        s_lse[tid] = t < n ? lse[o] * l2e : INFINITY;
+        s_D[tid] = t < n ? dlt[o] : 0.f;
+      }
+      __syncthreads();
+      if (t0 + TQ <= jw) continue;  // every token of the tile is earlier than the wave's entries
+      // scores and output-gradient products of the two 16-token halves
+      f32x4 sc[2], dp[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sc[h] = dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 qa = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&q_r[16 * h + (lane & 15)][32 * s + 8 * g]));
+          const bf16x8 oa = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&o_r[16 * h + (lane & 15)][32 * s + 8 * g]));
+          sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[s].v, sc[h], 0, 0, 0);
+          dp[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[s].v, dp[h], 0, 0, 0);
+        }
+      }
+      // lane holds token rows 16 h + 4 g + i of entry column jl
+      bf16x8 pb, zb;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tr = 16 * h + 4 * g + i, t = t0 + tr;
+          const bool ok = t < n && t >= jl && jl < n;
+          const float pj = ok ? __builtin_amdgcn_exp2f(sc[h][i] * c2 - s_lse[tr]) : 0.f;
+          pb[4 * h + i] = (bf16)pj;
+          zb[4 * h + i] = (bf16)(pj * (dp[h][i] - s_D[tr]));
+        }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        // B operands: dims 16 c + lane % 16, tokens in the lanes' contraction order
+        const bf16* op = &o_t[16 * c + (lane & 15)][0];
+        const bf16* qp = &q_t[16 * c + (lane & 15)][0];
+        const uint2 olo = *reinterpret_cast<const uint2*>(op + 4 * g);
+        const uint2 ohi = *reinterpret_cast<const uint2*>(op + 16 + 4 * g);
+        const uint2 qlo = *reinterpret_cast<const uint2*>(qp + 4 * g);
+        const uint2 qhi = *reinterpret_cast<const uint2*>(qp + 16 + 4 * g);
+        const u32x4 orw = {olo.x, olo.y, ohi.x, ohi.y};
+        const u32x4 qrw = {qlo.x, qlo.y, qhi.x, qhi.y};
+        gv[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, __builtin_bit_cast(bf16x8, orw), gv[c],
+                                                        0, 0, 0);
+        gk[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zb, __builtin_bit_cast(bf16x8, qrw), gk[c],
+                                                        0, 0, 0);
+      }
+    }
+  }
+  // lane holds rows (entries) jw + 4 g + i, column (dim) 16 c + lane % 16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = jw + 4 * g + i;
+    if (j >= n) continue;
+    bf16* o = dkv + ((int64_t)b * n + j) * 2 * d + hh * HD + (lane & 15);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      o[16 * c] = (bf16)(scale * gk[c][i]);
+      o[d + 16 * c] = (bf16)gv[c][i];
+    }
+  }
+}
+
 // ---- weight gradients: C[K][N] += X[M][K]^T Y[M][N] ----------------------------------------------
 // Both operands are first transposed to [features][rows] in MFMA fragment order (rows padded with
 // zeros to a multiple of 32), which makes the contraction over rows the fragments' k dimension;
@@ -1425,14 +1559,23 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     const int l0 = D.G == 1 ? 0 : gi, l1 = D.G == 1 ? L : gi + 1;
     const int64_t grp = (int64_t)gi * B * n * d;
     const double nl = l1 - l0;
-    RLT_TRY(launch(k_mem_back<T, HD>, dim3((unsigned)((n + 63) / 64), B * H), dim3(kThreads),
-                   tm.at(RLT_K_BWD_MEM,
-                         rows * dsz * (4 * es + nl * (4 + es)) + nl * rows * H * 8,
-                         nl * 4.0 * b * dsz * (double)n * (double)(n + 1)),
-                   el<T>(M.k, grp), el<T>(M.v, grp),
-                   (const float*)w.template at<float>(TL.qcs), (const T*)w.template at<T>(TL.docs),
-                   (const float*)w.template at<float>(TL.lse),
-                   (const float*)w.template at<float>(TL.dlt), l0, l1, B, n, H, scale, dkv));
+    const Exec xm = tm.at(RLT_K_BWD_MEM,
+                          rows * dsz * (4 * es + nl * (4 + es)) + nl * rows * H * 8,
+                          nl * 4.0 * b * dsz * (double)n * (double)(n + 1));
+    const dim3 mgrid((unsigned)((n + 63) / 64), B * H);
+    if constexpr (std::is_same<T, bf16>::value)
+      RLT_TRY(launch(k_mem_back_mfma<HD>, mgrid, dim3(kThreads), xm, el<T>(M.k, grp),
+                     el<T>(M.v, grp), (const float*)w.template at<float>(TL.qcs),
+                     (const T*)w.template at<T>(TL.docs),
+                     (const float*)w.template at<float>(TL.lse),
+                     (const float*)w.template at<float>(TL.dlt), l0, l1, B, (int)n, H, scale,
+                     dkv));
+    else
+      RLT_TRY(launch(k_mem_back<T, HD>, mgrid, dim3(kThreads), xm, el<T>(M.k, grp),
+                     el<T>(M.v, grp), (const float*)w.template at<float>(TL.qcs),
+                     (const T*)w.template at<T>(TL.docs),
+                     (const float*)w.template at<float>(TL.lse),
+                     (const float*)w.template at<float>(TL.dlt), l0, l1, B, n, H, scale, dkv));
     for (int64_t r0 = 0; r0 < (int64_t)B * n; r0 += TL.Mc) {  // in chunks of rows
       const int64_t rc = std::min<int64_t>(TL.Mc, (int64_t)B * n - r0);
       RLT_TRY(wgrad<T>(e + r0 * d, d, dkv + r0 * 2 * d, 2 * d, rc, d, 2 * d,
