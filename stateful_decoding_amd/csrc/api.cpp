@@ -18,6 +18,9 @@ struct rlt_model {
   rlt_config cfg;
   Dims D;
   Packed P;
+  // second stream and fork/join events of rlt_bptt's row groups, created on its first call
+  hipStream_t bwd_aux = nullptr;
+  hipEvent_t bwd_fork = nullptr, bwd_join = nullptr;
 };
 
 struct rlt_state {
@@ -256,7 +259,13 @@ rlt_status rlt_model_create(const rlt_config* cfg, const rlt_weights* w, void* w
   return ok();
 }
 
-void rlt_model_destroy(rlt_model* model) { delete model; }
+void rlt_model_destroy(rlt_model* model) {
+  if (!model) return;
+  if (model->bwd_aux) (void)hipStreamDestroy(model->bwd_aux);
+  if (model->bwd_fork) (void)hipEventDestroy(model->bwd_fork);
+  if (model->bwd_join) (void)hipEventDestroy(model->bwd_join);
+  delete model;
+}
 
 size_t rlt_state_bytes(const rlt_config* cfg, int32_t batch) {
   if (check_config(cfg) != RLT_OK || !valid_batch(batch)) return 0;
@@ -744,8 +753,17 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
     prof.mask = timing->kernels;
     prof.stride = timing->token_stride;
   }
-  hipError_t err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, st,
-                               timed ? &prof : nullptr);
+  rlt_model* mm = const_cast<rlt_model*>(model);
+  hipError_t err = hipSuccess;
+  if (batch >= 2 * kGroupRows && !mm->bwd_aux) {
+    err = hipStreamCreateWithFlags(&mm->bwd_aux, hipStreamNonBlocking);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&mm->bwd_fork, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&mm->bwd_join, hipEventDisableTiming);
+    if (err != hipSuccess) return hip_fail(err, "creating the backward pass's second stream");
+  }
+  err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, st,
+                    batch >= 2 * kGroupRows ? mm->bwd_aux : nullptr, mm->bwd_fork, mm->bwd_join,
+                    timed ? &prof : nullptr);
   if (timed) {
     for (int k = 0; k < RLT_K_COUNT; ++k) stats[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
     if (err == hipSuccess) err = hipStreamSynchronize(st);

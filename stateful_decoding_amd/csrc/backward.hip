@@ -111,6 +111,7 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.dkv = take(b * N * 2 * d * es);
   // weight-gradient operands transposed to [features][rows] (rows padded to 32)
   const size_t Mp = (Mc + 31) / 32 * 32;
+  t.o2 = take((b + 15) / 16 * 16 * d * es);  // second attention-output operand (forward)
   t.tx = take(Mp * std::max(2 * d, F) * es);
   t.ty = take(Mp * std::max(3 * d, 2 * F) * es);
   t.total = o;
@@ -148,22 +149,24 @@ __global__ __launch_bounds__(kThreads) void k_fill_start(float* __restrict__ dst
   if (i < total) dst[i] = s_star[i % d];
 }
 
-// Copies of the forward's working buffers at three points of each layer of token i.
-//   stage 0 (after the q/k/v projection): x = h, q, and this token's key/value ring slot
-//   stage 1 (after the cross-attention query): y = h, qc, o (self-attention output)
-//   stage 2 (after the cross-attention output projection): z = h, oc (cross output)
+// Copies of the forward's working buffers that the reverse walk keeps (the residual streams and
+// the queries are written straight into their save slots by the forward's own kernels):
+//   stage 0 (after the gated merge): x = h of layer 0
+//   stage 1 (after a layer's cross-attention output projection): the self-attention output o
+//           and the cross-attention output oc (fragment order -> rows), and this token's
+//           key/value ring slot -> the key/value history
 struct SaveArgs {
   int stage, B, d, H, hd, W;
   int64_t n, i;
   const float* h;
-  const float* q;
-  const void* o;  // fragment order [B16][d]
+  float* h_dst;        // [B][d] rows of token i
+  const void* o;       // fragment order [B16][d]
+  const void* oc;
+  void* o_dst;         // row-major [B][d]
+  void* oc_dst;
   const void* ring_k;  // this layer's ring block [B][H][W][hd]
   const void* ring_v;
-  float* h_dst;  // [B][d] rows of token i
-  float* q_dst;
-  void* o_dst;   // row-major [B][d]
-  void* k_dst;   // this layer's history block [B][H][n][hd]
+  void* k_dst;         // this layer's history block [B][H][n][hd]
   void* v_dst;
 };
 
@@ -171,18 +174,19 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_save(SaveArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)a.B * a.d) return;
-  const int b = (int)(idx / a.d), c = (int)(idx - (int64_t)b * a.d);
-  a.h_dst[idx] = a.h[idx];
-  if (a.stage < 2) a.q_dst[idx] = a.q[idx];
   if (a.stage == 0) {
-    const int hh = c / a.hd, dd = c - hh * a.hd;
-    const int64_t ring = (((int64_t)b * a.H + hh) * a.W + (int)(a.i % a.W)) * a.hd + dd;
-    const int64_t hist = (((int64_t)b * a.H + hh) * a.n + a.i) * a.hd + dd;
-    static_cast<T*>(a.k_dst)[hist] = static_cast<const T*>(a.ring_k)[ring];
-    static_cast<T*>(a.v_dst)[hist] = static_cast<const T*>(a.ring_v)[ring];
-  } else {
-    static_cast<T*>(a.o_dst)[idx] = static_cast<const T*>(a.o)[frag_off(b, c, a.d / 32)];
+    a.h_dst[idx] = a.h[idx];
+    return;
   }
+  const int b = (int)(idx / a.d), c = (int)(idx - (int64_t)b * a.d);
+  const int64_t f = frag_off(b, c, a.d / 32);
+  static_cast<T*>(a.o_dst)[idx] = static_cast<const T*>(a.o)[f];
+  static_cast<T*>(a.oc_dst)[idx] = static_cast<const T*>(a.oc)[f];
+  const int hh = c / a.hd, dd = c - hh * a.hd;
+  const int64_t ring = (((int64_t)b * a.H + hh) * a.W + (int)(a.i % a.W)) * a.hd + dd;
+  const int64_t hist = (((int64_t)b * a.H + hh) * a.n + a.i) * a.hd + dd;
+  static_cast<T*>(a.k_dst)[hist] = static_cast<const T*>(a.ring_k)[ring];
+  static_cast<T*>(a.v_dst)[hist] = static_cast<const T*>(a.ring_v)[ring];
 }
 
 // s_traj[b][i] = s_hist[i + 1][b]
@@ -1189,28 +1193,40 @@ static hipError_t colsums(const float* P, int nmat, int64_t rows, int64_t stride
 }
 
 template <typename T>
-struct Walk {  // pointers into the workspace of one call
+struct Walk {  // pointers into the workspace of one call, for the rows [b0, b0 + rows)
   const Dims& D;
-  int B;
+  int B;  // all rows: the stride of every row-indexed buffer
   int64_t n;
   const TrainLayout& TL;
   void* ws;
+  int b0 = 0, rows = 0;
   template <typename P>
   P* at(size_t off) const {
     return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
   }
   // rows of chunk-local token li in a per-layer chunk buffer of `width` columns
   T* chunk(size_t base, int l, int64_t width, int64_t li) const {
-    return at<T>(base) + ((int64_t)l * TL.Mc + li * B) * width;
+    return at<T>(base) + ((int64_t)l * TL.Mc + li * B + b0) * width;
   }
   // fp32 gain/bias-gradient rows: matrix m (3 l + which, or 3 L for the gate bias)
   float* pg(int m, int64_t li) const {
-    return at<float>(TL.pg) + ((int64_t)m * TL.Mc + li * B) * D.d;
+    return at<float>(TL.pg) + ((int64_t)m * TL.Mc + li * B + b0) * D.d;
   }
   // [L][n][B][d] saved rows of layer l, token i
   template <typename P>
   P* saved(size_t base, int l, int64_t i) const {
-    return at<P>(base) + (((int64_t)l * n + i) * B) * D.d;
+    return at<P>(base) + (((int64_t)l * n + i) * B + b0) * D.d;
+  }
+  // per-row scratch of `width` values per row
+  template <typename P>
+  P* row(size_t base, int64_t width) const {
+    return at<P>(base) + (int64_t)b0 * width;
+  }
+  Walk group(int g0, int nrows) const {
+    Walk w = *this;
+    w.b0 = g0;
+    w.rows = nrows;
+    return w;
   }
 };
 
@@ -1235,22 +1251,28 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                              bool sampled) {
   const Dims& D = w.D;
   const TrainLayout& TL = w.TL;
-  const int B = w.B, d = D.d, F = D.F, L = D.L, H = D.H, BH = B * D.H;
+  // B: this group's rows (GEMM rows, grids); Bt: all rows (strides); b0: the group's first row
+  const int B = w.rows, Bt = w.B, b0 = w.b0, d = D.d, F = D.F, L = D.L, H = D.H, BH = B * D.H;
   const int64_t n = w.n;
   const BwOff bo = bw_off(D);
   const T* bw = w.template at<T>(TL.bw);
-  float* dres = w.template at<float>(TL.dres);
-  float* dn = w.template at<float>(TL.dn);
-  float* dattn = w.template at<float>(TL.dattn);
-  float* rinv = w.template at<float>(TL.rinv);
-  float* u13 = w.template at<float>(TL.u13);
-  float* gsave = w.template at<float>(TL.gsave);
-  float* carry = w.template at<float>(TL.carry);
+  float* dres = w.template row<float>(TL.dres, d);
+  float* dn = w.template row<float>(TL.dn, d);
+  float* dattn = w.template row<float>(TL.dattn, d);
+  float* rinv = w.template row<float>(TL.rinv, 3);
+  float* u13 = w.template row<float>(TL.u13, 2 * F);
+  float* gsave = w.template row<float>(TL.gsave, d);
+  float* carry = w.template row<float>(TL.carry, d);
+  G += (int64_t)b0 * n * d;
+  e += (int64_t)b0 * n * d;
+  if (de) de += (int64_t)b0 * n * d;
   const int64_t dd = (int64_t)d * d;
   const double b = B, es = (double)D.es, rows32 = b * d * 4, rowsT = b * d * es;
   // a per-token projection: N x K weights, A rows of K, `out` bytes of results
+  // weights are charged in proportion to this group's rows: once per token over all groups
+  const double share = (double)B / Bt;
   auto proj = [&](double N, double K, double out) {
-    return tm.at(RLT_K_BWD_PROJ, N * K * es + b * K * es + out, 2 * b * N * K, sampled);
+    return tm.at(RLT_K_BWD_PROJ, N * K * es * share + b * K * es + out, 2 * b * N * K, sampled);
   };
   auto other = [&](double bytes) { return tm.at(RLT_K_BWD_OTHER, bytes, 0, sampled); };
 
@@ -1295,9 +1317,9 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wco + l * dd, ARows<T>{yco, d, B}, to_dattn,
                              proj(d, d, rows32)));
     const int g = D.G == 1 ? 0 : l;
-    const int64_t grp = (int64_t)g * B * n * d;
+    const int64_t grp = ((int64_t)g * Bt + b0) * n * d;
     T* ycq = w.chunk(TL.ycq, l, d, li);
-    const int64_t stat = ((int64_t)l * n + i) * BH;
+    const int64_t stat = ((int64_t)l * n + i) * Bt * H + (int64_t)b0 * H;
     const double ntok = (double)(i + 1);
     RLT_TRY(xattn_back<T, HD>(BH, w.template saved<float>(TL.qcs, l, i), dattn,
                               el<T>(M.k, grp), el<T>(M.v, grp), n * HD, (int)(i + 1), H, ycq,
@@ -1315,15 +1337,16 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn,
                              proj(d, d, rows32)));
     T* yqkv = w.chunk(TL.yqkv, l, 3 * d, li);
-    const int64_t hist = (int64_t)l * B * n * d;
-    const int64_t rd = (int64_t)l * D.W * B * d, rs = (int64_t)l * D.W * BH;
+    const int64_t hist = ((int64_t)l * Bt + b0) * n * d;
+    const int64_t rd = (int64_t)l * D.W * Bt * d + (int64_t)b0 * d;
+    const int64_t rs = (int64_t)l * D.W * Bt * H + (int64_t)b0 * H;
     const double nk = (double)std::min<int64_t>(i + 1, D.W);
     const double nq = (double)std::min<int64_t>(n - i, D.W);
-    RLT_TRY(swa_back<T, HD>(BH, B, w.template at<float>(TL.qs) + (int64_t)l * n * B * d, dattn,
-                            w.template at<T>(TL.khist) + hist, w.template at<T>(TL.vhist) + hist,
-                            n, i, D.W, H, w.template at<T>(TL.dkacc) + rd,
-                            w.template at<float>(TL.dvacc) + rs,
-                            w.template at<float>(TL.dvacc) + (int64_t)L * D.W * BH + rs, yqkv,
+    RLT_TRY(swa_back<T, HD>(BH, Bt, w.template at<float>(TL.qs) + (int64_t)l * n * Bt * d + b0 * d,
+                            dattn, w.template at<T>(TL.khist) + hist,
+                            w.template at<T>(TL.vhist) + hist, n, i, D.W, H,
+                            w.template at<T>(TL.dkacc) + rd, w.template at<float>(TL.dvacc) + rs,
+                            w.template at<float>(TL.dvacc) + (int64_t)L * D.W * Bt * H + rs, yqkv,
                             tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * es + nq * b * d * (4 + es) +
                                       2 * rows32 + 4 * rowsT, (10 * nk + 8 * nq) * b * d,
                                   sampled)));
@@ -1335,14 +1358,14 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
   }
   // gated merge: recompute g, then dz, then de_t and the carry to s_{t-1}
   const T* et = e + i * d;
-  const float* s_prev = w.template at<float>(TL.s_hist) + i * B * d;
-  T* yg = w.template at<T>(TL.yg) + li * B * d;
+  const float* s_prev = w.template at<float>(TL.s_hist) + (i * Bt + b0) * d;
+  T* yg = w.template at<T>(TL.yg) + (li * Bt + b0) * d;
   {
     AGate<T> al{et, n * d, s_prev, D.alpha, B, d};
     EpiGateBack<T> ep;
     ep.e = et; ep.lde = n * d; ep.s = s_prev; ep.b = P.b_gate; ep.dres = dres; ep.alpha = D.alpha;
     ep.dz = yg; ep.dz32 = w.pg(3 * L, li); ep.g = gsave;
-    ep.xg = w.template at<T>(TL.xg) + li * B * 2 * d; ep.M = B; ep.d = d;
+    ep.xg = w.template at<T>(TL.xg) + (li * Bt + b0) * 2 * d; ep.M = B; ep.d = d;
     RLT_TRY(run_step_gemm<T>(B, d, 2 * d, P.w_gate_t, al, ep,
                              proj(d, 2 * d, 3 * rows32 + rowsT + b * 2 * d * es)));
   }
@@ -1399,7 +1422,8 @@ static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, i
 template <typename T, int HD>
 static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const void* e_v,
                          const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                         hipStream_t st, Profiler* prof) {
+                         hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
+                         Profiler* prof) {
   const TrainLayout TL = train_layout(D, B, n);
   const Walk<T> w{D, B, n, TL, ws};
   const int d = D.d, F = D.F, L = D.L, H = D.H;
@@ -1408,7 +1432,6 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
   Timer tm{prof, st};
   const int64_t stride = prof ? prof->stride : 1;
   const double b = B, es = (double)D.es, dsz = d, Fd = F;
-  const double act32 = b * d * 4, actd = b * d * es;
   // backward copies of the weights
   {
     const BwOff bo = bw_off(D);
@@ -1460,68 +1483,106 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
   }
   RLT_TRY(launch(k_fill_start, dim3(blocks_for((int64_t)B * d)), dim3(kThreads), x, s_hist,
                  (const float*)P.s_star, d, (int64_t)B * d));
+  // row groups: two halves of the batch on two streams (the caller's and `aux`), as the decoder
+  // step runs them, when the batch is large enough; joined around the weight-gradient GEMMs
+  const int ng = aux && B >= 2 * kGroupRows ? 2 : 1;
+  const int half = ng == 2 ? ((B + 1) / 2 + 15) / 16 * 16 : B;
+  const int row0[3] = {0, half, B};
+  Timer gtm[2] = {Timer{prof, st}, Timer{prof, aux}};
+  auto fork = [&]() -> hipError_t {
+    if (ng < 2) return hipSuccess;
+    RLT_TRY(hipEventRecord(ev_fork, st));
+    return hipStreamWaitEvent(aux, ev_fork, 0);
+  };
+  auto join = [&]() -> hipError_t {
+    if (ng < 2) return hipSuccess;
+    RLT_TRY(hipEventRecord(ev_join, aux));
+    return hipStreamWaitEvent(st, ev_join, 0);
+  };
   // forward, saving x, y, z, q, qc, o, oc and every key/value (bytes counted as in the decoder
   // step)
   const int64_t ring_layer = (int64_t)B * H * D.W * D.hd;
+  RLT_TRY(fork());
+  StateBufs Sg[2];
+  MemBufs Mg[2];
+  for (int gi = 0; gi < ng; ++gi) {
+    Sg[gi] = state_rows(D, S, row0[gi]);
+    Mg[gi] = memory_rows(D, M, row0[gi]);
+  }
   for (int64_t i = 0; i < n; ++i) {
-    S.t_uniform = i;
     const bool smp = i % stride == 0;
     const double nv = (double)std::min<int64_t>(i + 1, D.W), t = (double)(i + 1);
-    RLT_TRY(gemm_gate(D, B, P, S, e + i * d, n * d,
-                      tm.at(RLT_K_GATE, 2 * dsz * dsz * es + actd + 2 * act32, 4 * b * dsz * dsz,
-                            smp)));
-    for (int l = 0; l < L; ++l) {
-      const bool last = l == L - 1;
-      SaveArgs a;
-      a.B = B; a.d = d; a.H = H; a.hd = D.hd; a.W = D.W; a.n = n; a.i = i;
-      a.h = S.h;
-      a.ring_k = el<T>(S.ring_k, l * ring_layer);
-      a.ring_v = el<T>(S.ring_v, l * ring_layer);
-      a.k_dst = w.template at<T>(TL.khist) + (int64_t)l * B * n * d;
-      a.v_dst = w.template at<T>(TL.vhist) + (int64_t)l * B * n * d;
-      const dim3 grid(blocks_for((int64_t)B * d));
-      RLT_TRY(gemm_qkv(D, B, l, P, S,
-                       tm.at(RLT_K_QKV, 3 * dsz * dsz * es + 2 * act32 + 2 * actd,
-                             6 * b * dsz * dsz, smp)));
-      a.stage = 0; a.q = S.q; a.o = nullptr; a.o_dst = nullptr;
-      a.h_dst = w.template saved<float>(TL.xs, l, i);
-      a.q_dst = w.template saved<float>(TL.qs, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
-                     tm.at(RLT_K_BWD_OTHER, 4 * act32 + 4 * actd, 0, smp), a));
-      RLT_TRY(attn_self(D, B, l, S,
-                        tm.at(RLT_K_SELF_ATTN, nv * b * 2 * dsz * es + act32 + actd,
-                              4 * b * dsz * nv, smp)));
-      RLT_TRY(gemm_residual(D, B, l, 0, P, S, false, nullptr, 0,
-                            tm.at(RLT_K_SELF_OUT, dsz * dsz * es + actd + 2 * act32,
-                                  2 * b * dsz * dsz, smp)));
-      RLT_TRY(gemm_cq(D, B, l, P, S,
-                      tm.at(RLT_K_CROSS_Q, dsz * dsz * es + 2 * act32, 2 * b * dsz * dsz, smp)));
-      a.stage = 1; a.q = S.qc; a.o = S.o;
-      a.h_dst = w.template saved<float>(TL.ys, l, i);
-      a.q_dst = w.template saved<float>(TL.qcs, l, i);
-      a.o_dst = w.template saved<T>(TL.os, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
-                     tm.at(RLT_K_BWD_OTHER, 4 * act32 + 2 * actd, 0, smp), a));
-      RLT_TRY(attn_cross(D, B, l, S, M,
-                         tm.at(RLT_K_CROSS_ATTN, t * b * 2 * dsz * es + act32 + actd,
-                               4 * b * dsz * t, smp)));
-      RLT_TRY(gemm_residual(D, B, l, 1, P, S, false, nullptr, 0,
-                            tm.at(RLT_K_CROSS_OUT, dsz * dsz * es + actd + 2 * act32,
-                                  2 * b * dsz * dsz, smp)));
-      a.stage = 2; a.q = nullptr; a.q_dst = nullptr;
-      a.h_dst = w.template saved<float>(TL.zs, l, i);
-      a.o_dst = w.template saved<T>(TL.ocs, l, i);
-      RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
-                     tm.at(RLT_K_BWD_OTHER, 2 * act32 + 2 * actd, 0, smp), a));
-      RLT_TRY(gemm_w13(D, B, l, P, S,
-                       tm.at(RLT_K_FFN_UP, 2 * Fd * dsz * es + act32 + b * Fd * es,
-                             4 * b * dsz * Fd, smp)));
-      RLT_TRY(gemm_residual(D, B, l, 2, P, S, last, last ? s_hist + (i + 1) * B * d : nullptr, d,
-                            tm.at(RLT_K_FFN_DOWN, Fd * dsz * es + b * Fd * es + 2 * act32 +
-                                                      (last ? act32 : 0),
-                                  2 * b * dsz * Fd, smp)));
+    for (int gi = 0; gi < ng; ++gi) {
+      const int b0 = row0[gi], rb = row0[gi + 1] - b0;
+      const Walk<T> wg = w.group(b0, rb);
+      Timer& tg = gtm[gi];
+      StateBufs& Sx = Sg[gi];
+      Sx.t_uniform = i;
+      const double bg = rb, a32 = bg * d * 4, ad = bg * d * es;
+      const double sh = bg / B;  // this group's share of each weight read
+      RLT_TRY(gemm_gate(D, rb, P, Sx, e + ((int64_t)b0 * n + i) * d, n * d,
+                        tg.at(RLT_K_GATE, 2 * dsz * dsz * es * sh + ad + 2 * a32,
+                              4 * bg * dsz * dsz, smp)));
+      const dim3 grid(blocks_for((int64_t)rb * d));
+      {
+        SaveArgs a{};
+        a.stage = 0; a.B = rb; a.d = d;
+        a.h = Sx.h;
+        a.h_dst = wg.template saved<float>(TL.xs, 0, i);
+        RLT_TRY(launch(k_save<T>, grid, dim3(kThreads), tg.at(RLT_K_BWD_OTHER, 2 * a32, 0, smp),
+                       a));
+      }
+      for (int l = 0; l < L; ++l) {
+        const bool last = l == L - 1;
+        // queries straight into their save slots; the cross-attention output into a second
+        // buffer, so both outputs survive to the layer's single copy
+        StateBufs Sl = Sx;
+        Sl.q = wg.template saved<float>(TL.qs, l, i);
+        Sl.qc = wg.template saved<float>(TL.qcs, l, i);
+        StateBufs Sc = Sl;
+        Sc.o = w.template at<char>(TL.o2) + (size_t)b0 * d * D.es;
+        RLT_TRY(gemm_qkv(D, rb, l, P, Sl,
+                         tg.at(RLT_K_QKV, 3 * dsz * dsz * es * sh + 2 * a32 + 2 * ad,
+                               6 * bg * dsz * dsz, smp)));
+        RLT_TRY(attn_self(D, rb, l, Sl,
+                          tg.at(RLT_K_SELF_ATTN, nv * bg * 2 * dsz * es + a32 + ad,
+                                4 * bg * dsz * nv, smp)));
+        RLT_TRY(gemm_residual(D, rb, l, 0, P, Sl, false, wg.template saved<float>(TL.ys, l, i), d,
+                              tg.at(RLT_K_SELF_OUT, dsz * dsz * es * sh + ad + 3 * a32,
+                                    2 * bg * dsz * dsz, smp)));
+        RLT_TRY(gemm_cq(D, rb, l, P, Sl,
+                        tg.at(RLT_K_CROSS_Q, dsz * dsz * es * sh + 2 * a32, 2 * bg * dsz * dsz,
+                              smp)));
+        RLT_TRY(attn_cross(D, rb, l, Sc, Mg[gi],
+                           tg.at(RLT_K_CROSS_ATTN, t * bg * 2 * dsz * es + a32 + ad,
+                                 4 * bg * dsz * t, smp)));
+        RLT_TRY(gemm_residual(D, rb, l, 1, P, Sc, false, wg.template saved<float>(TL.zs, l, i), d,
+                              tg.at(RLT_K_CROSS_OUT, dsz * dsz * es * sh + ad + 3 * a32,
+                                    2 * bg * dsz * dsz, smp)));
+        SaveArgs a{};
+        a.stage = 1; a.B = rb; a.d = d; a.H = H; a.hd = D.hd; a.W = D.W; a.n = n; a.i = i;
+        a.o = Sl.o;
+        a.oc = Sc.o;
+        a.o_dst = wg.template saved<T>(TL.os, l, i);
+        a.oc_dst = wg.template saved<T>(TL.ocs, l, i);
+        a.ring_k = el<T>(Sx.ring_k, l * ring_layer);
+        a.ring_v = el<T>(Sx.ring_v, l * ring_layer);
+        a.k_dst = w.template at<T>(TL.khist) + ((int64_t)l * B + b0) * n * d;
+        a.v_dst = w.template at<T>(TL.vhist) + ((int64_t)l * B + b0) * n * d;
+        RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
+                       tg.at(RLT_K_BWD_OTHER, 8 * ad, 0, smp), a));
+        RLT_TRY(gemm_w13(D, rb, l, P, Sl,
+                         tg.at(RLT_K_FFN_UP, 2 * Fd * dsz * es * sh + a32 + bg * Fd * es,
+                               4 * bg * dsz * Fd, smp)));
+        float* next = last ? s_hist + ((i + 1) * B + b0) * d
+                           : wg.template saved<float>(TL.xs, l + 1, i);
+        RLT_TRY(gemm_residual(D, rb, l, 2, P, Sl, last, next, d,
+                              tg.at(RLT_K_FFN_DOWN, Fd * dsz * es * sh + bg * Fd * es + 3 * a32,
+                                    2 * bg * dsz * Fd, smp)));
+      }
     }
   }
+  RLT_TRY(join());
   if (s_traj)
     RLT_TRY(launch(k_traj, dim3(blocks_for((int64_t)B * n * d)), dim3(kThreads), x,
                    (const float*)s_hist, s_traj, B, n, d));
@@ -1542,8 +1603,12 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
   // the reverse walk, one chunk of Tc tokens at a time (newest chunk first)
   for (int64_t i1 = n; i1 > 0;) {
     const int64_t i0 = std::max<int64_t>(0, i1 - TL.Tc);
+    RLT_TRY(fork());
     for (int64_t i = i1 - 1; i >= i0; --i)
-      RLT_TRY(walk_token<T, HD>(w, P, M, e, G, de, i, i - i0, tm, i % stride == 0));
+      for (int gi = 0; gi < ng; ++gi)
+        RLT_TRY(walk_token<T, HD>(w.group(row0[gi], row0[gi + 1] - row0[gi]), P, M, e, G, de,
+                                  i, i - i0, gtm[gi], i % stride == 0));
+    RLT_TRY(join());
     RLT_TRY(chunk_grads<T>(w, g, i0, i1, tm));
     i1 = i0;
   }
@@ -1595,15 +1660,21 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
                 2 * rows * dsz * 2 * dsz)));
     }
   }
+  RLT_TRY(gtm[0].err);
+  RLT_TRY(gtm[1].err);
   return tm.err;
 }
 
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st, Profiler* prof) {
-#define RLT_BPTT(HDV)                                                                           \
-  return D.dtype == RLT_BF16 ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, prof) \
-                             : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, prof)
+                       hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
+                       Profiler* prof) {
+#define RLT_BPTT(HDV)                                                                        \
+  return D.dtype == RLT_BF16                                                                 \
+             ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, aux, ev_fork,     \
+                                 ev_join, prof)                                              \
+             : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, aux, ev_fork,    \
+                                  ev_join, prof)
   switch (D.hd) {
     case 32: RLT_BPTT(32);
     case 64: RLT_BPTT(64);

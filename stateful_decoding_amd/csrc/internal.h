@@ -229,7 +229,7 @@ struct TrainLayout {
   int64_t Tc, Mc;
   size_t state, mem_k, mem_v, bw, s_hist, xs, ys, zs, qs, qcs, os, ocs, docs, khist, vhist, lse,
       dlt, dres, dn, dattn, u13, gsave, carry, rinv, dkacc, dvacc, ca, cc, cf, cm, yqkv, yo, ycq,
-      yco, y13, y2, pg, xg, yg, part, dkv, tx, ty, total;
+      yco, y13, y2, pg, xg, yg, part, dkv, o2, tx, ty, total;
 };
 TrainLayout train_layout(const Dims& D, int B, int64_t n);
 
@@ -238,9 +238,11 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n);
 // `g` is overwritten with dLoss/dparam for Loss = sum_{b,t} G[b][t] . s_t(b); de [B][n][d]
 // (optional) receives dLoss/de; s_traj [B][n][d] (optional) the forward trajectory.
 // With `prof`, launches of the kernels it times are timed in the steps of tokens
-// i % prof->stride == 0 and everywhere outside the token loops.
+// i % prof->stride == 0 and everywhere outside the token loops. With `aux` (a second stream,
+// and two events for forking to it and joining back), large batches run as two row groups.
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st, Profiler* prof);
+                       hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
+                       Profiler* prof);
 
 }  // namespace rlt
