@@ -202,60 +202,72 @@ __global__ __launch_bounds__(kThreads) void k_traj(const float* __restrict__ s_h
   out[idx] = s_hist[((i + 1) * B + b) * d + c];
 }
 
-// Start of token i's walk: dres = G[:, i] + carry (carry = dLoss/ds_i through token i+1), and
-// its dtype copy (the operand of the FFN down-projection's backward).
+// The three RMSNorm outputs of one layer of one token, recomputed for the reverse walk from the
+// saved residual streams: a = gain0 x r_x, c = gain1 y r_y, f = gain2 z r_z (dtype rows, the
+// GEMM operands) and the scales r. x == NULL: nothing to do.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_walk_begin(const float* __restrict__ G,
-                                                         const float* __restrict__ carry,
-                                                         float* __restrict__ dres,
-                                                         T* __restrict__ dres_t, int B, int d,
-                                                         int64_t n, int64_t i) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)B * d) return;
-  const int b = (int)(idx / d), c = (int)(idx - (int64_t)b * d);
-  const float v = G[((int64_t)b * n + i) * d + c] + carry[idx];
-  dres[idx] = v;
-  dres_t[idx] = to_elem<T>(v);
-}
+struct NormRows {
+  const float* x;
+  const float* y;
+  const float* z;
+  const float* gamma;  // [3][d]
+  T* a;
+  T* c;
+  T* f;
+  float eps;
+};
 
-// The three RMSNorm operands of one layer of one token, from the saved residual streams:
-// a = gain0 x r_x, c = gain1 y r_y, f = gain2 z r_z (dtype rows), and the scales r. One
-// workgroup per row.
+// Row b of NormRows, by one workgroup; rinv[b * 3 + w] receives the scales.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_norm_rows3(const float* __restrict__ x,
-                                                         const float* __restrict__ y,
-                                                         const float* __restrict__ z,
-                                                         const float* __restrict__ gamma, int d,
-                                                         float eps, T* __restrict__ a,
-                                                         T* __restrict__ c, T* __restrict__ f,
-                                                         float* __restrict__ rinv) {
-  __shared__ float red[4];
-  const int b = blockIdx.x;
-  const float* src[3] = {x + (int64_t)b * d, y + (int64_t)b * d, z + (int64_t)b * d};
-  T* dst[3] = {a + (int64_t)b * d, c + (int64_t)b * d, f + (int64_t)b * d};
+__device__ void norm_rows3(const NormRows<T>& nr, int b, int d, float* __restrict__ rinv,
+                           float* red) {
+  const float* src[3] = {nr.x + (int64_t)b * d, nr.y + (int64_t)b * d, nr.z + (int64_t)b * d};
+  T* dst[3] = {nr.a + (int64_t)b * d, nr.c + (int64_t)b * d, nr.f + (int64_t)b * d};
 #pragma unroll
   for (int w = 0; w < 3; ++w) {
     float ss = 0.f;
     for (int j = threadIdx.x; j < d; j += kThreads) ss += src[w][j] * src[w][j];
-    const float r = rsqrtf(block_sum(ss, red) / (float)d + eps);
+    const float r = rsqrtf(block_sum(ss, red) / (float)d + nr.eps);
     for (int j = threadIdx.x; j < d; j += kThreads)
-      dst[w][j] = to_elem<T>(gamma[w * d + j] * src[w][j] * r);
+      dst[w][j] = to_elem<T>(nr.gamma[w * d + j] * src[w][j] * r);
     if (threadIdx.x == 0) rinv[b * 3 + w] = r;
   }
+}
+
+// Start of token i's walk, one workgroup per row: dres = G[:, i] + carry (carry = dLoss/ds_i
+// through token i+1), its dtype copy (the operand of the FFN down-projection's backward), and
+// the norm rows of the last layer.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_walk_begin(const float* __restrict__ G,
+                                                         const float* __restrict__ carry,
+                                                         float* __restrict__ dres,
+                                                         T* __restrict__ dres_t, int d,
+                                                         int64_t n, int64_t i, NormRows<T> nr,
+                                                         float* __restrict__ rinv) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int64_t o = (int64_t)b * d;
+  for (int j = threadIdx.x; j < d; j += kThreads) {
+    const float v = G[((int64_t)b * n + i) * d + j] + carry[o + j];
+    dres[o + j] = v;
+    dres_t[o + j] = to_elem<T>(v);
+  }
+  norm_rows3(nr, b, d, rinv, red);
 }
 
 // Backward of an RMSNorm y = gain * x * r at one row per workgroup, added to the residual
 // gradient: dres += gain * dn * r - x * r^3 * sum(gain * dn * x) / d. Also writes dres in the
 // working dtype (the next GEMM operand, when res_t != NULL) and the row's gain-gradient terms
-// dn * x * r (fp32, summed over rows later).
+// dn * x * r (fp32, summed over rows later); then, when nr.x != NULL, the norm rows of the
+// layer below (which replace this layer's scales in rinv).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_norm_back(const float* __restrict__ dn,
                                                         const float* __restrict__ x,
                                                         const float* __restrict__ gain,
-                                                        const float* __restrict__ rinv, int which,
+                                                        float* __restrict__ rinv, int which,
                                                         int d, float* __restrict__ dres,
                                                         T* __restrict__ res_t,
-                                                        float* __restrict__ pgain) {
+                                                        float* __restrict__ pgain, NormRows<T> nr) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int64_t o = (int64_t)b * d;
@@ -271,6 +283,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_back(const float* __restrict_
     if (res_t) res_t[o + j] = to_elem<T>(v);
     pgain[o + j] = g * xv * r;
   }
+  if (nr.x) norm_rows3(nr, b, d, rinv, red);
 }
 
 // Column sums of nmat row-major [rows][d] fp32 matrices (matrix m at P + m * stride * d),
@@ -1276,19 +1289,23 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
   };
   auto other = [&](double bytes) { return tm.at(RLT_K_BWD_OTHER, bytes, 0, sampled); };
 
-  RLT_TRY(launch(k_walk_begin<T>, dim3(blocks_for((int64_t)B * d)), dim3(kThreads),
-                 other(3 * rows32 + rowsT), G, (const float*)carry, dres,
-                 w.chunk(TL.y2, L - 1, d, li), B, d, n, i));
+  // the norm rows of layer l (the three saved residual streams of token i)
+  auto rows_of = [&](int l) {
+    return NormRows<T>{w.template saved<float>(TL.xs, l, i), w.template saved<float>(TL.ys, l, i),
+                       w.template saved<float>(TL.zs, l, i), P.gamma + (int64_t)l * 3 * d,
+                       w.chunk(TL.ca, l, d, li), w.chunk(TL.cc, l, d, li),
+                       w.chunk(TL.cf, l, d, li), D.eps};
+  };
+  const double nrb = 3 * rows32 + 3 * rowsT;  // bytes of one set of norm rows
+  RLT_TRY(launch(k_walk_begin<T>, dim3(B), dim3(kThreads), other(3 * rows32 + rowsT + nrb), G,
+                 (const float*)carry, dres, w.chunk(TL.y2, L - 1, d, li), d, n, i, rows_of(L - 1),
+                 rinv));
   for (int l = L - 1; l >= 0; --l) {
     const float* gam = P.gamma + (int64_t)l * 3 * d;
     const float* xs = w.template saved<float>(TL.xs, l, i);
     const float* ys = w.template saved<float>(TL.ys, l, i);
     const float* zs = w.template saved<float>(TL.zs, l, i);
-    T* ca = w.chunk(TL.ca, l, d, li);
-    T* cc = w.chunk(TL.cc, l, d, li);
     T* cf = w.chunk(TL.cf, l, d, li);
-    RLT_TRY(launch(k_norm_rows3<T>, dim3(B), dim3(kThreads), other(3 * rows32 + 3 * rowsT), xs, ys,
-                   zs, gam, d, D.eps, ca, cc, cf, rinv));
     // feed-forward: recompute u, then dm -> du -> df -> dres
     {
       EpiU13<T> ep{u13, w.chunk(TL.cm, l, F, li), B, F};
@@ -1311,8 +1328,9 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                              ARows<T>{y13, 2 * F, B}, to_dn, proj(d, 2 * F, rows32)));
     T* yco = w.chunk(TL.yco, l, d, li);
     const double nb = 5 * rows32 + rowsT;  // dn, x, dres in, dres out, gain terms; dtype copy
+    const NormRows<T> none{};
     RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, zs,
-                   gam + 2 * d, (const float*)rinv, 2, d, dres, yco, w.pg(3 * l + 2, li)));
+                   gam + 2 * d, rinv, 2, d, dres, yco, w.pg(3 * l + 2, li), none));
     // cross-attention
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wco + l * dd, ARows<T>{yco, d, B}, to_dattn,
                              proj(d, d, rows32)));
@@ -1332,7 +1350,7 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                              proj(d, d, rows32)));
     T* yo = w.chunk(TL.yo, l, d, li);
     RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, ys,
-                   gam + d, (const float*)rinv, 1, d, dres, yo, w.pg(3 * l + 1, li)));
+                   gam + d, rinv, 1, d, dres, yo, w.pg(3 * l + 1, li), none));
     // self-attention
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wo + l * dd, ARows<T>{yo, d, B}, to_dattn,
                              proj(d, d, rows32)));
@@ -1352,9 +1370,10 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                                   sampled)));
     RLT_TRY(run_step_gemm<T>(B, d, 3 * d, bw + bo.wqkv + (int64_t)l * 3 * dd,
                              ARows<T>{yqkv, 3 * d, B}, to_dn, proj(d, 3 * d, rows32)));
-    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb), (const float*)dn, xs, gam,
-                   (const float*)rinv, 0, d, dres,
-                   l > 0 ? w.chunk(TL.y2, l - 1, d, li) : (T*)nullptr, w.pg(3 * l, li)));
+    RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb + (l > 0 ? nrb : 0)),
+                   (const float*)dn, xs, gam, rinv, 0, d, dres,
+                   l > 0 ? w.chunk(TL.y2, l - 1, d, li) : (T*)nullptr, w.pg(3 * l, li),
+                   l > 0 ? rows_of(l - 1) : none));
   }
   // gated merge: recompute g, then dz, then de_t and the carry to s_{t-1}
   const T* et = e + i * d;
