@@ -144,3 +144,37 @@ def test_full_size_bptt_early_tokens_match_oracle():
     assert not np.any(de_h[mask]) and not np.any(de_h[seqs, n_or:])
     worst = max(errs, key=errs.get)
     assert errs[worst] <= TOL["bf16"], (worst, errs[worst])
+
+
+@pytest.mark.parametrize("B", [5, 300])
+def test_bptt_forward_equals_decoder_path_bitwise(B):
+    """The forward inside rlt_bptt runs the decoder-step kernels with the same row groups as
+    rlt_run_sequence, writing its saves on the side: the trajectories are bitwise equal."""
+    cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=4)
+    T = 12
+    p, e = inputs(cfg, B, T, seed=B)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    traj = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+    sd.rlt_bptt(model, ed, torch.zeros(B, T, cfg.d, device="cuda"), sd.grad_buffers(model),
+                s_traj=traj)
+    state, mem = sd.State(model, B), sd.Memory(model, B, T)
+    ref = torch.empty_like(traj)
+    sd.rlt_run_sequence(model, state, mem, ed, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(traj, ref)
+
+
+def test_bptt_feedback_zero_start_state_gradient_is_exactly_zero():
+    """With alpha = 0 nothing flows back into s_{t-1}: the start state's gradient is exactly
+    zero and the rest still matches the oracle."""
+    cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=5, alpha=0.0)
+    errs, worst = run_case(cfg, 4, 20, seed=11)
+    assert errs[worst] <= TOL["bf16"], (worst, errs[worst])
+    p, e = inputs(cfg, 4, 20, seed=11, random_gains=True, random_gate_bias=True)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    grads = sd.grad_buffers(model)
+    sd.rlt_bptt(model, ed, torch.randn(4, 20, cfg.d, device="cuda"), grads)
+    torch.cuda.synchronize()
+    assert not torch.any(grads["s_star"])
