@@ -73,6 +73,8 @@ CASES = [
     dict(dtype="bf16", B=3, T=12, d=256, n_heads=2, head_dim=128, ffn=512, window=20,
          n_groups=1),                                                            # W > T
     dict(dtype="bf16", B=300, T=40, d=128, n_heads=4, head_dim=32, ffn=192, window=6),
+    dict(dtype="fp32", B=2, T=6, d=256, n_heads=2, head_dim=128, ffn=256, window=2),
+    dict(dtype="bf16", B=3, T=1, d=128, n_heads=2, head_dim=64, ffn=256, window=5),  # one token
 ]
 
 
