@@ -180,3 +180,25 @@ def test_bptt_feedback_zero_start_state_gradient_is_exactly_zero():
     sd.rlt_bptt(model, ed, torch.randn(4, 20, cfg.d, device="cuda"), grads)
     torch.cuda.synchronize()
     assert not torch.any(grads["s_star"])
+
+
+def test_bptt_is_deterministic_across_calls():
+    """No atomics and fixed reduction orders: two calls (two row groups on two streams) give
+    bitwise identical gradients."""
+    cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=6)
+    B, T = 272, 20
+    p, e = inputs(cfg, B, T, seed=21)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    ds = torch.randn(B, T, cfg.d, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+    ws = sd.bptt_workspace(model, B, T)
+    runs = []
+    for _ in range(2):
+        g = sd.grad_buffers(model)
+        de = torch.empty(B, T, cfg.d, device="cuda")
+        sd.rlt_bptt(model, ed, ds, g, de=de, ws=ws)
+        torch.cuda.synchronize()
+        runs.append((g, de))
+    for k in sd.binding.WEIGHT_FIELDS:
+        assert torch.equal(runs[0][0][k], runs[1][0][k]), k
+    assert torch.equal(runs[0][1], runs[1][1])
