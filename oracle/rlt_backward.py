@@ -105,14 +105,26 @@ def sequence_loss(traj: np.ndarray, G: np.ndarray) -> float:
     return float(np.sum(np.asarray(traj, np.float64) * np.asarray(G, np.float64)))
 
 
-def bptt(params: dict, cfg, e: np.ndarray, G: np.ndarray, dtype=np.float64):
+def bptt(params: dict, cfg, e: np.ndarray, G: np.ndarray, dtype=np.float64, segment: int = 0,
+         detach=()):
     """Forward pass from the start state (s*, empty caches, memory projected from e) over the
     n tokens of e [B, n, d], then the reverse traversal for upstream gradients G [B, n, d].
 
     Returns (s_traj [B, n, d], grads, de): grads maps every name in GRAD_NAMES to an array of
     that parameter's shape; de [B, n, d] is the gradient with respect to the encoder outputs
     (through the gated merge and through the memory projection).
+
+    Truncation (the training section of the first page asks that every detached tensor be
+    named): with segment = k > 0 the tokens form segments [0, k), [k, 2k), ... and at every
+    segment start the tensors named in `detach` carry no gradient back into the previous
+    segment: "state" = the carried output s (the gated merge's input u), "window" = the
+    self-attention keys/values of earlier tokens still inside the window. The memory is never
+    detached. Detaching "state" alone leaves the window path open.
     """
+    detach = set(detach)
+    unknown = detach - {"state", "window"}
+    if unknown:
+        raise ValueError(f"unknown detached tensors {sorted(unknown)}")
     p = params if params["w_gate"].dtype == dtype else prepare_params(params, dtype)
     e = np.asarray(e, dtype)
     G = np.asarray(G, dtype)
@@ -170,6 +182,8 @@ def bptt(params: dict, cfg, e: np.ndarray, G: np.ndarray, dtype=np.float64):
     carry = np.zeros((B, d), dtype)  # dLoss/ds_t through token t+1's gated merge
     for t in range(n - 1, -1, -1):
         step = tape[t]
+        if segment and "state" in detach and (t + 1) % segment == 0:
+            carry = np.zeros_like(carry)  # s_t enters the next segment as a constant
         dh = G[:, t] + carry
         for l in range(L - 1, -1, -1):
             r = step["layers"][l]
@@ -205,6 +219,11 @@ def bptt(params: dict, cfg, e: np.ndarray, G: np.ndarray, dtype=np.float64):
             keys = np.stack(k_all[l][lo:t + 1], axis=1)
             vals = np.stack(v_all[l][lo:t + 1], axis=1)
             dq, dkeys, dvals = _attention_backward(r["q"], keys, vals, r["pw"], do, H)
+            if segment and "window" in detach:
+                # keys/values of tokens before this token's segment enter it as constants
+                first = (t // segment) * segment
+                dkeys[:, :max(0, first - lo)] = 0.0
+                dvals[:, :max(0, first - lo)] = 0.0
             dk_all[l][:, lo:t + 1] += dkeys
             dv_all[l][:, lo:t + 1] += dvals
             # every later token that saw this token's key/value has been walked: complete

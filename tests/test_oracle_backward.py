@@ -5,7 +5,10 @@
 * torch autograd through a forward written here with torch operations (every entry);
 * invariants: feedback scale zero cuts the start state out of every gradient; encoder
   outputs after the last token that carries loss get exactly zero gradient; the gradient is
-  linear in the upstream gradient.
+  linear in the upstream gradient;
+* truncation: the truncated gradients equal finite differences of a forward in which the
+  detached tensors are frozen at their values at every segment start; detaching the state
+  alone leaves the window path open.
 """
 import numpy as np
 import pytest
@@ -167,3 +170,87 @@ def test_gradient_is_linear_in_the_upstream_gradient():
     for name in oracle.GRAD_NAMES:
         np.testing.assert_allclose(c[name], 2.0 * a[name] - b[name], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(dc, 2.0 * da - db, rtol=1e-9, atol=1e-12)
+
+
+# --- truncation: every detached tensor named -----------------------------------------------
+
+def frozen_forward_loss(p, cfg, e, G, seg, detach, base):
+    """The loss of a forward in which, at every segment start, the detached tensors are
+    replaced by their values in the unperturbed run (`base`: state before each segment start),
+    so they enter the segment as constants; the memory is recomputed from p and e."""
+    km, vm = oracle.memory_projection(p, e)
+    st = oracle.init_state(p, cfg, e.shape[0])
+    loss = 0.0
+    for t in range(e.shape[1]):
+        if t > 0 and t % seg == 0:
+            s0, ck, cv = base[t]
+            if "state" in detach:
+                st.s = s0.copy()
+            if "window" in detach:
+                st.cache_k = [list(x) for x in ck]
+                st.cache_v = [list(x) for x in cv]
+        s_t = oracle.decoder_step(p, cfg, st, km, vm, e[:, t])
+        loss += float(np.sum(G[:, t] * s_t))
+    return loss
+
+
+def base_states(p, cfg, e, seg):
+    km, vm = oracle.memory_projection(p, e)
+    st = oracle.init_state(p, cfg, e.shape[0])
+    out = {}
+    for t in range(e.shape[1]):
+        if t > 0 and t % seg == 0:
+            out[t] = (st.s.copy(), [list(x) for x in st.cache_k], [list(x) for x in st.cache_v])
+        oracle.decoder_step(p, cfg, st, km, vm, e[:, t])
+    return out
+
+
+@pytest.mark.parametrize("detach", [("state",), ("window",), ("state", "window")])
+def test_truncated_bptt_matches_finite_differences_of_the_frozen_forward(detach):
+    cfg = tiny(window=3, seq_len=8)
+    p, e, G = setup(cfg, seed=13)
+    seg = 3
+    _, gr, de = oracle.bptt(p, cfg, e, G, segment=seg, detach=detach)
+    base = base_states(p, cfg, e, seg)
+    rng = np.random.default_rng(17)
+    h = 1e-5
+    checks = [(name, tuple(int(rng.integers(0, s)) for s in p[name].shape))
+              for name in oracle.GRAD_NAMES for _ in range(2)]
+    for name, idx in checks:
+        pp = {k: v.copy() for k, v in p.items()}
+        pp[name][idx] += h
+        lp = frozen_forward_loss(pp, cfg, e, G, seg, detach, base)
+        pp[name][idx] -= 2 * h
+        lm = frozen_forward_loss(pp, cfg, e, G, seg, detach, base)
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - gr[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, gr[name][idx])
+    for _ in range(6):
+        idx = tuple(int(rng.integers(0, s)) for s in e.shape)
+        ee = e.copy()
+        ee[idx] += h
+        lp = frozen_forward_loss(p, cfg, ee, G, seg, detach, base)
+        ee[idx] -= 2 * h
+        lm = frozen_forward_loss(p, cfg, ee, G, seg, detach, base)
+        assert abs((lp - lm) / (2 * h) - de[idx]) <= 1e-6 * max(1.0, abs(de[idx])), idx
+
+
+def test_detaching_the_state_alone_leaves_the_window_path_open():
+    """The trap named on the first page: with no memory path (zero memory projections) and loss
+    only on the second segment, detaching s still lets gradient into the first segment through
+    the window's keys/values of its last W - 1 tokens, and from there, along the first segment's
+    own (undetached) state, to every token of it; detaching s and the window cuts it."""
+    cfg = tiny(window=3, seq_len=8)
+    p, e, G = setup(cfg, seed=19)
+    p["wmk"][:] = 0.0
+    p["wmv"][:] = 0.0
+    seg = 4
+    G[:, :seg] = 0.0
+    _, _, de_full = oracle.bptt(p, cfg, e, G)
+    _, _, de_s = oracle.bptt(p, cfg, e, G, segment=seg, detach=("state",))
+    _, _, de_sw = oracle.bptt(p, cfg, e, G, segment=seg, detach=("state", "window"))
+    first = np.linalg.norm(de_full[:, :seg], axis=-1)
+    assert np.all(first > 0)
+    leak = np.linalg.norm(de_s[:, :seg], axis=-1)
+    assert np.all(leak > 0)
+    assert not np.any(de_sw[:, :seg])
+    np.testing.assert_allclose(de_sw[:, seg:], de_s[:, seg:], rtol=1e-12, atol=1e-14)
