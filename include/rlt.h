@@ -227,6 +227,21 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
  * keys/values; "16 per-token recurrence, no quality gain": a backward pass that walks the
  * tokens in reverse) ------------------------------------------------------------------------ */
 
+/* Truncated backpropagation for rlt_bptt ("RLT Runs 96 Blocks Per Token With Recurrent State,
+ * No Resets", "Training and serving implications": detaching s_t alone leaves gradient paths
+ * open through the decoder's keys/values, so a truncated scheme must name every detached
+ * tensor). The tokens form segments of `segment` tokens; at every segment start the tensors
+ * named in `detach` carry no gradient back into the previous segment. The memory is never
+ * detached. */
+enum {
+  RLT_DETACH_STATE = 1,  /* the carried output s (the gated merge's feedback input)     */
+  RLT_DETACH_WINDOW = 2  /* self-attention keys/values of earlier tokens in the window */
+};
+typedef struct rlt_truncation {
+  int64_t segment;  /* >= 1 */
+  uint32_t detach;  /* RLT_DETACH_* bits */
+} rlt_truncation;
+
 /* Optional kernel timing of rlt_bptt (see rlt_kernel and rlt_kernel_stats below). */
 typedef struct rlt_timing {
   uint32_t kernels;     /* bit (1 << rlt_kernel) per kernel to time */
@@ -267,7 +282,9 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
  * is overwritten with dLoss/dparameter (float32, summed over the batch); de [B][n][d] float32
  * (device, or NULL to skip) receives dLoss/de through the gated merge and the memory
  * projection; s_traj [B][n][d] float32 (device, or NULL) receives the forward trajectory.
- * Gradients through the self-attention keys/values of later tokens are included. Independent
+ * Gradients through the self-attention keys/values of later tokens are included; `trunc`
+ * (NULL: full backpropagation) truncates them and the state's at segment starts as it names
+ * (RLT_ERR_ARG for a segment < 1 or unknown bits). Independent
  * of any rlt_state or rlt_memory. `ws`: device, 256-byte aligned, >= rlt_bptt_ws_bytes bytes,
  * scratch owned by the caller (RLT_ERR_CAPACITY if smaller). Asynchronous on `stream`, unless
  * `timing` is non-NULL with kernels != 0: then the launches of those kernels (rlt_kernel bits)
@@ -279,8 +296,8 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
  * not overlap (they share that stream and its events); other calls on the model may. */
 rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
                     const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
-                    size_t ws_bytes, const struct rlt_timing* timing, struct rlt_kernel_stats* stats,
-                    void* stream);
+                    size_t ws_bytes, const rlt_truncation* trunc, const struct rlt_timing* timing,
+                    struct rlt_kernel_stats* stats, void* stream);
 
 /* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
 

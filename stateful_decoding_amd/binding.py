@@ -47,6 +47,13 @@ class rlt_grads(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in WEIGHT_FIELDS]
 
 
+class rlt_truncation(ctypes.Structure):
+    _fields_ = [("segment", c_int64), ("detach", ctypes.c_uint32)]
+
+
+DETACH_BITS = {"state": 1, "window": 2}  # RLT_DETACH_STATE, RLT_DETACH_WINDOW
+
+
 class rlt_timing(ctypes.Structure):
     _fields_ = [("kernels", ctypes.c_uint32), ("token_stride", c_int32)]
 
@@ -109,7 +116,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_state_import_ragged": (c_int32, [P, P, P, P, P, c_uint64, P]),
         "rlt_bptt_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
         "rlt_bptt": (c_int32, [P, P, c_int32, c_int64, P, P, POINTER(rlt_grads), P, P, c_size_t,
-                               POINTER(rlt_timing), P, P]),
+                               POINTER(rlt_truncation), POINTER(rlt_timing), P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -375,12 +382,16 @@ def grad_buffers(model: Model) -> dict:
 def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
              de: torch.Tensor | None = None, s_traj: torch.Tensor | None = None,
              ws: torch.Tensor | None = None, stream=None, time_kernels=None,
-             token_stride: int = 1):
+             token_stride: int = 1, segment: int = 0, detach=()):
     """Forward from s* over e [B, n, d] and backpropagation through time of the upstream
     gradients ds [B, n, d] float32 into `grads` (from grad_buffers; overwritten), de [B, n, d]
     float32 and s_traj [B, n, d] float32 (both optional); `ws` from bptt_workspace. With
     `time_kernels` (names from KERNEL_NAMES) the call waits for the stream and returns
-    {name: {launches, total_ms, bytes, flops}} of those kernels' sampled launches."""
+    {name: {launches, total_ms, bytes, flops}} of those kernels' sampled launches.
+
+    segment = k > 0 truncates the backpropagation: at every start of a k-token segment the
+    tensors named in `detach` ("state": the carried output s; "window": the self-attention
+    keys/values of earlier tokens) pass no gradient back into the previous segment."""
     B, n = int(e.shape[0]), int(e.shape[1])
     d = model.cfg.d
     _need(e, (B, n, d), model.dtype, "e")
@@ -396,6 +407,14 @@ def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
     if ws is None:
         ws = bptt_workspace(model, B, n)
     g = rlt_grads(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    trunc = None
+    if segment:
+        bits = 0
+        for k in detach:
+            if k not in DETACH_BITS:
+                raise ValueError(f"unknown detached tensor {k!r}")
+            bits |= DETACH_BITS[k]
+        trunc = rlt_truncation(int(segment), bits)
     timing = None
     stats = None
     if time_kernels:
@@ -406,6 +425,7 @@ def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
         stats = (rlt_kernel_stats * len(KERNEL_NAMES))()
     _check(model.lib.rlt_bptt(model.handle, e.data_ptr(), B, n, ds.data_ptr(), _ptr(s_traj),
                               byref(g), _ptr(de), ws.data_ptr(), ws.numel() * ws.element_size(),
+                              None if trunc is None else byref(trunc),
                               None if timing is None else byref(timing), stats, _stream(stream)))
     if stats is None:
         return None

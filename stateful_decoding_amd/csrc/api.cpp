@@ -716,8 +716,8 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
 
 rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
                     const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
-                    size_t ws_bytes, const rlt_timing* timing, rlt_kernel_stats* stats,
-                    void* stream) {
+                    size_t ws_bytes, const rlt_truncation* trunc, const rlt_timing* timing,
+                    rlt_kernel_stats* stats, void* stream) {
   if (!model) return fail(RLT_ERR_ARG, "model is NULL");
   if (!e || !ds || !grads || !ws) return fail(RLT_ERR_ARG, "e, ds, grads and ws must be non-NULL");
   float* const gp[] = {grads->s_star, grads->w_gate, grads->b_gate, grads->gamma, grads->wq,
@@ -732,6 +732,11 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
   if ((int64_t)batch * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "batch * n too large");
   if (!aligned16(e) || !aligned(ws))
     return fail(RLT_ERR_ARG, "e must be 16-byte aligned, ws 256-byte aligned");
+  if (trunc && trunc->segment < 1)
+    return fail(RLT_ERR_ARG, "truncation segment must be >= 1, got %lld",
+                (long long)trunc->segment);
+  if (trunc && (trunc->detach & ~(uint32_t)(RLT_DETACH_STATE | RLT_DETACH_WINDOW)))
+    return fail(RLT_ERR_ARG, "unknown detach bits 0x%x", trunc->detach);
   const bool timed = timing && timing->kernels;
   if (timed) {
     if (!stats) return fail(RLT_ERR_ARG, "stats must be non-NULL when timing kernels");
@@ -761,7 +766,8 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
     if (err == hipSuccess) err = hipEventCreateWithFlags(&mm->bwd_join, hipEventDisableTiming);
     if (err != hipSuccess) return hip_fail(err, "creating the backward pass's second stream");
   }
-  err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, st,
+  err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, trunc ? trunc->segment : 0,
+                    trunc ? trunc->detach : 0u, st,
                     batch >= 2 * kGroupRows ? mm->bwd_aux : nullptr, mm->bwd_fork, mm->bwd_join,
                     timed ? &prof : nullptr);
   if (timed) {

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_walk_begin(const float* __restrict
   const int b = blockIdx.x;
   const int64_t o = (int64_t)b * d;
   for (int j = threadIdx.x; j < d; j += kThreads) {
-    const float v = G[((int64_t)b * n + i) * d + j] + carry[o + j];
+    const float v = G[((int64_t)b * n + i) * d + j] + (carry ? carry[o + j] : 0.f);
     dres[o + j] = v;
     dres_t[o + j] = to_elem<T>(v);
   }
@@ -636,9 +636,9 @@ __global__ __launch_bounds__(NW * kWave) void k_xattn_back(
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_swa_back(
     const float* __restrict__ qs, const float* __restrict__ dout, const T* __restrict__ K,
-    const T* __restrict__ V, int64_t n, int64_t t, int W, int B, int H, float scale,
-    T* __restrict__ ring_do, float* __restrict__ ring_lse, float* __restrict__ ring_dlt,
-    T* __restrict__ out) {
+    const T* __restrict__ V, int64_t n, int64_t t, int64_t hi_cap, int W, int B, int H,
+    float scale, T* __restrict__ ring_do, float* __restrict__ ring_lse,
+    float* __restrict__ ring_dlt, T* __restrict__ out) {
   using G = AGeo<T, HD>;
   constexpr int VEC = G::VEC, RPB = G::RPW * NW;
   __shared__ float s_m[NW], s_l[NW], s_c[NW];
@@ -780,7 +780,9 @@ __global__ __launch_bounds__(NW * kWave) void k_swa_back(
       gv[i] = 0.f;
     }
   }
-  const int64_t hi = t + W - 1 < n - 1 ? t + W - 1 : n - 1;  // last token whose window holds t
+  // last token whose window holds t (and, with the window detached at segment starts, that is
+  // in t's segment: hi_cap is the segment's last token)
+  const int64_t hi = t + W - 1 < hi_cap ? t + W - 1 : hi_cap;
   const int nq = (int)(hi - t + 1);
   for (int r = first; r < nq; r += RPB) {
     const int64_t tp = t + r;
@@ -1182,13 +1184,13 @@ static hipError_t xattn_back(int BH, const float* q, const float* dout, const T*
 
 template <typename T, int HD>
 static hipError_t swa_back(int BH, int B, const float* qs, const float* dout, const T* K,
-                           const T* V, int64_t n, int64_t t, int W, int H, T* ring_do,
-                           float* ring_lse, float* ring_dlt, T* out, const Exec& x) {
+                           const T* V, int64_t n, int64_t t, int64_t hi_cap, int W, int H,
+                           T* ring_do, float* ring_lse, float* ring_dlt, T* out, const Exec& x) {
   const float scale = 1.f / sqrtf((float)HD);
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
 #define RLT_SB(NW)                                                                              \
-  return launch(k_swa_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, qs, dout, K, V, n, t, W, \
-                B, H, scale, ring_do, ring_lse, ring_dlt, out)
+  return launch(k_swa_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, qs, dout, K, V, n, t,   \
+                hi_cap, W, B, H, scale, ring_do, ring_lse, ring_dlt, out)
   if (nw == 4) RLT_SB(4);
   if (nw == 8) RLT_SB(8);
   RLT_SB(16);
@@ -1260,8 +1262,8 @@ struct Timer {
 // and results once each (es per dtype element, 4 per fp32 one).
 template <typename T, int HD>
 static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M, const T* e,
-                             const float* G, float* de, int64_t i, int64_t li, Timer& tm,
-                             bool sampled) {
+                             const float* G, float* de, int64_t i, int64_t li, int64_t segment,
+                             uint32_t detach, Timer& tm, bool sampled) {
   const Dims& D = w.D;
   const TrainLayout& TL = w.TL;
   // B: this group's rows (GEMM rows, grids); Bt: all rows (strides); b0: the group's first row
@@ -1297,9 +1299,14 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                        w.chunk(TL.cf, l, d, li), D.eps};
   };
   const double nrb = 3 * rows32 + 3 * rowsT;  // bytes of one set of norm rows
+  // the gradient of s_i through token i+1 is dropped when i+1 starts a segment that detaches s
+  const bool cut_state = segment > 0 && (detach & RLT_DETACH_STATE) && (i + 1) % segment == 0;
   RLT_TRY(launch(k_walk_begin<T>, dim3(B), dim3(kThreads), other(3 * rows32 + rowsT + nrb), G,
-                 (const float*)carry, dres, w.chunk(TL.y2, L - 1, d, li), d, n, i, rows_of(L - 1),
-                 rinv));
+                 cut_state ? (const float*)nullptr : (const float*)carry, dres,
+                 w.chunk(TL.y2, L - 1, d, li), d, n, i, rows_of(L - 1), rinv));
+  const int64_t hi_cap = segment > 0 && (detach & RLT_DETACH_WINDOW)
+                             ? std::min<int64_t>(n - 1, (i / segment + 1) * segment - 1)
+                             : n - 1;
   for (int l = L - 1; l >= 0; --l) {
     const float* gam = P.gamma + (int64_t)l * 3 * d;
     const float* xs = w.template saved<float>(TL.xs, l, i);
@@ -1359,10 +1366,10 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     const int64_t rd = (int64_t)l * D.W * Bt * d + (int64_t)b0 * d;
     const int64_t rs = (int64_t)l * D.W * Bt * H + (int64_t)b0 * H;
     const double nk = (double)std::min<int64_t>(i + 1, D.W);
-    const double nq = (double)std::min<int64_t>(n - i, D.W);
+    const double nq = (double)std::min<int64_t>(hi_cap - i + 1, D.W);
     RLT_TRY(swa_back<T, HD>(BH, Bt, w.template at<float>(TL.qs) + (int64_t)l * n * Bt * d + b0 * d,
                             dattn, w.template at<T>(TL.khist) + hist,
-                            w.template at<T>(TL.vhist) + hist, n, i, D.W, H,
+                            w.template at<T>(TL.vhist) + hist, n, i, hi_cap, D.W, H,
                             w.template at<T>(TL.dkacc) + rd, w.template at<float>(TL.dvacc) + rs,
                             w.template at<float>(TL.dvacc) + (int64_t)L * D.W * Bt * H + rs, yqkv,
                             tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * es + nq * b * d * (4 + es) +
@@ -1441,8 +1448,8 @@ static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, i
 template <typename T, int HD>
 static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const void* e_v,
                          const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                         hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
-                         Profiler* prof) {
+                         int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
+                         hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof) {
   const TrainLayout TL = train_layout(D, B, n);
   const Walk<T> w{D, B, n, TL, ws};
   const int d = D.d, F = D.F, L = D.L, H = D.H;
@@ -1626,7 +1633,7 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     for (int64_t i = i1 - 1; i >= i0; --i)
       for (int gi = 0; gi < ng; ++gi)
         RLT_TRY(walk_token<T, HD>(w.group(row0[gi], row0[gi + 1] - row0[gi]), P, M, e, G, de,
-                                  i, i - i0, gtm[gi], i % stride == 0));
+                                  i, i - i0, segment, detach, gtm[gi], i % stride == 0));
     RLT_TRY(join());
     RLT_TRY(chunk_grads<T>(w, g, i0, i1, tm));
     i1 = i0;
@@ -1686,14 +1693,14 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
 
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
-                       Profiler* prof) {
-#define RLT_BPTT(HDV)                                                                        \
-  return D.dtype == RLT_BF16                                                                 \
-             ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, aux, ev_fork,     \
-                                 ev_join, prof)                                              \
-             : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, st, aux, ev_fork,    \
-                                  ev_join, prof)
+                       int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
+                       hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof) {
+#define RLT_BPTT(HDV)                                                                         \
+  return D.dtype == RLT_BF16                                                                  \
+             ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, segment, detach, st,   \
+                                 aux, ev_fork, ev_join, prof)                                 \
+             : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, segment, detach, st,  \
+                                  aux, ev_fork, ev_join, prof)
   switch (D.hd) {
     case 32: RLT_BPTT(32);
     case 64: RLT_BPTT(64);

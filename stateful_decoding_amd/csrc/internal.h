@@ -240,9 +240,11 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n);
 // With `prof`, launches of the kernels it times are timed in the steps of tokens
 // i % prof->stride == 0 and everywhere outside the token loops. With `aux` (a second stream,
 // and two events for forking to it and joining back), large batches run as two row groups.
+// segment > 0: truncation at every segment start of the tensors named by `detach`
+// (RLT_DETACH_* bits).
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
-                       hipStream_t st, hipStream_t aux, hipEvent_t ev_fork, hipEvent_t ev_join,
-                       Profiler* prof);
+                       int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
+                       hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof);
 
 }  // namespace rlt

@@ -97,7 +97,7 @@ def test_null_arguments_rejected_without_gpu(lib):
     assert lib.rlt_decoder_step(None, None, None, None, None, None) == 1
     assert lib.rlt_run_sequence(None, None, None, None, 1, None, None) == 1
     assert lib.rlt_run_parallel(None, None, None, None, 1, None, None, 0, None) == 1
-    assert lib.rlt_bptt(None, None, 1, 1, None, None, None, None, None, 0, None, None,
+    assert lib.rlt_bptt(None, None, 1, 1, None, None, None, None, None, 0, None, None, None,
                          None) == 1
     assert lib.rlt_state_export(None, None, None, None, None, None, None, None) == 1
     assert lib.rlt_state_import(None, None, None, None, 0, 0, None) == 1

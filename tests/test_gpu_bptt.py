@@ -110,8 +110,16 @@ def test_bptt_argument_errors():
     g = sd.binding.rlt_grads(*[grads[k].data_ptr() for k in sd.binding.WEIGHT_FIELDS])
     g.w2 = None
     st = lib.rlt_bptt(model.handle, ed.data_ptr(), 2, 4, Gd.data_ptr(), None,
-                      sd.binding.byref(g), None, ws.data_ptr(), ws.numel(), None, None, None)
+                      sd.binding.byref(g), None, ws.data_ptr(), ws.numel(), None, None, None,
+                      None)
     assert sd.binding.STATUS_NAMES[st] == "RLT_ERR_ARG"
+    g.w2 = grads["w2"].data_ptr()
+    for seg, bits in ((0, 1), (2, 4)):
+        tr = sd.binding.rlt_truncation(seg, bits)
+        st = lib.rlt_bptt(model.handle, ed.data_ptr(), 2, 4, Gd.data_ptr(), None,
+                          sd.binding.byref(g), None, ws.data_ptr(), ws.numel(),
+                          sd.binding.byref(tr), None, None, None)
+        assert sd.binding.STATUS_NAMES[st] == "RLT_ERR_ARG", (seg, bits)
 
 
 def test_full_size_bptt_early_tokens_match_oracle():
@@ -202,3 +210,71 @@ def test_bptt_is_deterministic_across_calls():
     for k in sd.binding.WEIGHT_FIELDS:
         assert torch.equal(runs[0][0][k], runs[1][0][k]), k
     assert torch.equal(runs[0][1], runs[1][1])
+
+
+TRUNC_CASES = [
+    dict(dtype="fp32", B=3, T=13, segment=4, detach=("state", "window"), window=3),
+    dict(dtype="fp32", B=2, T=11, segment=3, detach=("state",), window=5, n_groups=1),
+    dict(dtype="fp32", B=2, T=10, segment=4, detach=("window",), window=6),
+    dict(dtype="bf16", B=5, T=24, segment=5, detach=("state", "window"), d=128, n_heads=2,
+         head_dim=64, ffn=256, window=7),
+    dict(dtype="bf16", B=300, T=30, segment=8, detach=("state", "window"), d=128, n_heads=4,
+         head_dim=32, ffn=192, window=6),
+    dict(dtype="fp32", B=2, T=9, segment=1, detach=("state", "window"), window=4),
+    dict(dtype="fp32", B=2, T=9, segment=20, detach=("state", "window"), window=4),
+]
+
+
+@pytest.mark.parametrize("case", TRUNC_CASES)
+def test_truncated_bptt_matches_oracle(case):
+    """Truncated backpropagation (segment length k, named detached tensors) against the
+    oracle's truncated reverse traversal; segment 1 cuts at every token, a segment longer than
+    the sequence cuts nothing."""
+    case = dict(case)
+    B, T = case.pop("B"), case.pop("T")
+    seg, det = case.pop("segment"), case.pop("detach")
+    cfg = cfg_small(**case)
+    p, e = inputs(cfg, B, T, seed=B + T + seg, random_gains=True, random_gate_bias=True)
+    G = np.random.default_rng(seg).standard_normal((B, T, cfg.d)).astype(np.float32)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    grads = sd.grad_buffers(model)
+    de = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+    print(f"truncated case {cfg.dtype} B={B} T={T} W={cfg.window} segment={seg} "
+          f"detach={det}", flush=True)
+    sd.rlt_bptt(model, ed, torch.from_numpy(G).cuda(), grads, de=de, segment=seg, detach=det)
+    torch.cuda.synchronize()
+    _, ref, ref_de = oracle.bptt(p, cfg, e, G, segment=seg, detach=det)
+    errs = grad_errors({k: v.cpu().numpy() for k, v in grads.items()}, ref)
+    errs["de"] = rel_l2(de.cpu().numpy(), ref_de)
+    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    worst = max(errs, key=errs.get)
+    assert errs[worst] <= TOL[cfg.dtype], (worst, errs[worst])
+
+
+def test_detaching_the_state_alone_leaves_the_window_path_open():
+    """With the memory projections zeroed and the loss on the second segment only, detaching
+    the state alone still sends gradient into the first segment's encoder outputs (through the
+    window's keys and values); detaching the window too leaves exactly zero there."""
+    cfg = cfg_small(dtype="fp32", window=4, n_groups=1)
+    B, T, k = 2, 8, 4
+    p, e = inputs(cfg, B, T, seed=5, random_gains=True, random_gate_bias=True)
+    p = dict(p)
+    p["wmk"] = np.zeros_like(p["wmk"])
+    p["wmv"] = np.zeros_like(p["wmv"])
+    G = np.zeros((B, T, cfg.d), np.float32)
+    G[:, k:] = np.random.default_rng(1).standard_normal((B, T - k, cfg.d))
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    out = {}
+    for det in (("state",), ("state", "window")):
+        de = torch.empty(B, T, cfg.d, dtype=torch.float32, device="cuda")
+        sd.rlt_bptt(model, ed, torch.from_numpy(G).cuda(), sd.grad_buffers(model), de=de,
+                    segment=k, detach=det)
+        torch.cuda.synchronize()
+        out[det] = de.cpu().numpy()
+        _, _, ref_de = oracle.bptt(p, cfg, e, G, segment=k, detach=det)
+        assert rel_l2(out[det], ref_de) <= TOL["fp32"], det
+    leak = np.linalg.norm(out[("state",)][:, :k], axis=-1)
+    assert np.all(leak > 0)
+    assert not np.any(out[("state", "window")][:, :k])
