@@ -122,9 +122,10 @@ def main():
                     help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-stride", type=int, default=16,
+    ap.add_argument("--profile-stride", type=int, default=1,
                     help="time the memory-attention launches of every N-th token (1 = all); "
-                         "timing every launch costs a few percent of throughput")
+                         "the launches time themselves by the GPU clock, with nothing queued "
+                         "around them")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run 5 plain device copies of MIB MiB (fp32) and exit: the known-size "
                          "kernel that scales the HBM byte counters of a profiler")
@@ -189,6 +190,8 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
+    # one clock slot pair per workgroup (sequence, head) of every timed memory attention
+    state.profile_clock(args.steps * T * cfg.n_layers * B * cfg.n_heads)
     state.profile_begin(["cross_attn", "memproj"], token_stride=args.profile_stride)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -229,7 +232,9 @@ def main():
                      "avg_launch_us": round(ca["total_ms"] * 1e3 / ca["launches"], 2),
                      "bytes_per_launch": round(ca["bytes"] / ca["launches"]),
                      "timed": f"every launch in the steps of tokens t with t % "
-                              f"{args.profile_stride} == 0 (all layers and row groups)"},
+                              f"{args.profile_stride} == 0 (all layers and row groups), each "
+                              f"by the kernel's own clock stamps: first wave's start to last "
+                              f"wave's end"},
         "step_roofline": {"ideal_s": round(ideal, 4), "measured_s": round(secs / args.steps, 4),
                           "frac": round(ideal / (secs / args.steps), 4),
                           "peaks": "HBM 8.0 TB/s, bf16 MFMA 2.5 PFLOP/s"},
@@ -354,6 +359,7 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
         one_step()
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    state.profile_clock(args.steps * T * L * B * cfg.n_heads)
     state.profile_begin(["cross_attn"], token_stride=args.profile_stride)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -389,7 +395,8 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
                      "launches": ca["launches"],
                      "avg_launch_us": round(ca["total_ms"] * 1e3 / ca["launches"], 2),
-                     "timed": f"every launch in the steps s with s % {args.profile_stride} == 0"},
+                     "timed": f"every launch in the steps s with s % {args.profile_stride} == 0, "
+                              f"by the kernel's own clock stamps"},
     }
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)

@@ -355,22 +355,39 @@ typedef enum rlt_kernel {
 
 typedef struct rlt_kernel_stats {
   int64_t launches;  /* launches timed                                                   */
-  double total_ms;   /* sum over launches of the kernel's duration (HIP events)           */
+  double total_ms;   /* sum over launches of the kernel's duration (HIP events, or the     *
+                      * kernel's own clock stamps, see rlt_profile_clock)                 */
   double bytes;      /* algorithmic bytes: each operand read once, each result written once */
   double flops;      /* algorithmic floating-point operations                            */
 } rlt_kernel_stats;
 
 /* Starts timing, for this state, launches of the kernels whose bit (1 << rlt_kernel) is set in
  * `mask`: each timed launch records a pair of HIP events at the start and at the end of its
- * kernel (hipExtLaunchKernel), on the stream it runs on; no extra packets are queued. Decoder
+ * kernel (hipExtLaunchKernel), on the stream it runs on, except the attention kernels while a
+ * clock buffer is attached (rlt_profile_clock), which time themselves. Decoder
  * launches are timed in the steps of tokens t (0-based position before the step) with
  * t % token_stride == 0 (token_stride >= 1; 1 = every step), memory projections always.
  * Events are pooled by the state and kept until rlt_state_destroy. */
 rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride);
 
-/* Stops timing, waits for the recorded events and writes RLT_K_COUNT entries to `out`
- * (host array, indexed by rlt_kernel). */
+/* Stops timing, waits for the recorded events (and, when clock slots were used, for the
+ * device) and writes RLT_K_COUNT entries to `out` (host array, indexed by rlt_kernel).
+ * RLT_ERR_CAPACITY (after writing `out`) when the clock buffer was too small for the launches
+ * to be timed. */
 rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out);
+
+/* Attaches a caller-owned device buffer (16-byte aligned; NULL detaches) in which later timing
+ * sessions of this state time the two attention kernels (RLT_K_SELF_ATTN, RLT_K_CROSS_ATTN)
+ * by their own clock instead of by events: every workgroup writes the GPU's constant-rate wall
+ * clock to a slot pair of its own when it starts and when all its waves are done, and
+ * rlt_profile_end takes each launch's earliest start and latest end. Nothing is queued around
+ * the launch that could change how concurrent streams overlap, and no two workgroups write the
+ * same address. The kernels run one workgroup per (sequence, head): a timed launch takes
+ * 16 * H bytes per sequence of its batch. rlt_profile_begin clears the slots (it waits for the
+ * device); launches that no longer fit are not timed and make rlt_profile_end return
+ * RLT_ERR_CAPACITY. Not while a session runs (RLT_ERR_ARG). The buffer must stay allocated
+ * while attached. */
+rlt_status rlt_profile_clock(rlt_state* state, void* buf, size_t bytes);
 
 #ifdef __cplusplus
 }

@@ -104,6 +104,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_memory_reset": (c_int32, [P]),
         "rlt_profile_begin": (c_int32, [P, ctypes.c_uint32, c_int32]),
         "rlt_profile_end": (c_int32, [P, POINTER(rlt_kernel_stats)]),
+        "rlt_profile_clock": (c_int32, [P, P, c_size_t]),
         "rlt_memory_destroy": (None, [P]),
         "rlt_memproj": (c_int32, [P, P, P, c_int64, c_int64, P]),
         "rlt_decoder_step": (c_int32, [P, P, P, P, P, P]),
@@ -222,6 +223,18 @@ class State:
         out = (c_int64 * self.batch)()
         _check(self.lib.rlt_state_positions(self.handle, out, _stream(stream)))
         return list(out)
+
+    def profile_clock(self, slots: int | None):
+        """Attach a device buffer of `slots` clock slot pairs (one per workgroup of each
+        self-timed attention launch, i.e. H per sequence and launch): later sessions time the
+        attention kernels by their own clock stamps instead of events. None detaches it."""
+        if slots is None:
+            _check(self.lib.rlt_profile_clock(self.handle, None, 0))
+            self._clk = None
+            return
+        buf = torch.empty(int(slots) * 16, dtype=torch.uint8, device=self.buf.device)
+        _check(self.lib.rlt_profile_clock(self.handle, buf.data_ptr(), buf.numel()))
+        self._clk = buf  # kept alive while attached
 
     def profile_begin(self, kernels=KERNEL_NAMES, token_stride: int = 1):
         """Time launches of `kernels` in the steps of every token_stride-th token."""

@@ -3,6 +3,7 @@
 // anything is enqueued, so a rejected call leaves every handle and buffer untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -613,10 +614,36 @@ rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stri
   if (!state) return fail(RLT_ERR_ARG, "state is NULL");
   if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");
   if (token_stride < 1) return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", token_stride);
-  state->prof.stride = token_stride;
-  state->prof.mask = mask;
-  state->prof.recs.clear();
-  state->prof.used = 0;
+  Profiler& P = state->prof;
+  P.stride = token_stride;
+  P.mask = mask;
+  P.recs.clear();
+  P.used = 0;
+  P.clk_used = 0;
+  P.clk_dropped = 0;
+  if (P.clk_buf) {
+    // every slot pair starts at (max, 0): the kernels fold their stamps in with min / max
+    std::vector<unsigned long long> init(2 * (size_t)P.clk_cap);
+    for (size_t i = 0; i < init.size(); i += 2) {
+      init[i] = ~0ull;
+      init[i + 1] = 0ull;
+    }
+    const hipError_t e = hipMemcpy(P.clk_buf, init.data(), init.size() * 8, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      P.mask = 0;
+      return hip_fail(e, "clearing the clock buffer");
+    }
+  }
+  return ok();
+}
+
+rlt_status rlt_profile_clock(rlt_state* state, void* buf, size_t bytes) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  if (buf && (bytes < 16 || reinterpret_cast<uintptr_t>(buf) % 16))
+    return fail(RLT_ERR_ARG, "the clock buffer must be 16-byte aligned and hold one launch");
+  if (state->prof.mask) return fail(RLT_ERR_ARG, "a timing session is running");
+  state->prof.clk_buf = static_cast<unsigned long long*>(buf);
+  state->prof.clk_cap = buf ? (int64_t)(bytes / 16) : 0;
   return ok();
 }
 
@@ -625,12 +652,42 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
   Profiler& P = state->prof;
   for (int k = 0; k < RLT_K_COUNT; ++k) out[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
   hipError_t e = hipSuccess;
+  std::vector<unsigned long long> clk;
+  double ticks_per_ms = 0.0;
+  if (P.clk_used > 0) {
+    // self-stamped launches may have run on any of the state's streams
+    int dev = 0, khz = 0;
+    e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e == hipSuccess && khz <= 0) e = hipErrorInvalidValue;
+    if (e == hipSuccess) {
+      clk.resize(2 * (size_t)P.clk_used);
+      e = hipMemcpy(clk.data(), P.clk_buf, clk.size() * 8, hipMemcpyDeviceToHost);
+    }
+    ticks_per_ms = khz;  // kHz = clock ticks per millisecond
+  }
   for (const Profiler::Rec& r : P.recs) {
-    // launches of different row groups ran on different streams: wait for each one
-    float ms = 0.f;
-    e = hipEventSynchronize(P.events[r.ev + 1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, P.events[r.ev], P.events[r.ev + 1]);
     if (e != hipSuccess) break;
+    float ms = 0.f;
+    if (r.ev < 0) {
+      // earliest workgroup start to latest workgroup end
+      unsigned long long a = ~0ull, b = 0ull;
+      for (int64_t w = r.clk; w < r.clk + r.nclk; ++w) {
+        a = std::min(a, clk[2 * w]);
+        b = std::max(b, clk[2 * w + 1]);
+      }
+      if (a == ~0ull || b < a) {
+        e = hipErrorInvalidValue;  // a workgroup of the launch left no stamps
+        break;
+      }
+      ms = (float)((double)(b - a) / ticks_per_ms);
+    } else {
+      // launches of different row groups ran on different streams: wait for each one
+      e = hipEventSynchronize(P.events[r.ev + 1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, P.events[r.ev], P.events[r.ev + 1]);
+      if (e != hipSuccess) break;
+    }
     rlt_kernel_stats& o = out[r.kind];
     o.launches += 1;
     o.total_ms += ms;
@@ -640,7 +697,13 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
   P.mask = 0;
   P.recs.clear();
   P.used = 0;
+  const int64_t dropped = P.clk_dropped;
+  P.clk_used = 0;
+  P.clk_dropped = 0;
   if (e != hipSuccess) return hip_fail(e, "reading kernel timers");
+  if (dropped > 0)
+    return fail(RLT_ERR_CAPACITY, "the clock buffer holds %lld launches; %lld more were not timed",
+                (long long)P.clk_cap, (long long)dropped);
   return ok();
 }
 

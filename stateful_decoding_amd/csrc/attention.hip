@@ -138,22 +138,34 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
   }
 }
 
-// The two uses get kernels of their own, so that traces tell them apart.
+// The two uses get kernels of their own, so that traces tell them apart. With clk != NULL
+// (a timed launch) every workgroup writes the GPU's constant-rate clock to its own slot pair:
+// clk[2 blockIdx] when it starts, clk[2 blockIdx + 1] when all its waves are done. The host
+// takes the earliest start and the latest end, so the launch measures itself with nothing
+// queued around it, and no two workgroups write the same address.
 template <typename T, int HD, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_attend_window(const float* q, const T* K,
-                                                              const T* V, int64_t bh_stride,
-                                                              const int64_t* pos,
-                                                              int64_t t_uniform, int window,
-                                                              int H, float scale, T* out) {
+__device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
+                                             int64_t bh_stride, const int64_t* pos,
+                                             int64_t t_uniform, int window, int H, float scale,
+                                             T* out, unsigned long long* clk) {
+  if (clk && threadIdx.x == 0) clk[2 * blockIdx.x] = wall_clock64();
   attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
+  if (clk) {
+    __syncthreads();
+    if (threadIdx.x == 0) clk[2 * blockIdx.x + 1] = wall_clock64();
+  }
 }
 template <typename T, int HD, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_attend_memory(const float* q, const T* K,
-                                                              const T* V, int64_t bh_stride,
-                                                              const int64_t* pos,
-                                                              int64_t t_uniform, int window,
-                                                              int H, float scale, T* out) {
-  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
+__global__ __launch_bounds__(NW * kWave) void k_attend_window(
+    const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
+    int64_t t_uniform, int window, int H, float scale, T* out, unsigned long long* clk) {
+  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, clk);
+}
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_attend_memory(
+    const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
+    int64_t t_uniform, int window, int H, float scale, T* out, unsigned long long* clk) {
+  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, clk);
 }
 
 template <typename T>
@@ -171,7 +183,7 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
 #define RLT_ATTEND(NW)                                                                     \
   return launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,   \
                 dim3(BH), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, window, \
-                H, scale, out)
+                H, scale, out, st.clk)
   if (nw == 4) RLT_ATTEND(4);
   if (nw == 8) RLT_ATTEND(8);
   RLT_ATTEND(16);

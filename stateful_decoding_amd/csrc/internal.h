@@ -23,12 +23,14 @@ constexpr int64_t kMaxCapacity = (int64_t)1 << 20;  // memory entries per sequen
 constexpr int kGroupRows = RLT_GROUP_ROWS;
 constexpr int kMaxGroups = 4;
 
-// Where a kernel runs: its stream and, when it is being timed, a pair of events that the
-// launch itself records at the start and at the end of the kernel (hipExtLaunchKernel), so the
-// measured span is the kernel alone, without extra event packets around it.
+// Where a kernel runs: its stream and, when it is being timed, either a pair of events that the
+// launch itself records at the start and at the end of the kernel (hipExtLaunchKernel), or,
+// for kernels that stamp themselves (the attention kernels), device slots of two clock values
+// per workgroup (its start, its end) that the kernel fills.
 struct Exec {
   hipStream_t st;
   hipEvent_t start = nullptr, stop = nullptr;
+  unsigned long long* clk = nullptr;
   Exec(hipStream_t s) : st(s) {}  // NOLINT: a plain stream is an untimed Exec
   Exec(hipStream_t s, hipEvent_t a, hipEvent_t b) : st(s), start(a), stop(b) {}
 };
@@ -145,7 +147,9 @@ hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& 
 struct Profiler {
   struct Rec {
     int kind;
-    int ev;  // index of the start event in `events`; the end event follows it
+    int ev;       // index of the start event in `events` (the end event follows it), or -1
+    int64_t clk;  // with ev = -1: index of the launch's first slot pair in clk_buf
+    int64_t nclk; // with ev = -1: slot pairs of the launch (one per workgroup)
     double bytes, flops;
   };
   uint32_t mask = 0;
@@ -153,10 +157,15 @@ struct Profiler {
   std::vector<hipEvent_t> events;  // pool, reused across sessions
   std::vector<Rec> recs;
   size_t used = 0;
+  // caller-owned device buffer of clk_cap slot pairs (16 bytes each) for self-stamping
+  // kernels, one pair per workgroup of each timed launch (or NULL)
+  unsigned long long* clk_buf = nullptr;
+  int64_t clk_cap = 0, clk_used = 0, clk_dropped = 0;
   bool on(int kind) const { return (mask >> kind) & 1u; }
-  // If `kind` is profiled, gives x a fresh pair of timing events for its next launch and
-  // records that launch's algorithmic bytes and flops.
-  hipError_t arm(int kind, double bytes, double flops, Exec& x);
+  // If `kind` is profiled, gives x a fresh pair of timing events for its next launch (or, for
+  // a self-stamping kernel of `grid` workgroups while clk_buf is attached, `grid` slot pairs)
+  // and records that launch's algorithmic bytes and flops.
+  hipError_t arm(int kind, double bytes, double flops, Exec& x, int64_t grid = 0);
   void destroy();
 };
 

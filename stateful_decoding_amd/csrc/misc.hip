@@ -186,8 +186,18 @@ MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0) {
 }
 
 // ---- kernel timing ---------------------------------------------------------------------------
-hipError_t Profiler::arm(int kind, double bytes, double flops, Exec& x) {
+hipError_t Profiler::arm(int kind, double bytes, double flops, Exec& x, int64_t grid) {
   if (!on(kind)) return hipSuccess;
+  if (clk_buf && grid > 0) {
+    if (clk_used + grid > clk_cap) {
+      ++clk_dropped;  // reported by rlt_profile_end
+      return hipSuccess;
+    }
+    x.clk = clk_buf + 2 * clk_used;
+    recs.push_back(Rec{kind, -1, clk_used, grid, bytes, flops});
+    clk_used += grid;
+    return hipSuccess;
+  }
   while (events.size() < used + 2) {
     hipEvent_t e;
     hipError_t err = hipEventCreate(&e);
@@ -196,7 +206,7 @@ hipError_t Profiler::arm(int kind, double bytes, double flops, Exec& x) {
   }
   x.start = events[used];
   x.stop = events[used + 1];
-  recs.push_back(Rec{kind, (int)used, bytes, flops});
+  recs.push_back(Rec{kind, (int)used, -1, 0, bytes, flops});
   used += 2;
   return hipSuccess;
 }
@@ -219,11 +229,14 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
   const double b = B, d = D.d, F = D.F, es = (double)D.es;
   const double act32 = b * d * 4, actd = b * d * es;
   // `call` launches one kernel on Exec x.
-#define RLT_TIMED(kind, bytes, flops, call)                                      \
-  do {                                                                           \
-    Exec x(st);                                                                  \
-    if (prof && (e = prof->arm(kind, bytes, flops, x)) != hipSuccess) return e;  \
-    if ((e = (call)) != hipSuccess) return e;                                    \
+  // the attention kernels (one workgroup per sequence and head) can time themselves
+  const int64_t attn_grid = (int64_t)B * D.H;
+#define RLT_TIMED(kind, bytes, flops, call)                                                 \
+  do {                                                                                      \
+    Exec x(st);                                                                             \
+    const int64_t grid = kind == RLT_K_SELF_ATTN || kind == RLT_K_CROSS_ATTN ? attn_grid : 0; \
+    if (prof && (e = prof->arm(kind, bytes, flops, x, grid)) != hipSuccess) return e;       \
+    if ((e = (call)) != hipSuccess) return e;                                               \
   } while (0)
   RLT_TIMED(RLT_K_GATE, 2 * d * d * es + actd + 2 * act32, 4 * b * d * d,
             gemm_gate(D, B, P, S, e_t, e_ld, x));

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     raw = ctypes.CDLL(sd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -102,6 +102,7 @@ def test_null_arguments_rejected_without_gpu(lib):
     assert lib.rlt_state_export(None, None, None, None, None, None, None, None) == 1
     assert lib.rlt_state_import(None, None, None, None, 0, 0, None) == 1
     assert lib.rlt_state_reset(None, None) == 1
+    assert lib.rlt_profile_clock(None, None, 0) == 1
     assert lib.rlt_state_position(None) == -1
     assert lib.rlt_memory_length(None) == -1
     assert b"NULL" in lib.rlt_last_error()

@@ -180,6 +180,44 @@ def test_kernel_timing_counts_sampled_launches():
     assert prof["cross_attn"]["bytes"] == pytest.approx(kv + act)
 
 
+def test_kernel_clock_timing_leaves_results_unchanged():
+    """With a clock buffer attached the attention kernels time themselves (every launch of
+    every row group), the other kinds keep their events, the trajectories stay bitwise equal to
+    an untimed run, and a buffer too small for the session is reported."""
+    cfg = cfg_small(n_layers=2, window=3)
+    B, T = 300, 9
+    p, e = inputs(cfg, B, T)
+    g = GpuRun(cfg, p, B, T)
+    ref = g.run(e)
+    groups = min(4, max(1, B // 128))  # row groups of at least 128 sequences
+    n_attn = T * cfg.n_layers * groups
+    slots = T * cfg.n_layers * B * cfg.n_heads  # one per workgroup of each launch of one kind
+    g.state.profile_clock(2 * slots)
+    g.state.reset()
+    g.mem.reset()
+    g.state.profile_begin(["qkv", "self_attn", "cross_attn"], token_stride=1)
+    got = g.run(e)
+    prof = g.state.profile_end()
+    assert np.array_equal(got, ref)
+    for k in ("qkv", "self_attn", "cross_attn"):
+        assert prof[k]["launches"] == n_attn, k
+        assert 0 < prof[k]["total_ms"] < 1e3, k
+    g.state.profile_clock(slots)  # room for one attention kind but not for both
+    g.state.reset()
+    g.mem.reset()
+    g.state.profile_begin(["self_attn", "cross_attn"], token_stride=1)
+    g.run(e)
+    with pytest.raises(sd.RLTError) as ex:
+        g.state.profile_end()
+    assert ex.value.status_name == "RLT_ERR_CAPACITY"
+    g.state.profile_clock(None)
+    g.state.reset()
+    g.mem.reset()
+    g.state.profile_begin(["cross_attn"], token_stride=1)
+    g.run(e)
+    assert g.state.profile_end()["cross_attn"]["launches"] == n_attn
+
+
 # --- full-size workloads, sampled sequences ---------------------------------------------------
 #
 # With these random weights the recurrence of the ~140M-scale and long-context (alpha = 1)
