@@ -246,6 +246,11 @@ typedef struct rlt_truncation {
 typedef struct rlt_timing {
   uint32_t kernels;     /* bit (1 << rlt_kernel) per kernel to time */
   int32_t token_stride; /* >= 1 */
+  void* clk;            /* NULL (events), or a device buffer, 16-byte aligned, in which the
+                         * backward attention kernels (RLT_K_BWD_SELF, RLT_K_BWD_CROSS) time
+                         * themselves as with rlt_profile_clock: 16 * H bytes per sequence of
+                         * each timed launch; too small: RLT_ERR_CAPACITY after the pass */
+  size_t clk_bytes;
 } rlt_timing;
 struct rlt_kernel_stats;
 

@@ -55,7 +55,8 @@ DETACH_BITS = {"state": 1, "window": 2}  # RLT_DETACH_STATE, RLT_DETACH_WINDOW
 
 
 class rlt_timing(ctypes.Structure):
-    _fields_ = [("kernels", ctypes.c_uint32), ("token_stride", c_int32)]
+    _fields_ = [("kernels", ctypes.c_uint32), ("token_stride", c_int32), ("clk", c_void_p),
+                ("clk_bytes", c_size_t)]
 
 
 class rlt_kernel_stats(ctypes.Structure):
@@ -232,7 +233,7 @@ class State:
             _check(self.lib.rlt_profile_clock(self.handle, None, 0))
             self._clk = None
             return
-        buf = torch.empty(int(slots) * 16, dtype=torch.uint8, device=self.buf.device)
+        buf = clock_buffer(slots, self.buf.device)
         _check(self.lib.rlt_profile_clock(self.handle, buf.data_ptr(), buf.numel()))
         self._clk = buf  # kept alive while attached
 
@@ -392,15 +393,25 @@ def grad_buffers(model: Model) -> dict:
             for k in WEIGHT_FIELDS}
 
 
+def clock_buffer(slots: int, device="cuda") -> torch.Tensor:
+    """Device buffer of `slots` clock slot pairs (16 bytes each): one per workgroup of each
+    self-timed launch, i.e. H per sequence and launch for the attention kernels."""
+    return torch.empty(int(slots) * 16, dtype=torch.uint8, device=device)
+
+
 def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
              de: torch.Tensor | None = None, s_traj: torch.Tensor | None = None,
              ws: torch.Tensor | None = None, stream=None, time_kernels=None,
-             token_stride: int = 1, segment: int = 0, detach=()):
+             token_stride: int = 1, segment: int = 0, detach=(),
+             clock: torch.Tensor | None = None):
     """Forward from s* over e [B, n, d] and backpropagation through time of the upstream
     gradients ds [B, n, d] float32 into `grads` (from grad_buffers; overwritten), de [B, n, d]
     float32 and s_traj [B, n, d] float32 (both optional); `ws` from bptt_workspace. With
     `time_kernels` (names from KERNEL_NAMES) the call waits for the stream and returns
     {name: {launches, total_ms, bytes, flops}} of those kernels' sampled launches.
+
+    `clock` (a device buffer from clock_buffer) makes the backward attention kernels time
+    themselves by their own clock stamps instead of events.
 
     segment = k > 0 truncates the backpropagation: at every start of a k-token segment the
     tensors named in `detach` ("state": the carried output s; "window": the self-attention
@@ -434,7 +445,8 @@ def rlt_bptt(model: Model, e: torch.Tensor, ds: torch.Tensor, grads: dict,
         mask = 0
         for k in time_kernels:
             mask |= 1 << KERNEL_NAMES.index(k)
-        timing = rlt_timing(mask, int(token_stride))
+        timing = rlt_timing(mask, int(token_stride), _ptr(clock),
+                            0 if clock is None else clock.numel() * clock.element_size())
         stats = (rlt_kernel_stats * len(KERNEL_NAMES))()
     _check(model.lib.rlt_bptt(model.handle, e.data_ptr(), B, n, ds.data_ptr(), _ptr(s_traj),
                               byref(g), _ptr(de), ws.data_ptr(), ws.numel() * ws.element_size(),

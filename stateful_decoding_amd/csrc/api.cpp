@@ -610,52 +610,25 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
   return ok();
 }
 
-rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride) {
-  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
-  if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");
-  if (token_stride < 1) return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", token_stride);
-  Profiler& P = state->prof;
-  P.stride = token_stride;
-  P.mask = mask;
+// Starts a session of P: clears its records and, with a clock buffer attached, queues the
+// clearing of every slot pair on stream st (ordered before the session's launches on st).
+static hipError_t session_start(Profiler& P, hipStream_t st) {
   P.recs.clear();
   P.used = 0;
   P.clk_used = 0;
   P.clk_dropped = 0;
-  if (P.clk_buf) {
-    // every slot pair starts at (max, 0): the kernels fold their stamps in with min / max
-    std::vector<unsigned long long> init(2 * (size_t)P.clk_cap);
-    for (size_t i = 0; i < init.size(); i += 2) {
-      init[i] = ~0ull;
-      init[i + 1] = 0ull;
-    }
-    const hipError_t e = hipMemcpy(P.clk_buf, init.data(), init.size() * 8, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      P.mask = 0;
-      return hip_fail(e, "clearing the clock buffer");
-    }
-  }
-  return ok();
+  return P.clear_clock(st);
 }
 
-rlt_status rlt_profile_clock(rlt_state* state, void* buf, size_t bytes) {
-  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
-  if (buf && (bytes < 16 || reinterpret_cast<uintptr_t>(buf) % 16))
-    return fail(RLT_ERR_ARG, "the clock buffer must be 16-byte aligned and hold one launch");
-  if (state->prof.mask) return fail(RLT_ERR_ARG, "a timing session is running");
-  state->prof.clk_buf = static_cast<unsigned long long*>(buf);
-  state->prof.clk_cap = buf ? (int64_t)(bytes / 16) : 0;
-  return ok();
-}
-
-rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
-  if (!state || !out) return fail(RLT_ERR_ARG, "state and out must be non-NULL");
-  Profiler& P = state->prof;
+// Ends a session of P: the durations of its timed launches, summed per kind into
+// out[RLT_K_COUNT] (zeroed first); *dropped = launches that did not fit the clock buffer.
+static hipError_t session_collect(Profiler& P, rlt_kernel_stats* out, int64_t* dropped) {
   for (int k = 0; k < RLT_K_COUNT; ++k) out[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
   hipError_t e = hipSuccess;
   std::vector<unsigned long long> clk;
   double ticks_per_ms = 0.0;
   if (P.clk_used > 0) {
-    // self-stamped launches may have run on any of the state's streams
+    // self-stamped launches may have run on any of the streams
     int dev = 0, khz = 0;
     e = hipDeviceSynchronize();
     if (e == hipSuccess) e = hipGetDevice(&dev);
@@ -694,16 +667,52 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
     o.bytes += r.bytes;
     o.flops += r.flops;
   }
+  *dropped = P.clk_dropped;
   P.mask = 0;
   P.recs.clear();
   P.used = 0;
-  const int64_t dropped = P.clk_dropped;
   P.clk_used = 0;
   P.clk_dropped = 0;
+  return e;
+}
+
+static bool clock_buffer_ok(const void* buf, size_t bytes) {
+  return !buf || (bytes >= 16 && reinterpret_cast<uintptr_t>(buf) % 16 == 0);
+}
+
+rlt_status rlt_profile_begin(rlt_state* state, uint32_t mask, int32_t token_stride) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  if (mask >> RLT_K_COUNT) return fail(RLT_ERR_ARG, "mask has bits beyond RLT_K_COUNT");
+  if (token_stride < 1) return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", token_stride);
+  Profiler& P = state->prof;
+  P.mask = 0;
+  // the state's launches may run on any stream: clear, then wait for the device
+  hipError_t e = session_start(P, nullptr);
+  if (e == hipSuccess && P.clk_buf) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "clearing the clock buffer");
+  P.stride = token_stride;
+  P.mask = mask;
+  return ok();
+}
+
+rlt_status rlt_profile_clock(rlt_state* state, void* buf, size_t bytes) {
+  if (!state) return fail(RLT_ERR_ARG, "state is NULL");
+  if (!clock_buffer_ok(buf, bytes))
+    return fail(RLT_ERR_ARG, "the clock buffer must be 16-byte aligned and hold one slot pair");
+  if (state->prof.mask) return fail(RLT_ERR_ARG, "a timing session is running");
+  state->prof.clk_buf = static_cast<unsigned long long*>(buf);
+  state->prof.clk_cap = buf ? (int64_t)(bytes / 16) : 0;
+  return ok();
+}
+
+rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out) {
+  if (!state || !out) return fail(RLT_ERR_ARG, "state and out must be non-NULL");
+  int64_t dropped = 0;
+  const hipError_t e = session_collect(state->prof, out, &dropped);
   if (e != hipSuccess) return hip_fail(e, "reading kernel timers");
   if (dropped > 0)
-    return fail(RLT_ERR_CAPACITY, "the clock buffer holds %lld launches; %lld more were not timed",
-                (long long)P.clk_cap, (long long)dropped);
+    return fail(RLT_ERR_CAPACITY, "the clock buffer holds %lld workgroup slots; %lld more "
+                "launches were not timed", (long long)state->prof.clk_cap, (long long)dropped);
   return ok();
 }
 
@@ -807,6 +816,8 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
       return fail(RLT_ERR_ARG, "timing has kernel bits beyond RLT_K_COUNT");
     if (timing->token_stride < 1)
       return fail(RLT_ERR_ARG, "token_stride must be >= 1, got %d", timing->token_stride);
+    if (!clock_buffer_ok(timing->clk, timing->clk_bytes))
+      return fail(RLT_ERR_ARG, "the clock buffer must be 16-byte aligned and hold one slot pair");
   }
   const Dims& D = model->D;
   const size_t need = train_layout(D, batch, n).total;
@@ -817,12 +828,16 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
              grads->w2,     grads->wmk,    grads->wmv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   Profiler prof;
+  hipError_t err = hipSuccess;
   if (timed) {
+    prof.clk_buf = static_cast<unsigned long long*>(timing->clk);
+    prof.clk_cap = timing->clk ? (int64_t)(timing->clk_bytes / 16) : 0;
+    err = session_start(prof, st);
+    if (err != hipSuccess) return hip_fail(err, "clearing the clock buffer");
     prof.mask = timing->kernels;
     prof.stride = timing->token_stride;
   }
   rlt_model* mm = const_cast<rlt_model*>(model);
-  hipError_t err = hipSuccess;
   if (batch >= 2 * kGroupRows && !mm->bwd_aux) {
     err = hipStreamCreateWithFlags(&mm->bwd_aux, hipStreamNonBlocking);
     if (err == hipSuccess) err = hipEventCreateWithFlags(&mm->bwd_fork, hipEventDisableTiming);
@@ -833,22 +848,16 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
                     trunc ? trunc->detach : 0u, st,
                     batch >= 2 * kGroupRows ? mm->bwd_aux : nullptr, mm->bwd_fork, mm->bwd_join,
                     timed ? &prof : nullptr);
+  int64_t dropped = 0;
   if (timed) {
-    for (int k = 0; k < RLT_K_COUNT; ++k) stats[k] = rlt_kernel_stats{0, 0.0, 0.0, 0.0};
     if (err == hipSuccess) err = hipStreamSynchronize(st);
-    for (const Profiler::Rec& r : prof.recs) {
-      if (err != hipSuccess) break;
-      float ms = 0.f;
-      err = hipEventElapsedTime(&ms, prof.events[r.ev], prof.events[r.ev + 1]);
-      rlt_kernel_stats& o = stats[r.kind];
-      o.launches += 1;
-      o.total_ms += ms;
-      o.bytes += r.bytes;
-      o.flops += r.flops;
-    }
+    if (err == hipSuccess) err = session_collect(prof, stats, &dropped);
     prof.destroy();
   }
   if (err != hipSuccess) return hip_fail(err, "backward pass");
+  if (dropped > 0)
+    return fail(RLT_ERR_CAPACITY, "the clock buffer holds %lld workgroup slots; %lld more "
+                "launches were not timed", (long long)prof.clk_cap, (long long)dropped);
   return ok();
 }
 

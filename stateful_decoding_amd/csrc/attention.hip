@@ -138,22 +138,17 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
   }
 }
 
-// The two uses get kernels of their own, so that traces tell them apart. With clk != NULL
-// (a timed launch) every workgroup writes the GPU's constant-rate clock to its own slot pair:
-// clk[2 blockIdx] when it starts, clk[2 blockIdx + 1] when all its waves are done. The host
-// takes the earliest start and the latest end, so the launch measures itself with nothing
-// queued around it, and no two workgroups write the same address.
+// The two uses get kernels of their own, so that traces tell them apart. clk != NULL: a timed
+// launch (LaunchClock).
 template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
                                              int64_t bh_stride, const int64_t* pos,
                                              int64_t t_uniform, int window, int H, float scale,
                                              T* out, unsigned long long* clk) {
-  if (clk && threadIdx.x == 0) clk[2 * blockIdx.x] = wall_clock64();
+  const LaunchClock lc{clk};
+  lc.start();
   attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
-  if (clk) {
-    __syncthreads();
-    if (threadIdx.x == 0) clk[2 * blockIdx.x + 1] = wall_clock64();
-  }
+  lc.stop();
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_window(

@@ -502,7 +502,7 @@ struct BwdState {
 // query-projection backward's operand), lse = m + log l and D (for the memory gradients formed
 // after the walk), and a dtype copy of do (same use).
 template <typename T, int HD, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_xattn_back(
+__device__ __forceinline__ void xattn_back_body(
     const float* __restrict__ q, const float* __restrict__ dout, const T* __restrict__ K,
     const T* __restrict__ V, int64_t bh_stride, int ntok, int H, float scale,
     T* __restrict__ dq, float* __restrict__ lse, float* __restrict__ dlt, T* __restrict__ do_t) {
@@ -625,6 +625,18 @@ __global__ __launch_bounds__(NW * kWave) void k_xattn_back(
   }
 }
 
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_xattn_back(
+    const float* __restrict__ q, const float* __restrict__ dout, const T* __restrict__ K,
+    const T* __restrict__ V, int64_t bh_stride, int ntok, int H, float scale,
+    T* __restrict__ dq, float* __restrict__ lse, float* __restrict__ dlt, T* __restrict__ do_t,
+    unsigned long long* clk) {
+  const LaunchClock lc{clk};
+  lc.start();
+  xattn_back_body<T, HD, NW, U>(q, dout, K, V, bh_stride, ntok, H, scale, dq, lse, dlt, do_t);
+  lc.stop();
+}
+
 // Self-attention backward of token t for one (sequence, head) per workgroup.
 //   dq_t: one online pass over the window keys j = lo..t (lo = max(0, t - W + 1)) of the layer's
 //         key/value history, as for the memory prefix; it also yields lse_t and D_t, which go
@@ -634,7 +646,7 @@ __global__ __launch_bounds__(NW * kWave) void k_xattn_back(
 //         p_t't = exp(scale q_t'.k_t - lse_t') and dz = p (do_t'.v_t - D_t'), from the saved
 //         queries and the rings. Writes [dq | dk | dv] (dtype) to out [M][3d].
 template <typename T, int HD, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_swa_back(
+__device__ __forceinline__ void swa_back_body(
     const float* __restrict__ qs, const float* __restrict__ dout, const T* __restrict__ K,
     const T* __restrict__ V, int64_t n, int64_t t, int64_t hi_cap, int W, int B, int H,
     float scale, T* __restrict__ ring_do, float* __restrict__ ring_lse,
@@ -852,6 +864,20 @@ __global__ __launch_bounds__(NW * kWave) void k_swa_back(
     out[ro + d + tid] = to_elem<T>(k);
     out[ro + 2 * d + tid] = to_elem<T>(v);
   }
+}
+
+template <typename T, int HD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_swa_back(
+    const float* __restrict__ qs, const float* __restrict__ dout, const T* __restrict__ K,
+    const T* __restrict__ V, int64_t n, int64_t t, int64_t hi_cap, int W, int B, int H,
+    float scale, T* __restrict__ ring_do, float* __restrict__ ring_lse,
+    float* __restrict__ ring_dlt, T* __restrict__ out,
+    unsigned long long* clk) {
+  const LaunchClock lc{clk};
+  lc.start();
+  swa_back_body<T, HD, NW, U>(qs, dout, K, V, n, t, hi_cap, W, B, H, scale, ring_do, ring_lse,
+                              ring_dlt, out);
+  lc.stop();
 }
 
 // ---- memory gradients after the walk ------------------------------------------------------------
@@ -1175,7 +1201,7 @@ static hipError_t xattn_back(int BH, const float* q, const float* dout, const T*
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
 #define RLT_XB(NW)                                                                             \
   return launch(k_xattn_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, q, dout, K, V,        \
-                bh_stride, ntok, H, scale, dq, lse, dlt, do_t)
+                bh_stride, ntok, H, scale, dq, lse, dlt, do_t, x.clk)
   if (nw == 4) RLT_XB(4);
   if (nw == 8) RLT_XB(8);
   RLT_XB(16);
@@ -1190,7 +1216,7 @@ static hipError_t swa_back(int BH, int B, const float* qs, const float* dout, co
   const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
 #define RLT_SB(NW)                                                                              \
   return launch(k_swa_back<T, HD, NW, 4>, dim3(BH), dim3(NW * kWave), x, qs, dout, K, V, n, t,   \
-                hi_cap, W, B, H, scale, ring_do, ring_lse, ring_dlt, out)
+                hi_cap, W, B, H, scale, ring_do, ring_lse, ring_dlt, out, x.clk)
   if (nw == 4) RLT_SB(4);
   if (nw == 8) RLT_SB(8);
   RLT_SB(16);
@@ -1251,9 +1277,10 @@ struct Timer {
   Profiler* prof;
   hipStream_t st;
   hipError_t err = hipSuccess;
-  Exec at(int kind, double bytes, double flops, bool sampled = true) {
+  // grid > 0: a self-timing kernel of `grid` workgroups (clock slots when attached)
+  Exec at(int kind, double bytes, double flops, bool sampled = true, int64_t grid = 0) {
     Exec x(st);
-    if (prof && sampled && err == hipSuccess) err = prof->arm(kind, bytes, flops, x);
+    if (prof && sampled && err == hipSuccess) err = prof->arm(kind, bytes, flops, x, grid);
     return x;
   }
 };
@@ -1352,7 +1379,7 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                               w.template at<float>(TL.dlt) + stat,
                               w.template saved<T>(TL.docs, l, i),
                               tm.at(RLT_K_BWD_CROSS, ntok * b * 2 * d * es + 2 * rows32 +
-                                        2 * rowsT + 8 * b * H, 8 * b * d * ntok, sampled)));
+                                        2 * rowsT + 8 * b * H, 8 * b * d * ntok, sampled, BH)));
     RLT_TRY(run_step_gemm<T>(B, d, d, bw + bo.wcq + l * dd, ARows<T>{ycq, d, B}, to_dn,
                              proj(d, d, rows32)));
     T* yo = w.chunk(TL.yo, l, d, li);
@@ -1374,7 +1401,7 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
                             w.template at<float>(TL.dvacc) + (int64_t)L * D.W * Bt * H + rs, yqkv,
                             tm.at(RLT_K_BWD_SELF, nk * b * 2 * d * es + nq * b * d * (4 + es) +
                                       2 * rows32 + 4 * rowsT, (10 * nk + 8 * nq) * b * d,
-                                  sampled)));
+                                  sampled, BH)));
     RLT_TRY(run_step_gemm<T>(B, d, 3 * d, bw + bo.wqkv + (int64_t)l * 3 * dd,
                              ARows<T>{yqkv, 3 * d, B}, to_dn, proj(d, 3 * d, rows32)));
     RLT_TRY(launch(k_norm_back<T>, dim3(B), dim3(kThreads), other(nb + (l > 0 ? nrb : 0)),

@@ -16,6 +16,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWave = 64;
 
+// Self-timing of a launch (clk != NULL): every workgroup writes the GPU's constant-rate clock
+// to its own slot pair, clk[2 blockIdx] when it starts and clk[2 blockIdx + 1] when all its
+// waves are done; the host takes the earliest start and the latest end. No two workgroups
+// write the same address and nothing is queued around the launch.
+struct LaunchClock {
+  unsigned long long* clk;
+  __device__ __forceinline__ void start() const {
+    if (clk && threadIdx.x == 0) clk[2 * blockIdx.x] = wall_clock64();
+  }
+  __device__ __forceinline__ void stop() const {
+    if (clk) {
+      __syncthreads();
+      if (threadIdx.x == 0) clk[2 * blockIdx.x + 1] = wall_clock64();
+    }
+  }
+};
+
 // Elements of T in one 16-byte vector.
 template <typename T> struct Vec16;
 template <> struct Vec16<float> { static constexpr int N = 4; };

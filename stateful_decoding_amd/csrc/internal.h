@@ -166,6 +166,9 @@ struct Profiler {
   // a self-stamping kernel of `grid` workgroups while clk_buf is attached, `grid` slot pairs)
   // and records that launch's algorithmic bytes and flops.
   hipError_t arm(int kind, double bytes, double flops, Exec& x, int64_t grid = 0);
+  // Sets every clock slot pair to (max, 0) on stream st (a workgroup that left no stamps then
+  // shows as a start after its end).
+  hipError_t clear_clock(hipStream_t st) const;
   void destroy();
 };
 

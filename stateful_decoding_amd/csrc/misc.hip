@@ -186,6 +186,22 @@ MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0) {
 }
 
 // ---- kernel timing ---------------------------------------------------------------------------
+// Sets `pairs` clock slot pairs to (max, 0), so that a workgroup that left no stamps shows.
+__global__ void k_clock_clear(unsigned long long* __restrict__ p, int64_t pairs) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    p[2 * i] = ~0ull;
+    p[2 * i + 1] = 0ull;
+  }
+}
+
+hipError_t Profiler::clear_clock(hipStream_t st) const {
+  if (!clk_buf || clk_cap <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((clk_cap + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_clock_clear, dim3((unsigned)blocks), dim3(256), 0, st, clk_buf, clk_cap);
+  return hipGetLastError();
+}
+
 hipError_t Profiler::arm(int kind, double bytes, double flops, Exec& x, int64_t grid) {
   if (!on(kind)) return hipSuccess;
   if (clk_buf && grid > 0) {

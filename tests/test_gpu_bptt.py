@@ -278,3 +278,34 @@ def test_detaching_the_state_alone_leaves_the_window_path_open():
     leak = np.linalg.norm(out[("state",)][:, :k], axis=-1)
     assert np.all(leak > 0)
     assert not np.any(out[("state", "window")][:, :k])
+
+
+def test_bptt_clock_timing_leaves_gradients_unchanged():
+    """The backward attention kernels timed by their own clock stamps (every launch of both
+    row groups) give the same gradients bitwise as an untimed pass; a clock buffer too small
+    for the pass is reported after it."""
+    cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=4)
+    B, T = 272, 10
+    p, e = inputs(cfg, B, T, seed=4)
+    model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
+    ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
+    ds = torch.randn(B, T, cfg.d, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    ws = sd.bptt_workspace(model, B, T)
+    ref = sd.grad_buffers(model)
+    sd.rlt_bptt(model, ed, ds, ref, ws=ws)
+    slots = T * cfg.n_layers * B * cfg.n_heads  # one per workgroup of each launch of one kind
+    got = sd.grad_buffers(model)
+    stats = sd.rlt_bptt(model, ed, ds, got, ws=ws, time_kernels=["bwd_cross_attn",
+                                                                 "bwd_self_attn"],
+                        clock=sd.clock_buffer(2 * slots))
+    torch.cuda.synchronize()
+    for k in sd.binding.WEIGHT_FIELDS:
+        assert torch.equal(got[k], ref[k]), k
+    groups = 2  # 272 sequences: two row groups
+    for k in ("bwd_cross_attn", "bwd_self_attn"):
+        assert stats[k]["launches"] == T * cfg.n_layers * groups, k
+        assert 0 < stats[k]["total_ms"] < 1e3, k
+    with pytest.raises(sd.RLTError) as ex:
+        sd.rlt_bptt(model, ed, ds, got, ws=ws, time_kernels=["bwd_cross_attn", "bwd_self_attn"],
+                    clock=sd.clock_buffer(slots))
+    assert ex.value.status_name == "RLT_ERR_CAPACITY"
