@@ -322,18 +322,104 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tokens(int N, int K, const T*
   ep.template tile<FM, FN>(acc, rw + (lane >> 4) * 4, cw, lane);
 }
 
-// Tile shape of the memory projection: (WM, WN, FM, FN).
+// The same product for bf16 with 128 x 128 workgroup tiles staged through LDS: every k-step's
+// 8 A fragments (from the loader) and 8 B fragments are fetched once per workgroup, one 16-byte
+// load per thread and operand pair, into one of two LDS buffers while the other is multiplied;
+// each wave then reads its 4 + 4 fragments from LDS (64 x 64 per wave). The next k-step's loads
+// are issued before the current one's MFMAs. Every output element accumulates its k-steps in
+// the same order with the same instruction as k_gemm_tokens, so the results are identical.
+template <class AL, class EP>
+__global__ __launch_bounds__(kThreads) void k_gemm_tokens_lds(int N, int K,
+                                                             const bf16* __restrict__ Wt, AL al,
+                                                             EP ep) {
+  constexpr int FM = 4, FN = 4, BM = 128, BN = 128;
+  __shared__ __attribute__((aligned(16))) u32x4 as[2][8][kWave];
+  __shared__ __attribute__((aligned(16))) u32x4 bs[2][8][kWave];
+  const int tiles_n = N / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int ksteps = K / 32, kl = (lane >> 4) * 8;
+  // this thread stages fragments wave and wave + 4 of A (row tiles) and of B (column tiles)
+  int arow[2];
+  const bf16* bp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    arow[u] = tm * BM + (wave + 4 * u) * 16 + (lane & 15);
+    bp[u] = Wt + ((((int64_t)(tn * 8 + wave + 4 * u) * ksteps) << 6) + lane) * 8;
+  }
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ra[2], rb[2];
+  float unused = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    ra[u] = __builtin_bit_cast(u32x4, al.load(arow[u], kl, unused).v);
+    rb[u] = ld16(bp[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    as[0][wave + 4 * u][lane] = ra[u];
+    bs[0][wave + 4 * u][lane] = rb[u];
+  }
+  __syncthreads();
+  for (int s = 0; s < ksteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < ksteps) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        ra[u] = __builtin_bit_cast(u32x4, al.load(arow[u], (s + 1) * 32 + kl, unused).v);
+        rb[u] = ld16(bp[u] + (s + 1) * 512);
+      }
+    }
+    Frag<bf16> a[FM], b[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i].from_raw(&as[cur][wm * 4 + i][lane]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j].from_raw(&bs[cur][wn * 4 + j][lane]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_16x16x32(acc[i][j], a[i], b[j]);
+    if (s + 1 < ksteps) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        as[cur ^ 1][wave + 4 * u][lane] = ra[u];
+        bs[cur ^ 1][wave + 4 * u][lane] = rb[u];
+      }
+    }
+    __syncthreads();
+  }
+  ep.template tile<FM, FN>(acc, tm * BM + wm * 64 + (lane >> 4) * 4, tn * BN + wn * 64, lane);
+}
+
+// Tile shape of the register-tiled token GEMM: (WM, WN, FM, FN).
 struct Shape {
   int wm, wn, fm, fn;
 };
 constexpr Shape kBig{2, 2, 2, 2};  // 64 x 64
 
+// C = A W over M rows: bf16 products whose N is a multiple of 128 and that still make at least
+// 1024 workgroups of 128 x 128 (four per compute unit) take the LDS-staged kernel, the rest the
+// register-tiled one with (WM, WN, FM, FN) tiles, which makes four times as many workgroups.
 template <typename T, int WM, int WN, int FM, int FN, class AL, class EP>
 static hipError_t run_gemm(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
                            const Exec& st) {
+  if (K % 32 != 0 || M <= 0) return hipErrorInvalidValue;
+  if constexpr (std::is_same<T, bf16>::value) {
+    const int64_t blocks = (int64_t)((M + 127) / 128) * (N / 128);
+    if (N % 128 == 0 && blocks >= 1024) {
+      if (blocks > INT32_MAX) return hipErrorInvalidValue;
+      return launch(k_gemm_tokens_lds<AL, EP>, dim3((unsigned)blocks), dim3(kThreads), st, N, K,
+                    static_cast<const bf16*>(Wt), al, ep);
+    }
+  }
   constexpr int BM = 16 * FM * WM, BN = 16 * FN * WN;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
-  if (N % BN != 0 || K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (N % BN != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
   return launch(k_gemm_tokens<T, WM, WN, FM, FN, AL, EP>, dim3((unsigned)blocks), dim3(kThreads),
                 st, N, K, static_cast<const T*>(Wt), al, ep);
 }

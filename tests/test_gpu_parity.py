@@ -78,6 +78,24 @@ def test_memory_projection_matches_oracle():
         assert max_rel_l2(got[:, :, :, :19], ref) < 1e-5
 
 
+def test_memory_projection_bf16_large_ragged_rows():
+    """A bf16 projection of 37 x 451 = 16,687 rows (not a multiple of the 128-row tiles) into
+    N = 2 groups x 2d = 1024 columns: enough workgroups for the LDS-staged token GEMM. Each
+    entry is a bf16 rounding of an fp32-accumulated product, so the relative L2 error against
+    the float64 oracle is bounded by half a bf16 ulp (2^-9) plus accumulation error."""
+    cfg = cfg_small(dtype="bf16", d=256, n_heads=4, head_dim=64, ffn=512, n_groups=2)
+    B, T = 37, 451
+    p, e = inputs(cfg, B, T, seed=8)
+    g = GpuRun(cfg, p, B, T)
+    sd.rlt_memproj(g.model, g.mem, g.to_dev(e), 0)
+    K, V = (x.float().cpu().numpy() for x in g.mem.views())
+    km, vm = oracle.memory_projection(oracle.prepare_params(p), e.astype(np.float64))
+    H, hd = cfg.n_heads, cfg.head_dim
+    for got, ref in ((K, km), (V, vm)):
+        ref = ref.reshape(2, B, T, H, hd).transpose(0, 1, 3, 2, 4)
+        assert max_rel_l2(got[:, :, :, :T], ref) < 2.5e-3
+
+
 @pytest.mark.parametrize("B", [6, 280])
 def test_decoder_steps_equal_run_sequence_and_split(B):
     cfg = cfg_small(window=4, n_groups=2)
