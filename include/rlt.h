@@ -297,8 +297,10 @@ size_t rlt_bptt_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
  * t % token_stride == 0 and in every launch outside the token loops, and the call waits for the
  * stream and writes RLT_K_COUNT entries to `stats` (host array, required then).
  * Batches of 256 or more sequences run as two row groups, the second on a stream the model
- * creates on first use and keeps until rlt_model_destroy: calls of rlt_bptt on one model must
- * not overlap (they share that stream and its events); other calls on the model may. */
+ * creates on first use, and the weight gradients of each chunk of tokens run on a third such
+ * stream while the walk goes on; both are kept until rlt_model_destroy. Calls of rlt_bptt on
+ * one model must not overlap (they share those streams and their events); other calls on the
+ * model may. */
 rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_t n,
                     const float* ds, float* s_traj, const rlt_grads* grads, float* de, void* ws,
                     size_t ws_bytes, const rlt_truncation* trunc, const struct rlt_timing* timing,

@@ -22,6 +22,9 @@ struct rlt_model {
   // second stream and fork/join events of rlt_bptt's row groups, created on its first call
   hipStream_t bwd_aux = nullptr;
   hipEvent_t bwd_fork = nullptr, bwd_join = nullptr;
+  // the backward pass's weight-gradient stream and its events (walked[2], done[2])
+  hipStream_t bwd_grads = nullptr;
+  hipEvent_t bwd_gev[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 
 struct rlt_state {
@@ -265,6 +268,9 @@ void rlt_model_destroy(rlt_model* model) {
   if (model->bwd_aux) (void)hipStreamDestroy(model->bwd_aux);
   if (model->bwd_fork) (void)hipEventDestroy(model->bwd_fork);
   if (model->bwd_join) (void)hipEventDestroy(model->bwd_join);
+  if (model->bwd_grads) (void)hipStreamDestroy(model->bwd_grads);
+  for (hipEvent_t ev : model->bwd_gev)
+    if (ev) (void)hipEventDestroy(ev);
   delete model;
 }
 
@@ -844,10 +850,26 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
     if (err == hipSuccess) err = hipEventCreateWithFlags(&mm->bwd_join, hipEventDisableTiming);
     if (err != hipSuccess) return hip_fail(err, "creating the backward pass's second stream");
   }
+  if (!mm->bwd_grads) {
+    // created as a whole or not at all, so a failed attempt is retried by the next call
+    hipStream_t gs = nullptr;
+    hipEvent_t gev[4] = {nullptr, nullptr, nullptr, nullptr};
+    err = hipStreamCreateWithFlags(&gs, hipStreamNonBlocking);
+    for (int i = 0; i < 4 && err == hipSuccess; ++i)
+      err = hipEventCreateWithFlags(&gev[i], hipEventDisableTiming);
+    if (err != hipSuccess) {
+      if (gs) (void)hipStreamDestroy(gs);
+      for (hipEvent_t ev : gev)
+        if (ev) (void)hipEventDestroy(ev);
+      return hip_fail(err, "creating the backward pass's gradient stream");
+    }
+    mm->bwd_grads = gs;
+    for (int i = 0; i < 4; ++i) mm->bwd_gev[i] = gev[i];
+  }
   err = launch_bptt(D, batch, n, model->P, e, ds, s_traj, g, de, ws, trunc ? trunc->segment : 0,
                     trunc ? trunc->detach : 0u, st,
                     batch >= 2 * kGroupRows ? mm->bwd_aux : nullptr, mm->bwd_fork, mm->bwd_join,
-                    timed ? &prof : nullptr);
+                    mm->bwd_grads, mm->bwd_gev, timed ? &prof : nullptr);
   int64_t dropped = 0;
   if (timed) {
     if (err == hipSuccess) err = hipStreamSynchronize(st);

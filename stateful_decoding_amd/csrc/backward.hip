@@ -94,6 +94,9 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.rinv = take(b * 3 * 4);
   t.dkacc = take(L * D.W * b * d * es);      // window-backward rings: do of the last W tokens
   t.dvacc = take(2 * L * D.W * b * H * 4);  // and their lse, D
+  // per-chunk operand rows of the weight gradients, twice: the walk fills one copy while the
+  // gradients of the previous chunk read the other
+  const size_t c0 = o;
   t.ca = take(L * Mc * d * es);
   t.cc = take(L * Mc * d * es);
   t.cf = take(L * Mc * d * es);
@@ -107,13 +110,16 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.pg = take((3 * L + 1) * Mc * d * 4);
   t.xg = take(Mc * 2 * d * es);
   t.yg = take(Mc * d * es);
+  t.cspan = o - c0;
+  take(t.cspan);
   t.part = take((3 * L + 1) * kRowSplits * d * 4);
   t.dkv = take(b * N * 2 * d * es);
   // weight-gradient operands transposed to [features][rows] (rows padded to 32)
   const size_t Mp = (Mc + 31) / 32 * 32;
   t.o2 = take((b + 15) / 16 * 16 * d * es);  // second attention-output operand (forward)
-  t.tx = take(Mp * std::max(2 * d, F) * es);
-  t.ty = take(Mp * std::max(3 * d, 2 * F) * es);
+  // (one matrix per layer: the weight gradients of all layers are formed in one batch)
+  t.tx = take(L * Mp * std::max(2 * d, F) * es);
+  t.ty = take(L * Mp * std::max(3 * d, 2 * F) * es);
   t.total = o;
   return t;
 }
@@ -1099,10 +1105,14 @@ __global__ __launch_bounds__(kThreads) void k_mem_back_mfma(
 
 // dst[frag_off(c, m, Mp / 32)] = src[m][c] for m < M, zero for M <= m < Mp. One workgroup per
 // 32 x 32 tile, staged in LDS; each store is 8 consecutive rows of one column (16 bytes bf16).
+// blockIdx.z = z transposes matrix z of a batch: src + z src_z, dst + z dst_z.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_mfrag(const T* __restrict__ src, int64_t ld,
-                                                    int64_t M, int64_t Mp, T* __restrict__ dst) {
+                                                    int64_t M, int64_t Mp, T* __restrict__ dst,
+                                                    int64_t src_z, int64_t dst_z) {
   __shared__ T tile[32][33];
+  src += blockIdx.z * src_z;
+  dst += blockIdx.z * dst_z;
   const int64_t m0 = (int64_t)blockIdx.y * 32;
   const int c0 = blockIdx.x * 32;
   const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
@@ -1126,6 +1136,7 @@ struct AMfrag {  // A = [rows][K] in fragment order (ksteps = K / 32); token-GEM
   const T* a;
   int ksteps;
   int M;
+  int64_t zs = 0;  // elements between the operands of consecutive products of a batch
   __device__ Frag<T> load(int row, int k, float&) const {
     Frag<T> f;
     if (row < M) f.load(a + frag_off(row, k, ksteps));
@@ -1144,6 +1155,7 @@ struct WDst {
 struct EpiAddSplit {
   WDst dst;
   int M;
+  int64_t zs = 0;  // elements between the outputs of consecutive products of a batch
   template <int FM, int FN>
   __device__ void tile(const f32x4 (&acc)[FM][FN], int rbase, int cwave, int lane) const {
 #pragma unroll
@@ -1159,6 +1171,19 @@ struct EpiAddSplit {
         }
   }
 };
+
+template <typename T>
+__device__ __forceinline__ AMfrag<T> batch_at(const AMfrag<T>& a, int z) {
+  AMfrag<T> r = a;
+  r.a += z * a.zs;
+  return r;
+}
+__device__ __forceinline__ EpiAddSplit batch_at(const EpiAddSplit& e, int z) {
+  EpiAddSplit r = e;
+  for (int i = 0; i < 3; ++i)
+    if (r.dst.p[i]) r.dst.p[i] += z * e.zs;
+  return r;
+}
 
 // ---- host side ---------------------------------------------------------------------------------
 
@@ -1186,11 +1211,33 @@ static hipError_t wgrad(const T* X, int64_t ldx, const T* Y, int64_t ldy, int64_
   if (K % 64 || N % 64 || M <= 0 || M > INT32_MAX / 2) return hipErrorInvalidValue;
   const int64_t Mp = (M + 31) / 32 * 32;
   RLT_TRY(launch(k_mfrag<T>, dim3(K / 32, (unsigned)(Mp / 32)), dim3(kThreads), xt, X, ldx, M, Mp,
-                 tx));
+                 tx, (int64_t)0, (int64_t)0));
   RLT_TRY(launch(k_mfrag<T>, dim3(N / 32, (unsigned)(Mp / 32)), dim3(kThreads), Exec(xt.st), Y,
-                 ldy, M, Mp, ty));
+                 ldy, M, Mp, ty, (int64_t)0, (int64_t)0));
   return run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(
       K, N, (int)Mp, ty, AMfrag<T>{tx, (int)(Mp / 32), K}, EpiAddSplit{dst, K}, x);
+}
+
+// The same for the L layers of one weight kind at once (bf16, K and N multiples of 128): layer l
+// reads X + l xz and Y + l yz and adds into the destinations shifted by l dz; one transpose
+// launch per operand and one batched GEMM.
+template <typename T>
+static hipError_t wgrad_layers(const T* X, int64_t ldx, int64_t xz, const T* Y, int64_t ldy,
+                               int64_t yz, int64_t M, int K, int N, int L, WDst dst, int64_t dz,
+                               T* tx, T* ty, const Exec& xt, const Exec& x) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (K % 128 || N % 128 || M <= 0 || M > INT32_MAX / 2 || L < 1) return hipErrorInvalidValue;
+    const int64_t Mp = (M + 31) / 32 * 32;
+    RLT_TRY(launch(k_mfrag<T>, dim3(K / 32, (unsigned)(Mp / 32), L), dim3(kThreads), xt, X, ldx,
+                   M, Mp, tx, xz, (int64_t)K * Mp));
+    RLT_TRY(launch(k_mfrag<T>, dim3(N / 32, (unsigned)(Mp / 32), L), dim3(kThreads),
+                   Exec(xt.st), Y, ldy, M, Mp, ty, yz, (int64_t)N * Mp));
+    return run_gemm_batched(K, N, (int)Mp, L, ty, (int64_t)N * Mp,
+                            AMfrag<T>{tx, (int)(Mp / 32), K, (int64_t)K * Mp},
+                            EpiAddSplit{dst, K, dz}, x);
+  } else {
+    return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, int HD>
@@ -1241,17 +1288,23 @@ struct Walk {  // pointers into the workspace of one call, for the rows [b0, b0 
   const TrainLayout& TL;
   void* ws;
   int b0 = 0, rows = 0;
+  size_t cpar = 0;  // byte offset of the chunk-buffer copy in use (0 or TL.cspan)
   template <typename P>
   P* at(size_t off) const {
     return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
   }
+  // a chunk buffer (ca .. yg) in the copy in use
+  template <typename P>
+  P* cat(size_t off) const {
+    return at<P>(off + cpar);
+  }
   // rows of chunk-local token li in a per-layer chunk buffer of `width` columns
   T* chunk(size_t base, int l, int64_t width, int64_t li) const {
-    return at<T>(base) + ((int64_t)l * TL.Mc + li * B + b0) * width;
+    return cat<T>(base) + ((int64_t)l * TL.Mc + li * B + b0) * width;
   }
   // fp32 gain/bias-gradient rows: matrix m (3 l + which, or 3 L for the gate bias)
   float* pg(int m, int64_t li) const {
-    return at<float>(TL.pg) + ((int64_t)m * TL.Mc + li * B + b0) * D.d;
+    return cat<float>(TL.pg) + ((int64_t)m * TL.Mc + li * B + b0) * D.d;
   }
   // [L][n][B][d] saved rows of layer l, token i
   template <typename P>
@@ -1412,13 +1465,13 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
   // gated merge: recompute g, then dz, then de_t and the carry to s_{t-1}
   const T* et = e + i * d;
   const float* s_prev = w.template at<float>(TL.s_hist) + (i * Bt + b0) * d;
-  T* yg = w.template at<T>(TL.yg) + (li * Bt + b0) * d;
+  T* yg = w.template cat<T>(TL.yg) + (li * Bt + b0) * d;
   {
     AGate<T> al{et, n * d, s_prev, D.alpha, B, d};
     EpiGateBack<T> ep;
     ep.e = et; ep.lde = n * d; ep.s = s_prev; ep.b = P.b_gate; ep.dres = dres; ep.alpha = D.alpha;
     ep.dz = yg; ep.dz32 = w.pg(3 * L, li); ep.g = gsave;
-    ep.xg = w.template at<T>(TL.xg) + (li * Bt + b0) * 2 * d; ep.M = B; ep.d = d;
+    ep.xg = w.template cat<T>(TL.xg) + (li * Bt + b0) * 2 * d; ep.M = B; ep.d = d;
     RLT_TRY(run_step_gemm<T>(B, d, 2 * d, P.w_gate_t, al, ep,
                              proj(d, 2 * d, 3 * rows32 + rowsT + b * 2 * d * es)));
   }
@@ -1450,21 +1503,46 @@ static hipError_t chunk_grads(const Walk<T>& w, const GradPtrs& g, int64_t i0, i
                     tm.at(RLT_K_BWD_WGRAD, rows * (K + N) * es + (double)K * N * 8,
                           2.0 * rows * K * N));
   };
-  for (int l = 0; l < L; ++l) {
-    RLT_TRY(gw(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, d, 3 * d,
-               WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}));
-    RLT_TRY(gw(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, d, d,
-               WDst{{g.wo + l * dd, nullptr, nullptr}, d}));
-    RLT_TRY(gw(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, d, d,
-               WDst{{g.wcq + l * dd, nullptr, nullptr}, d}));
-    RLT_TRY(gw(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, d, d,
-               WDst{{g.wco + l * dd, nullptr, nullptr}, d}));
-    RLT_TRY(gw(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, d, 2 * F,
-               WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}));
-    RLT_TRY(gw(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, F, d,
-               WDst{{g.w2 + l * dF, nullptr, nullptr}, d}));
+  if (std::is_same<T, bf16>::value && d % 128 == 0 && F % 128 == 0) {
+    // every layer of one weight kind in one batch: layer strides of the chunk buffers (Mc rows
+    // of `width`), of the saved rows ([L][n][B][d]) and of the gradients
+    const int64_t Mc = TL.Mc, sz = w.n * B * d;
+    auto gl = [&](const T* X, int64_t ldx, int64_t xz, const T* Y, int64_t ldy, int64_t yz,
+                  int K, int N, WDst dst, int64_t dz) {
+      return wgrad_layers<T>(X, ldx, xz, Y, ldy, yz, rows, K, N, L, dst, dz, tx, ty,
+                             tm.at(RLT_K_BWD_OTHER, L * 2.0 * rows * (K + N) * es, 0),
+                             tm.at(RLT_K_BWD_WGRAD, L * (rows * (K + N) * es + (double)K * N * 8),
+                                   L * 2.0 * rows * K * N));
+    };
+    RLT_TRY(gl(w.chunk(TL.ca, 0, d, 0), d, Mc * d, w.chunk(TL.yqkv, 0, 3 * d, 0), 3 * d,
+               Mc * 3 * d, d, 3 * d, WDst{{g.wq, g.wk, g.wv}, d}, dd));
+    RLT_TRY(gl(w.template saved<T>(TL.os, 0, i0), d, sz, w.chunk(TL.yo, 0, d, 0), d, Mc * d, d,
+               d, WDst{{g.wo, nullptr, nullptr}, d}, dd));
+    RLT_TRY(gl(w.chunk(TL.cc, 0, d, 0), d, Mc * d, w.chunk(TL.ycq, 0, d, 0), d, Mc * d, d, d,
+               WDst{{g.wcq, nullptr, nullptr}, d}, dd));
+    RLT_TRY(gl(w.template saved<T>(TL.ocs, 0, i0), d, sz, w.chunk(TL.yco, 0, d, 0), d, Mc * d,
+               d, d, WDst{{g.wco, nullptr, nullptr}, d}, dd));
+    RLT_TRY(gl(w.chunk(TL.cf, 0, d, 0), d, Mc * d, w.chunk(TL.y13, 0, 2 * F, 0), 2 * F,
+               Mc * 2 * F, d, 2 * F, WDst{{g.w1, g.w3, nullptr}, F}, dF));
+    RLT_TRY(gl(w.chunk(TL.cm, 0, F, 0), F, Mc * F, w.chunk(TL.y2, 0, d, 0), d, Mc * d, F, d,
+               WDst{{g.w2, nullptr, nullptr}, d}, dF));
+  } else {
+    for (int l = 0; l < L; ++l) {
+      RLT_TRY(gw(w.chunk(TL.ca, l, d, 0), d, w.chunk(TL.yqkv, l, 3 * d, 0), 3 * d, d, 3 * d,
+                 WDst{{g.wq + l * dd, g.wk + l * dd, g.wv + l * dd}, d}));
+      RLT_TRY(gw(w.template saved<T>(TL.os, l, i0), d, w.chunk(TL.yo, l, d, 0), d, d, d,
+                 WDst{{g.wo + l * dd, nullptr, nullptr}, d}));
+      RLT_TRY(gw(w.chunk(TL.cc, l, d, 0), d, w.chunk(TL.ycq, l, d, 0), d, d, d,
+                 WDst{{g.wcq + l * dd, nullptr, nullptr}, d}));
+      RLT_TRY(gw(w.template saved<T>(TL.ocs, l, i0), d, w.chunk(TL.yco, l, d, 0), d, d, d,
+                 WDst{{g.wco + l * dd, nullptr, nullptr}, d}));
+      RLT_TRY(gw(w.chunk(TL.cf, l, d, 0), d, w.chunk(TL.y13, l, 2 * F, 0), 2 * F, d, 2 * F,
+                 WDst{{g.w1 + l * dF, g.w3 + l * dF, nullptr}, F}));
+      RLT_TRY(gw(w.chunk(TL.cm, l, F, 0), F, w.chunk(TL.y2, l, d, 0), d, F, d,
+                 WDst{{g.w2 + l * dF, nullptr, nullptr}, d}));
+    }
   }
-  RLT_TRY(gw(w.template at<T>(TL.xg), 2 * d, w.template at<T>(TL.yg), d, 2 * d, d,
+  RLT_TRY(gw(w.template cat<T>(TL.xg), 2 * d, w.template cat<T>(TL.yg), d, 2 * d, d,
              WDst{{g.w_gate, nullptr, nullptr}, d}));
   const double cs = (3.0 * L + 1) * rows * d * 4;
   return colsums(w.pg(0, 0), 3 * L + 1, rows, TL.Mc, d, w.template at<float>(TL.part),
@@ -1476,7 +1554,8 @@ template <typename T, int HD>
 static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const void* e_v,
                          const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
                          int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
-                         hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof) {
+                         hipEvent_t ev_fork, hipEvent_t ev_join, hipStream_t gs,
+                         const hipEvent_t* gev, Profiler* prof) {
   const TrainLayout TL = train_layout(D, B, n);
   const Walk<T> w{D, B, n, TL, ws};
   const int d = D.d, F = D.F, L = D.L, H = D.H;
@@ -1653,18 +1732,39 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     if (de) RLT_TRY(hipMemsetAsync(de, 0, sizeof(float) * B * n * d, st));
     RLT_TRY(hipMemsetAsync(w.template at<float>(TL.carry), 0, sizeof(float) * B * d, st));
   }
-  // the reverse walk, one chunk of Tc tokens at a time (newest chunk first)
-  for (int64_t i1 = n; i1 > 0;) {
+  // the reverse walk, one chunk of Tc tokens at a time (newest chunk first). With the gradient
+  // stream gs, chunk c's weight gradients run there while the walk goes on with chunk c + 1 in
+  // the other copy of the chunk buffers; the walk of chunk c + 2 waits until they are done.
+  // The gradients still accumulate chunk after chunk in the same order.
+  Timer gtg{prof, gs ? gs : st};
+  bool done_rec[2] = {false, false};
+  int64_t c = 0;
+  for (int64_t i1 = n; i1 > 0; ++c) {
     const int64_t i0 = std::max<int64_t>(0, i1 - TL.Tc);
+    const int p = (int)(c & 1);
+    Walk<T> wc = w;
+    wc.cpar = p ? TL.cspan : 0;
+    if (done_rec[p]) RLT_TRY(hipStreamWaitEvent(st, gev[2 + p], 0));
     RLT_TRY(fork());
     for (int64_t i = i1 - 1; i >= i0; --i)
       for (int gi = 0; gi < ng; ++gi)
-        RLT_TRY(walk_token<T, HD>(w.group(row0[gi], row0[gi + 1] - row0[gi]), P, M, e, G, de,
+        RLT_TRY(walk_token<T, HD>(wc.group(row0[gi], row0[gi + 1] - row0[gi]), P, M, e, G, de,
                                   i, i - i0, segment, detach, gtm[gi], i % stride == 0));
     RLT_TRY(join());
-    RLT_TRY(chunk_grads<T>(w, g, i0, i1, tm));
+    if (gs) {
+      RLT_TRY(hipEventRecord(gev[p], st));
+      RLT_TRY(hipStreamWaitEvent(gs, gev[p], 0));
+      RLT_TRY(chunk_grads<T>(wc, g, i0, i1, gtg));
+      RLT_TRY(hipEventRecord(gev[2 + p], gs));
+      done_rec[p] = true;
+    } else {
+      RLT_TRY(chunk_grads<T>(wc, g, i0, i1, tm));
+    }
     i1 = i0;
   }
+  for (int p = 0; p < 2; ++p)
+    if (done_rec[p]) RLT_TRY(hipStreamWaitEvent(st, gev[2 + p], 0));
+  RLT_TRY(gtg.err);
   // s_0 = s* for every sequence
   RLT_TRY(colsums(w.template at<float>(TL.carry), 1, B, B, d, w.template at<float>(TL.part),
                   ColOut{nullptr, g.s_star, 0}, x, x));
@@ -1721,13 +1821,14 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
                        int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
-                       hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof) {
+                       hipEvent_t ev_fork, hipEvent_t ev_join, hipStream_t gs,
+                       const hipEvent_t* gev, Profiler* prof) {
 #define RLT_BPTT(HDV)                                                                         \
   return D.dtype == RLT_BF16                                                                  \
              ? bptt_t<bf16, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, segment, detach, st,   \
-                                 aux, ev_fork, ev_join, prof)                                 \
+                                 aux, ev_fork, ev_join, gs, gev, prof)                        \
              : bptt_t<float, HDV>(D, B, n, P, e, G, s_traj, g, de, ws, segment, detach, st,  \
-                                  aux, ev_fork, ev_join, prof)
+                                  aux, ev_fork, ev_join, gs, gev, prof)
   switch (D.hd) {
     case 32: RLT_BPTT(32);
     case 64: RLT_BPTT(64);

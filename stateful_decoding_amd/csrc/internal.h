@@ -241,7 +241,7 @@ struct TrainLayout {
   int64_t Tc, Mc;
   size_t state, mem_k, mem_v, bw, s_hist, xs, ys, zs, qs, qcs, os, ocs, docs, khist, vhist, lse,
       dlt, dres, dn, dattn, u13, gsave, carry, rinv, dkacc, dvacc, ca, cc, cf, cm, yqkv, yo, ycq,
-      yco, y13, y2, pg, xg, yg, part, dkv, o2, tx, ty, total;
+      yco, y13, y2, pg, xg, yg, cspan, part, dkv, o2, tx, ty, total;
 };
 TrainLayout train_layout(const Dims& D, int B, int64_t n);
 
@@ -253,10 +253,12 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n);
 // i % prof->stride == 0 and everywhere outside the token loops. With `aux` (a second stream,
 // and two events for forking to it and joining back), large batches run as two row groups.
 // segment > 0: truncation at every segment start of the tensors named by `detach`
-// (RLT_DETACH_* bits).
+// (RLT_DETACH_* bits). With `gs` (a third stream and four events gev: walked[2], done[2]) each
+// chunk's weight gradients run there, overlapping the walk of the next chunk.
 hipError_t launch_bptt(const Dims& D, int B, int64_t n, const Packed& P, const void* e,
                        const float* G, float* s_traj, const GradPtrs& g, float* de, void* ws,
                        int64_t segment, uint32_t detach, hipStream_t st, hipStream_t aux,
-                       hipEvent_t ev_fork, hipEvent_t ev_join, Profiler* prof);
+                       hipEvent_t ev_fork, hipEvent_t ev_join, hipStream_t gs,
+                       const hipEvent_t* gev, Profiler* prof);
 
 }  // namespace rlt

@@ -322,17 +322,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm_tokens(int N, int K, const T*
   ep.template tile<FM, FN>(acc, rw + (lane >> 4) * 4, cw, lane);
 }
 
+// Batched products: product z (blockIdx.y) shifts its operand loader and its epilogue with an
+// overload of batch_at found by argument-dependent lookup; this default is for loaders and
+// epilogues of single products, where only z = 0 occurs.
+template <class X>
+__device__ __forceinline__ X batch_at(const X& x, int) {
+  return x;
+}
+
 // The same product for bf16 with 128 x 128 workgroup tiles staged through LDS: every k-step's
 // 8 A fragments (from the loader) and 8 B fragments are fetched once per workgroup, one 16-byte
 // load per thread and operand pair, into one of two LDS buffers while the other is multiplied;
 // each wave then reads its 4 + 4 fragments from LDS (64 x 64 per wave). The next k-step's loads
 // are issued before the current one's MFMAs. Every output element accumulates its k-steps in
 // the same order with the same instruction as k_gemm_tokens, so the results are identical.
+// blockIdx.y = z selects product z of a batch: W at Wt + z wt_stride, batch_at(al / ep, z).
 template <class AL, class EP>
 __global__ __launch_bounds__(kThreads) void k_gemm_tokens_lds(int N, int K,
-                                                             const bf16* __restrict__ Wt, AL al,
-                                                             EP ep) {
+                                                             const bf16* __restrict__ Wt,
+                                                             int64_t wt_stride, AL al_, EP ep_) {
   constexpr int FM = 4, FN = 4, BM = 128, BN = 128;
+  const int z = blockIdx.y;
+  const AL al = batch_at(al_, z);
+  const EP ep = batch_at(ep_, z);
+  Wt += z * wt_stride;
   __shared__ __attribute__((aligned(16))) u32x4 as[2][8][kWave];
   __shared__ __attribute__((aligned(16))) u32x4 bs[2][8][kWave];
   const int tiles_n = N / BN;
@@ -414,7 +427,7 @@ static hipError_t run_gemm(int M, int N, int K, const void* Wt, const AL& al, co
     if (N % 128 == 0 && blocks >= 1024) {
       if (blocks > INT32_MAX) return hipErrorInvalidValue;
       return launch(k_gemm_tokens_lds<AL, EP>, dim3((unsigned)blocks), dim3(kThreads), st, N, K,
-                    static_cast<const bf16*>(Wt), al, ep);
+                    static_cast<const bf16*>(Wt), (int64_t)0, al, ep);
     }
   }
   constexpr int BM = 16 * FM * WM, BN = 16 * FN * WN;
@@ -422,6 +435,19 @@ static hipError_t run_gemm(int M, int N, int K, const void* Wt, const AL& al, co
   if (N % BN != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
   return launch(k_gemm_tokens<T, WM, WN, FM, FN, AL, EP>, dim3((unsigned)blocks), dim3(kThreads),
                 st, N, K, static_cast<const T*>(Wt), al, ep);
+}
+
+// `batch` products of M x N x K in one launch of the LDS-staged kernel (bf16, N a multiple of
+// 128): product z reads W at Wt + z wt_stride and batch_at(al / ep, z).
+template <class AL, class EP>
+static hipError_t run_gemm_batched(int M, int N, int K, int batch, const bf16* Wt,
+                                   int64_t wt_stride, const AL& al, const EP& ep, const Exec& st) {
+  const int64_t blocks = (int64_t)((M + 127) / 128) * (N / 128);
+  if (K % 32 != 0 || M <= 0 || N % 128 != 0 || batch < 1 || batch > 65535 || blocks <= 0 ||
+      blocks > INT32_MAX)
+    return hipErrorInvalidValue;
+  return launch(k_gemm_tokens_lds<AL, EP>, dim3((unsigned)blocks, (unsigned)batch),
+                dim3(kThreads), st, N, K, Wt, wt_stride, al, ep);
 }
 
 template <typename T, int FM, int FN, int NW, class AL, class EP>
