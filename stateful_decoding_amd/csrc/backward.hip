@@ -88,7 +88,7 @@ TrainLayout train_layout(const Dims& D, int B, int64_t n) {
   t.dres = take(b * d * 4);
   t.dn = take(b * d * 4);
   t.dattn = take(b * d * 4);
-  t.u13 = take(b * 2 * F * 4);
+  t.u13 = take(L * N * b * 2 * F * 4);  // the forward's up-projections u1 | u3, [L][n][B][2F]
   t.gsave = take(b * d * 4);
   t.carry = take(b * d * 4);
   t.rinv = take(b * 3 * 4);
@@ -355,37 +355,14 @@ struct ARows {  // A = row-major [M][ld] dtype rows
   }
 };
 
-// FFN recompute: u1 = f W1, u3 = f W3 (packed columns interleave 16 of each per 32); keeps u1
-// and u3 (fp32, [M][2F]: u1 then u3) and writes m = silu(u1) u3 (dtype rows [M][F]).
-template <typename T>
-struct EpiU13 {
-  float* u;
-  T* m;
-  int M, F;
-  template <int NT, int BM, int BN, int E>
-  __device__ void prefetch(Pre<E>&, int, int) const {}
-  template <int NT, int BM, int BN, int E>
-  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>&) const {
-    constexpr int half = BN / 2;
-    for (int i = threadIdx.x; i < BM * half; i += NT) {
-      const int r = i / half, j = i - r * half;
-      const int row = r0 + r;
-      if (row >= M) continue;
-      const int cp = (j / 16) * 32 + (j % 16);
-      const float z1 = tile[r * ld + cp], z3 = tile[r * ld + cp + 16];
-      const int f = c0 / 2 + j;
-      u[(int64_t)row * 2 * F + f] = z1;
-      u[(int64_t)row * 2 * F + F + f] = z3;
-      m[(int64_t)row * F + f] = to_elem<T>(z1 * sigmoidf_(z1) * z3);
-    }
-  }
-};
-
-// dm -> du1 = dm u3 sigma(u1) (1 + u1 (1 - sigma(u1))), du3 = dm silu(u1), dtype rows [M][2F].
+// From the forward's u1 | u3: dm -> du1 = dm u3 sigma(u1) (1 + u1 (1 - sigma(u1))),
+// du3 = dm silu(u1) (dtype rows [M][2F]), and the product m = silu(u1) u3 (dtype rows [M][F],
+// the down projection's weight-gradient operand, as the forward rounded it).
 template <typename T>
 struct EpiSiluBack : EpiTile<EpiSiluBack<T>> {
   const float* u;
   T* du;
+  T* m;
   int M, F;
   __device__ void op(int row, int col, float dm) const {
     if (row >= M) return;
@@ -393,6 +370,7 @@ struct EpiSiluBack : EpiTile<EpiSiluBack<T>> {
     const float sg = sigmoidf_(u1);
     du[(int64_t)row * 2 * F + col] = to_elem<T>(dm * u3 * sg * (1.f + u1 * (1.f - sg)));
     du[(int64_t)row * 2 * F + F + col] = to_elem<T>(dm * u1 * sg);
+    m[(int64_t)row * F + col] = to_elem<T>(u1 * sg * u3);
   }
 };
 
@@ -1355,7 +1333,6 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
   float* dn = w.template row<float>(TL.dn, d);
   float* dattn = w.template row<float>(TL.dattn, d);
   float* rinv = w.template row<float>(TL.rinv, 3);
-  float* u13 = w.template row<float>(TL.u13, 2 * F);
   float* gsave = w.template row<float>(TL.gsave, d);
   float* carry = w.template row<float>(TL.carry, d);
   G += (int64_t)b0 * n * d;
@@ -1392,20 +1369,15 @@ static hipError_t walk_token(const Walk<T>& w, const Packed& P, const MemBufs& M
     const float* xs = w.template saved<float>(TL.xs, l, i);
     const float* ys = w.template saved<float>(TL.ys, l, i);
     const float* zs = w.template saved<float>(TL.zs, l, i);
-    T* cf = w.chunk(TL.cf, l, d, li);
-    // feed-forward: recompute u, then dm -> du -> df -> dres
-    {
-      EpiU13<T> ep{u13, w.chunk(TL.cm, l, F, li), B, F};
-      RLT_TRY(run_step_gemm<T>(B, 2 * F, d, el<T>(P.w13_t, (int64_t)l * 2 * F * d),
-                               ARows<T>{cf, d, B}, ep, proj(2 * F, d, b * F * (8 + es))));
-    }
+    // feed-forward: from the forward's u1 | u3, dm -> du -> df -> dres
+    const float* u13 = w.template at<float>(TL.u13) + (((int64_t)l * n + i) * Bt + b0) * 2 * F;
     T* y13 = w.chunk(TL.y13, l, 2 * F, li);
     {
       EpiSiluBack<T> ep;
-      ep.u = u13; ep.du = y13; ep.M = B; ep.F = F;
+      ep.u = u13; ep.du = y13; ep.m = w.chunk(TL.cm, l, F, li); ep.M = B; ep.F = F;
       RLT_TRY(run_step_gemm<T>(B, F, d, bw + bo.w2 + (int64_t)l * F * d,
                                ARows<T>{w.chunk(TL.y2, l, d, li), d, B}, ep,
-                               proj(F, d, b * 2 * F * (4 + es))));
+                               proj(F, d, b * F * (8 + 3 * es))));
     }
     EpiStoreF32 to_dn;
     to_dn.out = dn; to_dn.ld = d; to_dn.M = B;
@@ -1704,8 +1676,9 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
         RLT_TRY(launch(k_save<T>, grid, dim3(kThreads),
                        tg.at(RLT_K_BWD_OTHER, 8 * ad, 0, smp), a));
         RLT_TRY(gemm_w13(D, rb, l, P, Sl,
-                         tg.at(RLT_K_FFN_UP, 2 * Fd * dsz * es * sh + a32 + bg * Fd * es,
-                               4 * bg * dsz * Fd, smp)));
+                         tg.at(RLT_K_FFN_UP, 2 * Fd * dsz * es * sh + a32 + bg * Fd * (es + 8),
+                               4 * bg * dsz * Fd, smp),
+                         w.template at<float>(TL.u13) + (((int64_t)l * n + i) * B + b0) * 2 * F));
         float* next = last ? s_hist + ((i + 1) * B + b0) * d
                            : wg.template saved<float>(TL.xs, l + 1, i);
         RLT_TRY(gemm_residual(D, rb, l, 2, P, Sl, last, next, d,

@@ -183,6 +183,7 @@ struct EpiSiluMul {  // packed columns come in blocks of 32: 16 of W1, then the 
                      // act is written in fragment order (the down projection's operand)
   T* act;
   int M, F;
+  float* u = nullptr;  // optional fp32 [M][2F] copy of x W1 | x W3 (kept for the backward pass)
   template <int NT, int BM, int BN, int E>
   __device__ void prefetch(Pre<E>&, int, int) const {}
   template <int NT, int BM, int BN, int E>
@@ -195,6 +196,10 @@ struct EpiSiluMul {  // packed columns come in blocks of 32: 16 of W1, then the 
       const int cp = (j / 16) * 32 + (j % 16);
       const float z1 = tile[r * ld + cp], z3 = tile[r * ld + cp + 16];
       act[frag_off(row, c0 / 2 + j, F / 32)] = to_elem<T>(z1 * sigmoidf_(z1) * z3);
+      if (u) {
+        u[(int64_t)row * 2 * F + c0 / 2 + j] = z1;
+        u[(int64_t)row * 2 * F + F + c0 / 2 + j] = z3;
+      }
     }
   }
 };
@@ -288,8 +293,8 @@ static hipError_t cq_t(const Dims& D, int B, int l, const Packed& P, const State
 
 template <typename T>
 static hipError_t w13_t(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                        const Exec& st) {
-  EpiSiluMul<T> ep{static_cast<T*>(S.act), B, D.F};
+                        const Exec& st, float* u_save) {
+  EpiSiluMul<T> ep{static_cast<T*>(S.act), B, D.F, u_save};
   return run_step_gemm<T>(B, 2 * D.F, D.d, elem<T>(P.w13_t, (int64_t)l * 2 * D.F * D.d),
                           normed<T>(D, B, S), ep, st);
 }
@@ -355,8 +360,9 @@ hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs
   return D.dtype == RLT_BF16 ? cq_t<bf16>(D, B, l, P, S, st) : cq_t<float>(D, B, l, P, S, st);
 }
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                    const Exec& st) {
-  return D.dtype == RLT_BF16 ? w13_t<bf16>(D, B, l, P, S, st) : w13_t<float>(D, B, l, P, S, st);
+                    const Exec& st, float* u_save) {
+  return D.dtype == RLT_BF16 ? w13_t<bf16>(D, B, l, P, S, st, u_save)
+                             : w13_t<float>(D, B, l, P, S, st, u_save);
 }
 hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P,
                          const StateBufs& S, bool dst_s, float* out, int64_t out_ld,

@@ -213,8 +213,9 @@ hipError_t gemm_qkv(const Dims& D, int B, int l, const Packed& P, const StateBuf
                     const Exec& st);
 hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                    const Exec& st);
+// u_save (optional): fp32 [B][2F] copy of the two up-projections (u1 | u3) for the backward pass
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
-                    const Exec& st);
+                    const Exec& st, float* u_save = nullptr);
 // h (+)= A W for the output projections: which = 0 (self-attn O), 1 (cross O), 2 (FFN down).
 // When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h, and
 // the positions of the active rows advance: this is the last launch of the step.
