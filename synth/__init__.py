@@ -29,8 +29,12 @@ import numpy as np
 
 __all__ = [
     "RLTConfig", "CONFIGS", "round_bf16", "make_params", "make_encoder_outputs",
-    "MATRIX_NAMES", "tensor_id",
+    "MATRIX_NAMES", "tensor_id", "VOCAB", "make_head_params", "make_tokens", "make_uniforms",
 ]
+
+# Vocabulary size of the encoder's embedding and the readout (the pages name none; a power of
+# two in the range of common language-model vocabularies).
+VOCAB = 32768
 
 
 @dataclass(frozen=True)
@@ -90,6 +94,10 @@ _ID_S_STAR, _ID_W_GATE, _ID_B_GATE, _ID_GAMMA = 0, 1, 2, 3
 _ID_LAYER0 = 16
 _ID_GROUP0 = 1 << 20
 _ID_E0 = 1 << 24
+_HEAD_NAMES = ("embed", "enc_gamma", "enc_gamma_out", "out_gamma", "w_out")
+_ID_HEAD0 = 1 << 28
+_ID_TOKENS0 = 1 << 29
+_ID_UNIFORM0 = 1 << 30
 
 
 def tensor_id(name: str, index: int = 0) -> int:
@@ -110,6 +118,12 @@ def tensor_id(name: str, index: int = 0) -> int:
         return _ID_GROUP0 + 2 * index + 1
     if name == "e":
         return _ID_E0 + index
+    if name in _HEAD_NAMES:
+        return _ID_HEAD0 + _HEAD_NAMES.index(name)
+    if name == "tokens":
+        return _ID_TOKENS0 + index
+    if name == "u":
+        return _ID_UNIFORM0 + index
     raise KeyError(name)
 
 
@@ -205,3 +219,47 @@ def make_encoder_outputs(cfg: RLTConfig, seqs, seq_len: int | None = None,
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(run, range(len(seqs))))
     return out
+
+
+def make_head_params(cfg: RLTConfig, vocab: int = VOCAB, seed: int = 0,
+                     random_gains: bool = False) -> dict[str, np.ndarray]:
+    """Parameters of the encoder and the readout around the decoder (float32 arrays,
+    bf16-representable matrices for bf16 configs). The encoder's attention and FFN matrices
+    are the decoder's (make_params), so only these are new:
+      embed [V, d]             token embedding, N(0, 1)
+      enc_gamma [L, 2, d]      encoder RMSNorm gains before attention and FFN
+      enc_gamma_out [d]        gain of the norm that gives e_t
+      out_gamma [d]            gain of the readout's norm of s_t
+      w_out [d, V]             readout matrix, N(0, sigma)
+    Gains are ones unless ``random_gains`` (then 1 + 0.1 N(0, 1))."""
+    d, L = cfg.d, cfg.n_layers
+    rounding = round_bf16 if cfg.dtype == "bf16" else (lambda a: a)
+
+    def gains(name, shape):
+        if not random_gains:
+            return np.ones(shape, np.float32)
+        return (1.0 + _normal(seed, tensor_id(name), shape, 0.1)).astype(np.float32)
+
+    return {"embed": rounding(_normal(seed, tensor_id("embed"), (vocab, d), 1.0)),
+            "enc_gamma": gains("enc_gamma", (L, 2, d)),
+            "enc_gamma_out": gains("enc_gamma_out", (d,)),
+            "out_gamma": gains("out_gamma", (d,)),
+            "w_out": rounding(_normal(seed, tensor_id("w_out"), (d, vocab), cfg.sigma))}
+
+
+def make_tokens(seqs, seq_len: int, vocab: int = VOCAB, seed: int = 0) -> np.ndarray:
+    """Token ids [len(seqs), seq_len] (int32), uniform over the vocabulary, one stream per
+    sequence number."""
+    out = np.empty((len(list(seqs)), seq_len), np.int32)
+    for i, b in enumerate(seqs):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id(
+            "tokens", b)])))
+        out[i] = rng.integers(0, vocab, seq_len, dtype=np.int32)
+    return out
+
+
+def make_uniforms(n: int, step: int = 0, seed: int = 0) -> np.ndarray:
+    """n uniform draws in [0, 1) (float32) for the sampler's step `step`."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id(
+        "u", step)])))
+    return rng.random(n, dtype=np.float32)
