@@ -29,7 +29,6 @@ HBM_PEAK = 8.0e12        # MI355X HBM3E, bytes/s
 BF16_PEAK = 2.5e15       # MI355X dense bf16 MFMA, flop/s
 FP32_PEAK = 157.3e12
 METRIC = "RLT decoder tokens/sec (B seqs x T) on 1 MI355X; % of per-step roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cross_attn_traffic.json")
 
 
 def step_roofline_seconds(cfg, B: int, T: int) -> float:
@@ -91,22 +90,6 @@ def cpu_baseline(cfg, params, budget_s: float, n_seqs: int = 16) -> dict:
             "host_cpus": len(os.sched_getaffinity(0)), "param_prep_s": round(t_prep, 2)}
 
 
-def traffic_from_profile(kernel_src: str, workload: str, T: int, stride: int):
-    """Calibrated HBM bytes per memory-attention launch from committed PMC counters, averaged
-    over the launches this run timed (tokens t0 % stride == 0), if they were taken on this
-    kernel source and workload."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    by_t = rec.get("bytes_per_launch_by_token")
-    if (rec.get("source_sha256_16") != source_hash(kernel_src) or
-            not rec.get("workload", "").startswith(workload + " ") or not by_t or len(by_t) != T):
-        return None
-    sampled = by_t[::stride]
-    return round(sum(sampled) / len(sampled))
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,10 +105,10 @@ def main():
                     help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-stride", type=int, default=1,
-                    help="time the memory-attention launches of every N-th token (1 = all); "
-                         "the launches time themselves by the GPU clock, with nothing queued "
-                         "around them")
+    ap.add_argument("--profile-stride", type=int, default=0,
+                    help="time the memory-attention launches of every N-th token (default: "
+                         "every token, or every 16th when the attention is split); the launches "
+                         "time themselves by the GPU clock, with nothing queued around them")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run 5 plain device copies of MIB MiB (fp32) and exit: the known-size "
                          "kernel that scales the HBM byte counters of a profiler")
@@ -190,9 +173,13 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
-    # one clock slot pair per workgroup (sequence, head) of every timed memory attention
-    state.profile_clock(args.steps * T * cfg.n_layers * B * cfg.n_heads)
-    state.profile_begin(["cross_attn", "memproj"], token_stride=args.profile_stride)
+    # one clock slot pair per workgroup (sequence, head, and slice of the prefix when fewer
+    # than 1024 sequence-head pairs split it into up to 16) of every timed memory attention
+    per_bh = 1 if B * cfg.n_heads >= 1024 else 16
+    stride = args.profile_stride or (1 if per_bh == 1 else 16)
+    timed_tokens = (T + stride - 1) // stride
+    state.profile_clock(args.steps * timed_tokens * cfg.n_layers * B * cfg.n_heads * per_bh)
+    state.profile_begin(["cross_attn", "memproj"], token_stride=stride)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -213,8 +200,7 @@ def main():
     ideal = step_roofline_seconds(cfg, B, T)
     ca = prof["cross_attn"]
     achieved = ca["bytes"] / (ca["total_ms"] / 1e3)
-    kernel_src = os.path.join(ROOT, "stateful_decoding_amd", "csrc", "attention.hip")
-    traffic = traffic_from_profile(kernel_src, cfg.name, T, args.profile_stride)
+    traffic = None
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -232,7 +218,7 @@ def main():
                      "avg_launch_us": round(ca["total_ms"] * 1e3 / ca["launches"], 2),
                      "bytes_per_launch": round(ca["bytes"] / ca["launches"]),
                      "timed": f"every launch in the steps of tokens t with t % "
-                              f"{args.profile_stride} == 0 (all layers and row groups), each "
+                              f"{stride} == 0 (all layers and row groups), each "
                               f"by the kernel's own clock stamps: first wave's start to last "
                               f"wave's end"},
         "step_roofline": {"ideal_s": round(ideal, 4), "measured_s": round(secs / args.steps, 4),
@@ -359,8 +345,10 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
         one_step()
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
-    state.profile_clock(args.steps * T * L * B * cfg.n_heads)
-    state.profile_begin(["cross_attn"], token_stride=args.profile_stride)
+    stride = args.profile_stride or 1
+    per_bh = 1 if B * cfg.n_heads >= 1024 else 16
+    state.profile_clock(args.steps * ((T + stride - 1) // stride) * L * B * cfg.n_heads * per_bh)
+    state.profile_begin(["cross_attn"], token_stride=stride)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -373,7 +361,7 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
     assert state.positions() == pos.tolist(), "positions differ from the schedule"
     secs = ms_total / 1e3
     ca = prof["cross_attn"]
-    sampled = [s_ for s_ in range(T) if s_ % args.profile_stride == 0]
+    sampled = [s_ for s_ in range(T) if s_ % stride == 0]
     by = sum(L * (float((before[s_] + 1).sum()) * 2 * d * es + B * d * (4 + es))
              for s_ in sampled) * args.steps
     achieved = by / (ca["total_ms"] / 1e3)
@@ -395,7 +383,7 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
                      "launches": ca["launches"],
                      "avg_launch_us": round(ca["total_ms"] * 1e3 / ca["launches"], 2),
-                     "timed": f"every launch in the steps s with s % {args.profile_stride} == 0, "
+                     "timed": f"every launch in the steps s with s % {stride} == 0, "
                               f"by the kernel's own clock stamps"},
     }
     if not args.no_cpu_baseline:

@@ -121,15 +121,22 @@ void rlt_model_destroy(rlt_model* model);
 /* --- decoder state H_t = (s_t, C_t^D) ------------------------------------------------- */
 
 /* Bytes of device memory for the state of B sequences: s [B][d] float32, the per-layer
- * self-attention caches, and the working buffers of one decoder step. */
+ * self-attention caches, and the working buffers of one decoder step. The state is
+ * H_t = (s_t, C_t^D) of "RLT Runs 96 Blocks Per Token With Recurrent State, No Resets",
+ * "Architecture: encoder memory meets recurrent decoder". 0 if the configuration or batch
+ * (1 .. 2^20) is invalid. */
 size_t rlt_state_bytes(const rlt_config* cfg, int32_t batch);
 
 /* Binds `buf` (device, >= rlt_state_bytes, 256-byte aligned) as the state of `batch`
- * sequences and resets it on `stream` (see rlt_state_reset). */
+ * sequences and resets it on `stream` (see rlt_state_reset). RLT_ERR_CAPACITY if `buf` is too
+ * small, RLT_ERR_ARG if misaligned or NULL. The buffer stays owned by the caller and must
+ * outlive the handle. */
 rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, size_t bytes,
                             void* stream, rlt_state** out);
 
-/* s_0 = s* for every sequence, empty caches, position t = 0 (before the first token). */
+/* s_0 = s* for every sequence, empty caches, position t = 0 (before the first token): the
+ * one-time initialisation by the learned start state and an empty cache of the architecture
+ * section; nothing resets the state afterwards (no reset at the prompt-response boundary). */
 rlt_status rlt_state_reset(rlt_state* state, void* stream);
 
 /* Number of tokens every sequence of the state has processed (t), or -1 once a step with an
@@ -143,11 +150,14 @@ void rlt_state_destroy(rlt_state* state);
 
 /* --- encoder memory M ----------------------------------------------------------------- */
 
-/* Bytes for the key and value memory of B sequences up to `capacity` tokens:
- * K and V, each [G][B][H][capacity][hd] dtype. 1 <= capacity <= 2^20. */
+/* Bytes for the key and value memory M of B sequences up to `capacity` tokens: K and V, each
+ * [G][B][H][capacity][hd] dtype, shared by all blocks (G = 1) or one per block (G = L_D), as
+ * the architecture section allows. 1 <= capacity <= 2^20; 0 if invalid. */
 size_t rlt_memory_bytes(const rlt_config* cfg, int32_t batch, int64_t capacity);
 
-/* Binds `buf` (device, >= rlt_memory_bytes, 256-byte aligned) as empty memory (length 0). */
+/* Binds `buf` (device, >= rlt_memory_bytes, 256-byte aligned) as empty memory (length 0).
+ * RLT_ERR_CAPACITY if `buf` or `capacity` is out of range, RLT_ERR_ARG if misaligned. The
+ * buffer stays owned by the caller and must outlive the handle. */
 rlt_status rlt_memory_create(const rlt_model* model, int32_t batch, int64_t capacity, void* buf,
                              size_t bytes, rlt_memory** out);
 
@@ -159,18 +169,27 @@ rlt_status rlt_memory_reset(rlt_memory* mem);
 void rlt_memory_destroy(rlt_memory* mem);
 
 /* Token-parallel memory projection of tokens t0 .. t0+n-1 (0-based) from encoder outputs
- * e [B][n][d] dtype (device). Requires 0 <= t0 <= length (no holes), n >= 1 and
- * t0 + n <= capacity; afterwards length = max(length, t0 + n). */
+ * e [B][n][d] dtype (device): K_j = e_j W_mK^(g), V_j = e_j W_mV^(g) for every group g, the
+ * prefix-restricted key/value memory M_{<=t} the decoder reads ("RLT Runs 96 Blocks Per Token
+ * With Recurrent State, No Resets", "Architecture: encoder memory meets recurrent decoder";
+ * run token-parallel per "Three design principles and their caveats"). Requires
+ * 0 <= t0 <= length (no holes, else RLT_ERR_NOT_PROJECTED), n >= 1 (RLT_ERR_ARG) and
+ * t0 + n <= capacity (RLT_ERR_CAPACITY); afterwards length = max(length, t0 + n). e must
+ * stay valid until `stream` has passed the call. */
 rlt_status rlt_memproj(const rlt_model* model, rlt_memory* mem, const void* e, int64_t t0,
                        int64_t n, void* stream);
 
 /* --- the recurrent transition --------------------------------------------------------- */
 
-/* One decoder step for every sequence: consumes e_t [B][d] dtype (device) for token
- * t+1 (1-based), where t = rlt_state_position; needs memory length >= t+1 (else
- * RLT_ERR_NOT_PROJECTED). Writes s_{t+1} to s_out [B][d] float32 (device) unless NULL, and
- * advances the position. The state and the memory must belong to `model` and have the
- * same batch. */
+/* One decoder step for every sequence, the transition H_t -> H_{t+1} ("RLT Runs 96 Blocks Per
+ * Token With Recurrent State, No Resets", "Architecture: encoder memory meets recurrent
+ * decoder": gated merge of e with the previous output, then per block window self-attention,
+ * cross-attention to M_{<=t+1} and FFN; the window keeps W-1 past entries): consumes
+ * e_t [B][d] dtype (device) for token t+1 (1-based), where t = rlt_state_position; needs
+ * memory length >= t+1 (else RLT_ERR_NOT_PROJECTED). Writes s_{t+1} to s_out [B][d] float32
+ * (device) unless NULL, and advances the position. The state and the memory must belong to
+ * `model` (RLT_ERR_ARG) and have the same batch (RLT_ERR_SHAPE); e_t and s_out 16-byte
+ * aligned (RLT_ERR_ARG). */
 rlt_status rlt_decoder_step(const rlt_model* model, rlt_state* state, const rlt_memory* mem,
                             const void* e_t, float* s_out, void* stream);
 
@@ -188,10 +207,14 @@ rlt_status rlt_decoder_step_ragged(const rlt_model* model, rlt_state* state,
                                    float* s_out, void* stream);
 
 /* n consecutive steps over e [B][n][d] dtype (device), the encoder outputs of tokens
- * t+1 .. t+n. First projects every one of those tokens that the memory does not hold yet
- * (same as rlt_memproj on the missing range; requires t <= length and t + n <= capacity),
- * then runs n steps. s_traj [B][n][d] float32 (device) receives every s unless NULL. The
- * result equals rlt_memproj followed by n calls of rlt_decoder_step. */
+ * t+1 .. t+n: the sequential chain of transitions, which no parallel scan replaces ("RLT Runs
+ * 96 Blocks Per Token With Recurrent State, No Resets", "Three design principles and their
+ * caveats"). First projects every one of those tokens that the memory does not hold yet
+ * (same as rlt_memproj on the missing range; requires t <= length, else
+ * RLT_ERR_NOT_PROJECTED, and t + n <= capacity, else RLT_ERR_CAPACITY), then runs n steps.
+ * s_traj [B][n][d] float32 (device) receives every s unless NULL. The result equals
+ * rlt_memproj followed by n calls of rlt_decoder_step, bitwise; so does any split of the n
+ * tokens into consecutive calls (the split invariance of the same section). */
 rlt_status rlt_run_sequence(const rlt_model* model, rlt_state* state, rlt_memory* mem,
                             const void* e, int64_t n, float* s_traj, void* stream);
 
@@ -320,13 +343,15 @@ rlt_status rlt_state_export(const rlt_state* state, float* s, void* k, void* v,
 
 /* Loads a snapshot in the layout rlt_state_export writes (k/v rows beyond min(t, W-1) are
  * ignored). Fails with RLT_ERR_VERSION, changing nothing, if `version` differs from the
- * model's tag. Waits for the stream. */
+ * model's tag. Stream-ordered, like the steps: s, k and v (device) must stay valid until
+ * `stream` has passed the call. */
 rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, const void* v,
                             int64_t position, uint64_t version, void* stream);
 
 /* The same for a snapshot whose sequences are at different positions: `positions` is a host
  * array of B positions (as rlt_state_positions reads them, each in [0, 2^20]); sequence b's
- * canonical k/v rows hold its min(positions[b], W-1) retained entries. Waits for the stream.
+ * canonical k/v rows hold its min(positions[b], W-1) retained entries. Waits for the stream,
+ * so that the host array may be reused on return (the one import that synchronises).
  * Together with rlt_state_export and rlt_state_positions this splits and resumes a batch of
  * ragged sequences ("exact prefix snapshot"). */
 rlt_status rlt_state_import_ragged(rlt_state* state, const float* s, const void* k,
@@ -390,7 +415,10 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out);
  * rlt_profile_end takes each launch's earliest start and latest end. Nothing is queued around
  * the launch that could change how concurrent streams overlap, and no two workgroups write the
  * same address. The kernels run one workgroup per (sequence, head): a timed launch takes
- * 16 * H bytes per sequence of its batch. rlt_profile_begin clears the slots (it waits for the
+ * 16 * H bytes per sequence of its batch; a memory attention whose batch has fewer than 1024
+ * sequence-head pairs splits each prefix into up to 16 slices of at least 256 entries, one
+ * workgroup each (16 * H * slices bytes per sequence), and merges them in a second, untimed
+ * launch. rlt_profile_begin clears the slots (it waits for the
  * device); launches that no longer fit are not timed and make rlt_profile_end return
  * RLT_ERR_CAPACITY. Not while a session runs (RLT_ERR_ARG). The buffer must stay allocated
  * while attached. */

@@ -172,6 +172,7 @@ StateLayout state_layout(const Dims& D, int B) {
   s.o = take(b16 * d * es);
   s.act = take(b16 * D.F * es);
   s.pos = take(b * 8);
+  s.part = take(b * D.H * kMaxSplits * (D.hd + 2) * 4);
   s.total = o;
   return s;
 }
@@ -303,8 +304,10 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
   s->S.o = at<char>(buf, L.o);
   s->S.act = at<char>(buf, L.act);
   s->S.pos = at<int64_t>(buf, L.pos);
+  s->S.part = at<float>(buf, L.part);
   s->S.active = nullptr;
   s->S.t_uniform = -1;
+  s->S.t_max = 0;
   s->S.Bt = batch;
   s->ragged = false;
   s->fork = nullptr;
@@ -333,7 +336,7 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
   }
   e = launch_reset(model->D, batch, model->P, s->S, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
-    delete s;
+    rlt_state_destroy(s);  // also frees the row-group streams and events created above
     return hip_fail(e, "state reset");
   }
   *out = s;
@@ -461,7 +464,10 @@ static hipError_t run_steps(const rlt_model* model, rlt_state* state, const rlt_
   const char* eb = static_cast<const char*>(e);
   for (int64_t i = 0; i < n && err == hipSuccess; ++i) {
     const int64_t t0 = state->t + i;
-    for (int g = 0; g < ng; ++g) Sg[g].t_uniform = state->ragged ? -1 : t0;
+    for (int g = 0; g < ng; ++g) {
+      Sg[g].t_uniform = state->ragged ? -1 : t0;
+      Sg[g].t_max = t0;
+    }
     for (int g = 0; g < ng && err == hipSuccess; ++g) {
       const int b0 = state->row0[g], rows = state->row0[g + 1] - b0;
       const char* et = eb + ((size_t)b0 * e_ld + (size_t)i * D.d) * D.es;
@@ -745,8 +751,9 @@ rlt_status rlt_state_import(rlt_state* state, const float* s, const void* k, con
     return fail(RLT_ERR_VERSION, "snapshot version %llu != model version %llu",
                 (unsigned long long)version, (unsigned long long)state->model->cfg.version);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // stream-ordered: every source is device memory the caller keeps until the stream has
+  // passed this point
   hipError_t e = launch_import(state->model->D, state->B, state->S, position, s, k, v, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "state import");
   state->t = position;
   state->ragged = false;

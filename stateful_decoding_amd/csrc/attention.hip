@@ -14,6 +14,8 @@
 // section).
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -39,31 +41,39 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = mn;
 }
 
-// One workgroup of NW waves per (sequence, head): softmax attention of one query over the
-// rows [0, n) of a contiguous [rows][HD] key block and value block, in a single pass; n comes
-// from the sequence's own position, so sequences of one batch may be at different tokens. Each row
-// slot (LPR lanes) walks its rows with a running softmax state, U rows at a time with one
-// rescale per batch; slots merge through lane shuffles, waves through LDS. The query is q[b]
-// (fp32, head hh), K/V blocks start at K + bh * bh_stride; the output row o[b] (dtype) is
-// written in MFMA fragment order, as the output projection reads it.
+// NW waves per (sequence, head, part): softmax attention of one query over the rows of a
+// contiguous [rows][HD] key block and value block, in a single pass. The sequence attends rows
+// [0, n), n from its own position, so sequences of one batch may be at different tokens; with
+// `parts` > 1 (gridDim.x = sequences x heads x parts) workgroup p takes the p-th of `parts`
+// contiguous slices of those rows. Each row slot (LPR lanes) walks its rows with a running
+// softmax state, U rows at a time with one rescale per batch; slots merge through lane
+// shuffles, waves through LDS. The query is q[b] (fp32, head hh), K/V blocks start at
+// K + bh * bh_stride. One part: the output row o[b] (dtype) is written in MFMA fragment order,
+// as the output projection reads it. Several parts: the unnormalised output, the max and the
+// sum of the slice go to part[(bh * parts + p) * (HD + 2)] (an empty slice leaves max -inf,
+// sum 0) for k_attend_merge.
 template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __restrict__ K,
                                        const T* __restrict__ V, int64_t bh_stride,
                                        const int64_t* __restrict__ pos, int64_t t_uniform,
-                                       int window, int H, float scale, T* __restrict__ out) {
+                                       int window, int H, float scale, T* __restrict__ out,
+                                       int parts, float* __restrict__ part) {
   using G = Geo<T, HD>;
   constexpr int RPB = G::RPW * NW;  // rows per block per batch step
   __shared__ float lds_m[NW], lds_l[NW];
   __shared__ float lds_acc[NW][HD];
-  const int bh = blockIdx.x, b = bh / H, hh = bh - b * H, d = H * HD;
+  const int bh = blockIdx.x / parts, pi = blockIdx.x - bh * parts;
+  const int b = bh / H, hh = bh - b * H, d = H * HD;
   // rows attended: the memory prefix 1..t+1 of this sequence, or its window of
   // min(t + 1, W) ring slots (t = tokens the sequence has processed before this step)
   const int64_t tb = (t_uniform >= 0 ? t_uniform : pos[b]) + 1;
-  const int n = window > 0 ? (int)(tb < window ? tb : window) : (int)tb;
+  const int nb = window > 0 ? (int)(tb < window ? tb : window) : (int)tb;
+  const int chunk = (nb + parts - 1) / parts;
+  const int lo = min(nb, pi * chunk), n = min(nb, lo + chunk) - lo;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int sub = lane % G::LPR, slot = lane / G::LPR;
-  const T* Kb = K + (int64_t)bh * bh_stride + sub * G::VEC;
-  const T* Vb = V + (int64_t)bh * bh_stride + sub * G::VEC;
+  const T* Kb = K + (int64_t)bh * bh_stride + (int64_t)lo * HD + sub * G::VEC;
+  const T* Vb = V + (int64_t)bh * bh_stride + (int64_t)lo * HD + sub * G::VEC;
   float qv[G::VEC];
   const float* qp = q + (int64_t)b * d + hh * HD + sub * G::VEC;
 #pragma unroll
@@ -134,8 +144,34 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
   if (tid < HD) {
     float M = lds_m[0], L = lds_l[0], A = lds_acc[0][tid];
     for (int w = 1; w < NW; ++w) merge_state(M, L, &A, lds_m[w], lds_l[w], &lds_acc[w][tid], 1);
-    out[frag_off(b, hh * HD + tid, d / 32)] = to_elem<T>(A / L);
+    if (parts == 1) {
+      out[frag_off(b, hh * HD + tid, d / 32)] = to_elem<T>(A / L);
+    } else {
+      float* pp = part + (int64_t)blockIdx.x * (HD + 2);
+      pp[tid] = A;
+      if (tid == 0) {
+        pp[HD] = M;
+        pp[HD + 1] = L;
+      }
+    }
   }
+}
+
+// Merge of the `parts` partial softmax states of each (sequence, head) in part order; thread
+// (bh, j) writes output element j of head hh of row b in fragment order.
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restrict__ part,
+                                                            int parts, int BH, int H,
+                                                            T* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)BH * HD) return;
+  const int bh = (int)(i / HD), j = (int)(i - (int64_t)bh * HD);
+  const int b = bh / H, hh = bh - b * H;
+  const float* pp = part + (int64_t)bh * parts * (HD + 2);
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int p = 0; p < parts; ++p, pp += HD + 2)
+    merge_state(M, L, &A, pp[HD], pp[HD + 1], pp + j, 1);
+  out[frag_off(b, hh * HD + j, H * HD / 32)] = to_elem<T>(A / L);
 }
 
 // The two uses get kernels of their own, so that traces tell them apart. clk != NULL: a timed
@@ -144,23 +180,28 @@ template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
                                              int64_t bh_stride, const int64_t* pos,
                                              int64_t t_uniform, int window, int H, float scale,
-                                             T* out, unsigned long long* clk) {
+                                             T* out, int parts, float* part,
+                                             unsigned long long* clk) {
   const LaunchClock lc{clk};
   lc.start();
-  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out);
+  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts, part);
   lc.stop();
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_window(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, unsigned long long* clk) {
-  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, clk);
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    unsigned long long* clk) {
+  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
+                             part, clk);
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_memory(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, unsigned long long* clk) {
-  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, clk);
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    unsigned long long* clk) {
+  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
+                             part, clk);
 }
 
 template <typename T>
@@ -168,29 +209,48 @@ static inline T* elem(void* base, int64_t off) {
   return static_cast<T*>(base) + off;
 }
 
-// Waves per workgroup: enough workgroups x waves to keep the chip streaming.
+// Waves per workgroup: enough workgroups x waves to keep the chip streaming. With parts > 1
+// the slices' partial states are merged by a second launch (untimed: the clock stamps, when
+// attached, time the streaming launch).
 template <typename T, int HD, bool MEMORY>
 static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
                            const int64_t* pos, int64_t t_uniform, int window, int H, T* out,
-                           const Exec& st) {
+                           int parts, float* part, const Exec& st) {
   const float scale = 1.f / sqrtf((float)HD);
-  const int nw = BH >= 1024 ? 4 : BH >= 512 ? 8 : 16;
+  const int64_t blocks = (int64_t)BH * parts;
+  if (parts < 1 || parts > kMaxSplits || blocks > INT32_MAX) return hipErrorInvalidValue;
+  const int nw = blocks >= 1024 ? 4 : blocks >= 512 ? 8 : 16;
+  hipError_t e = hipSuccess;
 #define RLT_ATTEND(NW)                                                                     \
-  return launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,   \
-                dim3(BH), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, window, \
-                H, scale, out, st.clk)
+  e = launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,       \
+             dim3((unsigned)blocks), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, \
+             window, H, scale, out, parts, part, st.clk)
   if (nw == 4) RLT_ATTEND(4);
-  if (nw == 8) RLT_ATTEND(8);
-  RLT_ATTEND(16);
+  else if (nw == 8) RLT_ATTEND(8);
+  else RLT_ATTEND(16);
 #undef RLT_ATTEND
+  if (e != hipSuccess || parts == 1) return e;
+  const int64_t threads = (int64_t)BH * HD;
+  return launch(k_attend_merge<T, HD>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                dim3(kThreads), Exec(st.st), (const float*)part, parts, BH, H, out);
+}
+
+int cross_splits(const Dims& D, int B, int64_t t_max) {
+  // about 2048 workgroups in all (eight 4-wave workgroups per compute unit), and at least 256
+  // memory entries per slice
+  const int64_t bh = (int64_t)B * D.H, n = t_max + 1;
+  if (bh >= 1024) return 1;
+  int64_t parts = (2048 + bh - 1) / bh;
+  parts = std::min<int64_t>(parts, n / 256);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kMaxSplits));
 }
 
 template <typename T, int HD>
 static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, const Exec& st) {
   const int64_t layer = (int64_t)S.Bt * D.H * D.W * HD;
   return attend_t<T, HD, false>(B * D.H, S.q, elem<T>(S.ring_k, l * layer),
-                                elem<T>(S.ring_v, l * layer), (int64_t)D.W * HD, S.pos, S.t_uniform, D.W, D.H,
-                                static_cast<T*>(S.o), st);
+                                elem<T>(S.ring_v, l * layer), (int64_t)D.W * HD, S.pos,
+                                S.t_uniform, D.W, D.H, static_cast<T*>(S.o), 1, nullptr, st);
 }
 
 template <typename T, int HD>
@@ -200,7 +260,7 @@ static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const
   const int64_t grp = (int64_t)g * M.Bt * D.H * M.capacity * HD;
   return attend_t<T, HD, true>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
                                M.capacity * HD, S.pos, S.t_uniform, 0, D.H,
-                               static_cast<T*>(S.o), st);
+                               static_cast<T*>(S.o), cross_splits(D, B, S.t_max), S.part, st);
 }
 
 #define RLT_HD_DISPATCH(fn, ...)                                              \

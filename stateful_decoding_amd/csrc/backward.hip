@@ -1572,8 +1572,10 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     S.o = base + SL.o;
     S.act = base + SL.act;
     S.pos = reinterpret_cast<int64_t*>(base + SL.pos);
+    S.part = reinterpret_cast<float*>(base + SL.part);
     S.active = nullptr;
     S.t_uniform = 0;
+    S.t_max = 0;
   }
   MemBufs M{w.template at<void>(TL.mem_k), w.template at<void>(TL.mem_v), n, B};
   float* s_hist = w.template at<float>(TL.s_hist);
@@ -1622,6 +1624,7 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
       Timer& tg = gtm[gi];
       StateBufs& Sx = Sg[gi];
       Sx.t_uniform = i;
+      Sx.t_max = i;
       const double bg = rb, a32 = bg * d * 4, ad = bg * d * es;
       const double sh = bg / B;  // this group's share of each weight read
       RLT_TRY(gemm_gate(D, rb, P, Sx, e + ((int64_t)b0 * n + i) * d, n * d,

@@ -13,6 +13,10 @@
 namespace rlt {
 
 constexpr int kMaxWindow = 1024;
+// The memory attention of a small batch (fewer than 1024 sequence-head pairs) splits each
+// prefix into up to kMaxSplits contiguous parts, one workgroup each, and merges their partial
+// softmax states in a second launch.
+constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxCapacity = (int64_t)1 << 20;  // memory entries per sequence
 // Large batches run as row groups of about kGroupRows sequences (multiples of 16), each on its
 // own stream, at most kMaxGroups of them: one group's latency-bound projections then overlap
@@ -84,6 +88,8 @@ struct Packed {
 //   o     [B16][d] dtype       attention output (operand of the output projections)
 //   act   [B16][F] dtype       SiLU(f W1) * (f W3)
 //   pos   [B] int64            tokens each sequence has processed (its position t)
+//   part  [B][H][kMaxSplits][hd + 2] f32  partial softmax states of a split memory attention:
+//                              per part the unnormalised output (hd), its running max, its sum
 // hg, o and act are projection operands in MFMA fragment order, B16 = B rounded up to 16.
 struct StateBufs {
   int Bt;  // batch of the whole state: row stride of the per-layer ring blocks
@@ -98,12 +104,15 @@ struct StateBufs {
   void* o;
   void* act;
   int64_t* pos;
+  float* part;
   // rows that take part in the current step (device, one byte per row; NULL: all of them).
   // Other rows compute along but store nothing: their s, ring and position stay as they are.
   const uint8_t* active;
   // the position of every row when the host knows they are all equal, else -1 (kernels then
   // read pos per row); saves a dependent load at the start of each attention block
   int64_t t_uniform;
+  // the largest position any row can have (sizes the split of the memory attention)
+  int64_t t_max;
 };
 
 struct MemBufs {
@@ -121,7 +130,7 @@ MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0);
 
 // Byte layout of the state buffer; offsets are 256-byte aligned.
 struct StateLayout {
-  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, pos, total;
+  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, pos, part, total;
 };
 StateLayout state_layout(const Dims& D, int B);
 
@@ -227,6 +236,10 @@ hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P
 hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec& st);
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
                       const Exec& st);
+// Parts the memory attention of B rows splits each prefix into when the largest row position is
+// t_max (1: one workgroup per sequence and head, no merge launch). The timed main launch has
+// B * H * parts workgroups.
+int cross_splits(const Dims& D, int B, int64_t t_max);
 
 // ---- backward pass (backpropagation through time) ----------------------------------------------
 

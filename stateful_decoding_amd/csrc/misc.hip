@@ -170,6 +170,7 @@ StateBufs state_rows(const Dims& D, const StateBufs& S, int b0) {
   v.o = static_cast<char*>(S.o) + b0 * d * D.es;
   v.act = static_cast<char*>(S.act) + (int64_t)b0 * D.F * D.es;
   v.pos += b0;
+  v.part += (int64_t)b0 * D.H * kMaxSplits * (D.hd + 2);
   if (S.active) v.active += b0;
   const int64_t ring_row = (int64_t)D.H * D.W * D.hd * D.es;
   v.ring_k = static_cast<char*>(S.ring_k) + b0 * ring_row;
@@ -245,12 +246,15 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
   const double b = B, d = D.d, F = D.F, es = (double)D.es;
   const double act32 = b * d * 4, actd = b * d * es;
   // `call` launches one kernel on Exec x.
-  // the attention kernels (one workgroup per sequence and head) can time themselves
-  const int64_t attn_grid = (int64_t)B * D.H;
+  // the attention kernels (one workgroup per sequence and head, times the parts of a split
+  // memory prefix) can time themselves
+  const int64_t self_grid = (int64_t)B * D.H;
+  const int64_t cross_grid = self_grid * cross_splits(D, B, t0);
 #define RLT_TIMED(kind, bytes, flops, call)                                                 \
   do {                                                                                      \
     Exec x(st);                                                                             \
-    const int64_t grid = kind == RLT_K_SELF_ATTN || kind == RLT_K_CROSS_ATTN ? attn_grid : 0; \
+    const int64_t grid = kind == RLT_K_SELF_ATTN ? self_grid                                \
+                         : kind == RLT_K_CROSS_ATTN ? cross_grid : 0;                        \
     if (prof && (e = prof->arm(kind, bytes, flops, x, grid)) != hipSuccess) return e;       \
     if ((e = (call)) != hipSuccess) return e;                                               \
   } while (0)

@@ -1,8 +1,21 @@
 """Backpropagation through time on the GPU (rlt_bptt) against the float64 oracle's reverse
 traversal (oracle.bptt), for the loss sum_{b,t} G[b, t] . s_t(b) with seeded random G.
 
-Every gradient tensor is compared as a whole: relative L2 error ||gpu - oracle|| / ||oracle||,
-bounded by the same figure as the forward parity (1e-4 fp32, 3e-2 bf16)."""
+Every gradient tensor is compared as a whole and row by row. The whole tensor's relative L2
+error ||gpu - oracle|| / ||oracle|| is bounded by the figure of the forward parity (TOL: 1e-4
+fp32, 3e-2 bf16). Every row along the last axis of each weight gradient (one input feature's
+gradient over all outputs, per layer or group) and every [d] row of dLoss/de (one sequence and
+token) also has its own relative L2 error, bounded by ROW_TOL, so a wrong layer, head, row or
+token cannot hide inside the norm of a whole tensor: such a mistake leaves an error of the size
+of the row itself.
+
+ROW_TOL for bf16 is the whole-tensor bound times 10/3: the squared whole-tensor error is the
+mean of the squared row errors (rows of similar size), and the largest of R roughly Gaussian
+row errors exceeds their RMS by about sqrt(2 ln R), 3.0 to 4.8 for the 10^2 to 10^5 rows of
+these tensors. fp32 rows keep 1e-4: their errors sit at 1e-7 to 1e-6. The denominator of a row
+is its own norm, but never less than a quarter of its tensor's RMS row norm: a gradient row is
+a sum of products over batch and tokens whose rounding error scales with the magnitudes of its
+terms, i.e. with a typical row of the tensor, not with this row's (possibly cancelling) sum."""
 import numpy as np
 import pytest
 import torch
@@ -28,18 +41,63 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
 
 
+ROW_TOL = {"fp32": 1e-4, "bf16": 1e-1}  # largest per-row error (module docstring)
+ROW_FLOOR = 0.25  # a row's denominator is at least this fraction of its tensor's RMS row norm
+
+
+def row_rel_l2(got, ref, zero_scale: float):
+    """(whole-tensor, largest per-row) relative L2 error of one gradient tensor, rows along
+    the last axis.
+
+    A tensor whose exact gradient is zero (every row of the query and key weights when the
+    window holds one token) is judged on `zero_scale`, the typical row norm of the loss's
+    other gradients, so a rounding residue passes and a real leak does not. Rows are judged on
+    at least ROW_FLOOR times their tensor's RMS row norm (the module docstring says why)."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    g = g.reshape(-1, g.shape[-1]) if g.ndim > 1 else g.reshape(1, -1)
+    r = r.reshape(-1, r.shape[-1]) if r.ndim > 1 else r.reshape(1, -1)
+    num = np.linalg.norm(g - r, axis=-1)
+    den = np.linalg.norm(r, axis=-1)
+    rms = float(np.sqrt(np.mean(den ** 2)))
+    if rms == 0:
+        x = float(np.linalg.norm(g) / zero_scale)
+        return x, float(np.max(num) / zero_scale)
+    whole = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    return whole, float(np.max(num / np.maximum(den, ROW_FLOOR * rms)))
+
+
 def grad_errors(got: dict, ref: dict) -> dict:
-    """Relative L2 error per gradient tensor. A tensor whose exact gradient is zero (e.g. the
-    query and key weights when the window holds one token) is judged on the scale of the
-    loss's other gradients: ||got|| over their mean norm, so a rounding residue passes and a
-    real leak does not."""
-    norms = [float(np.linalg.norm(np.asarray(ref[k], np.float64))) for k in oracle.GRAD_NAMES]
-    scale = float(np.mean([x for x in norms if x > 0]))
-    out = {}
-    for k, nr in zip(oracle.GRAD_NAMES, norms):
-        diff = np.linalg.norm(np.asarray(got[k], np.float64) - np.asarray(ref[k], np.float64))
-        out[k] = float(diff / (nr if nr > 0 else scale))
-    return out
+    """(whole-tensor, largest per-row) relative L2 error of every gradient tensor
+    (row_rel_l2). The scale for exactly-zero tensors is the mean RMS row norm of the nonzero
+    gradient tensors."""
+    rms = []
+    for k in oracle.GRAD_NAMES:
+        r = np.asarray(ref[k], np.float64)
+        r = r.reshape(-1, r.shape[-1]) if r.ndim > 1 else r.reshape(1, -1)
+        x = float(np.sqrt(np.mean(np.sum(r * r, axis=-1))))
+        if x > 0:
+            rms.append(x)
+    scale = float(np.mean(rms))
+    return {k: row_rel_l2(got[k], ref[k], scale) for k in oracle.GRAD_NAMES}
+
+
+def de_errors(got, ref):
+    """(whole, largest per-row) relative L2 error of dLoss/de, rows of one sequence and token."""
+    r = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    den = np.linalg.norm(r, axis=-1)
+    scale = float(np.sqrt(np.mean(den[den > 0] ** 2))) if np.any(den > 0) else 1.0
+    return row_rel_l2(got, ref, scale)
+
+
+def check(errs: dict, dtype: str):
+    """Every (whole, row) pair within (TOL, ROW_TOL); plain floats (s_traj) within TOL."""
+    print("  rel L2 (whole/row):", " ".join(
+        f"{k}={v[0]:.1e}/{v[1]:.1e}" if isinstance(v, tuple) else f"{k}={v:.1e}"
+        for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        whole, row = v if isinstance(v, tuple) else (v, 0.0)
+        assert whole <= TOL[dtype] and row <= ROW_TOL[dtype], (k, whole, row)
 
 
 def run_case(cfg, B, T, seed):
@@ -58,11 +116,9 @@ def run_case(cfg, B, T, seed):
     got = {k: v.cpu().numpy() for k, v in grads.items()}
     ref_traj, ref, ref_de = oracle.bptt(p, cfg, e, G)
     errs = grad_errors(got, ref)
-    errs["de"] = rel_l2(de.cpu().numpy(), ref_de)
+    errs["de"] = de_errors(de.cpu().numpy(), ref_de)
     errs["s_traj"] = max_rel_l2(traj.cpu().numpy(), ref_traj)
-    worst = max(errs, key=errs.get)
-    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
-    return errs, worst
+    return errs
 
 
 CASES = [
@@ -75,6 +131,11 @@ CASES = [
     dict(dtype="bf16", B=300, T=40, d=128, n_heads=4, head_dim=32, ffn=192, window=6),
     dict(dtype="fp32", B=2, T=6, d=256, n_heads=2, head_dim=128, ffn=256, window=2),
     dict(dtype="bf16", B=3, T=1, d=128, n_heads=2, head_dim=64, ffn=256, window=5),  # one token
+    # d and F multiples of 128 in bf16: the weight gradients of all layers are formed by one
+    # batched launch per weight kind on the gradient stream. 272 sequences make 16-token
+    # chunks, so 40 tokens take three chunks, using both copies of the chunk buffers, with
+    # loss on every token
+    dict(dtype="bf16", B=272, T=40, d=128, n_heads=2, head_dim=64, ffn=256, window=6),
 ]
 
 
@@ -83,16 +144,14 @@ def test_bptt_matches_oracle(case):
     case = dict(case)
     B, T = case.pop("B"), case.pop("T")
     cfg = cfg_small(**case)
-    errs, worst = run_case(cfg, B, T, seed=B + T)
-    assert errs[worst] <= TOL[cfg.dtype], (worst, errs[worst])
+    check(run_case(cfg, B, T, seed=B + T), cfg.dtype)
 
 
 def test_bptt_chunked_rows_span_several_weight_gradient_chunks():
     """B = 300 sequences make 14-token weight-gradient chunks, so 40 tokens take three
     chunks, the first one short; fp32 holds that bookkeeping to the tight bound."""
     cfg = cfg_small(dtype="fp32", d=64, ffn=128, window=5)
-    errs, worst = run_case(cfg, 300, 40, seed=3)
-    assert errs[worst] <= TOL["fp32"], (worst, errs[worst])
+    check(run_case(cfg, 300, 40, seed=3), "fp32")
 
 
 def test_bptt_argument_errors():
@@ -147,13 +206,11 @@ def test_full_size_bptt_early_tokens_match_oracle():
     _, ref, ref_de = oracle.bptt(p, cfg, e_or, G[seqs, :n_or])
     errs = grad_errors({k: v.cpu().numpy() for k, v in grads.items()}, ref)
     de_h = de.cpu().numpy()
-    errs["de"] = rel_l2(de_h[seqs, :n_or], ref_de)
-    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    errs["de"] = de_errors(de_h[seqs, :n_or], ref_de)
     mask = np.ones(B, bool)
     mask[seqs] = False
     assert not np.any(de_h[mask]) and not np.any(de_h[seqs, n_or:])
-    worst = max(errs, key=errs.get)
-    assert errs[worst] <= TOL["bf16"], (worst, errs[worst])
+    check(errs, "bf16")
 
 
 @pytest.mark.parametrize("B", [5, 300])
@@ -179,8 +236,7 @@ def test_bptt_feedback_zero_start_state_gradient_is_exactly_zero():
     """With alpha = 0 nothing flows back into s_{t-1}: the start state's gradient is exactly
     zero and the rest still matches the oracle."""
     cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=5, alpha=0.0)
-    errs, worst = run_case(cfg, 4, 20, seed=11)
-    assert errs[worst] <= TOL["bf16"], (worst, errs[worst])
+    check(run_case(cfg, 4, 20, seed=11), "bf16")
     p, e = inputs(cfg, 4, 20, seed=11, random_gains=True, random_gate_bias=True)
     model = sd.Model(cfg, sd.upload_weights(p, sd.make_config(cfg)))
     ed = torch.from_numpy(np.ascontiguousarray(e)).to("cuda", model.dtype).contiguous()
@@ -246,10 +302,8 @@ def test_truncated_bptt_matches_oracle(case):
     torch.cuda.synchronize()
     _, ref, ref_de = oracle.bptt(p, cfg, e, G, segment=seg, detach=det)
     errs = grad_errors({k: v.cpu().numpy() for k, v in grads.items()}, ref)
-    errs["de"] = rel_l2(de.cpu().numpy(), ref_de)
-    print("  rel L2:", " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
-    worst = max(errs, key=errs.get)
-    assert errs[worst] <= TOL[cfg.dtype], (worst, errs[worst])
+    errs["de"] = de_errors(de.cpu().numpy(), ref_de)
+    check(errs, cfg.dtype)
 
 
 def test_detaching_the_state_alone_leaves_the_window_path_open():

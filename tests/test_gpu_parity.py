@@ -50,7 +50,12 @@ def test_tiny_fp32_config():
     dict(dtype="bf16", head_dim=64, window=7, n_groups=2, alpha=-0.5, B=33, T=30),
     dict(dtype="bf16", head_dim=128, n_heads=2, d=256, ffn=512, window=9, B=5, T=70,
          sigma=0.03),
-    dict(dtype="bf16", head_dim=64, window=16, B=3, T=300),  # memory split over 5 workgroups
+    dict(dtype="bf16", head_dim=64, window=16, B=3, T=300),
+    # few sequence-head pairs and long prefixes: the memory attention splits every prefix into
+    # up to 4 (fp32) or 5 (bf16) slices and merges them in a second launch
+    dict(dtype="fp32", head_dim=32, n_heads=4, window=6, B=3, T=1100, n_layers=1),
+    dict(dtype="bf16", head_dim=128, n_heads=2, d=256, ffn=512, window=9, B=2, T=1400,
+         n_layers=1, sigma=0.03),
     dict(dtype="fp32", head_dim=64, window=33, B=2, T=200, n_layers=1),
     # batches of >= 256 sequences run as row groups on separate streams
     dict(dtype="bf16", head_dim=64, window=6, n_groups=2, B=300, T=40),
@@ -271,17 +276,23 @@ def test_full_size_s50m():
     _full_size("s50m_bf16", seqs=(0, 37, 63), sample_ts=(1, 63, 64, 65, 1024), traj_T=1024)
 
 
+@pytest.mark.timeout(900)
 def test_full_size_s140m_bench_configuration():
-    # the benchmark's workload: one rlt_run_sequence over B=256, T=1024
-    _full_size("s140m_bf16", seqs=(0, 128, 255), sample_ts=(1, 2, 127, 128, 129, 512, 1024),
-               traj_T=32)
+    # the benchmark's workload: one rlt_run_sequence over B=256, T=1024 (two row groups of 128
+    # sequences: rows 127 and 128 are the last of the first group and the first of the second)
+    _full_size("s140m_bf16", seqs=(0, 1, 64, 127, 128, 191, 254, 255),
+               sample_ts=(1, 2, 127, 128, 129, 256, 384, 512, 640, 768, 896, 1024), traj_T=32)
 
 
+@pytest.mark.timeout(1200)
 def test_full_size_depth48():
-    _full_size("depth48_bf16", T=1024, seqs=(0, 31), sample_ts=(1, 255, 256, 257, 1024),
+    # the 48-layer workload at its stated length T = 4096: memory prefixes beyond 1024 entries
+    # at head size 128, and the caches retained after the last token
+    _full_size("depth48_bf16", seqs=(0, 31), sample_ts=(1, 255, 256, 257, 1024, 2048, 4096),
                traj_T=16)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["long_a1_bf16", "long_a0_bf16"])
 def test_full_size_long_context(name):
     cfg = CONFIGS[name]

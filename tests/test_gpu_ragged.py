@@ -30,10 +30,16 @@ def step(g, e_rows, active, B, d):
     dict(B=5, steps=24, dtype="bf16"),
     dict(B=37, steps=20, dtype="fp32", window=3, head_dim=32, n_heads=4),
     dict(B=300, steps=12, dtype="bf16", window=6),  # two row groups on two streams
+    # 12 sequence-head pairs and prefixes past 511 entries: the memory attention is split in
+    # two slices per row, merged by a second launch; the rarely ready row leaves its second
+    # slice empty
+    dict(B=3, steps=700, dtype="fp32", window=5, head_dim=32, n_heads=4, n_layers=1,
+         n_groups=1, probs=(0.9, 0.6, 0.01)),
 ])
 def test_ragged_schedule_matches_oracle(case):
     case = dict(case)
     B, steps = case.pop("B"), case.pop("steps")
+    probs = np.array(case.pop("probs", (0.6,) * B))
     cfg = cfg_small(**case)
     T = steps
     p, e = inputs(cfg, B, T, seed=B + steps, random_gains=True, random_gate_bias=True)
@@ -44,7 +50,7 @@ def test_ragged_schedule_matches_oracle(case):
     outs = {b: [] for b in range(B)}
     s_prev = np.broadcast_to(p["s_star"].astype(np.float32), (B, cfg.d)).copy()
     for i in range(steps):
-        active = rng.random(B) < 0.6
+        active = rng.random(B) < probs
         if i == 3:
             active[:] = False  # a step where nothing is ready
         rows = np.stack([e[b, min(pos[b], T - 1)] for b in range(B)])
