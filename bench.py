@@ -95,12 +95,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--mode", choices=("recurrent", "parallel", "train", "ragged"),
+    ap.add_argument("--mode", choices=("recurrent", "parallel", "train", "ragged", "head"),
                     default="recurrent",
                     help="recurrent: rlt_run_sequence (the headline); parallel: the token-parallel "
                          "pass for alpha = 0 (rlt_run_parallel); train: forward + "
                          "backpropagation through time (rlt_bptt); ragged: ready updates "
-                         "(rlt_decoder_step_ragged) with a random 75%% of sequences ready per step")
+                         "(rlt_decoder_step_ragged) with a random 75%% of sequences ready per step; "
+                         "head: the causal encoder over the prompt (rlt_encode) and the readout "
+                         "with sampling (rlt_readout)")
     ap.add_argument("--workload", default=None,
                     help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -162,6 +164,9 @@ def main():
         return bench_train(args, cfg, params, model, e, traj, stream)
     if args.mode == "ragged":
         return bench_ragged(args, cfg, params, model, state, mem, e, stream)
+    if args.mode == "head":
+        del state, mem, e, traj
+        return bench_head(args, cfg, params, model, stream)
 
     def one_step():
         state.reset(stream)
@@ -174,8 +179,8 @@ def main():
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
     # one clock slot pair per workgroup (sequence, head, and slice of the prefix when fewer
-    # than 1024 sequence-head pairs split it into up to 16) of every timed memory attention
-    per_bh = 1 if B * cfg.n_heads >= 1024 else 16
+    # than 128 sequence-head pairs split it into up to 16) of every timed memory attention
+    per_bh = 1 if B * cfg.n_heads >= 128 else 16
     stride = args.profile_stride or (1 if per_bh == 1 else 16)
     timed_tokens = (T + stride - 1) // stride
     state.profile_clock(args.steps * timed_tokens * cfg.n_layers * B * cfg.n_heads * per_bh)
@@ -346,7 +351,7 @@ def bench_ragged(args, cfg, params, model, state, mem, e, stream, ready: float =
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
     stride = args.profile_stride or 1
-    per_bh = 1 if B * cfg.n_heads >= 1024 else 16
+    per_bh = 1 if B * cfg.n_heads >= 128 else 16
     state.profile_clock(args.steps * ((T + stride - 1) // stride) * L * B * cfg.n_heads * per_bh)
     state.profile_begin(["cross_attn"], token_stride=stride)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -430,6 +435,82 @@ def cpu_baseline_train(cfg, params, budget_s: float, n_seqs: int = 2) -> dict:
                       f"sequences, tokens 1..{n} of {cfg.seq_len}, {wall:.1f} s; short prefixes "
                       "overstate the whole-run rate",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def encoder_flops(cfg, B: int, n: int) -> float:
+    """Algorithmic flops of the encoder over n tokens of B sequences: per token and block the
+    q/k/v/o, up and down products and causal attention over positions 1..t."""
+    d, L, F = cfg.d, cfg.n_layers, cfg.ffn
+    per_token = 2 * (4 * d * d + 3 * d * F)
+    attn = 4 * d * (n * (n + 1) / 2)  # scores and weighted values, all positions of a sequence
+    return L * B * (n * per_token + attn)
+
+
+def bench_head(args, cfg, params, model, stream):
+    """One step: the encoder over the whole prompt (B x T token ids) and one readout with
+    sampling of B rows. value = prompt tokens encoded per second."""
+    import numpy as np
+    import torch
+
+    import stateful_decoding_amd as sd
+    from synth import VOCAB, make_head_params, make_tokens, make_uniforms
+
+    B, T, V = cfg.batch, cfg.seq_len, VOCAB
+    head = sd.Head(model, V, sd.upload_head_weights(make_head_params(cfg, V), model.cfg))
+    tok = torch.from_numpy(make_tokens(range(B), T, V)).cuda()
+    e = torch.empty(B, T, cfg.d, dtype=model.dtype, device="cuda")
+    ws = torch.empty(model.lib.rlt_encode_ws_bytes(sd.binding.byref(model.cfg), B, T),
+                     dtype=torch.uint8, device="cuda")
+    s = torch.randn(B, cfg.d, device="cuda", generator=torch.Generator("cuda").manual_seed(0))
+    u = torch.from_numpy(make_uniforms(B)).cuda()
+    rws = sd.readout_workspace(head, B)
+    lg = torch.empty(B, V, device="cuda")
+
+    def encode():
+        sd.rlt_encode(head, tok, e, ws, stream)
+
+    def readout():
+        return sd.rlt_readout(head, s, u, 0.8, 50, 0.95, logits=lg, ws=rws, stream=stream)
+
+    for _ in range(args.warmup):
+        encode()
+        readout()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        encode()
+    b.record(stream)
+    torch.cuda.synchronize()
+    enc_ms = a.elapsed_time(b) / args.steps
+    reps = 20
+    a.record(stream)
+    for _ in range(reps * args.steps):
+        readout()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ro_us = a.elapsed_time(b) * 1e3 / (reps * args.steps)
+    assert bool(torch.isfinite(e.float()).all()), "non-finite encoder output"
+    fl = encoder_flops(cfg, B, T)
+    ro_bytes = 2 * V * cfg.d + B * V * 4 + B * cfg.d * 4  # W_out once, logits written once
+    out = {
+        "metric": "RLT causal encoder prompt tokens/sec (B seqs x T) on 1 MI355X",
+        "value": round(B * T / (enc_ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(enc_ms, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "mode": "head", "batch": B, "seq_len": T,
+                   "vocab": V, "d": cfg.d, "encoder_blocks": cfg.n_layers,
+                   "inputs": "token ids uniform over the vocabulary, weights ~ N(0,0.02), seed 0"},
+        "roofline": {"bound": "mfma", "kernel": "whole encoder pass",
+                     "achieved": round(fl / (enc_ms / 1e3) / 1e12, 1),
+                     "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": round(fl / (enc_ms / 1e3) / BF16_PEAK, 4), "traffic": None},
+        "readout": {"us_per_call": round(ro_us, 1), "rows": B, "vocab": V,
+                    "sampling": "temperature 0.8, top-k 50, top-p 0.95",
+                    "hbm_bound_us": round(ro_bytes / HBM_PEAK * 1e6, 2)},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_train(args, cfg, params, model, e, traj, stream):

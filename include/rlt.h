@@ -329,6 +329,83 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
                     size_t ws_bytes, const rlt_truncation* trunc, const struct rlt_timing* timing,
                     struct rlt_kernel_stats* stats, void* stream);
 
+/* --- encoder and readout around the decoder ------------------------------------------------
+ * "RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", "Architecture: encoder memory
+ * meets recurrent decoder": a causal encoder processes the tokens in parallel and produces the
+ * e_t the memory is projected from; in the tied configuration its blocks share the decoder
+ * blocks' attention and FFN weights; the next-token distribution is read from s_t. Same page,
+ * "Three design principles and their caveats" (model-RL co-design): the sampler records each
+ * action's behaviour log-probability under the distribution it sampled from, temperature and
+ * truncation included. Readings (the pages give no formulas):
+ *   x_0 = E[token];  encoder block l: x += Attn_causal(RMSNorm(x; g_l0)) W_o[l] (positions
+ *   1..t, W_q/W_k/W_v/W_o of decoder block l), x += FFN_l(RMSNorm(x; g_l1)) (decoder block l's
+ *   W_1, W_3, W_2);  e = RMSNorm(x; g_out).  logits = RMSNorm(s; gamma_out) W_out.
+ *   Sampling: q = softmax(logits / temperature); order tokens by descending logit, ties by
+ *   ascending id; top-k keeps the first k (0: all), top-p the shortest prefix of those whose
+ *   mass reaches top_p times their mass (1: all); pi = q on the kept tokens, renormalised; the
+ *   action is the first kept token, in ascending id, at which the running sum of pi exceeds u.
+ *   temperature 0 = greedy (first maximal logit, probability 1). */
+
+/* Head weights (device pointers, only read during rlt_head_create). */
+typedef struct rlt_head_weights {
+  const void* embed;          /* [V][d] dtype      token embedding E                          */
+  const float* enc_gamma;     /* [L][2][d]         encoder gains before attention and FFN     */
+  const float* enc_gamma_out; /* [d]               gain of the norm that gives e               */
+  const float* out_gamma;     /* [d]               gain of the readout's norm of s             */
+  const void* w_out;          /* [d][V] dtype      readout matrix                              */
+} rlt_head_weights;
+typedef struct rlt_head rlt_head;
+
+/* Bytes of device workspace rlt_head_create needs for vocabulary size V (0 if invalid: V must
+ * be a multiple of 64 in [64, 2^22]). */
+size_t rlt_head_ws_bytes(const rlt_config* cfg, int32_t vocab);
+
+/* Copies and packs the head weights into `ws` (device, 256-byte aligned, >= rlt_head_ws_bytes)
+ * on `stream` and waits for it, so the sources may be freed on return. The encoder uses the
+ * model's packed attention and FFN matrices, so the head is bound to `model`. */
+rlt_status rlt_head_create(const rlt_model* model, int32_t vocab, const rlt_head_weights* w,
+                           void* ws, size_t ws_bytes, void* stream, rlt_head** out);
+void rlt_head_destroy(rlt_head* head);
+
+/* Device workspace bytes of rlt_encode for B sequences of n tokens (0 if invalid, or for fp32
+ * models: the encoder is bf16 only). */
+size_t rlt_encode_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n);
+
+/* Token-parallel causal encoder: token ids [B][n] int32 (device, 4-byte aligned; ids outside
+ * [0, V) embed as zero vectors) -> e [B][n][d] dtype (device, 16-byte aligned), ready for
+ * rlt_memproj / rlt_run_sequence. ws: device, 256-byte aligned, >= rlt_encode_ws_bytes
+ * (RLT_ERR_CAPACITY), scratch owned by the caller. bf16 models only (RLT_ERR_DTYPE).
+ * Asynchronous on `stream`. */
+rlt_status rlt_encode(const rlt_model* model, const rlt_head* head, const int32_t* tokens,
+                      int32_t batch, int64_t n, void* e, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Sampling parameters: temperature >= 0 (0 = greedy), top_k >= 0 (0 = off), top_p in (0, 1]
+ * (1 = off). */
+typedef struct rlt_sampling {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} rlt_sampling;
+
+/* Device workspace bytes of rlt_readout for B rows (0 if invalid). */
+size_t rlt_readout_ws_bytes(const rlt_config* cfg, int32_t vocab, int32_t batch);
+
+/* Readout and sampling of B rows s [B][d] float32 (device; e.g. s_out of a decoder step): the
+ * logits (float32 [B][V] into `logits` when non-NULL, else into ws), then per row b, with the
+ * uniform u[b] in [0, 1) (device float32 [B], drawn by the caller), the action tokens[b]
+ * (device int32), its behaviour log-probability log pi(action) under the tempered, truncated
+ * distribution logp_behaviour[b] (0 when greedy) and its model log-probability
+ * log softmax(logits)(action) at temperature 1 without truncation logp_model[b] (device float32
+ * [B] each). Every decision (truncation sets, inverse CDF) is taken on exact integers: fixed-point
+ * probabilities (2^-40 units) and an order-preserving key of each logit. RLT_ERR_ARG for
+ * parameters out of range or NULL outputs; ws: device, 256-byte aligned,
+ * >= rlt_readout_ws_bytes (RLT_ERR_CAPACITY). Asynchronous on `stream`. */
+rlt_status rlt_readout(const rlt_model* model, const rlt_head* head, const float* s,
+                       int32_t batch, const rlt_sampling* sampling, const float* u,
+                       int32_t* tokens, float* logp_behaviour, float* logp_model, float* logits,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* --- snapshots ("exact prefix snapshot" of the serving section of the same page) ------ */
 
 /* Copies the state to caller buffers in canonical order and waits for the stream:
@@ -415,7 +492,7 @@ rlt_status rlt_profile_end(rlt_state* state, rlt_kernel_stats* out);
  * rlt_profile_end takes each launch's earliest start and latest end. Nothing is queued around
  * the launch that could change how concurrent streams overlap, and no two workgroups write the
  * same address. The kernels run one workgroup per (sequence, head): a timed launch takes
- * 16 * H bytes per sequence of its batch; a memory attention whose batch has fewer than 1024
+ * 16 * H bytes per sequence of its batch; a memory attention whose batch has fewer than 128
  * sequence-head pairs splits each prefix into up to 16 slices of at least 256 entries, one
  * workgroup each (16 * H * slices bytes per sequence), and merges them in a second, untimed
  * launch. rlt_profile_begin clears the slots (it waits for the

@@ -64,6 +64,18 @@ class rlt_kernel_stats(ctypes.Structure):
                 ("flops", ctypes.c_double)]
 
 
+HEAD_FIELDS = ("embed", "enc_gamma", "enc_gamma_out", "out_gamma", "w_out")
+HEAD_FP32_FIELDS = ("enc_gamma", "enc_gamma_out", "out_gamma")
+
+
+class rlt_head_weights(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in HEAD_FIELDS]
+
+
+class rlt_sampling(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("top_k", c_int32), ("top_p", c_float)]
+
+
 class RLTError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -117,6 +129,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
         "rlt_state_import_ragged": (c_int32, [P, P, P, P, P, c_uint64, P]),
         "rlt_bptt_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
+        "rlt_head_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32]),
+        "rlt_head_create": (c_int32, [P, c_int32, POINTER(rlt_head_weights), P, c_size_t, P,
+                                      POINTER(c_void_p)]),
+        "rlt_head_destroy": (None, [P]),
+        "rlt_encode_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
+        "rlt_encode": (c_int32, [P, P, P, c_int32, c_int64, P, P, c_size_t, P]),
+        "rlt_readout_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int32]),
+        "rlt_readout": (c_int32, [P, P, P, c_int32, POINTER(rlt_sampling), P, P, P, P, P, P,
+                                  c_size_t, P]),
         "rlt_bptt": (c_int32, [P, P, c_int32, c_int64, P, P, POINTER(rlt_grads), P, P, c_size_t,
                                POINTER(rlt_truncation), POINTER(rlt_timing), P, P]),
     }
@@ -502,3 +523,93 @@ def rlt_state_import_ragged(state: State, s: torch.Tensor, k: torch.Tensor, v: t
     pos = (c_int64 * state.batch)(*[int(x) for x in positions])
     _check(state.lib.rlt_state_import_ragged(state.handle, s.data_ptr(), k.data_ptr(),
                                              v.data_ptr(), pos, int(version), _stream(stream)))
+
+
+# ---- encoder and readout around the decoder ------------------------------------------------------
+
+def upload_head_weights(params: dict, cfg: rlt_config, device="cuda") -> dict:
+    """Host arrays -> contiguous device tensors in the layouts of rlt_head_weights (matrices and
+    the embedding in the config dtype, gains in float32)."""
+    out = {}
+    dt = torch_dtype(cfg)
+    for name in HEAD_FIELDS:
+        x = params[name]
+        x = torch.as_tensor(x) if not isinstance(x, torch.Tensor) else x
+        out[name] = x.to(device=device,
+                         dtype=torch.float32 if name in HEAD_FP32_FIELDS else dt).contiguous()
+    return out
+
+
+class Head:
+    """Encoder and readout weights bound to a model (rlt_head_create)."""
+
+    def __init__(self, model: Model, vocab: int, weights: dict, stream=None):
+        self.lib, self.model, self.vocab = model.lib, model, int(vocab)
+        nbytes = self.lib.rlt_head_ws_bytes(byref(model.cfg), self.vocab)
+        if nbytes == 0:
+            raise RLTError(2, f"invalid vocabulary size {vocab}")
+        self.ws = _device_buffer(nbytes, model.ws.device)
+        w = rlt_head_weights(*[_ptr(weights[n]) for n in HEAD_FIELDS])
+        h = c_void_p()
+        _check(self.lib.rlt_head_create(model.handle, self.vocab, byref(w), self.ws.data_ptr(),
+                                        nbytes, _stream(stream), byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self.lib.rlt_head_destroy(self.handle)
+            self.handle = None
+
+
+def rlt_encode(head: Head, tokens: torch.Tensor, e: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Token-parallel causal encoder over token ids [B, n] (int32, device) -> e [B, n, d]."""
+    m = head.model
+    B, n = tokens.shape
+    if tokens.dtype != torch.int32 or not tokens.is_contiguous():
+        raise ValueError("tokens must be a contiguous int32 tensor")
+    if e is None:
+        e = torch.empty(B, n, m.cfg.d, dtype=m.dtype, device=tokens.device)
+    _need(e, (B, n, m.cfg.d), m.dtype, "e")
+    if ws is None:
+        nbytes = head.lib.rlt_encode_ws_bytes(byref(m.cfg), int(B), int(n))
+        if nbytes == 0:
+            raise RLTError(3 if m.cfg.dtype != RLT_BF16 else 2,
+                           "the encoder needs a bf16 model and a valid batch and length")
+        ws = _device_buffer(nbytes, tokens.device)
+    _check(head.lib.rlt_encode(m.handle, head.handle, tokens.data_ptr(), int(B), int(n),
+                               e.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                               _stream(stream)))
+    return e
+
+
+def readout_workspace(head: Head, batch: int) -> torch.Tensor:
+    nbytes = head.lib.rlt_readout_ws_bytes(byref(head.model.cfg), head.vocab, int(batch))
+    if nbytes == 0:
+        raise RLTError(2, f"invalid batch {batch}")
+    return _device_buffer(nbytes, head.ws.device)
+
+
+def rlt_readout(head: Head, s: torch.Tensor, u: torch.Tensor, temperature: float = 1.0,
+                top_k: int = 0, top_p: float = 1.0, logits: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None, stream=None):
+    """Readout and sampling of s [B, d] (float32) with uniforms u [B] (float32): returns
+    (tokens [B] int32, logp_behaviour [B], logp_model [B]) as device tensors; `logits`
+    [B, V] float32 receives the logits when given."""
+    m = head.model
+    B = s.shape[0]
+    _need(s, (B, m.cfg.d), torch.float32, "s")
+    _need(u, (B,), torch.float32, "u")
+    if logits is not None:
+        _need(logits, (B, head.vocab), torch.float32, "logits")
+    if ws is None:
+        ws = readout_workspace(head, B)
+    tok = torch.empty(B, dtype=torch.int32, device=s.device)
+    lpb = torch.empty(B, dtype=torch.float32, device=s.device)
+    lpm = torch.empty(B, dtype=torch.float32, device=s.device)
+    sp = rlt_sampling(float(temperature), int(top_k), float(top_p))
+    _check(head.lib.rlt_readout(m.handle, head.handle, s.data_ptr(), int(B), byref(sp),
+                                u.data_ptr(), tok.data_ptr(), lpb.data_ptr(), lpm.data_ptr(),
+                                _ptr(logits), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+    return tok, lpb, lpm

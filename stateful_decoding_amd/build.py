@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlt.so")
 
-SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "misc.hip", "parallel.hip", "backward.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "misc.hip", "parallel.hip", "backward.hip",
+           "head.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -51,6 +51,11 @@ struct rlt_memory {
   MemBufs M;
 };
 
+struct rlt_head {
+  const rlt_model* model;
+  HeadBufs Hd;
+};
+
 namespace {
 
 thread_local std::string g_err;
@@ -147,6 +152,52 @@ P* at(void* base, size_t off) {
 }
 
 bool valid_batch(int B) { return B >= 1 && B <= (1 << 20); }
+
+constexpr int kMaxVocab = 1 << 22;
+
+struct HeadLayout {
+  size_t embed, w_out_t, enc_gamma, enc_gamma_out, out_gamma, total;
+};
+
+HeadLayout head_layout(const Dims& D, int V) {
+  HeadLayout h;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  h.embed = take((size_t)V * D.d * D.es);
+  h.w_out_t = take((size_t)V * D.d * D.es);
+  h.enc_gamma = take((size_t)D.L * 2 * D.d * 4);
+  h.enc_gamma_out = take((size_t)D.d * 4);
+  h.out_gamma = take((size_t)D.d * 4);
+  h.total = o;
+  return h;
+}
+
+bool valid_vocab(int V) { return V >= 64 && V <= kMaxVocab && V % 64 == 0; }
+
+struct ReadoutLayout {
+  size_t hg, ssq, logits, fq, total;
+};
+
+ReadoutLayout readout_layout(const Dims& D, int V, int B) {
+  ReadoutLayout r;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t b16 = ((size_t)B + 15) / 16 * 16;
+  r.hg = take(b16 * D.d * D.es);
+  r.ssq = take((size_t)B * (D.d / 32) * 4);
+  r.logits = take((size_t)B * V * 4);
+  r.fq = take((size_t)B * V * 8);
+  r.total = o;
+  return r;
+}
 
 }  // namespace
 
@@ -887,6 +938,127 @@ rlt_status rlt_bptt(const rlt_model* model, const void* e, int32_t batch, int64_
   if (dropped > 0)
     return fail(RLT_ERR_CAPACITY, "the clock buffer holds %lld workgroup slots; %lld more "
                 "launches were not timed", (long long)prof.clk_cap, (long long)dropped);
+  return ok();
+}
+
+// ---- encoder and readout around the decoder ----------------------------------------------------
+
+size_t rlt_head_ws_bytes(const rlt_config* cfg, int32_t vocab) {
+  if (check_config(cfg) != RLT_OK || !valid_vocab(vocab)) return 0;
+  return head_layout(dims_of(*cfg), vocab).total;
+}
+
+rlt_status rlt_head_create(const rlt_model* model, int32_t vocab, const rlt_head_weights* w,
+                           void* ws, size_t ws_bytes, void* stream, rlt_head** out) {
+  if (!model || !w || !ws || !out)
+    return fail(RLT_ERR_ARG, "model, weights, workspace and out must be non-NULL");
+  if (!w->embed || !w->enc_gamma || !w->enc_gamma_out || !w->out_gamma || !w->w_out)
+    return fail(RLT_ERR_ARG, "a head weight pointer is NULL");
+  if (!valid_vocab(vocab))
+    return fail(RLT_ERR_SHAPE, "vocab %d must be a multiple of 64 in [64, %d]", vocab, kMaxVocab);
+  if (!aligned(ws)) return fail(RLT_ERR_ARG, "workspace must be 256-byte aligned");
+  const Dims& D = model->D;
+  const HeadLayout L = head_layout(D, vocab);
+  if (ws_bytes < L.total)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  rlt_head* h = new (std::nothrow) rlt_head;
+  if (!h) return fail(RLT_ERR_ARG, "out of host memory");
+  h->model = model;
+  h->Hd.vocab = vocab;
+  h->Hd.embed = at<char>(ws, L.embed);
+  h->Hd.w_out_t = at<char>(ws, L.w_out_t);
+  h->Hd.enc_gamma = at<float>(ws, L.enc_gamma);
+  h->Hd.enc_gamma_out = at<float>(ws, L.enc_gamma_out);
+  h->Hd.out_gamma = at<float>(ws, L.out_gamma);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t d = D.d;
+  hipError_t e = hipMemcpyAsync(h->Hd.embed, w->embed, (size_t)vocab * d * D.es,
+                                hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = launch_pack_transpose(D.dtype, w->w_out, (int)d, vocab, h->Hd.w_out_t, 0, vocab, vocab,
+                              st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->Hd.enc_gamma, w->enc_gamma, (size_t)D.L * 2 * d * 4,
+                       hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->Hd.enc_gamma_out, w->enc_gamma_out, d * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->Hd.out_gamma, w->out_gamma, d * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "packing the head weights");
+  }
+  *out = h;
+  return ok();
+}
+
+void rlt_head_destroy(rlt_head* head) { delete head; }
+
+size_t rlt_encode_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
+  if (check_config(cfg) != RLT_OK || cfg->dtype != RLT_BF16 || !valid_batch(batch) || n < 1 ||
+      n > kMaxCapacity || (int64_t)batch * n > INT32_MAX / 2)
+    return 0;
+  return par_layout(dims_of(*cfg), batch, n).total;
+}
+
+rlt_status rlt_encode(const rlt_model* model, const rlt_head* head, const int32_t* tokens,
+                      int32_t batch, int64_t n, void* e, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!model || !head || !tokens || !e || !ws)
+    return fail(RLT_ERR_ARG, "model, head, tokens, e and ws must be non-NULL");
+  if (head->model != model) return fail(RLT_ERR_ARG, "head belongs to another model");
+  const Dims& D = model->D;
+  if (D.dtype != RLT_BF16) return fail(RLT_ERR_DTYPE, "the encoder is bf16 only");
+  if (!valid_batch(batch)) return fail(RLT_ERR_SHAPE, "batch %d out of range", batch);
+  if (n < 1 || n > kMaxCapacity)
+    return fail(RLT_ERR_SHAPE, "n = %lld must be in [1, %lld]", (long long)n,
+                (long long)kMaxCapacity);
+  if ((int64_t)batch * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "batch * n too large");
+  if (reinterpret_cast<uintptr_t>(tokens) % 4 != 0 || !aligned16(e) || !aligned(ws))
+    return fail(RLT_ERR_ARG, "tokens must be 4-byte, e 16-byte and ws 256-byte aligned");
+  const size_t need = par_layout(D, batch, n).total;
+  if (ws_bytes < need)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipError_t err = launch_encode(D, batch, n, model->P, head->Hd, tokens, e, ws,
+                                 static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "encoder");
+  return ok();
+}
+
+size_t rlt_readout_ws_bytes(const rlt_config* cfg, int32_t vocab, int32_t batch) {
+  if (check_config(cfg) != RLT_OK || !valid_vocab(vocab) || !valid_batch(batch)) return 0;
+  return readout_layout(dims_of(*cfg), vocab, batch).total;
+}
+
+rlt_status rlt_readout(const rlt_model* model, const rlt_head* head, const float* s,
+                       int32_t batch, const rlt_sampling* sp, const float* u, int32_t* tokens,
+                       float* logp_behaviour, float* logp_model, float* logits, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!model || !head || !s || !sp || !u || !tokens || !logp_behaviour || !logp_model || !ws)
+    return fail(RLT_ERR_ARG, "model, head, s, sampling, u, tokens, log-probability outputs and "
+                "ws must be non-NULL");
+  if (head->model != model) return fail(RLT_ERR_ARG, "head belongs to another model");
+  if (!valid_batch(batch)) return fail(RLT_ERR_SHAPE, "batch %d out of range", batch);
+  if (!std::isfinite(sp->temperature) || sp->temperature < 0.f)
+    return fail(RLT_ERR_ARG, "temperature must be finite and >= 0");
+  if (sp->top_k < 0) return fail(RLT_ERR_ARG, "top_k must be >= 0");
+  if (!(sp->top_p > 0.f && sp->top_p <= 1.f)) return fail(RLT_ERR_ARG, "top_p must be in (0, 1]");
+  if (!aligned16(s) || (logits && !aligned16(logits)) || !aligned(ws))
+    return fail(RLT_ERR_ARG, "s and logits must be 16-byte aligned, ws 256-byte aligned");
+  const Dims& D = model->D;
+  const int V = head->Hd.vocab;
+  const ReadoutLayout L = readout_layout(D, V, batch);
+  if (ws_bytes < L.total)
+    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* lg = logits ? logits : at<float>(ws, L.logits);
+  hipError_t err = launch_readout_logits(D, batch, head->Hd, s, at<char>(ws, L.hg),
+                                         at<float>(ws, L.ssq), lg, st);
+  if (err == hipSuccess)
+    err = launch_sample(batch, V, lg, sp->temperature, sp->top_k, sp->top_p, u,
+                        at<char>(ws, L.fq), tokens, logp_behaviour, logp_model, st);
+  if (err != hipSuccess) return hip_fail(err, "readout");
   return ok();
 }
 

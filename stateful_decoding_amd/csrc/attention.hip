@@ -21,6 +21,25 @@
 
 namespace rlt {
 
+// Rows per lane slot loaded per batch, and the largest grid of an attention launch (0: one
+// workgroup per item).
+#ifndef RLT_ATTN_U
+#define RLT_ATTN_U 4
+#endif
+#ifndef RLT_ATTN_CAP
+#define RLT_ATTN_CAP 0
+#endif
+#ifndef RLT_SPLIT_LIMIT
+#define RLT_SPLIT_LIMIT kMaxSplits
+#endif
+#ifndef RLT_ATTN_PIPE
+#define RLT_ATTN_PIPE 0
+#endif
+constexpr int kAttnU = RLT_ATTN_U;
+constexpr bool kAttnPipe = RLT_ATTN_PIPE != 0;
+constexpr int64_t kAttnCap = RLT_ATTN_CAP;
+constexpr int kSplitLimit = RLT_SPLIT_LIMIT;
+
 template <typename T, int HD>
 struct Geo {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte load
@@ -41,6 +60,45 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = mn;
 }
 
+// One batch of U rows per row slot: scores, one rescale of the running state to the batch's
+// max, then the weighted values. Rows past n (score -inf) contribute nothing.
+template <typename T, int HD, int U>
+__device__ __forceinline__ void step_batch(const u32x4* kr, const u32x4* vr, int base, int RPB,
+                                           int first, int n, const float* qv, float& m,
+                                           float& l, float* acc) {
+  using G = Geo<T, HD>;
+  float sc[U];
+  float mb = m;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float kf[G::VEC];
+    unpack(kr[u], kf);
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < G::VEC; ++i) dot += qv[i] * kf[i];
+#pragma unroll
+    for (int o = G::LPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+    const bool ok = base + u * RPB + first < n;
+    sc[u] = ok ? dot : -INFINITY;
+    mb = fmaxf(mb, sc[u]);
+  }
+  if (mb == -INFINITY) return;  // this slot had no rows in the batch
+  const float c = m == -INFINITY ? 0.f : __expf(m - mb);
+  l *= c;
+#pragma unroll
+  for (int i = 0; i < G::VEC; ++i) acc[i] *= c;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float p = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - mb);
+    float vf[G::VEC];
+    unpack(vr[u], vf);
+    l += p;
+#pragma unroll
+    for (int i = 0; i < G::VEC; ++i) acc[i] += p * vf[i];
+  }
+  m = mb;
+}
+
 // NW waves per (sequence, head, part): softmax attention of one query over the rows of a
 // contiguous [rows][HD] key block and value block, in a single pass. The sequence attends rows
 // [0, n), n from its own position, so sequences of one batch may be at different tokens; with
@@ -57,12 +115,12 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
                                        const T* __restrict__ V, int64_t bh_stride,
                                        const int64_t* __restrict__ pos, int64_t t_uniform,
                                        int window, int H, float scale, T* __restrict__ out,
-                                       int parts, float* __restrict__ part) {
+                                       int parts, float* __restrict__ part, int item) {
   using G = Geo<T, HD>;
   constexpr int RPB = G::RPW * NW;  // rows per block per batch step
   __shared__ float lds_m[NW], lds_l[NW];
   __shared__ float lds_acc[NW][HD];
-  const int bh = blockIdx.x / parts, pi = blockIdx.x - bh * parts;
+  const int bh = item / parts, pi = item - bh * parts;
   const int b = bh / H, hh = bh - b * H, d = H * HD;
   // rows attended: the memory prefix 1..t+1 of this sequence, or its window of
   // min(t + 1, W) ring slots (t = tokens the sequence has processed before this step)
@@ -83,45 +141,35 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
 #pragma unroll
   for (int i = 0; i < G::VEC; ++i) acc[i] = 0.f;
   const int first = wave * G::RPW + slot;
-  for (int base = 0; base < n; base += RPB * U) {
-    u32x4 kr[U], vr[U];
+  u32x4 kr[U], vr[U];
+  auto fetch = [&](int base, u32x4* kd, u32x4* vd) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = base + u * RPB + first;
       const bool ok = row < n;
-      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
-      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      kd[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vd[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
     }
-    float sc[U];
-    float mb = m;
+  };
+  if constexpr (kAttnPipe) fetch(0, kr, vr);
+  for (int base = 0; base < n; base += RPB * U) {
+    if constexpr (kAttnPipe) {
+      // the next batch's loads go out before this batch is used
+      u32x4 kn[U], vn[U];
+      fetch(base + RPB * U, kn, vn);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[G::VEC];
-      unpack(kr[u], kf);
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < G::VEC; ++i) dot += qv[i] * kf[i];
-#pragma unroll
-      for (int o = G::LPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-      const bool ok = base + u * RPB + first < n;
-      sc[u] = ok ? dot : -INFINITY;
-      mb = fmaxf(mb, sc[u]);
+      for (int u = 0; u < U; ++u) {
+        const u32x4 tk = kr[u], tv = vr[u];
+        kr[u] = kn[u];
+        vr[u] = vn[u];
+        kn[u] = tk;
+        vn[u] = tv;
+      }
+      step_batch<T, HD, U>(kn, vn, base, RPB, first, n, qv, m, l, acc);
+    } else {
+      fetch(base, kr, vr);
+      step_batch<T, HD, U>(kr, vr, base, RPB, first, n, qv, m, l, acc);
     }
-    if (mb == -INFINITY) continue;  // this slot had no rows in the batch
-    const float c = m == -INFINITY ? 0.f : __expf(m - mb);
-    l *= c;
-#pragma unroll
-    for (int i = 0; i < G::VEC; ++i) acc[i] *= c;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float p = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - mb);
-      float vf[G::VEC];
-      unpack(vr[u], vf);
-      l += p;
-#pragma unroll
-      for (int i = 0; i < G::VEC; ++i) acc[i] += p * vf[i];
-    }
-    m = mb;
   }
   // merge the row slots of the wave (lanes sharing `sub`)
 #pragma unroll
@@ -147,7 +195,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
     if (parts == 1) {
       out[frag_off(b, hh * HD + tid, d / 32)] = to_elem<T>(A / L);
     } else {
-      float* pp = part + (int64_t)blockIdx.x * (HD + 2);
+      float* pp = part + (int64_t)item * (HD + 2);
       pp[tid] = A;
       if (tid == 0) {
         pp[HD] = M;
@@ -176,32 +224,38 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
 
 // The two uses get kernels of their own, so that traces tell them apart. clk != NULL: a timed
 // launch (LaunchClock).
+// Workgroup g takes the items g, g + gridDim.x, ... of the items = sequences x heads x parts
+// (one each unless the launch caps its grid).
 template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
                                              int64_t bh_stride, const int64_t* pos,
                                              int64_t t_uniform, int window, int H, float scale,
-                                             T* out, int parts, float* part,
+                                             T* out, int parts, float* part, int items,
                                              unsigned long long* clk) {
   const LaunchClock lc{clk};
   lc.start();
-  attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts, part);
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts, part,
+                         item);
+    if (item + (int)gridDim.x < items) __syncthreads();  // LDS is reused by the next item
+  }
   lc.stop();
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_window(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part, int items,
     unsigned long long* clk) {
   attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, clk);
+                             part, items, clk);
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_memory(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part, int items,
     unsigned long long* clk) {
   attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, clk);
+                             part, items, clk);
 }
 
 template <typename T>
@@ -217,14 +271,15 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
                            const int64_t* pos, int64_t t_uniform, int window, int H, T* out,
                            int parts, float* part, const Exec& st) {
   const float scale = 1.f / sqrtf((float)HD);
-  const int64_t blocks = (int64_t)BH * parts;
-  if (parts < 1 || parts > kMaxSplits || blocks > INT32_MAX) return hipErrorInvalidValue;
-  const int nw = blocks >= 1024 ? 4 : blocks >= 512 ? 8 : 16;
+  const int64_t items = (int64_t)BH * parts;
+  if (parts < 1 || parts > kMaxSplits || items > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t blocks = attn_blocks(items);
+  const int nw = items >= 1024 ? 4 : items >= 512 ? 8 : 16;
   hipError_t e = hipSuccess;
 #define RLT_ATTEND(NW)                                                                     \
-  e = launch(MEMORY ? k_attend_memory<T, HD, NW, 4> : k_attend_window<T, HD, NW, 4>,       \
+  e = launch(MEMORY ? k_attend_memory<T, HD, NW, kAttnU> : k_attend_window<T, HD, NW, kAttnU>, \
              dim3((unsigned)blocks), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, \
-             window, H, scale, out, parts, part, st.clk)
+             window, H, scale, out, parts, part, (int)items, st.clk)
   if (nw == 4) RLT_ATTEND(4);
   else if (nw == 8) RLT_ATTEND(8);
   else RLT_ATTEND(16);
@@ -235,14 +290,20 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
                 dim3(kThreads), Exec(st.st), (const float*)part, parts, BH, H, out);
 }
 
+int64_t attn_blocks(int64_t items) {
+  return kAttnCap > 0 && items > kAttnCap ? kAttnCap : items;
+}
+
 int cross_splits(const Dims& D, int B, int64_t t_max) {
-  // about 2048 workgroups in all (eight 4-wave workgroups per compute unit), and at least 256
-  // memory entries per slice
+  // Only batches with fewer sequence-head pairs than half the compute units are split: from 128
+  // pairs up, 16-wave workgroups already stream the prefix at 5.7-5.9 TB/s (long-context and
+  // 48-layer workloads), and the merge launch would only lengthen the chain of dependent
+  // launches. Below that, about 256 workgroups in all, and at least 256 entries per slice.
   const int64_t bh = (int64_t)B * D.H, n = t_max + 1;
-  if (bh >= 1024) return 1;
-  int64_t parts = (2048 + bh - 1) / bh;
+  if (bh >= 128) return 1;
+  int64_t parts = (256 + bh - 1) / bh;
   parts = std::min<int64_t>(parts, n / 256);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kMaxSplits));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kSplitLimit));
 }
 
 template <typename T, int HD>

@@ -370,6 +370,51 @@ hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P
   return D.dtype == RLT_BF16 ? residual_t<bf16>(D, B, l, which, P, S, dst_s, out, out_ld, st)
                              : residual_t<float>(D, B, l, which, P, S, dst_s, out, out_ld, st);
 }
+// ---- readout: logits = RMSNorm(s; out_gamma) W_out ----------------------------------------------
+// The norm is split as in the decoder step: one thread per (row, 32-column chunk) writes
+// hg = s * gamma (dtype, fragment order) and the chunk's sum of s^2; the projection's loader
+// scales each output row by 1/rms. Rows B .. B16-1 of hg are zero.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_readout_prep(const float* __restrict__ s,
+                                                           const float* __restrict__ gamma,
+                                                           int B, int B16, int d,
+                                                           T* __restrict__ hg,
+                                                           float* __restrict__ ssq) {
+  const int nch = d / 32;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)B16 * nch) return;
+  const int row = (int)(i / nch), ch = (int)(i - (int64_t)row * nch);
+  float sum = 0.f;
+  for (int c = ch * 32; c < ch * 32 + 32; ++c) {
+    const float v = row < B ? s[(int64_t)row * d + c] : 0.f;
+    hg[frag_off(row, c, nch)] = to_elem<T>(v * gamma[c]);
+    sum += v * v;
+  }
+  if (row < B) ssq[(int64_t)row * nch + ch] = sum;
+}
+
+template <typename T>
+static hipError_t readout_t(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* hg,
+                            float* ssq, float* logits, hipStream_t st) {
+  const int B16 = (B + 15) / 16 * 16, nch = D.d / 32;
+  const int64_t threads = (int64_t)B16 * nch;
+  hipError_t e = launch(k_readout_prep<T>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                        dim3(kThreads), Exec(st), s, (const float*)Hd.out_gamma, B, B16, D.d,
+                        static_cast<T*>(hg), ssq);
+  if (e != hipSuccess) return e;
+  EpiStoreF32 ep;
+  ep.out = logits; ep.ld = Hd.vocab; ep.M = B;
+  return run_step_gemm<T>(B, Hd.vocab, D.d, Hd.w_out_t,
+                          ANormed<T>{static_cast<const T*>(hg), ssq, nch, D.eps, B, D.d}, ep,
+                          Exec(st));
+}
+
+hipError_t launch_readout_logits(const Dims& D, int B, const HeadBufs& Hd, const float* s,
+                                 void* hg, float* ssq, float* logits, hipStream_t st) {
+  return D.dtype == RLT_BF16 ? readout_t<bf16>(D, B, Hd, s, hg, ssq, logits, st)
+                             : readout_t<float>(D, B, Hd, s, hg, ssq, logits, st);
+}
+
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
                           const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st) {
   return D.dtype == RLT_BF16 ? memproj_t<bf16>(D, B, P, M, e, e_seq, t0, n, st)

@@ -13,7 +13,7 @@
 namespace rlt {
 
 constexpr int kMaxWindow = 1024;
-// The memory attention of a small batch (fewer than 1024 sequence-head pairs) splits each
+// The memory attention of a small batch (fewer than 128 sequence-head pairs) splits each
 // prefix into up to kMaxSplits contiguous parts, one workgroup each, and merges their partial
 // softmax states in a second launch.
 constexpr int kMaxSplits = 16;
@@ -205,6 +205,35 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
                            float* out, int64_t out_seq, void* ws, hipStream_t st,
                            Profiler* prof);
 
+// Parameters of the encoder and the readout around the decoder (inside a head workspace).
+//   embed [V][d] dtype (row-major), w_out_t [V][d] dtype (W_out^T in fragment order),
+//   enc_gamma [L][2][d], enc_gamma_out [d], out_gamma [d] f32
+struct HeadBufs {
+  int vocab;
+  void* embed;
+  void* w_out_t;
+  float* enc_gamma;
+  float* enc_gamma_out;
+  float* out_gamma;
+};
+
+// The causal encoder over token ids [B][n] (device int32): writes e [B][n][d] (dtype, row-major).
+// Its blocks use the decoder blocks' packed attention and FFN matrices. ws: par_layout(D, B, n)
+// bytes. bf16 only.
+hipError_t launch_encode(const Dims& D, int B, int64_t n, const Packed& P, const HeadBufs& Hd,
+                         const int32_t* tokens, void* e_out, void* ws, hipStream_t st);
+
+// Readout of B rows s [B][d] f32: logits [B][V] f32 = RMSNorm(s; out_gamma) W_out, through
+// hg [B16][d] dtype and ssq [B][d/32] f32 scratch.
+hipError_t launch_readout_logits(const Dims& D, int B, const HeadBufs& Hd, const float* s,
+                                 void* hg, float* ssq, float* logits, hipStream_t st);
+// Sampling from logits [B][V] (row stride V): temperature, top-k, top-p and a uniform u[b] per
+// row; token, behaviour log-probability and model log-probability per row. fq: scratch of
+// B * V * 8 bytes.
+hipError_t launch_sample(int B, int V, const float* logits, float temperature, int top_k,
+                         float top_p, const float* u, void* fq, int32_t* tokens,
+                         float* logp_behaviour, float* logp_model, hipStream_t st);
+
 // Canonical snapshot: row b's retained entries are its tokens pos[b]-n_b .. pos[b]-1 with
 // n_b = min(pos[b], W-1), oldest first, zero-padded to W-1. Import sets every position to t.
 hipError_t launch_export(const Dims& D, int B, const StateBufs& S, float* s, void* k, void* v,
@@ -240,6 +269,8 @@ hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const Mem
 // t_max (1: one workgroup per sequence and head, no merge launch). The timed main launch has
 // B * H * parts workgroups.
 int cross_splits(const Dims& D, int B, int64_t t_max);
+// Workgroups of an attention launch over `items` (sequence, head, part) items.
+int64_t attn_blocks(int64_t items);
 
 // ---- backward pass (backpropagation through time) ----------------------------------------------
 

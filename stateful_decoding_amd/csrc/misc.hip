@@ -248,8 +248,8 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
   // `call` launches one kernel on Exec x.
   // the attention kernels (one workgroup per sequence and head, times the parts of a split
   // memory prefix) can time themselves
-  const int64_t self_grid = (int64_t)B * D.H;
-  const int64_t cross_grid = self_grid * cross_splits(D, B, t0);
+  const int64_t self_grid = attn_blocks((int64_t)B * D.H);
+  const int64_t cross_grid = attn_blocks((int64_t)B * D.H * cross_splits(D, B, t0));
 #define RLT_TIMED(kind, bytes, flops, call)                                                 \
   do {                                                                                      \
     Exec x(st);                                                                             \

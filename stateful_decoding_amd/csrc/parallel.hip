@@ -481,6 +481,47 @@ __global__ __launch_bounds__(kThreads) void k_copy_last(const float* __restrict_
   s[i] = h[(b * n + (n - 1)) * d + i % d];
 }
 
+// ---- the causal encoder: embedding gather and the output norm -----------------------------------
+// x_0 = E[token] for every row (b, i) of the R = B n rows, widened to fp32; ids outside
+// [0, V) embed as zero rows.
+__global__ __launch_bounds__(kThreads) void k_embed(const int32_t* __restrict__ tok,
+                                                    const bf16* __restrict__ E, int d, int V,
+                                                    int64_t total, float* __restrict__ h) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / d;
+  const int c = (int)(i - row * d);
+  const int t = tok[row];
+  h[i] = t >= 0 && t < V ? (float)E[(int64_t)t * d + c] : 0.f;
+}
+
+// One wave per row: e = bf16(h * gamma / sqrt(mean(h^2) + eps)), row-major [R][d].
+__global__ __launch_bounds__(kThreads) void k_norm_out(const float* __restrict__ h,
+                                                       const float* __restrict__ gamma, int d,
+                                                       float eps, int R, bf16* __restrict__ e) {
+  const int row = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= R) return;
+  const float* x = h + (int64_t)row * d;
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const u32x4 r = ld16(x + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = __uint_as_float(r[i]);
+      ss += v * v;
+    }
+  }
+  ss = wave_sum(ss);
+  const float rinv = rsqrtf(ss / (float)d + eps);
+  for (int c = lane * 8; c < d; c += kWave * 8) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)(x[c + i] * gamma[c + i] * rinv);
+    st16(e + (int64_t)row * d + c, __builtin_bit_cast(u32x4, o));
+  }
+}
+
 // ---- host side ------------------------------------------------------------------------------------
 
 ParLayout par_layout(const Dims& D, int B, int64_t n) {
@@ -591,6 +632,68 @@ static hipError_t norm_rows(const ParCtx& c, const Dims& D, const float* h, cons
   if (e != hipSuccess) return e;
   return launch(k_norm_rows, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), x, h, gamma,
                 D.d, D.eps, R, a);
+}
+
+hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, const HeadBufs& Hd,
+                         const int32_t* tokens, void* e_out, void* ws, hipStream_t st) {
+  if (D.dtype != RLT_BF16 || n_ < 1 || (int64_t)B * n_ > INT32_MAX / 2) return hipErrorInvalidValue;
+  const ParCtx c{st, nullptr};
+  const int n = (int)n_, R = B * n, d = D.d, F = D.F, H = D.H, hd = D.hd;
+  const double Rd = (double)R * d;
+  const ParLayout Lp = par_layout(D, B, n);
+  char* w = static_cast<char*>(ws);
+  float* h = reinterpret_cast<float*>(w + Lp.h);
+  bf16* a = reinterpret_cast<bf16*>(w + Lp.a);
+  bf16* q = reinterpret_cast<bf16*>(w + Lp.q);
+  bf16* kk = reinterpret_cast<bf16*>(w + Lp.k);
+  bf16* vv = reinterpret_cast<bf16*>(w + Lp.v);
+  bf16* o = reinterpret_cast<bf16*>(w + Lp.o);
+  bf16* act = reinterpret_cast<bf16*>(w + Lp.act);
+  hipError_t err;
+  const int64_t total = (int64_t)R * d;
+  err = launch(k_embed, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads),
+               Exec(st), tokens, static_cast<const bf16*>(Hd.embed), d, Hd.vocab, total, h);
+  if (err != hipSuccess) return err;
+  for (int l = 0; l < D.L; ++l) {
+    const float* gam = Hd.enc_gamma + (int64_t)l * 2 * d;
+    const int64_t wdd = (int64_t)l * d * d;
+    // causal self-attention over positions 1..t with the decoder block's matrices
+    if ((err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
+    {
+      PHeads ep{{}, q, kk, vv, n, d, H, hd, R};
+      const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
+      if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
+          hipSuccess)
+        return err;
+    }
+    if ((err = flash(c, hd, q, kk, vv, (int64_t)n * hd, B, n, H, 0, o)) != hipSuccess) return err;
+    {
+      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const bf16* Wo = static_cast<const bf16*>(P.wo_t) + wdd;
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8)) !=
+          hipSuccess)
+        return err;
+    }
+    // SiLU-gated FFN with the decoder block's matrices
+    if ((err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
+    {
+      PSilu ep{act, F, R};
+      const bf16* W13 = static_cast<const bf16*>(P.w13_t) + (int64_t)l * 2 * F * d;
+      if ((err = gemm_rows(c, R, 2 * F, d, d / 32, W13, PA{a, d / 32, R}, ep,
+                           (double)R * F * 2)) != hipSuccess)
+        return err;
+    }
+    {
+      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const bf16* W2 = static_cast<const bf16*>(P.w2_t) + (int64_t)l * d * F;
+      if ((err = gemm_rows(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep, Rd * 8)) !=
+          hipSuccess)
+        return err;
+    }
+  }
+  const int per = kThreads / kWave;
+  return launch(k_norm_out, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), Exec(st),
+                (const float*)h, Hd.enc_gamma_out, d, D.eps, R, static_cast<bf16*>(e_out));
 }
 
 hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBufs& S,

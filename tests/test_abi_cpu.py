@@ -27,9 +27,14 @@ def lib():
     return sd.load_library()
 
 
+CORE = ("rlt_memproj", "rlt_decoder_step", "rlt_run_sequence", "rlt_state_create",
+        "rlt_state_export", "rlt_state_import", "rlt_model_create", "rlt_run_parallel",
+        "rlt_bptt", "rlt_encode", "rlt_readout", "rlt_head_create", "rlt_last_error")
+
+
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 30, names
+    assert set(CORE) <= set(names) and len(names) >= 37, names
     raw = ctypes.CDLL(sd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -85,6 +90,18 @@ def test_buffer_sizes(lib):
     assert bw >= 4 * 64 * c.n_layers * d * (5 * 4 + 5 * 2)
     assert lib.rlt_bptt_ws_bytes(byref(c), 4, 0) == 0
     assert lib.rlt_bptt_ws_bytes(byref(c), 0, 8) == 0
+    # head: embedding and readout matrix in bf16 plus the gains; vocabularies of 64k only
+    V = 32768
+    hw = lib.rlt_head_ws_bytes(byref(c), V)
+    assert 2 * V * d * 2 + 4 * (2 * L * d + 2 * d) <= hw <= 2 * V * d * 2 + 4 * (2 * L * d + 2 * d) + 5 * 256
+    for bad in (0, 100, 1000, (1 << 22) + 64):
+        assert lib.rlt_head_ws_bytes(byref(c), bad) == 0
+    assert lib.rlt_encode_ws_bytes(byref(c), 16, 1024) == lib.rlt_parallel_ws_bytes(byref(c), 16,
+                                                                                    1024)
+    assert lib.rlt_encode_ws_bytes(byref(good(dtype=RLT_F32)), 16, 1024) == 0
+    ro = lib.rlt_readout_ws_bytes(byref(c), V, 256)
+    assert ro >= 256 * V * (4 + 8)  # logits and fixed-point masses
+    assert lib.rlt_readout_ws_bytes(byref(c), V, 0) == 0
 
 
 def test_null_arguments_rejected_without_gpu(lib):
@@ -103,6 +120,10 @@ def test_null_arguments_rejected_without_gpu(lib):
     assert lib.rlt_state_import(None, None, None, None, 0, 0, None) == 1
     assert lib.rlt_state_reset(None, None) == 1
     assert lib.rlt_profile_clock(None, None, 0) == 1
+    assert lib.rlt_head_create(None, 32768, None, None, 0, None, byref(out)) == 1
+    assert lib.rlt_encode(None, None, None, 1, 1, None, None, 0, None) == 1
+    assert lib.rlt_readout(None, None, None, 1, None, None, None, None, None, None, None, 0,
+                           None) == 1
     assert lib.rlt_state_position(None) == -1
     assert lib.rlt_memory_length(None) == -1
     assert b"NULL" in lib.rlt_last_error()
