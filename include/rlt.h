@@ -244,6 +244,21 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
                             const void* e, int64_t n, float* s_traj, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call the allocator, harnesses that forbid it): rlt_run_parallel with the
+ * workspace taken from a scratch array the library holds on each GPU for the life of the
+ * process (rlt_scratch_bytes() bytes, 64 MiB). The call allocates nothing. A pass whose
+ * workspace (rlt_parallel_ws_bytes) exceeds the array fails with RLT_ERR_CAPACITY before
+ * anything is enqueued; every other argument and error is as for rlt_run_parallel. All calls
+ * on one GPU share that GPU's array and it keeps the last call's contents: calls that overlap
+ * on one GPU (several host threads, or several streams whose work runs concurrently) race on
+ * it and must be ordered by the caller. */
+rlt_status rlt_run_parallel_noalloc(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                                    const void* e, int64_t n, float* s_traj, void* stream);
+
+/* Bytes of the library-held scratch array of each GPU. */
+size_t rlt_scratch_bytes(void);
+
 /* --- backward pass ("RLT Runs 96 Blocks Per Token With Recurrent State, No Resets", section
  * "Training and serving implications": training backpropagates through the whole sequence,
  * and the gradient between consecutive states also runs through the decoder's self-attention

@@ -124,6 +124,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "rlt_run_sequence": (c_int32, [P, P, P, P, c_int64, P, P]),
         "rlt_parallel_ws_bytes": (c_size_t, [POINTER(rlt_config), c_int32, c_int64]),
         "rlt_run_parallel": (c_int32, [P, P, P, P, c_int64, P, P, c_size_t, P]),
+        "rlt_run_parallel_noalloc": (c_int32, [P, P, P, P, c_int64, P, P]),
+        "rlt_scratch_bytes": (c_size_t, []),
         "rlt_state_export": (c_int32, [P, P, P, P, POINTER(c_int32), POINTER(c_int64),
                                        POINTER(c_uint64), P]),
         "rlt_state_import": (c_int32, [P, P, P, P, c_int64, c_uint64, P]),
@@ -391,6 +393,19 @@ def rlt_run_parallel(model: Model, state: State, mem: Memory, e: torch.Tensor,
     _check(model.lib.rlt_run_parallel(model.handle, state.handle, mem.handle, e.data_ptr(),
                                       int(n), _ptr(s_traj), ws.data_ptr(),
                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rlt_run_parallel_noalloc(model: Model, state: State, mem: Memory, e: torch.Tensor,
+                             s_traj: torch.Tensor | None = None, stream=None):
+    """rlt_run_parallel with the library's own scratch array as workspace (nothing allocated;
+    passes whose workspace exceeds rlt_scratch_bytes() raise RLT_ERR_CAPACITY)."""
+    n = e.shape[1]
+    _need(e, (state.batch, n, model.cfg.d), model.dtype, "e")
+    if s_traj is not None:
+        _need(s_traj, (state.batch, n, model.cfg.d), torch.float32, "s_traj")
+    _check(model.lib.rlt_run_parallel_noalloc(model.handle, state.handle, mem.handle,
+                                              e.data_ptr(), int(n), _ptr(s_traj),
+                                              _stream(stream)))
 
 
 def bptt_workspace(model: Model, batch: int, n: int) -> torch.Tensor:

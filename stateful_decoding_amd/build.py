@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlt.so")
 
 SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "misc.hip", "parallel.hip", "backward.hip",
-           "head.hip"]
+           "head.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -629,18 +629,38 @@ size_t rlt_parallel_ws_bytes(const rlt_config* cfg, int32_t batch, int64_t n) {
   return par_layout(dims_of(*cfg), batch, n).total;
 }
 
+static rlt_status run_parallel(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                               const void* e, int64_t n, float* s_traj, void* ws,
+                               size_t ws_bytes, void* stream, bool library_ws);
+
 rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory* mem,
                             const void* e, int64_t n, float* s_traj, void* ws, size_t ws_bytes,
                             void* stream) {
+  return run_parallel(model, state, mem, e, n, s_traj, ws, ws_bytes, stream, false);
+}
+
+rlt_status rlt_run_parallel_noalloc(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                                    const void* e, int64_t n, float* s_traj, void* stream) {
+  return run_parallel(model, state, mem, e, n, s_traj, nullptr, kScratchBytes, stream, true);
+}
+
+size_t rlt_scratch_bytes(void) { return kScratchBytes; }
+
+// library_ws: the workspace is this device's library-held scratch array (looked up here, after
+// validation; ws is ignored), and a pass that does not fit it is refused with
+// RLT_ERR_CAPACITY before anything is enqueued.
+static rlt_status run_parallel(const rlt_model* model, rlt_state* state, rlt_memory* mem,
+                               const void* e, int64_t n, float* s_traj, void* ws,
+                               size_t ws_bytes, void* stream, bool library_ws) {
   if (rlt_status s = check_step_args(model, state, mem)) return s;
   const Dims& D = model->D;
   if (D.alpha != 0.f)
     return fail(RLT_ERR_ARG, "the token-parallel pass needs alpha = 0 (the model has %g)",
                 (double)D.alpha);
   if (D.dtype != RLT_BF16) return fail(RLT_ERR_DTYPE, "the token-parallel pass is bf16 only");
-  if (!e || !ws) return fail(RLT_ERR_ARG, "e and ws must be non-NULL");
+  if (!e || (!ws && !library_ws)) return fail(RLT_ERR_ARG, "e and ws must be non-NULL");
   if (n < 1) return fail(RLT_ERR_ARG, "n must be >= 1");
-  if (!aligned16(e) || (s_traj && !aligned16(s_traj)) || !aligned(ws))
+  if (!aligned16(e) || (s_traj && !aligned16(s_traj)) || (!library_ws && !aligned(ws)))
     return fail(RLT_ERR_ARG, "e and s_traj must be 16-byte aligned, ws 256-byte aligned");
   if (state->t != 0 || state->ragged)
     return fail(RLT_ERR_ARG, "the token-parallel pass starts from a reset state (position %lld)",
@@ -649,12 +669,15 @@ rlt_status rlt_run_parallel(const rlt_model* model, rlt_state* state, rlt_memory
   if ((int64_t)B * n > INT32_MAX / 2) return fail(RLT_ERR_SHAPE, "B * n too large");
   const size_t need = par_layout(D, B, n).total;
   if (ws_bytes < need)
-    return fail(RLT_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return fail(RLT_ERR_CAPACITY, "%s has %zu bytes, needs %zu",
+                library_ws ? "the library's scratch array" : "workspace", ws_bytes, need);
   if (n > mem->M.capacity)
     return fail(RLT_ERR_CAPACITY, "n = %lld exceeds memory capacity %lld", (long long)n,
                 (long long)mem->M.capacity);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
+  if (library_ws && (err = scratch_region(&ws)) != hipSuccess)
+    return hip_fail(err, "looking up the scratch array");
   if (mem->len < n) {
     const int64_t first = mem->len, cnt = n - first;
     const void* e_first = static_cast<const char*>(e) + (size_t)first * D.d * D.es;

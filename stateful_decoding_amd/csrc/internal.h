@@ -128,6 +128,11 @@ struct MemBufs {
 StateBufs state_rows(const Dims& D, const StateBufs& S, int b0);
 MemBufs memory_rows(const Dims& D, const MemBufs& M, int b0);
 
+// Size of the library-held scratch array of each GPU (rlt_run_parallel_noalloc's workspace).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// The device address of the current device's scratch array (looked up on first use per device).
+hipError_t scratch_region(void** out);
+
 // Byte layout of the state buffer; offsets are 256-byte aligned.
 struct StateLayout {
   size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, pos, part, total;
