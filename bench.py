@@ -105,6 +105,9 @@ def main():
                          "with sampling (rlt_readout)")
     ap.add_argument("--workload", default=None,
                     help="synth.CONFIGS name (default s140m_bf16, or long_a0_bf16 in parallel mode)")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="tokens per sequence (default: the workload's); for short profiling "
+                         "runs only, the headline is the workload's length")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-stride", type=int, default=0,
@@ -142,6 +145,8 @@ def main():
     if args.workload is None:
         args.workload = "long_a0_bf16" if args.mode == "parallel" else "s140m_bf16"
     cfg = CONFIGS[args.workload]
+    if args.seq_len:
+        cfg = cfg.replace(seq_len=args.seq_len)
     B, T = cfg.batch, cfg.seq_len
     torch.cuda.set_device(0)
     dev = "cuda"

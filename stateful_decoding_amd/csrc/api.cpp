@@ -119,7 +119,8 @@ Dims dims_of(const rlt_config& c) {
 }
 
 struct ModelLayout {
-  size_t w_gate_t, b_gate, s_star, gamma, wqkv_t, wo_t, wcq_t, wco_t, w13_t, w2_t, wm_t, total;
+  size_t w_gate_t, b_gate, s_star, gamma, wqkv_t, wo_t, wcq_t, wco_t, w13_t, w2_t, wm_t, wocq_t,
+      fuse_tmp, total;
 };
 
 ModelLayout model_layout(const Dims& D) {
@@ -142,6 +143,8 @@ ModelLayout model_layout(const Dims& D) {
   m.w13_t = take(L * 2 * F * d * es);
   m.w2_t = take(L * F * d * es);
   m.wm_t = take(G * 2 * d * d * es);
+  m.wocq_t = take(L * 4 * d * d * es);
+  m.fuse_tmp = take(d * d * es);
   m.total = o;
   return m;
 }
@@ -222,6 +225,7 @@ StateLayout state_layout(const Dims& D, int B) {
   s.ssq = take(b * (d / 32) * 4);
   s.o = take(b16 * d * es);
   s.act = take(b16 * D.F * es);
+  s.hb = take(b16 * d * es);
   s.pos = take(b * 8);
   s.part = take(b * D.H * kMaxSplits * (D.hd + 2) * 4);
   s.total = o;
@@ -270,6 +274,7 @@ rlt_status rlt_model_create(const rlt_config* cfg, const rlt_weights* w, void* w
   P.w13_t = at<char>(ws, m.w13_t);
   P.w2_t = at<char>(ws, m.w2_t);
   P.wm_t = at<char>(ws, m.wm_t);
+  P.wocq_t = at<char>(ws, m.wocq_t);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int d = D.d, F = D.F, dt = D.dtype;
@@ -305,6 +310,7 @@ rlt_status rlt_model_create(const rlt_config* cfg, const rlt_weights* w, void* w
     RLT_PACK(launch_pack_transpose(dt, src(w->wmk, dd), d, d, wm, 0, d, d, st));
     RLT_PACK(launch_pack_transpose(dt, src(w->wmv, dd), d, d, wm, d, d, d, st));
   }
+  RLT_PACK(launch_pack_fused_ocq(D, P, w->wo, w->wcq, w->gamma, at<char>(ws, m.fuse_tmp), st));
 #undef RLT_PACK
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
@@ -354,6 +360,7 @@ rlt_status rlt_state_create(const rlt_model* model, int32_t batch, void* buf, si
   s->S.ssq = at<float>(buf, L.ssq);
   s->S.o = at<char>(buf, L.o);
   s->S.act = at<char>(buf, L.act);
+  s->S.hb = at<char>(buf, L.hb);
   s->S.pos = at<int64_t>(buf, L.pos);
   s->S.part = at<float>(buf, L.part);
   s->S.active = nullptr;

@@ -110,12 +110,15 @@ __device__ __forceinline__ void step_batch(const u32x4* kr, const u32x4* vr, int
 // as the output projection reads it. Several parts: the unnormalised output, the max and the
 // sum of the slice go to part[(bh * parts + p) * (HD + 2)] (an empty slice leaves max -inf,
 // sum 0) for k_attend_merge.
+// qssq != NULL: q[b] is unnormalised and is scaled by 1/sqrt(sum(qssq[b]) / d + eps), the
+// 1/rms of the residual stream whose 32-column sums of squares qssq[b] holds.
 template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __restrict__ K,
                                        const T* __restrict__ V, int64_t bh_stride,
                                        const int64_t* __restrict__ pos, int64_t t_uniform,
                                        int window, int H, float scale, T* __restrict__ out,
-                                       int parts, float* __restrict__ part, int item) {
+                                       int parts, float* __restrict__ part,
+                                       const float* __restrict__ qssq, float eps, int item) {
   using G = Geo<T, HD>;
   constexpr int RPB = G::RPW * NW;  // rows per block per batch step
   __shared__ float lds_m[NW], lds_l[NW];
@@ -134,8 +137,15 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
   const T* Vb = V + (int64_t)bh * bh_stride + (int64_t)lo * HD + sub * G::VEC;
   float qv[G::VEC];
   const float* qp = q + (int64_t)b * d + hh * HD + sub * G::VEC;
+  float qs = scale;
+  if (qssq) {
+    const int nch = d / 32;  // <= 512 chunks
+    float ss = 0.f;
+    for (int c = lane; c < nch; c += kWave) ss += qssq[(int64_t)b * nch + c];
+    qs *= rsqrtf(wave_sum(ss) / (float)d + eps);
+  }
 #pragma unroll
-  for (int i = 0; i < G::VEC; ++i) qv[i] = qp[i] * scale;
+  for (int i = 0; i < G::VEC; ++i) qv[i] = qp[i] * qs;
 
   float m = -INFINITY, l = 0.f, acc[G::VEC];
 #pragma unroll
@@ -230,13 +240,13 @@ template <typename T, int HD, int NW, int U>
 __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
                                              int64_t bh_stride, const int64_t* pos,
                                              int64_t t_uniform, int window, int H, float scale,
-                                             T* out, int parts, float* part, int items,
-                                             unsigned long long* clk) {
+                                             T* out, int parts, float* part, const float* qssq,
+                                             float eps, int items, unsigned long long* clk) {
   const LaunchClock lc{clk};
   lc.start();
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts, part,
-                         item);
+                         qssq, eps, item);
     if (item + (int)gridDim.x < items) __syncthreads();  // LDS is reused by the next item
   }
   lc.stop();
@@ -244,18 +254,18 @@ __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_window(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part, int items,
-    unsigned long long* clk) {
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    const float* qssq, float eps, int items, unsigned long long* clk) {
   attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, items, clk);
+                             part, qssq, eps, items, clk);
 }
 template <typename T, int HD, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void k_attend_memory(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
-    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part, int items,
-    unsigned long long* clk) {
+    int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
+    const float* qssq, float eps, int items, unsigned long long* clk) {
   attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, items, clk);
+                             part, qssq, eps, items, clk);
 }
 
 template <typename T>
@@ -269,7 +279,8 @@ static inline T* elem(void* base, int64_t off) {
 template <typename T, int HD, bool MEMORY>
 static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
                            const int64_t* pos, int64_t t_uniform, int window, int H, T* out,
-                           int parts, float* part, const Exec& st) {
+                           int parts, float* part, const float* qssq, float eps,
+                           const Exec& st) {
   const float scale = 1.f / sqrtf((float)HD);
   const int64_t items = (int64_t)BH * parts;
   if (parts < 1 || parts > kMaxSplits || items > INT32_MAX) return hipErrorInvalidValue;
@@ -279,7 +290,7 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
 #define RLT_ATTEND(NW)                                                                     \
   e = launch(MEMORY ? k_attend_memory<T, HD, NW, kAttnU> : k_attend_window<T, HD, NW, kAttnU>, \
              dim3((unsigned)blocks), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, \
-             window, H, scale, out, parts, part, (int)items, st.clk)
+             window, H, scale, out, parts, part, qssq, eps, (int)items, st.clk)
   if (nw == 4) RLT_ATTEND(4);
   else if (nw == 8) RLT_ATTEND(8);
   else RLT_ATTEND(16);
@@ -311,17 +322,19 @@ static hipError_t self_t(const Dims& D, int B, int l, const StateBufs& S, const 
   const int64_t layer = (int64_t)S.Bt * D.H * D.W * HD;
   return attend_t<T, HD, false>(B * D.H, S.q, elem<T>(S.ring_k, l * layer),
                                 elem<T>(S.ring_v, l * layer), (int64_t)D.W * HD, S.pos,
-                                S.t_uniform, D.W, D.H, static_cast<T*>(S.o), 1, nullptr, st);
+                                S.t_uniform, D.W, D.H, static_cast<T*>(S.o), 1, nullptr,
+                                nullptr, 0.f, st);
 }
 
 template <typename T, int HD>
 static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                          const Exec& st) {
+                          const Exec& st, bool q_unnormalised) {
   const int g = D.G == 1 ? 0 : l;
   const int64_t grp = (int64_t)g * M.Bt * D.H * M.capacity * HD;
   return attend_t<T, HD, true>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
                                M.capacity * HD, S.pos, S.t_uniform, 0, D.H,
-                               static_cast<T*>(S.o), cross_splits(D, B, S.t_max), S.part, st);
+                               static_cast<T*>(S.o), cross_splits(D, B, S.t_max), S.part,
+                               q_unnormalised ? S.ssq : nullptr, D.eps, st);
 }
 
 #define RLT_HD_DISPATCH(fn, ...)                                              \
@@ -337,8 +350,8 @@ hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec
 }
 
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      const Exec& st) {
-  RLT_HD_DISPATCH(cross_t, D, B, l, S, M, st)
+                      const Exec& st, bool q_unnormalised) {
+  RLT_HD_DISPATCH(cross_t, D, B, l, S, M, st, q_unnormalised)
 }
 
 }  // namespace rlt

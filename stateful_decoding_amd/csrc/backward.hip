@@ -1571,6 +1571,7 @@ static hipError_t bptt_t(const Dims& D, int B, int64_t n, const Packed& P, const
     S.ssq = reinterpret_cast<float*>(base + SL.ssq);
     S.o = base + SL.o;
     S.act = base + SL.act;
+    S.hb = base + SL.hb;
     S.pos = reinterpret_cast<int64_t*>(base + SL.pos);
     S.part = reinterpret_cast<float*>(base + SL.part);
     S.active = nullptr;

@@ -36,6 +36,32 @@ struct ANormed {  // A = hg = h * gamma (dtype, fragment order); rows scaled by 
   }
 };
 
+// A = [hb | o] (K = 2d): h and the self-attention output, both [M][d] in fragment order. Tiles
+// of the first d outputs (the residual h1 = h + o W_o) start at k = d and read only o.
+template <typename T>
+struct AFused {
+  static constexpr bool kNorm = false;
+  static constexpr int kPer = sizeof(T) == 2 ? 1 : 2, kShared = 0;
+  const T* hb;
+  const T* o;
+  int dsteps;  // d / 32
+  int M, d;
+  __device__ int kstart(int c0) const { return c0 < d ? dsteps : 0; }
+  __device__ void issue(int rt, int, int step, int lane, u32x4* r) const {
+    const bool first = step < dsteps;
+    const T* p = (first ? hb : o) +
+                 ((((int64_t)rt * dsteps + (first ? step : step - dsteps)) << 6) + lane) * 8;
+    r[0] = ld16(p);
+    if constexpr (kPer == 2) r[1] = ld16(p + 4);
+  }
+  __device__ void issue_shared(int, u32x4*) const {}
+  __device__ Frag<T> make(const u32x4* r, const u32x4*) const {
+    Frag<T> f;
+    f.from_raw(r);
+    return f;
+  }
+};
+
 template <typename T, bool ROWS>
 struct EpiQKV : EpiTile<EpiQKV<T, ROWS>> {  // q -> fp32 buffer; k, v -> the row's ring slot
   float* q;
@@ -72,6 +98,8 @@ struct EpiH {
   const float* gamma;
   float* ssq;
   int nchunk;
+  T* hb = nullptr;        // also h itself in the working dtype (fragment order), when set
+  bool ssq_only = false;  // chunk sums of h^2 without hg (the scale of an unnormalised query)
   template <int NT, int BM, int BN, int E>
   __device__ void prefetch(Pre<E>& pre, int r0, int c0) const {
     const D& self = static_cast<const D&>(*this);
@@ -98,12 +126,13 @@ struct EpiH {
       if (row < self.M) {
         const float v = self.value(row, col, tile[r * ld + c], pre.a[j], pre.b[j]);
         if (hg) hg[frag_off(row, col, nchunk)] = to_elem<T>(v * pre.c[j]);
+        if (hb) hb[frag_off(row, col, nchunk)] = to_elem<T>(v);
         sq = v * v;
       }
       tile[r * ld + c] = sq;
     }
     self.finish(r0, c0, BM);
-    if (!hg) return;
+    if (!hg && !ssq_only) return;
     __syncthreads();
     constexpr int nch = BN / 32;
     for (int j = threadIdx.x; j < BM * nch; j += NT) {
@@ -175,6 +204,50 @@ struct EpiGate : EpiH<T, EpiGate<T>> {  // g = sigmoid(v + b); h = g e + (1 - g)
     const float r = g * ev + (1.f - g) * (alpha * sv);
     h[(int64_t)row * d + col] = r;
     return r;
+  }
+};
+
+// Outputs 0..d-1: the residual h1 = h + v (EpiResidual, with the chunk sums of h1^2);
+// outputs d..2d-1: the unnormalised cross query, stored as fp32 rows of qc. Tiles never straddle
+// d (BN divides d), so each workgroup takes one branch.
+template <typename T>
+struct EpiFusedOQ {
+  EpiResidual<T, false> res;
+  float* qc;
+  int M, d;
+  template <int NT, int BM, int BN, int E>
+  __device__ void prefetch(Pre<E>& pre, int r0, int c0) const {
+    if (c0 < d) res.template prefetch<NT, BM, BN>(pre, r0, c0);
+  }
+  template <int NT, int BM, int BN, int E>
+  __device__ void store(float* tile, int ld, int r0, int c0, const Pre<E>& pre) const {
+    if (c0 < d) {
+      res.template store<NT, BM, BN>(tile, ld, r0, c0, pre);
+      return;
+    }
+    for (int i = threadIdx.x; i < BM * BN; i += NT) {
+      const int r = i / BN, c = i - r * BN;
+      if (r0 + r < M) qc[(int64_t)(r0 + r) * d + (c0 - d) + c] = tile[r * ld + c];
+    }
+  }
+};
+
+// C[i][j] = (W_o diag(g1) W_cq)[i][j] into the fused matrix: output row d + j, k = d + i.
+template <typename T>
+struct EpiPackProduct {
+  T* dst;
+  int d;
+  template <int FM, int FN>
+  __device__ void tile(const f32x4 (&acc)[FM][FN], int rbase, int cwave, int lane) const {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = rbase + 16 * fm + e, j = cwave + 16 * fn + (lane & 15);
+          if (i < d) dst[frag_off(d + j, d + i, 2 * d / 32)] = to_elem<T>(acc[fm][fn][e]);
+        }
   }
 };
 
@@ -258,6 +331,7 @@ static hipError_t gate_t(const Dims& D, int B, const Packed& P, const StateBufs&
   ep.h = S.h; ep.e = static_cast<const T*>(e_t); ep.lde = e_ld; ep.s = S.s; ep.b = P.b_gate;
   ep.alpha = D.alpha; ep.M = B; ep.d = D.d;
   next_norm<T>(ep, D, S, P.gamma);  // layer 0, before self-attention
+  ep.hb = static_cast<T*>(S.hb);     // and layer 0's fused output + cross-query projection
   return run_step_gemm<T>(B, D.d, 2 * D.d, P.w_gate_t, al, ep, st);
 }
 
@@ -319,7 +393,60 @@ static hipError_t residual_kind_t(const Dims& D, int B, int l, int which, const 
   const float* g = which < 2 ? P.gamma + ((int64_t)l * 3 + which + 1) * D.d
                  : l + 1 < D.L ? P.gamma + (int64_t)(l + 1) * 3 * D.d : nullptr;
   next_norm<T>(ep, D, S, FINAL ? nullptr : g);
+  if (which == 2 && !FINAL) ep.hb = static_cast<T*>(S.hb);  // next layer's fused projection
   return run_step_gemm<T>(B, D.d, K, Wt, al, ep, st);
+}
+
+template <typename T>
+static hipError_t self_out_cq_t(const Dims& D, int B, int l, const Packed& P,
+                                const StateBufs& S, const Exec& st) {
+  AFused<T> al{static_cast<const T*>(S.hb), static_cast<const T*>(S.o), D.d / 32, B, D.d};
+  EpiFusedOQ<T> ep;
+  ep.res.h = S.h; ep.res.dst = S.h; ep.res.out = nullptr; ep.res.out_ld = 0; ep.res.M = B;
+  ep.res.d = D.d; ep.res.active = nullptr; ep.res.pos = nullptr;
+  next_norm<T>(ep.res, D, S, nullptr);
+  ep.res.ssq_only = true;  // the memory attention scales the query by 1/rms(h1)
+  ep.qc = S.qc; ep.M = B; ep.d = D.d;
+  return run_step_gemm<T>(B, 2 * D.d, 2 * D.d, elem<T>(P.wocq_t, (int64_t)l * 4 * D.d * D.d), al,
+                          ep, st);
+}
+
+// Fused-matrix construction (once per model): (diag(g1) W_cq)^T and W_o^T into their blocks.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_fuse_blocks(const T* __restrict__ wo,
+                                                          const T* __restrict__ wcq,
+                                                          const float* __restrict__ g1, int d,
+                                                          T* __restrict__ dst,
+                                                          T* __restrict__ tmp) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)d * d) return;
+  const int k = (int)(i / d), j = (int)(i - (int64_t)k * d);  // input k, output j
+  const int ks2 = 2 * d / 32;
+  const T v = to_elem<T>(g1[k] * to_f32<T>(wcq[i]));
+  dst[frag_off(d + j, k, ks2)] = v;
+  tmp[frag_off(j, k, d / 32)] = v;
+  dst[frag_off(j, d + k, ks2)] = wo[i];
+}
+
+template <typename T>
+static hipError_t pack_fused_t(const Dims& D, const Packed& P, const void* wo, const void* wcq,
+                               const float* gamma, void* tmp, hipStream_t st) {
+  const int d = D.d;
+  const int64_t dd = (int64_t)d * d;
+  hipError_t e = hipMemsetAsync(P.wocq_t, 0, (size_t)D.L * 4 * dd * sizeof(T), st);
+  for (int l = 0; l < D.L && e == hipSuccess; ++l) {
+    const T* wo_l = static_cast<const T*>(wo) + l * dd;
+    T* dst = elem<T>(P.wocq_t, (int64_t)l * 4 * dd);
+    e = launch(k_fuse_blocks<T>, dim3((unsigned)((dd + kThreads - 1) / kThreads)), dim3(kThreads),
+               Exec(st), wo_l, static_cast<const T*>(wcq) + l * dd,
+               gamma + ((int64_t)l * 3 + 1) * d, d, dst, static_cast<T*>(tmp));
+    if (e != hipSuccess) break;
+    // W_o diag(g1) W_cq: rows of W_o (row-major) times the scaled W_cq^T just packed in tmp
+    ATokens<T> al{wo_l, 0, d, d, d};
+    EpiPackProduct<T> ep{dst, d};
+    e = run_gemm<T, kBig.wm, kBig.wn, kBig.fm, kBig.fn>(d, d, d, tmp, al, ep, Exec(st));
+  }
+  return e;
 }
 
 // h (+)= A W for the output projections; the result feeds the next RMSNorm: after the
@@ -413,6 +540,18 @@ hipError_t launch_readout_logits(const Dims& D, int B, const HeadBufs& Hd, const
                                  void* hg, float* ssq, float* logits, hipStream_t st) {
   return D.dtype == RLT_BF16 ? readout_t<bf16>(D, B, Hd, s, hg, ssq, logits, st)
                              : readout_t<float>(D, B, Hd, s, hg, ssq, logits, st);
+}
+
+hipError_t gemm_self_out_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                            const Exec& st) {
+  return D.dtype == RLT_BF16 ? self_out_cq_t<bf16>(D, B, l, P, S, st)
+                             : self_out_cq_t<float>(D, B, l, P, S, st);
+}
+
+hipError_t launch_pack_fused_ocq(const Dims& D, const Packed& P, const void* wo, const void* wcq,
+                                 const float* gamma, void* tmp, hipStream_t st) {
+  return D.dtype == RLT_BF16 ? pack_fused_t<bf16>(D, P, wo, wcq, gamma, tmp, st)
+                             : pack_fused_t<float>(D, P, wo, wcq, gamma, tmp, st);
 }
 
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,

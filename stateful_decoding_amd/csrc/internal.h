@@ -64,6 +64,11 @@ struct Dims {
 //   w13_t    [L][2F][d]  rows in blocks of 32: 16 rows of W1^T then the same 16 of W3^T
 //   w2_t     [L][d][F]
 //   wm_t     [G][2d][d]  W_mK^T rows then W_mV^T rows
+//   wocq_t   [L][2d][2d] the self-attention output projection fused with the next
+//                        cross-attention query: rows 0..d-1 (outputs h) hold W_o^T in
+//                        k = d..2d-1 (k < d is never read); rows d..2d-1 (unnormalised cross
+//                        queries) hold (diag(g1) W_cq)^T in k < d and (W_o diag(g1) W_cq)^T in
+//                        k >= d, g1 = that layer's cross-attention RMSNorm gain
 struct Packed {
   void* w_gate_t;
   float* b_gate;
@@ -76,6 +81,7 @@ struct Packed {
   void* w13_t;
   void* w2_t;
   void* wm_t;
+  void* wocq_t;
 };
 
 // Device buffers of one decoder state (all inside the state buffer).
@@ -87,6 +93,8 @@ struct Packed {
 //   ssq   [B][d/32] f32        sums of h^2 over 32-column chunks (that norm's scale)
 //   o     [B16][d] dtype       attention output (operand of the output projections)
 //   act   [B16][F] dtype       SiLU(f W1) * (f W3)
+//   hb    [B16][d] dtype       h in the working dtype (fragment order): operand of the fused
+//                              output + cross-query projection
 //   pos   [B] int64            tokens each sequence has processed (its position t)
 //   part  [B][H][kMaxSplits][hd + 2] f32  partial softmax states of a split memory attention:
 //                              per part the unnormalised output (hd), its running max, its sum
@@ -103,6 +111,7 @@ struct StateBufs {
   float* ssq;
   void* o;
   void* act;
+  void* hb;
   int64_t* pos;
   float* part;
   // rows that take part in the current step (device, one byte per row; NULL: all of them).
@@ -135,7 +144,7 @@ hipError_t scratch_region(void** out);
 
 // Byte layout of the state buffer; offsets are 256-byte aligned.
 struct StateLayout {
-  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, pos, part, total;
+  size_t s, ring_k, ring_v, h, q, qc, hg, ssq, o, act, hb, pos, part, total;
 };
 StateLayout state_layout(const Dims& D, int B);
 
@@ -259,6 +268,16 @@ hipError_t gemm_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs
 // u_save (optional): fp32 [B][2F] copy of the two up-projections (u1 | u3) for the backward pass
 hipError_t gemm_w13(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
                     const Exec& st, float* u_save = nullptr);
+// Fused self-attention output + cross-attention query of layer l (the decoder step's path):
+// h1 = h + o W_o (fp32, in S.h, with the 32-column sums of h1^2 in S.ssq) and the unnormalised
+// cross query qc = hb diag(g1) W_cq + o W_o diag(g1) W_cq = (h1 * g1) W_cq (fp32, in S.qc); the
+// memory attention scales it by 1/rms(h1) (attn_cross with q_unnormalised).
+hipError_t gemm_self_out_cq(const Dims& D, int B, int l, const Packed& P, const StateBufs& S,
+                            const Exec& st);
+// Builds the fused matrices of every layer into P.wocq_t from the unpacked weights (wo, wcq
+// [L][d][d], gamma [L][3][d]); tmp: d * d dtype scratch.
+hipError_t launch_pack_fused_ocq(const Dims& D, const Packed& P, const void* wo, const void* wcq,
+                                 const float* gamma, void* tmp, hipStream_t st);
 // h (+)= A W for the output projections: which = 0 (self-attn O), 1 (cross O), 2 (FFN down).
 // When dst_s is set the result goes to S.s (and to out rows if out != NULL) instead of h, and
 // the positions of the active rows advance: this is the last launch of the step.
@@ -268,8 +287,9 @@ hipError_t gemm_residual(const Dims& D, int B, int l, int which, const Packed& P
 // Window attention over the min(t + 1, W) ring slots of each row, memory attention over its
 // entries 0..t (t = the row's position).
 hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec& st);
+// q_unnormalised: S.qc holds (h1 * g1) W_cq and each row's 1/rms(h1) comes from S.ssq.
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
-                      const Exec& st);
+                      const Exec& st, bool q_unnormalised = false);
 // Parts the memory attention of B rows splits each prefix into when the largest row position is
 // t_max (1: one workgroup per sequence and head, no merge launch). The timed main launch has
 // B * H * parts workgroups.

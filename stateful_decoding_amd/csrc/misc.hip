@@ -169,6 +169,7 @@ StateBufs state_rows(const Dims& D, const StateBufs& S, int b0) {
   v.ssq += b0 * (d / 32);
   v.o = static_cast<char*>(S.o) + b0 * d * D.es;
   v.act = static_cast<char*>(S.act) + (int64_t)b0 * D.F * D.es;
+  v.hb = static_cast<char*>(S.hb) + b0 * d * D.es;
   v.pos += b0;
   v.part += (int64_t)b0 * D.H * kMaxSplits * (D.hd + 2);
   if (S.active) v.active += b0;
@@ -268,11 +269,12 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
               gemm_qkv(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_SELF_ATTN, n_valid * b * 2 * d * es + act32 + actd, 4 * b * d * n_valid,
               attn_self(D, B, l, S, x));
-    RLT_TIMED(RLT_K_SELF_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
-              gemm_residual(D, B, l, 0, P, S, false, nullptr, 0, x));
-    RLT_TIMED(RLT_K_CROSS_Q, d * d * es + 2 * act32, 2 * b * d * d, gemm_cq(D, B, l, P, S, x));
+    // self-attention output fused with the cross-attention query (one launch; the memory
+    // attention applies the query's 1/rms)
+    RLT_TIMED(RLT_K_SELF_OUT, 3 * d * d * es + 2 * actd + 3 * act32, 2 * b * d * d * 3,
+              gemm_self_out_cq(D, B, l, P, S, x));
     RLT_TIMED(RLT_K_CROSS_ATTN, t * b * 2 * d * es + act32 + actd, 4 * b * d * t,
-              attn_cross(D, B, l, S, M, x));
+              attn_cross(D, B, l, S, M, x, true));
     RLT_TIMED(RLT_K_CROSS_OUT, d * d * es + actd + 2 * act32, 2 * b * d * d,
               gemm_residual(D, B, l, 1, P, S, false, nullptr, 0, x));
     RLT_TIMED(RLT_K_FFN_UP, 2 * F * d * es + act32 + b * F * es, 4 * b * d * F,

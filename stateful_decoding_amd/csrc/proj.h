@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -152,6 +153,12 @@ struct EpiStoreF32 : EpiTile<EpiStoreF32> {
 template <class AL> struct is_gate : std::false_type {};
 template <typename T> struct is_gate<AGate<T>> : std::true_type {};
 
+// Loaders whose output tiles skip a leading part of K provide kstart(first output column).
+template <class AL, class = void> struct has_kstart : std::false_type {};
+template <class AL>
+struct has_kstart<AL, std::void_t<decltype(std::declval<const AL&>().kstart(0))>>
+    : std::true_type {};
+
 // ---- decoder-step projections: split-K over the waves of a block --------------------------------
 //
 // A block owns a BM x BN output tile (BM = 16 FM, BN = 16 FN) and NW waves; its K range is cut
@@ -189,10 +196,13 @@ __global__ __launch_bounds__(NW * kWave) void k_proj(int N, int K, const T* __re
   Pre<EPT> pre;
   ep.template prefetch<NT, BM, BN>(pre, r0, c0);
 
-  // k-steps (of 32) of this wave
+  // k-steps (of 32) of this wave, out of the tile's [k0, ksteps)
   const int ksteps = K / 32;
-  const int per_w = (ksteps + NW - 1) / NW;
-  const int kb = min(ksteps, wave * per_w), ke = min(ksteps, (wave + 1) * per_w);
+  int k0 = 0;
+  if constexpr (has_kstart<AL>::value) k0 = al.kstart(c0);
+  const int kn = ksteps - k0;
+  const int per_w = (kn + NW - 1) / NW;
+  const int kb = k0 + min(kn, wave * per_w), ke = k0 + min(kn, (wave + 1) * per_w);
 
   const T* bp[FN];
 #pragma unroll
@@ -471,7 +481,11 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * (N / BN);
   if (tiles <= 0 || tiles > INT32_MAX) return hipErrorInvalidValue;
   const int ksteps = K / 32;
-  constexpr int kMaxNW = FM * FN <= 2 ? 16 : 8;  // 1024-thread blocks only for the small tile
+#ifndef RLT_PROJ_MAX_WAVES
+#define RLT_PROJ_MAX_WAVES 16
+#endif
+  constexpr int kMaxNW = FM * FN <= 2 ? (RLT_PROJ_MAX_WAVES < 16 ? RLT_PROJ_MAX_WAVES : 16)
+                                      : 8;  // 1024-thread blocks only for the small tile
   int nw = 4;
   while (nw < kMaxNW && (ksteps + nw - 1) / nw > U) nw *= 2;
   if (tiles < 128 && ksteps >= 32) nw = kMaxNW;
@@ -483,10 +497,15 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
 }
 
 // Largest tile that still gives enough blocks to fill the chip.
+#ifndef RLT_PROJ_MIN_TILES
+#define RLT_PROJ_MIN_TILES 320
+#endif
 template <typename T, class AL, class EP>
 static hipError_t run_step_gemm(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
                                 const Exec& st) {
-  auto blocks = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * (N / bn); };
+  auto blocks = [&](int bm, int bn) {
+    return (int64_t)((M + bm - 1) / bm) * (N / bn) * 320 / RLT_PROJ_MIN_TILES;
+  };
   if (N % 64 == 0 && blocks(32, 64) >= 320) return run_proj<T, 2, 4>(M, N, K, Wt, al, ep, st);
   if (blocks(32, 32) >= 320) return run_proj<T, 2, 2>(M, N, K, Wt, al, ep, st);
   return run_proj<T, 1, 2>(M, N, K, Wt, al, ep, st);

@@ -214,9 +214,12 @@ def test_full_size_bptt_early_tokens_match_oracle():
 
 
 @pytest.mark.parametrize("B", [5, 300])
-def test_bptt_forward_equals_decoder_path_bitwise(B):
+def test_bptt_forward_equals_decoder_path(B):
     """The forward inside rlt_bptt runs the decoder-step kernels with the same row groups as
-    rlt_run_sequence, writing its saves on the side: the trajectories are bitwise equal."""
+    rlt_run_sequence, writing its saves on the side, except that it keeps the output projection
+    and the cross-attention query as the two products it differentiates, where the decoder step
+    computes them in one fused launch (a reassociation): the trajectories agree within the
+    forward's bound."""
     cfg = cfg_small(dtype="bf16", d=128, n_heads=2, head_dim=64, ffn=256, window=4)
     T = 12
     p, e = inputs(cfg, B, T, seed=B)
@@ -229,7 +232,9 @@ def test_bptt_forward_equals_decoder_path_bitwise(B):
     ref = torch.empty_like(traj)
     sd.rlt_run_sequence(model, state, mem, ed, ref)
     torch.cuda.synchronize()
-    assert torch.equal(traj, ref)
+    err = max_rel_l2(traj.cpu().numpy(), ref.cpu().numpy())
+    print(f"  training forward vs decoder path: max rel L2 {err:.2e}", flush=True)
+    assert err <= TOL["bf16"]
 
 
 def test_bptt_feedback_zero_start_state_gradient_is_exactly_zero():
