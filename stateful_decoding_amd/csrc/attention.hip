@@ -32,11 +32,7 @@ namespace rlt {
 #ifndef RLT_SPLIT_LIMIT
 #define RLT_SPLIT_LIMIT kMaxSplits
 #endif
-#ifndef RLT_ATTN_PIPE
-#define RLT_ATTN_PIPE 0
-#endif
 constexpr int kAttnU = RLT_ATTN_U;
-constexpr bool kAttnPipe = RLT_ATTN_PIPE != 0;
 constexpr int64_t kAttnCap = RLT_ATTN_CAP;
 constexpr int kSplitLimit = RLT_SPLIT_LIMIT;
 
@@ -151,35 +147,16 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
 #pragma unroll
   for (int i = 0; i < G::VEC; ++i) acc[i] = 0.f;
   const int first = wave * G::RPW + slot;
-  u32x4 kr[U], vr[U];
-  auto fetch = [&](int base, u32x4* kd, u32x4* vd) {
+  for (int base = 0; base < n; base += RPB * U) {
+    u32x4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = base + u * RPB + first;
       const bool ok = row < n;
-      kd[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
-      vd[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
     }
-  };
-  if constexpr (kAttnPipe) fetch(0, kr, vr);
-  for (int base = 0; base < n; base += RPB * U) {
-    if constexpr (kAttnPipe) {
-      // the next batch's loads go out before this batch is used
-      u32x4 kn[U], vn[U];
-      fetch(base + RPB * U, kn, vn);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x4 tk = kr[u], tv = vr[u];
-        kr[u] = kn[u];
-        vr[u] = vn[u];
-        kn[u] = tk;
-        vn[u] = tv;
-      }
-      step_batch<T, HD, U>(kn, vn, base, RPB, first, n, qv, m, l, acc);
-    } else {
-      fetch(base, kr, vr);
-      step_batch<T, HD, U>(kr, vr, base, RPB, first, n, qv, m, l, acc);
-    }
+    step_batch<T, HD, U>(kr, vr, base, RPB, first, n, qv, m, l, acc);
   }
   // merge the row slots of the wave (lanes sharing `sub`)
 #pragma unroll

@@ -176,9 +176,22 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
       for (int shift = 24; shift >= 0; shift -= 8) {
         for (int j = tid; j < 256; j += kST) sh.cnt[j] = 0;
         __syncthreads();
-        for (int i = tid; i < V; i += kST) {
-          const uint32_t key = order_key(z[i]);
-          if ((key & pmask) == prefix) atomicAdd(&sh.cnt[(key >> shift) & 255u], 1u);
+        {
+          // runs of equal digits are counted in registers and added once (most logits share
+          // the leading digit, which would serialise the LDS atomics)
+          uint32_t cur = 256u, run = 0u;
+          for (int i = tid; i < V; i += kST) {
+            const uint32_t key = order_key(z[i]);
+            if ((key & pmask) != prefix) continue;
+            const uint32_t dg = (key >> shift) & 255u;
+            if (dg != cur) {
+              if (run) atomicAdd(&sh.cnt[cur], run);
+              cur = dg;
+              run = 0u;
+            }
+            ++run;
+          }
+          if (run) atomicAdd(&sh.cnt[cur], run);
         }
         __syncthreads();
         if (tid == 0) {
@@ -229,11 +242,28 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
           sh.mass[j] = 0;
         }
         __syncthreads();
-        for (int i = tid; i < V; i += kST) {
-          const uint32_t key = order_key(z[i]);
-          if ((key & pmask) == prefix && in_topk(i)) {
-            atomicAdd(&sh.cnt[(key >> shift) & 255u], 1u);
-            atomicAdd(&sh.mass[(key >> shift) & 255u], fq[i]);
+        {
+          uint32_t cur = 256u, run = 0u;
+          u64 msum = 0;
+          for (int i = tid; i < V; i += kST) {
+            const uint32_t key = order_key(z[i]);
+            if ((key & pmask) != prefix || !in_topk(i)) continue;
+            const uint32_t dg = (key >> shift) & 255u;
+            if (dg != cur) {
+              if (run) {
+                atomicAdd(&sh.cnt[cur], run);
+                atomicAdd(&sh.mass[cur], msum);
+              }
+              cur = dg;
+              run = 0u;
+              msum = 0;
+            }
+            ++run;
+            msum += fq[i];
+          }
+          if (run) {
+            atomicAdd(&sh.cnt[cur], run);
+            atomicAdd(&sh.mass[cur], msum);
           }
         }
         __syncthreads();

@@ -481,11 +481,7 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * (N / BN);
   if (tiles <= 0 || tiles > INT32_MAX) return hipErrorInvalidValue;
   const int ksteps = K / 32;
-#ifndef RLT_PROJ_MAX_WAVES
-#define RLT_PROJ_MAX_WAVES 16
-#endif
-  constexpr int kMaxNW = FM * FN <= 2 ? (RLT_PROJ_MAX_WAVES < 16 ? RLT_PROJ_MAX_WAVES : 16)
-                                      : 8;  // 1024-thread blocks only for the small tile
+  constexpr int kMaxNW = FM * FN <= 2 ? 16 : 8;  // 1024-thread blocks only for the small tile
   int nw = 4;
   while (nw < kMaxNW && (ksteps + nw - 1) / nw > U) nw *= 2;
   if (tiles < 128 && ksteps >= 32) nw = kMaxNW;
@@ -497,15 +493,10 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
 }
 
 // Largest tile that still gives enough blocks to fill the chip.
-#ifndef RLT_PROJ_MIN_TILES
-#define RLT_PROJ_MIN_TILES 320
-#endif
 template <typename T, class AL, class EP>
 static hipError_t run_step_gemm(int M, int N, int K, const void* Wt, const AL& al, const EP& ep,
                                 const Exec& st) {
-  auto blocks = [&](int bm, int bn) {
-    return (int64_t)((M + bm - 1) / bm) * (N / bn) * 320 / RLT_PROJ_MIN_TILES;
-  };
+  auto blocks = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * (N / bn); };
   if (N % 64 == 0 && blocks(32, 64) >= 320) return run_proj<T, 2, 4>(M, N, K, Wt, al, ep, st);
   if (blocks(32, 32) >= 320) return run_proj<T, 2, 2>(M, N, K, Wt, al, ep, st);
   return run_proj<T, 1, 2>(M, N, K, Wt, al, ep, st);
