@@ -71,6 +71,34 @@ def build(verbose: bool = False, jobs: int = 4, out_dir: str | None = None,
     return lib
 
 
+def build_host_asan(main_src: str, exe: str, jobs: int = 8) -> str:
+    """Compile every library source and ``main_src`` with AddressSanitizer on the host code
+    only (the device code is built as usual) and link the executable ``exe``. For checks of
+    the host logic that run without a GPU; nothing here is part of ``librlt.so``."""
+    objdir = os.path.join(os.path.dirname(os.path.abspath(exe)), "obj")
+    os.makedirs(objdir, exist_ok=True)
+    asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g", *asan]
+    cc = hipcc()
+    procs, objs = [], []
+    for src in [os.path.join(CSRC, s) for s in SOURCES] + [os.path.abspath(main_src)]:
+        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [cc, *flags, "-I", INCLUDE, "-I", CSRC, *lang, "-c", src, "-o", obj]
+        procs.append((os.path.basename(src), subprocess.Popen(
+            cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), False)
+    for p in procs:
+        _wait(p, False)
+    r = subprocess.run([cc, "--offload-arch=gfx950", *asan, *objs, "-o", exe],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}")
+    return exe
+
+
 def _wait(item, verbose):
     src, p = item
     out, _ = p.communicate()
