@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,9 +51,27 @@ def step_roofline_seconds(cfg, B: int, T: int) -> float:
     return total + max(mp_bytes / HBM_PEAK, mp_flops / peak)
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def traffic_record(workload: str):
+    """HBM bytes per memory-attention launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter's reading for a plain copy of known size) on this
+    workload, averaged over every launch of one step; None unless the committed record exists
+    for this workload and was taken on the current attention source."""
+    path = os.path.join(ROOT, "profiles", f"k_attend_memory_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```traffic-record\n(.*?)```", text, re.S)
+    if not m:
+        return None
+    rec = dict(line.split(": ", 1) for line in m.group(1).strip().splitlines())
+    csrc = os.path.join(ROOT, "stateful_decoding_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("attention.hip", "internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    if rec.get("workload") != workload or rec.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(rec["traffic_per_launch"])
 
 
 def cpu_baseline(cfg, params, budget_s: float, n_seqs: int = 16) -> dict:
@@ -210,7 +229,8 @@ def main():
     ideal = step_roofline_seconds(cfg, B, T)
     ca = prof["cross_attn"]
     achieved = ca["bytes"] / (ca["total_ms"] / 1e3)
-    traffic = None
+    # the record averages over every launch of a step, so it applies when every token is timed
+    traffic = traffic_record(cfg.name) if stride == 1 else None
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
