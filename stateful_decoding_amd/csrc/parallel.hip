@@ -162,8 +162,88 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(int N, int ksteps, const 
   ep.template tile<FM, FN>(acc, tm * BM + wm * 64 + (lane >> 4) * 4, tn * BN + wn * 64, lane);
 }
 
+// The large-row product for N a multiple of 256: a 256 x 256 block of 8 waves (2 x 4, each
+// 128 x 64 = 8 x 4 fragments). Each k-step's 16 A and 16 B fragments (32 KB) are copied from
+// global memory straight into LDS (global_load_lds, 16 bytes per lane: a fragment is 1 KB in
+// lane order in both places), four k-steps deep, so up to three stages are in flight while one
+// is multiplied; one barrier per k-step. The weights are the MFMA's first operand, so a lane's
+// accumulator holds 4 consecutive output columns of one row and the epilogues store 8 or 16
+// contiguous bytes. Workgroups are numbered XCD-major: the i-th workgroup dispatched to an XCD
+// takes the i-th tile of that XCD's contiguous share, so the tiles of one row block (sharing
+// their A fragments) meet in the same L2.
+constexpr int kBigThreads = 512;
+constexpr int kBigStages = 4;
+
+template <class EP>
+__global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
+                                                         const bf16* __restrict__ A, int R,
+                                                         const bf16* __restrict__ Wt, EP ep) {
+  constexpr int FM = 8, FN = 4, PER = 4;  // fragments each wave copies per k-step
+  __shared__ __attribute__((aligned(16))) u32x4 sm[kBigStages][32][kWave];
+  const int tiles_n = N / 256, nb = (int)gridDim.x;
+  int tile = (int)blockIdx.x;
+  if ((nb & 7) == 0) tile = (tile & 7) * (nb >> 3) + (tile >> 3);
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / 4, wn = wave % 4;
+  const int last_rt = (R - 1) >> 4;
+  // fragment slot f = wave + 8 u of a stage: slots 0..15 are A row tiles, 16..31 W column tiles
+  const bf16* gp[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int f = wave + 8 * u;
+    gp[u] = f < 16 ? A + ((((int64_t)min(tm * 16 + f, last_rt) * ksteps) << 6) + lane) * 8
+                   : Wt + ((((int64_t)(tn * 16 + f - 16) * ksteps) << 6) + lane) * 8;
+  }
+  auto issue = [&](int s) {
+    const int buf = s % kBigStages;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(gp[u] + (int64_t)s * 512),
+          (__attribute__((address_space(3))) void*)&sm[buf][wave + 8 * u][0], 16, 0, 0);
+  };
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kBigStages - 1 && s < ksteps; ++s) issue(s);
+  for (int s = 0; s < ksteps; ++s) {
+    // this wave's copies of stage s are complete once at most the later stages' remain in
+    // flight (s_waitcnt vmcnt(n); lgkmcnt(0) too); the barrier then makes every wave's copies
+    // visible and guarantees that stage s - 1's buffer, reused below, is no longer read
+    const int later = min(kBigStages - 2, ksteps - 1 - s);
+    asm volatile("" ::: "memory");
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * PER));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(0x0070 | PER);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + kBigStages - 1 < ksteps) issue(s + kBigStages - 1);
+    const int cur = s % kBigStages;
+    Frag<bf16> w[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) w[j].from_raw(&sm[cur][16 + wn * 4 + j][lane]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      Frag<bf16> a;
+      a.from_raw(&sm[cur][wm * 8 + i][lane]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_16x16x32(acc[i][j], w[j], a);
+    }
+  }
+  ep.template tile_t<FM, FN>(acc, tm * 256 + wm * 128 + (lane & 15),
+                             tn * 256 + wn * 64 + 4 * (lane >> 4), lane);
+}
+
 // Epilogues. Lane l of a wave holds acc[fm][fn][i] = C[rbase + 16 fm + i][cwave + 16 fn + l % 16]
-// (rbase already includes 4 (l / 16)). Rows >= R are padding and are never stored.
+// (rbase already includes 4 (l / 16)) after k_gemm_rows / k_gemm_lds, and
+// acc[fm][fn][i] = C[row0 + 16 fm][col0 + 16 fn + i] (row0 = rows of l % 16, col0 includes
+// 4 (l / 16)) after k_gemm_big (tile_t). Rows >= R are padding and are never stored.
 template <class D>
 struct PerElement {
   template <int FM, int FN>
@@ -179,7 +259,29 @@ struct PerElement {
             static_cast<const D*>(this)->op(row, cwave + 16 * fn + (lane & 15), acc[fm][fn][i]);
         }
   }
+  template <int FM, int FN>
+  __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int lane) const {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = row0 + 16 * fm;
+      if (row < static_cast<const D*>(this)->R) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          static_cast<const D*>(this)->op4(row, col0 + 16 * fn, acc[fm][fn]);
+      }
+    }
+  }
 };
+
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
+  bf16 b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
+  return uint2{(uint32_t)__builtin_bit_cast(uint16_t, b[0]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, b[1]) << 16),
+               (uint32_t)__builtin_bit_cast(uint16_t, b[2]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, b[3]) << 16)};
+}
 
 // h = sigmoid(v + b) * e  (the gated merge with alpha = 0)
 struct PGate : PerElement<PGate> {
@@ -192,6 +294,16 @@ struct PGate : PerElement<PGate> {
     const int bs = row / n, i = row - bs * n;
     const float ev = (float)e[((int64_t)bs * e_seq + i) * d + col];
     h[(int64_t)row * d + col] = sigmoidf_(v + b[col]) * ev;
+  }
+  __device__ void op4(int row, int col, f32x4 v) const {
+    const int bs = row / n, i = row - bs * n;
+    const uint2 eraw = *reinterpret_cast<const uint2*>(e + ((int64_t)bs * e_seq + i) * d + col);
+    const float ev[4] = {__uint_as_float(eraw.x << 16), __uint_as_float(eraw.x & 0xffff0000u),
+                         __uint_as_float(eraw.y << 16), __uint_as_float(eraw.y & 0xffff0000u)};
+    f32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = sigmoidf_(v[k] + b[col + k]) * ev[k];
+    *reinterpret_cast<f32x4*>(h + (int64_t)row * d + col) = r;
   }
 };
 
@@ -216,6 +328,21 @@ struct PHeads : PerElement<PHeads> {
     const int hh = col / hd, dd = col - hh * hd;
     dst[(((int64_t)b * H + hh) * n + i) * hd + dd] = (bf16)x;
   }
+  // four consecutive columns never straddle q / k / v or a head (d and hd are multiples of 4)
+  __device__ void op4(int row, int col, f32x4 x) const {
+    const int b = row / n, i = row - b * n;
+    bf16* dst = q;
+    if (col >= d) {
+      col -= d;
+      dst = k;
+      if (col >= d) {
+        col -= d;
+        dst = v;
+      }
+    }
+    const int hh = col / hd, dd = col - hh * hd;
+    *reinterpret_cast<uint2*>(dst + (((int64_t)b * H + hh) * n + i) * hd + dd) = pack_bf16x4(x);
+  }
 };
 
 // h += v (fp32, in place); at the last layer also s rows to out (row (b, i) at
@@ -232,6 +359,15 @@ struct PResidual : PerElement<PResidual> {
     if (out) {
       const int b = row / n, i = row - b * n;
       out[(int64_t)b * out_seq + (int64_t)i * d + col] = r;
+    }
+  }
+  __device__ void op4(int row, int col, f32x4 v) const {
+    f32x4* p = reinterpret_cast<f32x4*>(h + (int64_t)row * d + col);
+    const f32x4 r = *p + v;
+    *p = r;
+    if (out) {
+      const int b = row / n, i = row - b * n;
+      *reinterpret_cast<f32x4*>(out + (int64_t)b * out_seq + (int64_t)i * d + col) = r;
     }
   }
 };
@@ -257,6 +393,29 @@ struct PSilu {
           const int col = (cwave + 32 * j) / 2 + (lane & 15);
           act[frag_off(row, col, F / 32)] = (bf16)(z1 * sigmoidf_(z1) * z3);
         }
+  }
+  // after k_gemm_big: fragments 2j / 2j + 1 hold the same 4 consecutive output columns of the
+  // W1 and W3 halves, which are 4 consecutive k of one row in the fragment-ordered act
+  template <int FM, int FN>
+  __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int lane) const {
+    static_assert(FN % 2 == 0, "pairs of W1 / W3 fragments");
+    const int cbase = col0 - 4 * (lane >> 4);  // the wave's first packed column (multiple of 32)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = row0 + 16 * fm;
+      if (row >= R) continue;
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z1 = acc[fm][2 * j][i], z3 = acc[fm][2 * j + 1][i];
+          y[i] = z1 * sigmoidf_(z1) * z3;
+        }
+        const int col = (cbase + 32 * j) / 2 + 4 * (lane >> 4);
+        *reinterpret_cast<uint2*>(act + frag_off(row, col, F / 32)) = pack_bf16x4(y);
+      }
+    }
   }
 };
 
@@ -575,6 +734,16 @@ template <class AL, class EP>
 static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
                             const AL& al, const EP& ep, double out_bytes) {
   if constexpr (std::is_same<AL, PA>::value) {
+    if (N % 256 == 0 && wks == K / 32) {
+      const int64_t blocks = (int64_t)((R + 255) / 256) * (N / 256);
+      if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
+      Exec x(c.st);
+      hipError_t e = c.arm(RLT_K_PAR_GEMM, 2.0 * ((double)R * K + (double)K * N) + out_bytes,
+                           2.0 * R * N * K, x);
+      if (e != hipSuccess) return e;
+      return launch(k_gemm_big<EP>, dim3((unsigned)blocks), dim3(kBigThreads), x, N, K / 32,
+                    al.a, R, static_cast<const bf16*>(Wt), ep);
+    }
     if (N % 128 == 0 && wks == K / 32) {
       const int64_t blocks = (int64_t)((R + 127) / 128) * (N / 128);
       if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
