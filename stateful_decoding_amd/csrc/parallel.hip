@@ -451,20 +451,27 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
 // A workgroup takes 64 consecutive queries of one (sequence, head); wave w owns queries
 // q0 + 16 w .. + 15. Key blocks of 64 are staged in LDS (K as rows, V transposed) and each wave
 // computes S^T = K Q^T with MFMA, so a lane holds the scores of one query (lane % 16) against
-// keys 4 (lane / 16) + i of each 16-key tile. The softmax is online (running max and sum per
-// query, in fp32). For O^T = V^T P^T the MFMA's k index is taken in the order the lane already
+// keys 4 (lane / 16) + i of each 16-key tile. The softmax is online in fp32, against a
+// per-query reference maximum that moves only when a block's scores exceed it by more than 8
+// in log2 units, and the weight sums are taken by the matrix cores (ones x P^T). For O^T = V^T P^T the MFMA's k index is taken in the order the lane already
 // holds P (per 32 keys: keys 4 g + [0, 4) of the first 16-key tile, then of the second,
 // g = lane / 16), and V^T is read from LDS in that same order, so P never moves between lanes.
 // Masks: the key j of query t is used when j <= t, and for the window also j > t - W.
-template <int HD>
-__global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
+// VTG: the values come transposed from global memory (Vt = [B H][HD][vt_len], keys beyond n
+// zero up to vt_len, a multiple of 64), so staging them into LDS is a plain 16-byte copy;
+// otherwise V is [B H][keys][HD] and is transposed on its way into LDS with 2-byte stores.
+template <int HD, bool VTG>
+__global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ Q,
                                                     const bf16* __restrict__ K,
                                                     const bf16* __restrict__ V,
                                                     int64_t kv_bh_stride, int n, int H, int W,
-                                                    int qblocks, float scale, bf16* __restrict__ o) {
+                                                    int qblocks, float scale,
+                                                    const bf16* __restrict__ Vt, int vt_len,
+                                                    bf16* __restrict__ o) {
   constexpr int KB = 64, QB = 64, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
-  __shared__ __attribute__((aligned(16))) bf16 ks[KB][HD + 8];
-  __shared__ __attribute__((aligned(16))) bf16 vt[HD][KB + 8];
+  // two LDS buffers: block k + 1 is staged while block k is multiplied, one barrier per block
+  __shared__ __attribute__((aligned(16))) bf16 ks[2][KB][HD + 8];
+  __shared__ __attribute__((aligned(16))) bf16 vt[2][HD][KB + 8];
   // heavy blocks (late queries) first
   const int qb = qblocks - 1 - (int)(blockIdx.x % qblocks);
   const int bh = blockIdx.x / qblocks;
@@ -475,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
   const bf16* Qb = Q + ((int64_t)bh * n) * HD;
   const bf16* Kb = K + (int64_t)bh * kv_bh_stride;
   const bf16* Vb = V + (int64_t)bh * kv_bh_stride;
+  const bf16* VTb = VTG ? Vt + (int64_t)bh * HD * vt_len : nullptr;
 
   Frag<bf16> qf[KS];
 #pragma unroll
@@ -483,7 +491,11 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
   f32x4 acc[VT];
 #pragma unroll
   for (int c = 0; c < VT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  float mref = -INFINITY;
+  f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};  // every entry: this lane's query's weight sum
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
   const int kend = min(n, q0 + QB);                      // keys this block can use
   const int kbeg = W > 0 ? max(0, q0 - W + 1) / KB * KB : 0;
@@ -497,27 +509,33 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int c = tid + u * kThreads;
-      const int key = k0 + c % KB, dd = (c / KB) * 8;
-      kr[u] = vr[u] = u32x4{0, 0, 0, 0};
-      if (key < kend) {
-        kr[u] = ld16(Kb + (int64_t)key * HD + dd);
+      // keys past kend are clamped to the last usable one: their scores are masked to -inf
+      // and their weights are 0, so only finiteness matters
+      const int key = min(k0 + c % KB, kend - 1), dd = (c / KB) * 8;
+      kr[u] = ld16(Kb + (int64_t)key * HD + dd);
+      if (VTG)  // dim c / (KB / 8), keys k0 + 8 (c % (KB / 8)) .. + 7, all < vt_len
+        vr[u] = ld16(VTb + (int64_t)(c / (KB / 8)) * vt_len + k0 + 8 * (c % (KB / 8)));
+      else
         vr[u] = ld16(Vb + (int64_t)key * HD + dd);
-      }
     }
   };
   // scores go through exp2: fold log2(e) into the scale
   const float c2 = scale * 1.4426950408889634f;
   if (kbeg < kend) fetch(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += KB) {
-    __syncthreads();  // the previous block's LDS reads are done
+  for (int k0 = kbeg, buf = 0; k0 < kend; k0 += KB, buf ^= 1) {
+    // buffer `buf` was last read two blocks ago, before the previous block's barrier
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int c = tid + u * kThreads;
       const int kk = c % KB, dd = (c / KB) * 8;
-      *reinterpret_cast<u32x4*>(&ks[kk][dd]) = kr[u];
-      const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[u]);
+      *reinterpret_cast<u32x4*>(&ks[buf][kk][dd]) = kr[u];
+      if (VTG) {
+        *reinterpret_cast<u32x4*>(&vt[buf][c / (KB / 8)][8 * (c % (KB / 8))]) = vr[u];
+      } else {
+        const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[u]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vt[dd + i][kk] = v8[i];
+        for (int i = 0; i < 8; ++i) vt[buf][dd + i][kk] = v8[i];
+      }
     }
     __syncthreads();
     if (k0 + KB < kend) fetch(k0 + KB);
@@ -529,72 +547,77 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&ks[16 * j + (lane & 15)][32 * s + 8 * g]));
+            bf16x8, *reinterpret_cast<const u32x4*>(&ks[buf][16 * j + (lane & 15)][32 * s + 8 * g]));
         st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s].v, st[j], 0, 0, 0);
       }
     }
-    // scale (and mask, unless every key of the block is valid for every query of the wave:
-    // all keys exist, none is later than the wave's first query, none falls out of the window
-    // of its last)
+    // mask, unless every key of the block is valid for every query of the wave: all keys
+    // exist, none is later than the wave's first query, none falls out of the window of its
+    // last
     const bool interior = k0 + KB <= kend && k0 + KB - 1 <= qw && (W <= 0 || k0 > qw + 15 - W);
-    float p[4 * NT];
-    float mx = -INFINITY;
-    if (interior) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[4 * j + i] = st[j][i] * c2;
-          mx = fmaxf(mx, p[4 * j + i]);
-        }
-    } else {
+    if (!interior) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * j + 4 * g + i;
           const bool ok = key <= tq && key < kend && (W <= 0 || key > tq - W);
-          p[4 * j + i] = ok ? st[j][i] * c2 : -INFINITY;
-          mx = fmaxf(mx, p[4 * j + i]);
+          st[j][i] = ok ? st[j][i] : -INFINITY;
         }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[j][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    // a query with no key yet keeps m = -inf, l = 0 and adds zero weights (every wave runs the
-    // same MFMAs, so no lane leaves the loop early); exp2(-inf) = 0
-    const float mn = fmaxf(m, mx);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - ms);
-    float ps = 0.f;
-    bf16x8 pb[PK];
+    // The weights are exp2(c2 s - mref) against a reference mref that only moves when some
+    // query's block maximum exceeds it by more than 8 (log2 units), so a weight is at most
+    // 2^8 and the accumulators are rescaled only on those blocks; the result is the same
+    // softmax (the reference cancels between numerator and denominator). A query with no key
+    // yet keeps mref = -inf and adds zero weights (exp2(-inf) = 0); every wave runs the same
+    // MFMAs, so no lane leaves the loop early.
+    // V^T fragments of this block, read now so that the LDS latency overlaps the softmax:
+    // row 16 c + lane % 16 of V^T, the 8 keys of this lane's P order in k-step h (tile 2h keys
+    // 4g..4g+3, then tile 2h+1 keys 4g..4g+3)
+    bf16x8 vf[VT][PK];
 #pragma unroll
-    for (int e = 0; e < 4 * NT; ++e) {
-      const float x = __builtin_amdgcn_exp2f(p[e] - ms);
-      ps += x;
-      pb[e / 8][e % 8] = (bf16)x;
-    }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    l = l * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int c = 0; c < VT; ++c) {
-      acc[c] *= alpha;
+    for (int c = 0; c < VT; ++c)
 #pragma unroll
       for (int h = 0; h < PK; ++h) {
-        // V^T row 16 c + lane % 16, the 8 keys of this lane's P order in k-step h: tile 2h
-        // keys 4g..4g+3, then tile 2h+1 keys 4g..4g+3
-        const bf16* vp = &vt[16 * c + (lane & 15)][32 * h];
+        const bf16* vp = &vt[buf][16 * c + (lane & 15)][32 * h];
         const uint2 lo = *reinterpret_cast<const uint2*>(vp + 4 * g);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 + 4 * g);
-        const u32x4 raw = {lo.x, lo.y, hi.x, hi.y};
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw), pb[h],
-                                                         acc[c], 0, 0, 0);
+        vf[c][h] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       }
+    const float mnew = mx * c2;
+    if (__ballot(mnew > mref + 8.f) != 0) {
+      const float mr = fmaxf(mref, mnew);
+      const float alpha = mr == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mr);
+#pragma unroll
+      for (int c = 0; c < VT; ++c) acc[c] *= alpha;
+      lsum *= alpha;
+      mref = mr;
     }
+    const float mb = mref == -INFINITY ? 0.f : mref;
+    bf16x8 pb[PK];
+#pragma unroll
+    for (int e = 0; e < 4 * NT; ++e)
+      pb[e / 8][e % 8] = (bf16)__builtin_amdgcn_exp2f(fmaf(st[e / 4][e % 4], c2, -mb));
+    // the row sums of the weights as they are multiplied (bf16), by the matrix cores: every
+    // row of ones x P^T is the per-query sum
+#pragma unroll
+    for (int h = 0; h < PK; ++h)
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[h], lsum, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < VT; ++c)
+#pragma unroll
+      for (int h = 0; h < PK; ++h)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c][h], pb[h], acc[c], 0, 0, 0);
   }
   if (tq >= n) return;
-  const float inv = 1.f / l;
+  const float inv = 1.f / lsum[0];
   const int row = b * n + tq, d = H * HD;
 #pragma unroll
   for (int c = 0; c < VT; ++c) {
@@ -607,6 +630,34 @@ __global__ __launch_bounds__(kThreads) void k_flash(const bf16* __restrict__ Q,
     w.x = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
     w.y = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
     *reinterpret_cast<uint2*>(o + frag_off(row, dim, d / 32)) = w;
+  }
+}
+
+// ---- values transposed for the prefix attention ----------------------------------------------------
+// vt[bh][dd][j] = v[bh][j][dd] for keys j < n, 0 for n <= j < vt_len (vt_len a multiple of 64). One
+// workgroup per (bh, 64-key tile): 64 x HD elements through LDS, 16-byte loads and stores.
+template <int HD>
+__global__ __launch_bounds__(kThreads) void k_transpose_v(const bf16* __restrict__ v,
+                                                          int64_t bh_stride, int n, int vt_len,
+                                                          bf16* __restrict__ vt) {
+  __shared__ __attribute__((aligned(16))) bf16 t[64][HD + 8];
+  const int tiles = vt_len / 64;
+  const int64_t bh = blockIdx.x / tiles;
+  const int j0 = (int)(blockIdx.x % tiles) * 64;
+  const bf16* src = v + bh * bh_stride;
+  for (int c = threadIdx.x; c < 64 * HD / 8; c += kThreads) {
+    const int j = c / (HD / 8), dd = 8 * (c % (HD / 8));
+    const u32x4 r = j0 + j < n ? ld16(src + (int64_t)(j0 + j) * HD + dd) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&t[j][dd]) = r;
+  }
+  __syncthreads();
+  bf16* dst = vt + bh * HD * vt_len + j0;
+  for (int c = threadIdx.x; c < HD * 8; c += kThreads) {
+    const int dd = c / 8, j = 8 * (c % 8);
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = t[j + i][dd];
+    st16(dst + (int64_t)dd * vt_len + j, __builtin_bit_cast(u32x4, o));
   }
 }
 
@@ -699,6 +750,7 @@ ParLayout par_layout(const Dims& D, int B, int64_t n) {
   p.v = take(R * d * 2);
   p.o = take(R16 * d * 2);
   p.act = take(R16 * D.F * 2);
+  p.vt = take((size_t)B * d * ((n + 63) / 64 * 64) * 2);  // values transposed, one group
   p.total = o;
   return p;
 }
@@ -762,7 +814,8 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
 // W > 0: window attention (keys t-W+1..t of this layer); W = 0: memory prefix 0..t.
 template <int HD>
 static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const bf16* v,
-                          int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o) {
+                          int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
+                          bf16* vt) {
   const int qblocks = (n + 63) / 64;
   const int64_t blocks = (int64_t)B * H * qblocks;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -775,20 +828,36 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
     keys = (double)n * (n + 1) / 2;
   }
   const double bhd = (double)B * H * HD;
+  const int vt_len = qblocks * 64;
+  hipError_t e;
+  if (vt) {  // values transposed first (timed as its own kind)
+    Exec xt(c.st);
+    if ((e = c.arm(RLT_K_PAR_OTHER, bhd * (n + vt_len) * 2, 0, xt)) != hipSuccess) return e;
+    e = launch(k_transpose_v<HD>, dim3((unsigned)blocks), dim3(kThreads), xt, v, kv_bh_stride, n,
+               vt_len, vt);
+    if (e != hipSuccess) return e;
+  }
   Exec x(c.st);
-  hipError_t e = c.arm(W > 0 ? RLT_K_PAR_SELF : RLT_K_PAR_CROSS, bhd * n * 2 * 4.0,
-                       4.0 * bhd * keys, x);
-  if (e != hipSuccess) return e;
-  return launch(k_flash<HD>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v, kv_bh_stride, n,
-                H, W, qblocks, 1.f / sqrtf((float)HD), o);
+  if ((e = c.arm(W > 0 ? RLT_K_PAR_SELF : RLT_K_PAR_CROSS, bhd * n * 2 * 4.0, 4.0 * bhd * keys,
+                 x)) != hipSuccess)
+    return e;
+  if (vt)
+    return launch(k_flash<HD, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+                  kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
+                  static_cast<const bf16*>(vt), vt_len, o);
+  return launch(k_flash<HD, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+                kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
+                static_cast<const bf16*>(nullptr), 0, o);
 }
 
+// vt (optional): workspace of B H hd ceil(n / 64) 64 elements for the values transposed first
 static hipError_t flash(const ParCtx& c, int hd, const bf16* q, const bf16* k, const bf16* v,
-                        int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o) {
+                        int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
+                        bf16* vt = nullptr) {
   switch (hd) {
-    case 32: return flash_t<32>(c, q, k, v, kv_bh_stride, B, n, H, W, o);
-    case 64: return flash_t<64>(c, q, k, v, kv_bh_stride, B, n, H, W, o);
-    case 128: return flash_t<128>(c, q, k, v, kv_bh_stride, B, n, H, W, o);
+    case 32: return flash_t<32>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
+    case 64: return flash_t<64>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
+    case 128: return flash_t<128>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
     default: return hipErrorInvalidValue;
   }
 }
@@ -835,7 +904,9 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, cons
           hipSuccess)
         return err;
     }
-    if ((err = flash(c, hd, q, kk, vv, (int64_t)n * hd, B, n, H, 0, o)) != hipSuccess) return err;
+    if ((err = flash(c, hd, q, kk, vv, (int64_t)n * hd, B, n, H, 0, o,
+                     reinterpret_cast<bf16*>(w + Lp.vt))) != hipSuccess)
+      return err;
     {
       PResidual ep{{}, h, nullptr, 0, n, d, R};
       const bf16* Wo = static_cast<const bf16*>(P.wo_t) + wdd;
@@ -938,8 +1009,8 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
       const int gsel = D.G == 1 ? 0 : l;
       const int64_t grp = (int64_t)gsel * M.Bt * H * M.capacity * hd;
       if ((err = flash(c, hd, q, static_cast<const bf16*>(M.k) + grp,
-                       static_cast<const bf16*>(M.v) + grp, M.capacity * hd, B, n, H, 0, o)) !=
-          hipSuccess)
+                       static_cast<const bf16*>(M.v) + grp, M.capacity * hd, B, n, H, 0, o,
+                       reinterpret_cast<bf16*>(w + Lp.vt))) != hipSuccess)
         return err;
     }
     {
