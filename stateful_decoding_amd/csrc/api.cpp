@@ -182,7 +182,7 @@ HeadLayout head_layout(const Dims& D, int V) {
 bool valid_vocab(int V) { return V >= 64 && V <= kMaxVocab && V % 64 == 0; }
 
 struct ReadoutLayout {
-  size_t hg, ssq, logits, fq, total;
+  size_t hg, ssq, logits, total;
 };
 
 ReadoutLayout readout_layout(const Dims& D, int V, int B) {
@@ -197,7 +197,6 @@ ReadoutLayout readout_layout(const Dims& D, int V, int B) {
   r.hg = take(b16 * D.d * D.es);
   r.ssq = take((size_t)B * (D.d / 32) * 4);
   r.logits = take((size_t)B * V * 4);
-  r.fq = take((size_t)B * V * 8);
   r.total = o;
   return r;
 }
@@ -1086,8 +1085,8 @@ rlt_status rlt_readout(const rlt_model* model, const rlt_head* head, const float
   hipError_t err = launch_readout_logits(D, batch, head->Hd, s, at<char>(ws, L.hg),
                                          at<float>(ws, L.ssq), lg, st);
   if (err == hipSuccess)
-    err = launch_sample(batch, V, lg, sp->temperature, sp->top_k, sp->top_p, u,
-                        at<char>(ws, L.fq), tokens, logp_behaviour, logp_model, st);
+    err = launch_sample(batch, V, lg, sp->temperature, sp->top_k, sp->top_p, u, tokens,
+                        logp_behaviour, logp_model, st);
   if (err != hipSuccess) return hip_fail(err, "readout");
   return ok();
 }

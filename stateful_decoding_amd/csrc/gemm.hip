@@ -538,6 +538,10 @@ static hipError_t readout_t(const Dims& D, int B, const HeadBufs& Hd, const floa
 
 hipError_t launch_readout_logits(const Dims& D, int B, const HeadBufs& Hd, const float* s,
                                  void* hg, float* ssq, float* logits, hipStream_t st) {
+  // bf16 vocabularies that tile by 256 columns go through the large-row GEMM (many columns, so
+  // MFMA-shaped rather than weight-streaming); the rest through the split-K projection
+  if (D.dtype == RLT_BF16 && Hd.vocab % 256 == 0)
+    return launch_readout_rows(D, B, Hd, s, hg, logits, st);
   return D.dtype == RLT_BF16 ? readout_t<bf16>(D, B, Hd, s, hg, ssq, logits, st)
                              : readout_t<float>(D, B, Hd, s, hg, ssq, logits, st);
 }

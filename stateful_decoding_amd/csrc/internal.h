@@ -241,12 +241,15 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n, const Packed& P, const
 // hg [B16][d] dtype and ssq [B][d/32] f32 scratch.
 hipError_t launch_readout_logits(const Dims& D, int B, const HeadBufs& Hd, const float* s,
                                  void* hg, float* ssq, float* logits, hipStream_t st);
+// The same logits on the token-parallel 256 x 256 GEMM (bf16, V a multiple of 256): a receives
+// bf16(s * gamma / rms(s)) in fragment order (ceil(B / 16) * 16 rows of d).
+hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,
+                               float* logits, hipStream_t st);
 // Sampling from logits [B][V] (row stride V): temperature, top-k, top-p and a uniform u[b] per
-// row; token, behaviour log-probability and model log-probability per row. fq: scratch of
-// B * V * 8 bytes.
+// row; token, behaviour log-probability and model log-probability per row.
 hipError_t launch_sample(int B, int V, const float* logits, float temperature, int top_k,
-                         float top_p, const float* u, void* fq, int32_t* tokens,
-                         float* logp_behaviour, float* logp_model, hipStream_t st);
+                         float top_p, const float* u, int32_t* tokens, float* logp_behaviour,
+                         float* logp_model, hipStream_t st);
 
 // Canonical snapshot: row b's retained entries are its tokens pos[b]-n_b .. pos[b]-1 with
 // n_b = min(pos[b], W-1), oldest first, zero-padded to W-1. Import sets every position to t.

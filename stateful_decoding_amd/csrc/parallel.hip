@@ -372,6 +372,16 @@ struct PResidual : PerElement<PResidual> {
   }
 };
 
+// out[row][col] = v (fp32, row stride ld): the readout's logits
+struct PStoreF32 : PerElement<PStoreF32> {
+  float* out;
+  int ld, R;
+  __device__ void op(int row, int col, float v) const { out[(int64_t)row * ld + col] = v; }
+  __device__ void op4(int row, int col, f32x4 v) const {
+    *reinterpret_cast<f32x4*>(out + (int64_t)row * ld + col) = v;
+  }
+};
+
 // act = SiLU(x W1) * (x W3) in fragment order. The packed up-projection interleaves 16 columns
 // of W1 and the same 16 of W3 per 32 columns, and a wave's FN (even) fragments start on a
 // multiple of 32, so fragments 2j and 2j + 1 of a lane hold the two factors of one output.
@@ -448,19 +458,21 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
 }
 
 // ---- causal flash attention, all queries of a (sequence, head) block at once ----------------------
-// A workgroup takes 64 consecutive queries of one (sequence, head); wave w owns queries
-// q0 + 16 w .. + 15. Key blocks of 64 are staged in LDS (K as rows, V transposed) and each wave
-// computes S^T = K Q^T with MFMA, so a lane holds the scores of one query (lane % 16) against
-// keys 4 (lane / 16) + i of each 16-key tile. The softmax is online in fp32, against a
+// A workgroup takes QB = 64 QT consecutive queries of one (sequence, head); wave w owns the QT
+// 16-query tiles starting at q0 + 16 QT w. Key blocks of 64 are staged in LDS (K as rows, V
+// transposed) and each wave computes S^T = K Q^T with MFMA, every K fragment read from LDS
+// serving its QT query tiles, so a lane holds the scores of one query (lane % 16 of a tile)
+// against keys 4 (lane / 16) + i of each 16-key tile. The softmax is online in fp32, against a
 // per-query reference maximum that moves only when a block's scores exceed it by more than 8
-// in log2 units, and the weight sums are taken by the matrix cores (ones x P^T). For O^T = V^T P^T the MFMA's k index is taken in the order the lane already
-// holds P (per 32 keys: keys 4 g + [0, 4) of the first 16-key tile, then of the second,
-// g = lane / 16), and V^T is read from LDS in that same order, so P never moves between lanes.
+// in log2 units, and the weight sums are taken by the matrix cores (ones x P^T). For
+// O^T = V^T P^T the MFMA's k index is taken in the order the lane already holds P (per 32 keys:
+// keys 4 g + [0, 4) of the first 16-key tile, then of the second, g = lane / 16), and V^T is
+// read from LDS in that same order, so P never moves between lanes.
 // Masks: the key j of query t is used when j <= t, and for the window also j > t - W.
 // VTG: the values come transposed from global memory (Vt = [B H][HD][vt_len], keys beyond n
 // zero up to vt_len, a multiple of 64), so staging them into LDS is a plain 16-byte copy;
 // otherwise V is [B H][keys][HD] and is transposed on its way into LDS with 2-byte stores.
-template <int HD, bool VTG>
+template <int HD, int QT, bool VTG>
 __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ Q,
                                                     const bf16* __restrict__ K,
                                                     const bf16* __restrict__ V,
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
                                                     int qblocks, float scale,
                                                     const bf16* __restrict__ Vt, int vt_len,
                                                     bf16* __restrict__ o) {
-  constexpr int KB = 64, QB = 64, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
+  constexpr int KB = 64, QB = 64 * QT, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
   // two LDS buffers: block k + 1 is staged while block k is multiplied, one barrier per block
   __shared__ __attribute__((aligned(16))) bf16 ks[2][KB][HD + 8];
   __shared__ __attribute__((aligned(16))) bf16 vt[2][HD][KB + 8];
@@ -477,22 +489,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
   const int bh = blockIdx.x / qblocks;
   const int b = bh / H, hh = bh - b * H;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4;
-  const int q0 = qb * QB, qw = q0 + wave * 16;
-  const int tq = qw + (lane & 15);  // this lane's query (token index)
+  const int q0 = qb * QB, qw = q0 + wave * 16 * QT;  // the wave's first query
   const bf16* Qb = Q + ((int64_t)bh * n) * HD;
   const bf16* Kb = K + (int64_t)bh * kv_bh_stride;
   const bf16* Vb = V + (int64_t)bh * kv_bh_stride;
   const bf16* VTb = VTG ? Vt + (int64_t)bh * HD * vt_len : nullptr;
 
-  Frag<bf16> qf[KS];
+  int tq[QT];  // this lane's query (token index) in each tile
+  Frag<bf16> qf[QT][KS];
+  f32x4 acc[QT][VT];
+  float mref[QT];
+  f32x4 lsum[QT];  // every entry: this lane's query's weight sum
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s].load(Qb + (int64_t)min(tq, n - 1) * HD + 32 * s + 8 * g);
-
-  f32x4 acc[VT];
+  for (int t = 0; t < QT; ++t) {
+    tq[t] = qw + 16 * t + (lane & 15);
 #pragma unroll
-  for (int c = 0; c < VT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref = -INFINITY;
-  f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};  // every entry: this lane's query's weight sum
+    for (int s = 0; s < KS; ++s)
+      qf[t][s].load(Qb + (int64_t)min(tq[t], n - 1) * HD + 32 * s + 8 * g);
+#pragma unroll
+    for (int c = 0; c < VT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mref[t] = -INFINITY;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
@@ -539,45 +557,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
     }
     __syncthreads();
     if (k0 + KB < kend) fetch(k0 + KB);
-    // S^T for the NT 16-key tiles
-    f32x4 st[NT];
+    // S^T for the NT 16-key tiles of every query tile
+    f32x4 st[QT][NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < QT; ++t) st[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kf = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(&ks[buf][16 * j + (lane & 15)][32 * s + 8 * g]));
-        st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s].v, st[j], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          st[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][s].v, st[t][j], 0, 0, 0);
       }
     }
-    // mask, unless every key of the block is valid for every query of the wave: all keys
-    // exist, none is later than the wave's first query, none falls out of the window of its
-    // last
-    const bool interior = k0 + KB <= kend && k0 + KB - 1 <= qw && (W <= 0 || k0 > qw + 15 - W);
-    if (!interior) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * j + 4 * g + i;
-          const bool ok = key <= tq && key < kend && (W <= 0 || key > tq - W);
-          st[j][i] = ok ? st[j][i] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[j][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    // The weights are exp2(c2 s - mref) against a reference mref that only moves when some
-    // query's block maximum exceeds it by more than 8 (log2 units), so a weight is at most
-    // 2^8 and the accumulators are rescaled only on those blocks; the result is the same
-    // softmax (the reference cancels between numerator and denominator). A query with no key
-    // yet keeps mref = -inf and adds zero weights (exp2(-inf) = 0); every wave runs the same
-    // MFMAs, so no lane leaves the loop early.
     // V^T fragments of this block, read now so that the LDS latency overlaps the softmax:
     // row 16 c + lane % 16 of V^T, the 8 keys of this lane's P order in k-step h (tile 2h keys
     // 4g..4g+3, then tile 2h+1 keys 4g..4g+3)
@@ -591,45 +585,83 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 + 4 * g);
         vf[c][h] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       }
-    const float mnew = mx * c2;
-    if (__ballot(mnew > mref + 8.f) != 0) {
-      const float mr = fmaxf(mref, mnew);
-      const float alpha = mr == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mr);
 #pragma unroll
-      for (int c = 0; c < VT; ++c) acc[c] *= alpha;
-      lsum *= alpha;
-      mref = mr;
-    }
-    const float mb = mref == -INFINITY ? 0.f : mref;
-    bf16x8 pb[PK];
+    for (int t = 0; t < QT; ++t) {
+      const int qt0 = qw + 16 * t;  // first query of the tile
+      // mask, unless every key of the block is valid for every query of the tile: all keys
+      // exist, none is later than the tile's first query, none falls out of the window of its
+      // last
+      const bool interior =
+          k0 + KB <= kend && k0 + KB - 1 <= qt0 && (W <= 0 || k0 > qt0 + 15 - W);
+      if (!interior) {
 #pragma unroll
-    for (int e = 0; e < 4 * NT; ++e)
-      pb[e / 8][e % 8] = (bf16)__builtin_amdgcn_exp2f(fmaf(st[e / 4][e % 4], c2, -mb));
-    // the row sums of the weights as they are multiplied (bf16), by the matrix cores: every
-    // row of ones x P^T is the per-query sum
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int h = 0; h < PK; ++h)
-      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[h], lsum, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * j + 4 * g + i;
+            const bool ok = key <= tq[t] && key < kend && (W <= 0 || key > tq[t] - W);
+            st[t][j][i] = ok ? st[t][j][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < VT; ++c)
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][j][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // The weights are exp2(c2 s - mref) against a reference mref that only moves when some
+      // query's block maximum exceeds it by more than 8 (log2 units), so a weight is at most
+      // 2^8 and the accumulators are rescaled only on those blocks; the result is the same
+      // softmax (the reference cancels between numerator and denominator). A query with no
+      // key yet keeps mref = -inf and adds zero weights (exp2(-inf) = 0); every wave runs the
+      // same MFMAs, so no lane leaves the loop early.
+      const float mnew = mx * c2;
+      if (__ballot(mnew > mref[t] + 8.f) != 0) {
+        const float mr = fmaxf(mref[t], mnew);
+        const float alpha = mr == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mr);
+#pragma unroll
+        for (int c = 0; c < VT; ++c) acc[t][c] *= alpha;
+        lsum[t] *= alpha;
+        mref[t] = mr;
+      }
+      const float mb = mref[t] == -INFINITY ? 0.f : mref[t];
+      bf16x8 pb[PK];
+#pragma unroll
+      for (int e = 0; e < 4 * NT; ++e)
+        pb[e / 8][e % 8] = (bf16)__builtin_amdgcn_exp2f(fmaf(st[t][e / 4][e % 4], c2, -mb));
+      // the row sums of the weights as they are multiplied (bf16), by the matrix cores: every
+      // row of ones x P^T is the per-query sum
 #pragma unroll
       for (int h = 0; h < PK; ++h)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c][h], pb[h], acc[c], 0, 0, 0);
+        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[h], lsum[t], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < VT; ++c)
+#pragma unroll
+        for (int h = 0; h < PK; ++h)
+          acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[c][h], pb[h], acc[t][c], 0, 0, 0);
+    }
   }
-  if (tq >= n) return;
-  const float inv = 1.f / lsum[0];
-  const int row = b * n + tq, d = H * HD;
+  const int d = H * HD;
 #pragma unroll
-  for (int c = 0; c < VT; ++c) {
-    // lane holds O^T[dim 16 c + 4 g + i][query tq]
-    const int dim = hh * HD + 16 * c + 4 * g;
-    uint2 w;
-    bf16 v4[4];
+  for (int t = 0; t < QT; ++t) {
+    if (tq[t] >= n) continue;
+    const float inv = 1.f / lsum[t][0];
+    const int row = b * n + tq[t];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v4[i] = (bf16)(acc[c][i] * inv);
-    w.x = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
-    w.y = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
-    *reinterpret_cast<uint2*>(o + frag_off(row, dim, d / 32)) = w;
+    for (int c = 0; c < VT; ++c) {
+      // lane holds O^T[dim 16 c + 4 g + i][query tq]
+      const int dim = hh * HD + 16 * c + 4 * g;
+      uint2 w;
+      bf16 v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = (bf16)(acc[t][c][i] * inv);
+      w.x = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
+      w.y = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
+      *reinterpret_cast<uint2*>(o + frag_off(row, dim, d / 32)) = w;
+    }
   }
 }
 
@@ -816,9 +848,14 @@ template <int HD>
 static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const bf16* v,
                           int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
                           bf16* vt) {
-  const int qblocks = (n + 63) / 64;
+  // one 16-query tile per wave: two (each K / V fragment read from LDS serving both) measured
+  // no faster at hd = 64 (41.6 against 41.3 ms of memory attention per pass) with half the
+  // resident waves, and do not fit in 256 registers at hd = 128
+  constexpr int QT = 1;
+  const int qblocks = (n + 64 * QT - 1) / (64 * QT);
   const int64_t blocks = (int64_t)B * H * qblocks;
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const int vt_tiles = (n + 63) / 64;
+  if (blocks > INT32_MAX || (int64_t)B * H * vt_tiles > INT32_MAX) return hipErrorInvalidValue;
   // keys per query summed over t = 0..n-1: min(t + 1, W) or t + 1
   double keys = 0;
   if (W > 0) {
@@ -828,13 +865,13 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
     keys = (double)n * (n + 1) / 2;
   }
   const double bhd = (double)B * H * HD;
-  const int vt_len = qblocks * 64;
+  const int vt_len = vt_tiles * 64;
   hipError_t e;
   if (vt) {  // values transposed first (timed as its own kind)
     Exec xt(c.st);
     if ((e = c.arm(RLT_K_PAR_OTHER, bhd * (n + vt_len) * 2, 0, xt)) != hipSuccess) return e;
-    e = launch(k_transpose_v<HD>, dim3((unsigned)blocks), dim3(kThreads), xt, v, kv_bh_stride, n,
-               vt_len, vt);
+    e = launch(k_transpose_v<HD>, dim3((unsigned)((int64_t)B * H * vt_tiles)), dim3(kThreads), xt,
+               v, kv_bh_stride, n, vt_len, vt);
     if (e != hipSuccess) return e;
   }
   Exec x(c.st);
@@ -842,10 +879,10 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
                  x)) != hipSuccess)
     return e;
   if (vt)
-    return launch(k_flash<HD, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+    return launch(k_flash<HD, QT, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
                   kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
                   static_cast<const bf16*>(vt), vt_len, o);
-  return launch(k_flash<HD, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+  return launch(k_flash<HD, QT, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
                 kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
                 static_cast<const bf16*>(nullptr), 0, o);
 }
@@ -870,6 +907,21 @@ static hipError_t norm_rows(const ParCtx& c, const Dims& D, const float* h, cons
   if (e != hipSuccess) return e;
   return launch(k_norm_rows, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), x, h, gamma,
                 D.d, D.eps, R, a);
+}
+
+hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,
+                               float* logits, hipStream_t st) {
+  const int V = Hd.vocab, d = D.d;
+  if (D.dtype != RLT_BF16 || V % 256 != 0 || B < 1) return hipErrorInvalidValue;
+  const ParCtx c{st, nullptr};
+  bf16* ab = static_cast<bf16*>(a);
+  hipError_t e = norm_rows(c, D, s, Hd.out_gamma, B, ab);
+  if (e != hipSuccess) return e;
+  PStoreF32 ep;
+  ep.out = logits;
+  ep.ld = V;
+  ep.R = B;
+  return gemm_rows(c, B, V, d, d / 32, Hd.w_out_t, PA{ab, d / 32, B}, ep, (double)B * V * 4);
 }
 
 hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, const HeadBufs& Hd,

@@ -153,6 +153,27 @@ def test_readout_logits_and_samples_match_oracle(dtype):
     assert total_near <= 2
 
 
+def test_readout_large_vocabulary():
+    """A vocabulary above the 32768 logits the sampler stages in LDS: every pass then reads
+    the row from global memory. Same decisions as the oracle on the GPU's logits."""
+    cfg = cfg_small()
+    B, V = 6, 65536
+    p, h, model, head = setup(cfg, V, seed=11, head_sigma=0.2, dup_cols=((7, 40000),))
+    s = torch.from_numpy(np.random.default_rng(12).standard_normal((B, cfg.d)).astype(np.float32)
+                         * 3).cuda()
+    lg = torch.empty(B, V, device="cuda")
+    near = 0
+    for i, (temp, k, tp) in enumerate(((1.0, 0, 1.0), (0.8, 50, 0.95), (1.2, 0, 0.7),
+                                       (0.0, 0, 1.0), (1.0, 40001, 1.0))):
+        u = make_uniforms(B, step=20 + i)
+        tok, lpb, lpm = sd.rlt_readout(head, s, torch.from_numpy(u).cuda(), temp, k, tp,
+                                       logits=lg)
+        torch.cuda.synchronize()
+        near += check_samples(lg.cpu().numpy(), temp, k, tp, u, tok.cpu().numpy(),
+                              lpb.cpu().numpy(), lpm.cpu().numpy())
+    assert near <= 1
+
+
 def test_sampler_ties_keep_the_lowest_ids():
     """Identical readout columns give identical logits; with top-k cutting through the tie
     group, only its lowest ids survive, so only they are ever sampled."""
