@@ -105,16 +105,53 @@ struct Range {
   }
 };
 
+// Calls f(i, z[i]) for this lane's ids of the wave range r, eight 64-id strips at a time with
+// their eight loads issued before any is used.
+template <class F>
+__device__ __forceinline__ void for_lane(const Range& r, const float* z, F f) {
+  const int lane = threadIdx.x % kWave;
+  for (int b0 = r.lo; b0 < r.hi; b0 += 8 * kWave) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = b0 + q * kWave + lane;
+      v[q] = i < r.hi ? z[i] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = b0 + q * kWave + lane;
+      if (i < r.hi) f(i, v[q]);
+    }
+  }
+}
+
 // The first id, in ascending order, at which the running sum of w(i) over ids with w(i) > 0
 // exceeds thr (thr < 0: the first id with w(i) > 0); V if none. All threads get the result.
+// Within its wave range every lane owns a contiguous run of ids: the lane sums (integers, so
+// the order of addition is free; each lane starts at its own offset so that the 64 lanes read
+// different LDS banks), one lane scan in the wave that holds the crossing, and a sequential
+// walk by the one lane that holds it.
 template <class Wt>
 __device__ int first_crossing(int V, Wt w, long long thr, Shared& sh) {
   const Range r(V);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int per = (r.hi - r.lo + kWave - 1) / kWave;  // ids per lane (the last lanes fewer)
+  const int l0 = min(r.hi, r.lo + lane * per), l1 = min(r.hi, l0 + per), len = l1 - l0;
   u64 own = 0;
-  for (int i = r.lo + lane; i < r.hi; i += kWave) own += w(i);
-  own = wave_sum_u64(own);
-  if (lane == 0) sh.wtot[wave] = own;
+  const int start = len > 0 ? lane % len : 0;
+  for (int j0 = 0; j0 < len; j0 += 8) {
+    u64 x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int jj = start + j0 + q;
+      jj -= jj >= len ? len : 0;
+      x[q] = j0 + q < len ? w(l0 + jj) : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) own += x[q];
+  }
+  const u64 wsum = wave_sum_u64(own);
+  if (lane == 0) sh.wtot[wave] = wsum;
   if (threadIdx.x == 0) sh.sel[0] = V;
   __syncthreads();
   // the wave holding the crossing: the first with positive mass whose inclusive sum exceeds thr
@@ -129,16 +166,18 @@ __device__ int first_crossing(int V, Wt w, long long thr, Shared& sh) {
     run += x;
   }
   if (wave == cw) {
-    for (int base = r.lo; base < r.hi; base += kWave) {
-      const int i = base + lane;
-      const u64 x = i < r.hi ? w(i) : 0ull;
-      const u64 incl = wave_incl_scan(x);
-      const u64 hit = __ballot(x > 0 && (long long)(before + incl) > thr);
-      if (hit) {
-        if (lane == 0) sh.sel[0] = base + __ffsll((unsigned long long)hit) - 1;
-        break;
+    const u64 incl = wave_incl_scan(own);
+    const u64 hit = __ballot(own > 0 && (long long)(before + incl) > thr);
+    if (hit && lane == __ffsll((unsigned long long)hit) - 1) {
+      u64 acc = before + incl - own;
+      for (int i = l0; i < l1; ++i) {
+        const u64 x = w(i);
+        acc += x;
+        if (x > 0 && (long long)acc > thr) {
+          sh.sel[0] = i;
+          break;
+        }
       }
-      before += __shfl(incl, kWave - 1, kWave);
     }
   }
   __syncthreads();
@@ -210,6 +249,7 @@ __device__ void select_mass_digit(u64 above, double target, Shared& sh) {
 
 constexpr int kLdsVocab = 32768;  // rows up to this size are staged in LDS (128 KB)
 constexpr int kCand = 4096;       // top-k sets up to this size are compacted into LDS
+static_assert(kCand >= kNW * 256, "the candidate list holds the per-wave digit histograms");
 
 // One workgroup of 1024 threads per row. With kLds the row is copied into LDS once (16-byte
 // loads, all in flight together) and every pass reads it there; otherwise every pass reads the
@@ -235,14 +275,14 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
   const float* z = kLds ? zrow : zg;
   const Range rg(V);
   float mx = -INFINITY;
-  for (int i = rg.lo + lane; i < rg.hi; i += kWave) mx = fmaxf(mx, z[i]);
+  for_lane(rg, z, [&](int, float zi) { mx = fmaxf(mx, zi); });
   mx = block_max(mx, sh);
 
   int a;
   float lpb, log_z1;
   if (!(temperature > 0.f)) {
     float s1 = 0.f;
-    for (int i = rg.lo + lane; i < rg.hi; i += kWave) s1 += expf(z[i] - mx);
+    for_lane(rg, z, [&](int, float zi) { s1 += __expf(zi - mx); });
     log_z1 = logf(block_sum(s1, sh));
     // greedy: the first maximal logit
     a = first_crossing(V, [&](int i) -> u64 { return z[i] == mx ? 1ull : 0ull; }, -1, sh);
@@ -250,11 +290,12 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
   } else {
     const float inv_t = 1.f / temperature, mt = mx * inv_t;
     float s1 = 0.f, st = 0.f;
-    for (int i = rg.lo + lane; i < rg.hi; i += kWave) {
-      const float zi = z[i];
-      s1 += expf(zi - mx);
-      st += expf(fmaf(zi, inv_t, -mt));
-    }
+    // the normalisers use the hardware exponential: st scales every fixed-point mass by the
+    // same factor, which cancels in every decision (all of them compare ratios of masses)
+    for_lane(rg, z, [&](int, float zi) {
+      s1 += __expf(zi - mx);
+      st += __expf(fmaf(zi, inv_t, -mt));
+    });
     log_z1 = logf(block_sum(s1, sh));
     st = block_sum(st, sh);
     const float inv_st = 1.f / st;
@@ -266,29 +307,37 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
     // top-k: the k-th largest key, and how many of the tokens holding it are kept
     const bool use_k = top_k > 0 && top_k < V;
     uint32_t kth = 0;
-    int tie_cut_k = V;
+    int tie_cut_k = V, ties_kept = 0;
     if (use_k) {
       uint32_t prefix = 0, pmask = 0;
       int remaining = top_k;
       for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) sh.cnt[tid] = 0;
+        // per-wave histograms (in the candidate list's LDS, unused until the selection is
+        // done), so that waves do not contend for the few digits most logits share; runs of
+        // equal digits in a lane are added once
+        uint32_t* hist = reinterpret_cast<uint32_t*>(cand) + (tid / kWave) * 256;
+        for (int j = tid; j < kNW * 256; j += kST) reinterpret_cast<uint32_t*>(cand)[j] = 0;
         __syncthreads();
         {
-          // runs of equal digits are counted in registers and added once (most logits share
-          // the leading digit, which would serialise the LDS atomics)
           uint32_t cur = 256u, run = 0u;
-          for (int i = rg.lo + lane; i < rg.hi; i += kWave) {
-            const uint32_t key = order_key(z[i]);
-            if ((key & pmask) != prefix) continue;
+          for_lane(rg, z, [&](int, float zi) {
+            const uint32_t key = order_key(zi);
+            if ((key & pmask) != prefix) return;
             const uint32_t dg = (key >> shift) & 255u;
             if (dg != cur) {
-              if (run) atomicAdd(&sh.cnt[cur], run);
+              if (run) atomicAdd(&hist[cur], run);
               cur = dg;
               run = 0u;
             }
             ++run;
-          }
-          if (run) atomicAdd(&sh.cnt[cur], run);
+          });
+          if (run) atomicAdd(&hist[cur], run);
+        }
+        __syncthreads();
+        if (tid < 256) {
+          uint32_t c = 0;
+          for (int w = 0; w < kNW; ++w) c += reinterpret_cast<const uint32_t*>(cand)[w * 256 + tid];
+          sh.cnt[tid] = c;
         }
         __syncthreads();
         select_count_digit(remaining, sh);
@@ -298,10 +347,7 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
         __syncthreads();
       }
       kth = prefix;
-      // ties at the k-th key: the first `remaining` of them in ascending id
-      tie_cut_k = first_crossing(
-          V, [&](int i) -> u64 { return order_key(z[i]) == kth ? 1ull : 0ull; },
-          (long long)remaining - 1, sh);
+      ties_kept = remaining;  // the first `remaining` tokens holding the k-th key, by id
     }
     auto in_topk = [&](int i) -> bool {
       if (!use_k) return true;
@@ -397,31 +443,96 @@ __global__ __launch_bounds__(kST) void k_sample(const float* __restrict__ logits
       lpb = (z[a] * inv_t - mt - logf(st)) - logf((float)((double)mass / kFix));
     };
 
+    // The ids holding a key >= kth (the top-k and every tie at its boundary) in ascending
+    // order, when there are at most kCand: per-wave counts, then each wave writes its ids strip
+    // by strip at its offset (ballot positions within a strip). The ties kept are then found
+    // on that list; more ids, or no top-k, and the same is done over all V tokens.
+    int total = kCand + 1;
     if (use_k && top_k <= kCand) {
-      // the top-k ids in ascending order: per-wave counts, then each wave writes its members
-      // strip by strip at its offset (ballot positions within a strip)
       u64 cnt = 0;
-      for (int i = rg.lo + lane; i < rg.hi; i += kWave) cnt += in_topk(i) ? 1ull : 0ull;
+      for_lane(rg, z, [&](int, float zi) { cnt += order_key(zi) >= kth ? 1ull : 0ull; });
       cnt = wave_sum_u64(cnt);
       if (lane == 0) sh.wtot[tid / kWave] = cnt;
       __syncthreads();
-      int pos = 0, total = 0;
+      int pos = 0;
+      total = 0;
       for (int w = 0; w < kNW; ++w) {
         if (w < tid / kWave) pos += (int)sh.wtot[w];
         total += (int)sh.wtot[w];
       }
-      for (int b0 = rg.lo; b0 < rg.hi; b0 += kWave) {
-        const int i = b0 + lane;
-        const bool m = i < rg.hi && in_topk(i);
-        const u64 bal = __ballot(m);
-        const int at = pos + __popcll(bal & ((1ull << lane) - 1ull));
-        if (m && at < kCand) cand[at] = i;
-        pos += __popcll(bal);
+      if (total <= kCand) {
+        for (int b0 = rg.lo; b0 < rg.hi; b0 += 8 * kWave) {
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int i = b0 + q * kWave + lane;
+            v[q] = i < rg.hi ? z[i] : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int i = b0 + q * kWave + lane;
+            const bool m = i < rg.hi && order_key(v[q]) >= kth;
+            const u64 bal = __ballot(m);
+            if (m) cand[pos + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+            pos += __popcll(bal);
+          }
+        }
       }
       __syncthreads();
-      tail(min(total, kCand), [&](int j) -> int { return cand[j]; },
-           [](int) -> bool { return true; });
+    }
+    if (total <= kWave) {
+      // At most 64 candidates: wave 0 holds one per lane (ascending id = ascending lane) and
+      // takes every decision with lane operations. Top-k keeps the ties at kth of rank below
+      // ties_kept; top-p keeps a member when the mass of the members before it in the
+      // nucleus order (key descending, id ascending) is still below the target, which is the
+      // shortest prefix reaching it; the action is the first kept member, by id, whose
+      // inclusive kept mass exceeds floor(u * mass).
+      if (tid < kWave) {
+        const bool valid = lane < total;
+        const int i = valid ? cand[lane] : 0;
+        const uint32_t key = valid ? order_key(z[i]) : 0u;
+        const u64 ties = __ballot(valid && key == kth);
+        const int rank = __popcll(ties & ((1ull << lane) - 1ull));
+        const bool mem = valid && (key > kth || (key == kth && rank < ties_kept));
+        const u64 f = mem ? fq(i) : 0ull;
+        bool keep = mem;
+        if (top_p < 1.f) {
+          const double target = (double)top_p * (double)wave_sum_u64(f);
+          u64 before = 0;
+          for (int o = 0; o < kWave; ++o) {
+            const uint32_t ko = __shfl(key, o, kWave);
+            const u64 fo = __shfl(f, o, kWave);
+            before += (ko > key || (ko == key && o < lane)) ? fo : 0ull;
+          }
+          keep = mem && (double)before < target;
+        }
+        const u64 kf = keep ? f : 0ull;
+        const u64 incl = wave_incl_scan(kf);
+        const u64 mass = __shfl(incl, kWave - 1, kWave);
+        u64 tu = (u64)floor((double)u[row] * (double)mass);
+        if (tu >= mass) tu = mass - 1;
+        const u64 hit = __ballot(kf > 0 && incl > tu);
+        if (lane == 0) {
+          // hit != 0: the kept mass is positive and tu < mass
+          sh.sel[0] = hit ? cand[__ffsll((unsigned long long)hit) - 1] : V - 1;
+          sh.tot = mass;
+        }
+      }
+      __syncthreads();
+      a = sh.sel[0];
+      lpb = (z[a] * inv_t - mt - logf(st)) - logf((float)((double)sh.tot / kFix));
+    } else if (total <= kCand) {
+      const int jt = first_crossing(
+          total, [&](int j) -> u64 { return order_key(z[cand[j]]) == kth ? 1ull : 0ull; },
+          (long long)ties_kept - 1, sh);
+      tie_cut_k = cand[jt];  // jt < total: at least ties_kept ties are listed
+      tail(total, [&](int j) -> int { return cand[j]; },
+           [&](int j) -> bool { return in_topk(cand[j]); });
     } else {
+      if (use_k)
+        tie_cut_k = first_crossing(
+            V, [&](int i) -> u64 { return order_key(z[i]) == kth ? 1ull : 0ull; },
+            (long long)ties_kept - 1, sh);
       tail(V, [](int j) -> int { return j; }, [&](int j) -> bool { return in_topk(j); });
     }
   }

@@ -818,7 +818,8 @@ template <class AL, class EP>
 static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
                             const AL& al, const EP& ep, double out_bytes) {
   if constexpr (std::is_same<AL, PA>::value) {
-    if (N % 256 == 0 && wks == K / 32) {
+    // the 256 x 256 kernel when it has at least one workgroup per compute unit
+    if (N % 256 == 0 && wks == K / 32 && (int64_t)((R + 255) / 256) * (N / 256) >= 256) {
       const int64_t blocks = (int64_t)((R + 255) / 256) * (N / 256);
       if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
       Exec x(c.st);
