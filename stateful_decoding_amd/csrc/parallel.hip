@@ -430,7 +430,13 @@ struct PSilu {
 };
 
 // ---- RMSNorm of every row into the next GEMM's operand -------------------------------------------
-// One wave per row: a = bf16(h * gamma / sqrt(mean(h^2) + eps)) in fragment order.
+// One wave per row: a = bf16(h * gamma / sqrt(mean(h^2) + eps)) in fragment order (FRAG) or
+// row-major. Each lane owns 8-column chunks lane, lane + 64, ...; rows of up to 64 x 8 x kNC
+// columns are held in registers between the sum of squares and the scaling (one read of h),
+// wider ones are read again.
+constexpr int kNormChunks = 4;  // d <= 2048 from registers
+
+template <bool FRAG>
 __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict__ h,
                                                         const float* __restrict__ gamma, int d,
                                                         float eps, int R, bf16* __restrict__ a) {
@@ -438,22 +444,56 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
   const int lane = threadIdx.x % kWave;
   if (row >= R) return;
   const float* x = h + (int64_t)row * d;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const u32x4 r = ld16(x + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = __uint_as_float(r[i]);
-      ss += v * v;
-    }
-  }
-  ss = wave_sum(ss);
-  const float rinv = rsqrtf(ss / (float)d + eps);
-  for (int c = lane * 8; c < d; c += kWave * 8) {
+  auto store = [&](int c, const float (&v)[8], float rinv) {
+    const u32x4 g0 = ld16(gamma + c), g1 = ld16(gamma + c + 4);
     bf16x8 o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (bf16)(x[c + i] * gamma[c + i] * rinv);
-    st16(a + frag_off(row, c, d / 32), __builtin_bit_cast(u32x4, o));
+    for (int i = 0; i < 4; ++i) {
+      o[i] = (bf16)(v[i] * __uint_as_float(g0[i]) * rinv);
+      o[4 + i] = (bf16)(v[4 + i] * __uint_as_float(g1[i]) * rinv);
+    }
+    bf16* dst = FRAG ? a + frag_off(row, c, d / 32) : a + (int64_t)row * d + c;
+    st16(dst, __builtin_bit_cast(u32x4, o));
+  };
+  auto load8 = [&](int c, float (&v)[8]) {
+    const u32x4 r0 = ld16(x + c), r1 = ld16(x + c + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(r0[i]);
+      v[4 + i] = __uint_as_float(r1[i]);
+    }
+  };
+  float ss = 0.f;
+  if (d <= kWave * 8 * kNormChunks) {
+    float v[kNormChunks][8];
+#pragma unroll
+    for (int q = 0; q < kNormChunks; ++q) {
+      const int c = (lane + kWave * q) * 8;
+      if (c < d) {
+        load8(c, v[q]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += v[q][i] * v[q][i];
+      }
+    }
+    const float rinv = rsqrtf(wave_sum(ss) / (float)d + eps);
+#pragma unroll
+    for (int q = 0; q < kNormChunks; ++q) {
+      const int c = (lane + kWave * q) * 8;
+      if (c < d) store(c, v[q], rinv);
+    }
+  } else {
+    for (int c = lane * 8; c < d; c += kWave * 8) {
+      float v[8];
+      load8(c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    }
+    const float rinv = rsqrtf(wave_sum(ss) / (float)d + eps);
+    for (int c = lane * 8; c < d; c += kWave * 8) {
+      float v[8];
+      load8(c, v);
+      store(c, v, rinv);
+    }
   }
 }
 
@@ -737,33 +777,6 @@ __global__ __launch_bounds__(kThreads) void k_embed(const int32_t* __restrict__ 
   h[i] = t >= 0 && t < V ? (float)E[(int64_t)t * d + c] : 0.f;
 }
 
-// One wave per row: e = bf16(h * gamma / sqrt(mean(h^2) + eps)), row-major [R][d].
-__global__ __launch_bounds__(kThreads) void k_norm_out(const float* __restrict__ h,
-                                                       const float* __restrict__ gamma, int d,
-                                                       float eps, int R, bf16* __restrict__ e) {
-  const int row = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (row >= R) return;
-  const float* x = h + (int64_t)row * d;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const u32x4 r = ld16(x + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = __uint_as_float(r[i]);
-      ss += v * v;
-    }
-  }
-  ss = wave_sum(ss);
-  const float rinv = rsqrtf(ss / (float)d + eps);
-  for (int c = lane * 8; c < d; c += kWave * 8) {
-    bf16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (bf16)(x[c + i] * gamma[c + i] * rinv);
-    st16(e + (int64_t)row * d + c, __builtin_bit_cast(u32x4, o));
-  }
-}
-
 // ---- host side ------------------------------------------------------------------------------------
 
 ParLayout par_layout(const Dims& D, int B, int64_t n) {
@@ -848,7 +861,7 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
 template <int HD>
 static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const bf16* v,
                           int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
-                          bf16* vt) {
+                          bf16* vt, bool vt_fresh) {
   // one 16-query tile per wave: two (each K / V fragment read from LDS serving both) measured
   // no faster at hd = 64 (41.6 against 41.3 ms of memory attention per pass) with half the
   // resident waves, and do not fit in 256 registers at hd = 128
@@ -868,7 +881,7 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
   const double bhd = (double)B * H * HD;
   const int vt_len = vt_tiles * 64;
   hipError_t e;
-  if (vt) {  // values transposed first (timed as its own kind)
+  if (vt && !vt_fresh) {  // values transposed first (timed as its own kind)
     Exec xt(c.st);
     if ((e = c.arm(RLT_K_PAR_OTHER, bhd * (n + vt_len) * 2, 0, xt)) != hipSuccess) return e;
     e = launch(k_transpose_v<HD>, dim3((unsigned)((int64_t)B * H * vt_tiles)), dim3(kThreads), xt,
@@ -888,14 +901,15 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
                 static_cast<const bf16*>(nullptr), 0, o);
 }
 
-// vt (optional): workspace of B H hd ceil(n / 64) 64 elements for the values transposed first
+// vt (optional): workspace of B H hd ceil(n / 64) 64 elements for the values transposed first;
+// vt_fresh: it already holds these values transposed (the same memory group as the last call)
 static hipError_t flash(const ParCtx& c, int hd, const bf16* q, const bf16* k, const bf16* v,
                         int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
-                        bf16* vt = nullptr) {
+                        bf16* vt = nullptr, bool vt_fresh = false) {
   switch (hd) {
-    case 32: return flash_t<32>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
-    case 64: return flash_t<64>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
-    case 128: return flash_t<128>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt);
+    case 32: return flash_t<32>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt, vt_fresh);
+    case 64: return flash_t<64>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt, vt_fresh);
+    case 128: return flash_t<128>(c, q, k, v, kv_bh_stride, B, n, H, W, o, vt, vt_fresh);
     default: return hipErrorInvalidValue;
   }
 }
@@ -906,8 +920,8 @@ static hipError_t norm_rows(const ParCtx& c, const Dims& D, const float* h, cons
   Exec x(c.st);
   hipError_t e = c.arm(RLT_K_PAR_OTHER, (double)R * D.d * 6, 4.0 * R * D.d, x);
   if (e != hipSuccess) return e;
-  return launch(k_norm_rows, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), x, h, gamma,
-                D.d, D.eps, R, a);
+  return launch(k_norm_rows<true>, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), x, h,
+                gamma, D.d, D.eps, R, a);
 }
 
 hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,
@@ -985,8 +999,10 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, cons
     }
   }
   const int per = kThreads / kWave;
-  return launch(k_norm_out, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads), Exec(st),
-                (const float*)h, Hd.enc_gamma_out, d, D.eps, R, static_cast<bf16*>(e_out));
+  // e = the final norm's output, row-major (the layout rlt_memproj and the gate read)
+  return launch(k_norm_rows<false>, dim3((unsigned)((R + per - 1) / per)), dim3(kThreads),
+                Exec(st), (const float*)h, Hd.enc_gamma_out, d, D.eps, R,
+                static_cast<bf16*>(e_out));
 }
 
 hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBufs& S,
@@ -1061,9 +1077,10 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     {
       const int gsel = D.G == 1 ? 0 : l;
       const int64_t grp = (int64_t)gsel * M.Bt * H * M.capacity * hd;
+      // with one memory group for every layer its values are transposed once
       if ((err = flash(c, hd, q, static_cast<const bf16*>(M.k) + grp,
                        static_cast<const bf16*>(M.v) + grp, M.capacity * hd, B, n, H, 0, o,
-                       reinterpret_cast<bf16*>(w + Lp.vt))) != hipSuccess)
+                       reinterpret_cast<bf16*>(w + Lp.vt), D.G == 1 && l > 0)) != hipSuccess)
         return err;
     }
     {
