@@ -207,7 +207,7 @@ hipError_t launch_step(const Dims& D, int B, const Packed& P, const StateBufs& S
 //   h [B n][d] f32 residual stream; a [R][d] bf16 normed operand (fragment order);
 //   q, k, v [B][H][n][hd] bf16; o [R][d], act [R][F] bf16 (fragment order); R = B n rounded up
 struct ParLayout {
-  size_t h, a, q, k, v, o, act, vt, total;
+  size_t h, a, q, k, v, o, act, vt, ssq, total;
 };
 ParLayout par_layout(const Dims& D, int B, int64_t n);
 

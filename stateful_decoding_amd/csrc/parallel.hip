@@ -244,30 +244,53 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
 // (rbase already includes 4 (l / 16)) after k_gemm_rows / k_gemm_lds, and
 // acc[fm][fn][i] = C[row0 + 16 fm][col0 + 16 fn + i] (row0 = rows of l % 16, col0 includes
 // 4 (l / 16)) after k_gemm_big (tile_t). Rows >= R are padding and are never stored.
+// RMSNorm folded around a product: when ssq is set, the operand was bf16(h * gamma) and output
+// row r is scaled by 1/rms(h_r) = rsqrt(sum of the row's nslot partial sums of squares / d +
+// eps) (a per-row scalar commutes with the product); otherwise the scale is 1.
+struct RowScale {
+  const float* rinv = nullptr;  // [R] 1/rms of each row (k_row_rinv), or none
+  __device__ float scale(int row) const { return rinv ? rinv[row] : 1.f; }
+};
+
+// rinv[row] = rsqrt(sum of the row's nslot partial sums of squares / d + eps)
+__global__ __launch_bounds__(kThreads) void k_row_rinv(const float* __restrict__ ssq, int nslot,
+                                                       float inv_d, float eps, int R,
+                                                       float* __restrict__ rinv) {
+  const int row = blockIdx.x * kThreads + threadIdx.x;
+  if (row >= R) return;
+  const float* p = ssq + (int64_t)row * nslot;
+  float t = 0.f;
+  for (int j = 0; j < nslot; ++j) t += p[j];
+  rinv[row] = rsqrtf(t * inv_d + eps);
+}
+
 template <class D>
 struct PerElement {
   template <int FM, int FN>
   __device__ void tile(const f32x4 (&acc)[FM][FN], int rbase, int cwave, int lane) const {
+    const D& ep = *static_cast<const D*>(this);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int i = 0; i < 4; ++i) {
+        const int row = rbase + 16 * fm + i;
+        if (row >= ep.R) continue;
+        const float sc = ep.scale(row);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rbase + 16 * fm + i;
-          if (row < static_cast<const D*>(this)->R)
-            static_cast<const D*>(this)->op(row, cwave + 16 * fn + (lane & 15), acc[fm][fn][i]);
-        }
+        for (int fn = 0; fn < FN; ++fn)
+          ep.op(row, cwave + 16 * fn + (lane & 15), acc[fm][fn][i] * sc);
+      }
   }
   template <int FM, int FN>
   __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int lane) const {
+    const D& ep = *static_cast<const D*>(this);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int row = row0 + 16 * fm;
-      if (row < static_cast<const D*>(this)->R) {
+      if (row < ep.R) {
+        const float sc = ep.scale(row);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          static_cast<const D*>(this)->op4(row, col0 + 16 * fn, acc[fm][fn]);
+        for (int fn = 0; fn < FN; ++fn) ep.op4(row, col0 + 16 * fn, acc[fm][fn] * sc);
       }
     }
   }
@@ -284,7 +307,7 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
 }
 
 // h = sigmoid(v + b) * e  (the gated merge with alpha = 0)
-struct PGate : PerElement<PGate> {
+struct PGate : PerElement<PGate>, RowScale {
   float* h;
   const bf16* e;
   int64_t e_seq;
@@ -309,7 +332,7 @@ struct PGate : PerElement<PGate> {
 
 // Query / key / value of every token into per-head blocks [B][H][n][hd]; with N = d (the
 // cross-attention query) only q is written.
-struct PHeads : PerElement<PHeads> {
+struct PHeads : PerElement<PHeads>, RowScale {
   bf16* q;
   bf16* k;
   bf16* v;
@@ -347,11 +370,54 @@ struct PHeads : PerElement<PHeads> {
 
 // h += v (fp32, in place); at the last layer also s rows to out (row (b, i) at
 // out + b * out_seq + i * d).
-struct PResidual : PerElement<PResidual> {
+// With hg set (after k_gemm_big only), the epilogue also writes the next RMSNorm's operand
+// hg = bf16(h * gnext) in fragment order and, per row, the sum of h^2 over each wave's 64
+// columns into ssq[row][col / 64] (d / 64 slots, every one written, so nothing is cleared).
+struct PResidual : PerElement<PResidual>, RowScale {
   float* h;
   float* out;
   int64_t out_seq;
   int n, d, R;
+  bf16* hg = nullptr;
+  const float* gnext = nullptr;
+  float* ssq_out = nullptr;
+  template <int FM, int FN>
+  __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int lane) const {
+    if (!hg) {
+      PerElement<PResidual>::tile_t<FM, FN>(acc, row0, col0, lane);
+      return;
+    }
+    f32x4 g[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      g[fn] = *reinterpret_cast<const f32x4*>(gnext + col0 + 16 * fn);
+    const int slot = (col0 - 4 * (lane >> 4)) / 64;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = row0 + 16 * fm;
+      float ss = 0.f;
+      if (row < R) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = col0 + 16 * fn;
+          f32x4* p = reinterpret_cast<f32x4*>(h + (int64_t)row * d + col);
+          const f32x4 r = *p + acc[fm][fn];
+          *p = r;
+          if (out) {
+            const int b = row / n, i = row - b * n;
+            *reinterpret_cast<f32x4*>(out + (int64_t)b * out_seq + (int64_t)i * d + col) = r;
+          }
+          *reinterpret_cast<uint2*>(hg + frag_off(row, col, d / 32)) = pack_bf16x4(r * g[fn]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss += r[i] * r[i];
+        }
+      }
+      // the four lanes holding this row (lane % 16 equal) cover the wave's 64 columns
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      if (row < R && lane < 16) ssq_out[(int64_t)row * (d / 64) + slot] = ss;
+    }
+  }
   __device__ void op(int row, int col, float v) const {
     float* p = h + (int64_t)row * d + col;
     const float r = *p + v;
@@ -373,7 +439,7 @@ struct PResidual : PerElement<PResidual> {
 };
 
 // out[row][col] = v (fp32, row stride ld): the readout's logits
-struct PStoreF32 : PerElement<PStoreF32> {
+struct PStoreF32 : PerElement<PStoreF32>, RowScale {
   float* out;
   int ld, R;
   __device__ void op(int row, int col, float v) const { out[(int64_t)row * ld + col] = v; }
@@ -385,7 +451,7 @@ struct PStoreF32 : PerElement<PStoreF32> {
 // act = SiLU(x W1) * (x W3) in fragment order. The packed up-projection interleaves 16 columns
 // of W1 and the same 16 of W3 per 32 columns, and a wave's FN (even) fragments start on a
 // multiple of 32, so fragments 2j and 2j + 1 of a lane hold the two factors of one output.
-struct PSilu {
+struct PSilu : RowScale {
   bf16* act;
   int F, R;
   template <int FM, int FN>
@@ -399,7 +465,8 @@ struct PSilu {
         for (int i = 0; i < 4; ++i) {
           const int row = rbase + 16 * fm + i;
           if (row >= R) continue;
-          const float z1 = acc[fm][2 * j][i], z3 = acc[fm][2 * j + 1][i];
+          const float sc = scale(row);
+          const float z1 = acc[fm][2 * j][i] * sc, z3 = acc[fm][2 * j + 1][i] * sc;
           const int col = (cwave + 32 * j) / 2 + (lane & 15);
           act[frag_off(row, col, F / 32)] = (bf16)(z1 * sigmoidf_(z1) * z3);
         }
@@ -414,12 +481,13 @@ struct PSilu {
     for (int fm = 0; fm < FM; ++fm) {
       const int row = row0 + 16 * fm;
       if (row >= R) continue;
+      const float sc = scale(row);
 #pragma unroll
       for (int j = 0; j < FN / 2; ++j) {
         f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float z1 = acc[fm][2 * j][i], z3 = acc[fm][2 * j + 1][i];
+          const float z1 = acc[fm][2 * j][i] * sc, z3 = acc[fm][2 * j + 1][i] * sc;
           y[i] = z1 * sigmoidf_(z1) * z3;
         }
         const int col = (cbase + 32 * j) / 2 + 4 * (lane >> 4);
@@ -796,6 +864,7 @@ ParLayout par_layout(const Dims& D, int B, int64_t n) {
   p.o = take(R16 * d * 2);
   p.act = take(R16 * D.F * 2);
   p.vt = take((size_t)B * d * ((n + 63) / 64 * 64) * 2);  // values transposed, one group
+  p.ssq = take(R * (d / 64 + 1) * 4);  // per-row partial sums of squares (64 columns each), 1/rms
   p.total = o;
   return p;
 }
@@ -829,10 +898,13 @@ static hipError_t gemm_rows_t(const ParCtx& c, int R, int N, int K, int wks, con
 // multiple of 128, else 32 x 32 per wave. Fragment-ordered operands with such N go through LDS.
 template <class AL, class EP>
 static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
-                            const AL& al, const EP& ep, double out_bytes) {
+                            const AL& al, const EP& ep, double out_bytes,
+                            bool force_big = false) {
   if constexpr (std::is_same<AL, PA>::value) {
-    // the 256 x 256 kernel when it has at least one workgroup per compute unit
-    if (N % 256 == 0 && wks == K / 32 && (int64_t)((R + 255) / 256) * (N / 256) >= 256) {
+    // the 256 x 256 kernel when it has at least one workgroup per compute unit (always when
+    // force_big: epilogues that write the next norm's operand exist only in its layout)
+    if (N % 256 == 0 && wks == K / 32 &&
+        (force_big || (int64_t)((R + 255) / 256) * (N / 256) >= 256)) {
       const int64_t blocks = (int64_t)((R + 255) / 256) * (N / 256);
       if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
       Exec x(c.st);
@@ -924,6 +996,44 @@ static hipError_t norm_rows(const ParCtx& c, const Dims& D, const float* h, cons
                 gamma, D.d, D.eps, R, a);
 }
 
+// The RMSNorm before a projection is folded around it when the residual projection before it
+// can write the operand (d a multiple of 256, so every projection with N = d runs k_gemm_big):
+// the producer stores bf16(h * gamma) and per-row sums of squares, the consumer scales its
+// output rows by 1/rms. Otherwise a k_norm_rows launch writes the normalised operand.
+static bool norm_folds(const Dims& D) { return D.d % 256 == 0; }
+
+// 1/rms of every row from the partial sums the last residual projection left in ssq; returns
+// the consumer's RowScale (rinv sits after the R * d / 64 partial sums).
+static hipError_t row_scale(const ParCtx& c, const Dims& D, int R, float* ssq, RowScale* rs) {
+  float* rinv = ssq + (int64_t)R * (D.d / 64);
+  Exec x(c.st);
+  hipError_t e = c.arm(RLT_K_PAR_OTHER, (double)R * (D.d / 64 + 1) * 4, 0, x);
+  if (e != hipSuccess) return e;
+  e = launch(k_row_rinv, dim3((unsigned)((R + kThreads - 1) / kThreads)), dim3(kThreads), x,
+             (const float*)ssq, D.d / 64, 1.f / (float)D.d, D.eps, R, rinv);
+  rs->rinv = rinv;
+  return e;
+}
+
+// PResidual for h += x W; when the next RMSNorm (gain gnext) is folded, it also writes that
+// norm's operand into a and the row sums of squares into ssq.
+static PResidual residual(const Dims& D, float* h, float* out, int64_t out_seq, int n, int R,
+                          const float* gnext, bf16* a, float* ssq) {
+  PResidual ep;
+  ep.h = h;
+  ep.out = out;
+  ep.out_seq = out_seq;
+  ep.n = n;
+  ep.d = D.d;
+  ep.R = R;
+  if (gnext) {
+    ep.hg = a;
+    ep.gnext = gnext;
+    ep.ssq_out = ssq;
+  }
+  return ep;
+}
+
 hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,
                                float* logits, hipStream_t st) {
   const int V = Hd.vocab, d = D.d;
@@ -959,13 +1069,18 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, cons
   err = launch(k_embed, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads),
                Exec(st), tokens, static_cast<const bf16*>(Hd.embed), d, Hd.vocab, total, h);
   if (err != hipSuccess) return err;
+  const bool fold = norm_folds(D);
+  float* ssq = reinterpret_cast<float*>(w + Lp.ssq);
   for (int l = 0; l < D.L; ++l) {
     const float* gam = Hd.enc_gamma + (int64_t)l * 2 * d;
     const int64_t wdd = (int64_t)l * d * d;
-    // causal self-attention over positions 1..t with the decoder block's matrices
-    if ((err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
+    // causal self-attention over positions 1..t with the decoder block's matrices; its norm
+    // is folded from the previous block's down projection except in the first block
+    const bool norm_attn = !fold || l == 0;
+    if (norm_attn && (err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
     {
-      PHeads ep{{}, q, kk, vv, n, d, H, hd, R};
+      PHeads ep{{}, {}, q, kk, vv, n, d, H, hd, R};
+      if (!norm_attn && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
       if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
           hipSuccess)
@@ -975,25 +1090,27 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, cons
                      reinterpret_cast<bf16*>(w + Lp.vt))) != hipSuccess)
       return err;
     {
-      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const PResidual ep = residual(D, h, nullptr, 0, n, R, fold ? gam + d : nullptr, a, ssq);
       const bf16* Wo = static_cast<const bf16*>(P.wo_t) + wdd;
-      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8, fold)) !=
           hipSuccess)
         return err;
     }
     // SiLU-gated FFN with the decoder block's matrices
-    if ((err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
+    if (!fold && (err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
     {
-      PSilu ep{act, F, R};
+      PSilu ep{{}, act, F, R};
+      if (fold && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* W13 = static_cast<const bf16*>(P.w13_t) + (int64_t)l * 2 * F * d;
       if ((err = gemm_rows(c, R, 2 * F, d, d / 32, W13, PA{a, d / 32, R}, ep,
                            (double)R * F * 2)) != hipSuccess)
         return err;
     }
     {
-      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const float* gnext = fold && l + 1 < D.L ? gam + 2 * d : nullptr;
+      const PResidual ep = residual(D, h, nullptr, 0, n, R, gnext, a, ssq);
       const bf16* W2 = static_cast<const bf16*>(P.w2_t) + (int64_t)l * d * F;
-      if ((err = gemm_rows(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep, Rd * 8, fold)) !=
           hipSuccess)
         return err;
     }
@@ -1033,14 +1150,19 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
       return err;
   }
   const int keep = n < D.W - 1 ? n : D.W - 1;
+  const bool fold = norm_folds(D);
+  float* ssq = reinterpret_cast<float*>(w + Lp.ssq);
   for (int l = 0; l < D.L; ++l) {
     const bool last = l == D.L - 1;
     const float* gam = P.gamma + (int64_t)l * 3 * d;
     const int64_t wdd = (int64_t)l * d * d;
-    // self-attention sublayer
-    if ((err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
+    // self-attention sublayer; its norm is folded from the previous block's down projection
+    // except in the first block
+    const bool norm_attn = !fold || l == 0;
+    if (norm_attn && (err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
     {
-      PHeads ep{{}, q, kk, vv, n, d, H, hd, R};
+      PHeads ep{{}, {}, q, kk, vv, n, d, H, hd, R};
+      if (!norm_attn && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
       if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
           hipSuccess)
@@ -1059,16 +1181,17 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     }
     if ((err = flash(c, hd, q, kk, vv, (int64_t)n * hd, B, n, H, D.W, o)) != hipSuccess) return err;
     {
-      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const PResidual ep = residual(D, h, nullptr, 0, n, R, fold ? gam + d : nullptr, a, ssq);
       const bf16* Wo = static_cast<const bf16*>(P.wo_t) + wdd;
-      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wo, PA{o, d / 32, R}, ep, Rd * 8, fold)) !=
           hipSuccess)
         return err;
     }
     // cross-attention sublayer: memory entries 1..t of this layer's group
-    if ((err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
+    if (!fold && (err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
     {
-      PHeads ep{{}, q, nullptr, nullptr, n, d, H, hd, R};
+      PHeads ep{{}, {}, q, nullptr, nullptr, n, d, H, hd, R};
+      if (fold && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wc = static_cast<const bf16*>(P.wcq_t) + wdd;
       if ((err = gemm_rows(c, R, d, d, d / 32, Wc, PA{a, d / 32, R}, ep, Rd * 2)) !=
           hipSuccess)
@@ -1084,26 +1207,29 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
         return err;
     }
     {
-      PResidual ep{{}, h, nullptr, 0, n, d, R};
+      const PResidual ep =
+          residual(D, h, nullptr, 0, n, R, fold ? gam + 2 * d : nullptr, a, ssq);
       const bf16* Wco = static_cast<const bf16*>(P.wco_t) + wdd;
-      if ((err = gemm_rows(c, R, d, d, d / 32, Wco, PA{o, d / 32, R}, ep, Rd * 8)) !=
+      if ((err = gemm_rows(c, R, d, d, d / 32, Wco, PA{o, d / 32, R}, ep, Rd * 8, fold)) !=
           hipSuccess)
         return err;
     }
     // FFN sublayer
-    if ((err = norm_rows(c, D, h, gam + 2 * d, R, a)) != hipSuccess) return err;
+    if (!fold && (err = norm_rows(c, D, h, gam + 2 * d, R, a)) != hipSuccess) return err;
     {
-      PSilu ep{act, F, R};
+      PSilu ep{{}, act, F, R};
+      if (fold && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* W13 = static_cast<const bf16*>(P.w13_t) + (int64_t)l * 2 * F * d;
       if ((err = gemm_rows(c, R, 2 * F, d, d / 32, W13, PA{a, d / 32, R}, ep,
                                  (double)R * F * 2)) != hipSuccess)
         return err;
     }
     {
-      PResidual ep{{}, h, last ? out : nullptr, out_seq, n, d, R};
+      const float* gnext = fold && !last ? gam + 3 * d : nullptr;  // the next block's first gain
+      const PResidual ep = residual(D, h, last ? out : nullptr, out_seq, n, R, gnext, a, ssq);
       const bf16* W2 = static_cast<const bf16*>(P.w2_t) + (int64_t)l * d * F;
       if ((err = gemm_rows(c, R, d, F, F / 32, W2, PA{act, F / 32, R}, ep,
-                                 Rd * (last && out ? 12 : 8))) != hipSuccess)
+                                 Rd * (last && out ? 12 : 8), fold)) != hipSuccess)
         return err;
     }
   }

@@ -37,6 +37,9 @@ def run_parallel(g: GpuRun, e: np.ndarray) -> np.ndarray:
     dict(head_dim=64, window=64, B=2, T=200, n_layers=1),                    # window spans blocks
     dict(head_dim=64, window=40, B=1, T=17),                                 # T < W - 1
     dict(head_dim=64, window=6, B=19, T=64, ffn=192),                        # exactly one block
+    # d a multiple of 256: each RMSNorm folded into the projections around it (two 256-column
+    # tiles of the residual stream, 300 rows: a ragged row tile)
+    dict(head_dim=64, n_heads=8, d=512, ffn=1024, window=7, n_layers=2, B=3, T=100),
 ])
 def test_parallel_matches_oracle(case):
     case = dict(case)
