@@ -560,6 +560,10 @@ hipError_t launch_pack_fused_ocq(const Dims& D, const Packed& P, const void* wo,
 
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
                           const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st) {
+  // many bf16 tokens: the 256 x 256 GEMM, once it has a workgroup for every compute unit
+  if (D.dtype == RLT_BF16 && (D.G * 2 * D.d) % 256 == 0 &&
+      ((int64_t)B * n + 255) / 256 * (D.G * 2 * D.d / 256) >= 256)
+    return launch_memproj_rows(D, B, P, M, e, e_seq, t0, n, st);
   return D.dtype == RLT_BF16 ? memproj_t<bf16>(D, B, P, M, e, e_seq, t0, n, st)
                              : memproj_t<float>(D, B, P, M, e, e_seq, t0, n, st);
 }

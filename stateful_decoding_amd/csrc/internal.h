@@ -165,6 +165,10 @@ hipError_t launch_set_positions(int64_t* pos, int B, int64_t t, hipStream_t st);
 // sequence b, token i are at e + (b * e_seq + i) * d (elements).
 hipError_t launch_memproj(const Dims& D, int B, const Packed& P, const MemBufs& M,
                           const void* e, int64_t e_seq, int64_t t0, int64_t n, const Exec& st);
+// The same on the 256 x 256 GEMM (bf16, G * 2 d a multiple of 256), for many tokens.
+hipError_t launch_memproj_rows(const Dims& D, int B, const Packed& P, const MemBufs& M,
+                               const void* e, int64_t e_seq, int64_t t0, int64_t n,
+                               const Exec& st);
 
 // Event timing of selected kernels (owned by a state; see rlt_profile_begin).
 struct Profiler {

@@ -174,10 +174,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_lds(int N, int ksteps, const 
 constexpr int kBigThreads = 512;
 constexpr int kBigStages = 4;
 
-template <class EP>
+// ATok: A is not fragment-ordered but token rows, row (b, i) at A + (b * a_seq + i) * K (a_n
+// tokens per sequence): each lane then copies the 16 bytes of its own row, which lands in LDS
+// in the same fragment order.
+struct ATok {
+  int64_t a_seq;
+  int a_n;
+};
+
+template <class EP, bool TOK = false>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
                                                          const bf16* __restrict__ A, int R,
-                                                         const bf16* __restrict__ Wt, EP ep) {
+                                                         const bf16* __restrict__ Wt, EP ep,
+                                                         ATok tok) {
   constexpr int FM = 8, FN = 4, PER = 4;  // fragments each wave copies per k-step
   __shared__ __attribute__((aligned(16))) u32x4 sm[kBigStages][32][kWave];
   const int tiles_n = N / 256, nb = (int)gridDim.x;
@@ -189,18 +198,28 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
   const int last_rt = (R - 1) >> 4;
   // fragment slot f = wave + 8 u of a stage: slots 0..15 are A row tiles, 16..31 W column tiles
   const bf16* gp[PER];
+  int gstep[PER];  // elements from one k-step to the next
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int f = wave + 8 * u;
-    gp[u] = f < 16 ? A + ((((int64_t)min(tm * 16 + f, last_rt) * ksteps) << 6) + lane) * 8
-                   : Wt + ((((int64_t)(tn * 16 + f - 16) * ksteps) << 6) + lane) * 8;
+    gstep[u] = 512;
+    if (f >= 16) {
+      gp[u] = Wt + ((((int64_t)(tn * 16 + f - 16) * ksteps) << 6) + lane) * 8;
+    } else if (TOK) {
+      const int r = min(tm * 256 + f * 16 + (lane & 15), R - 1);
+      const int b = r / tok.a_n, i = r - b * tok.a_n;
+      gp[u] = A + ((int64_t)b * tok.a_seq + i) * (ksteps * 32) + (lane >> 4) * 8;
+      gstep[u] = 32;
+    } else {
+      gp[u] = A + ((((int64_t)min(tm * 16 + f, last_rt) * ksteps) << 6) + lane) * 8;
+    }
   }
   auto issue = [&](int s) {
     const int buf = s % kBigStages;
 #pragma unroll
     for (int u = 0; u < PER; ++u)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(gp[u] + (int64_t)s * 512),
+          (const void*)(gp[u] + (int64_t)s * gstep[u]),
           (__attribute__((address_space(3))) void*)&sm[buf][wave + 8 * u][0], 16, 0, 0);
   };
   f32x4 acc[FM][FN];
@@ -445,6 +464,28 @@ struct PStoreF32 : PerElement<PStoreF32>, RowScale {
   __device__ void op(int row, int col, float v) const { out[(int64_t)row * ld + col] = v; }
   __device__ void op4(int row, int col, f32x4 v) const {
     *reinterpret_cast<f32x4*>(out + (int64_t)row * ld + col) = v;
+  }
+};
+
+// Memory keys and values: row (b, i) = token t0 + i of sequence b, column (g, k|v, head, dim);
+// four consecutive columns never straddle a head.
+struct PMemproj : PerElement<PMemproj>, RowScale {
+  bf16* mk;
+  bf16* mv;
+  int64_t cap, t0;
+  int n, B, d, H, hd, R;
+  __device__ void op4(int row, int col, f32x4 x) const {
+    const int b = row / n, i = row - b * n;
+    const int g = col / (2 * d);
+    int c = col - g * 2 * d;
+    bf16* dst = mk;
+    if (c >= d) {
+      c -= d;
+      dst = mv;
+    }
+    const int hh = c / hd, dd = c - hh * hd;
+    *reinterpret_cast<uint2*>(dst + ((((int64_t)g * B + b) * H + hh) * cap + t0 + i) * hd + dd) =
+        pack_bf16x4(x);
   }
 };
 
@@ -911,8 +952,8 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
       hipError_t e = c.arm(RLT_K_PAR_GEMM, 2.0 * ((double)R * K + (double)K * N) + out_bytes,
                            2.0 * R * N * K, x);
       if (e != hipSuccess) return e;
-      return launch(k_gemm_big<EP>, dim3((unsigned)blocks), dim3(kBigThreads), x, N, K / 32,
-                    al.a, R, static_cast<const bf16*>(Wt), ep);
+      return launch(k_gemm_big<EP, false>, dim3((unsigned)blocks), dim3(kBigThreads), x, N,
+                    K / 32, al.a, R, static_cast<const bf16*>(Wt), ep, ATok{0, 1});
     }
     if (N % 128 == 0 && wks == K / 32) {
       const int64_t blocks = (int64_t)((R + 127) / 128) * (N / 128);
@@ -1032,6 +1073,30 @@ static PResidual residual(const Dims& D, float* h, float* out, int64_t out_seq, 
     ep.ssq_out = ssq;
   }
   return ep;
+}
+
+hipError_t launch_memproj_rows(const Dims& D, int B, const Packed& P, const MemBufs& M,
+                               const void* e, int64_t e_seq, int64_t t0, int64_t n,
+                               const Exec& st) {
+  const int64_t rows = (int64_t)B * n;
+  const int N = D.G * 2 * D.d;
+  const int64_t blocks = (rows + 255) / 256 * (N / 256);
+  if (D.dtype != RLT_BF16 || N % 256 != 0 || rows > INT32_MAX / 2 || blocks > INT32_MAX)
+    return hipErrorInvalidValue;
+  PMemproj ep;
+  ep.mk = static_cast<bf16*>(M.k);
+  ep.mv = static_cast<bf16*>(M.v);
+  ep.cap = M.capacity;
+  ep.t0 = t0;
+  ep.n = (int)n;
+  ep.B = B;
+  ep.d = D.d;
+  ep.H = D.H;
+  ep.hd = D.hd;
+  ep.R = (int)rows;
+  return launch(k_gemm_big<PMemproj, true>, dim3((unsigned)blocks), dim3(kBigThreads), st, N,
+                D.d / 32, static_cast<const bf16*>(e), (int)rows,
+                static_cast<const bf16*>(P.wm_t), ep, ATok{e_seq, (int)n});
 }
 
 hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,

@@ -85,7 +85,7 @@ def test_memory_projection_matches_oracle():
 
 def test_memory_projection_bf16_large_ragged_rows():
     """A bf16 projection of 37 x 451 = 16,687 rows (not a multiple of the 128-row tiles) into
-    N = 2 groups x 2d = 1024 columns: enough workgroups for the LDS-staged token GEMM. Each
+    N = 2 groups x 2d = 1024 columns: enough workgroups (264) for the 256 x 256 token GEMM. Each
     entry is a bf16 rounding of an fp32-accumulated product, so the relative L2 error against
     the float64 oracle is bounded by half a bf16 ulp (2^-9) plus accumulation error."""
     cfg = cfg_small(dtype="bf16", d=256, n_heads=4, head_dim=64, ffn=512, n_groups=2)
