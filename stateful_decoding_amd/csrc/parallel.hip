@@ -23,6 +23,17 @@
 
 namespace rlt {
 
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row swaps (VALU, no LDS):
+// each swap leaves the lane's own value and its partner's in the two results, in either order
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // ---- GEMM over all rows: C[R][N] = A[R][K] W[K][N], register tiles ------------------------------
 // Workgroup = 4 waves in a 2 x 2 grid, each wave FM x FN fragments of 16 x 16, so a block covers
 // (32 FM) x (32 FN). A and W are read in MFMA fragment order; the next k-step's fragments are
@@ -757,8 +768,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][j][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_xor16_32(mx);
       // The weights are exp2(c2 s - mref) against a reference mref that only moves when some
       // query's block maximum exceeds it by more than 8 (log2 units), so a weight is at most
       // 2^8 and the accumulators are rescaled only on those blocks; the result is the same
