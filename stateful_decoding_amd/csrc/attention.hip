@@ -72,8 +72,7 @@ __device__ __forceinline__ void step_batch(const u32x4* kr, const u32x4* vr, int
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < G::VEC; ++i) dot += qv[i] * kf[i];
-#pragma unroll
-    for (int o = G::LPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+    dot = group_sum<G::LPR>(dot);
     const bool ok = base + u * RPB + first < n;
     sc[u] = ok ? dot : -INFINITY;
     mb = fmaxf(mb, sc[u]);

@@ -128,6 +128,26 @@ __device__ __forceinline__ void mfma_16x16x32(f32x4& acc, const Frag<float>& a, 
 }
 
 // ---- reductions ----------------------------------------------------------------------------
+// Lane move within rows of 16 lanes (DPP; ctrl: 0x00-0xff quad permutation, 0x140 mirror of the
+// row, 0x141 mirror of each half row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// Sum over aligned groups of G lanes (G a power of two up to 64): DPP moves inside rows of 16,
+// cross-row shuffles beyond. Each step adds a partner that holds the other half-group's sum,
+// so every lane of a group ends with the same value.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_move<0xb1>(v);   // quad permutation [1, 0, 3, 2]
+  if constexpr (G >= 4) v += dpp_move<0x4e>(v);   // quad permutation [2, 3, 0, 1]
+  if constexpr (G >= 8) v += dpp_move<0x141>(v);  // lane i <-> 7 - i within 8
+  if constexpr (G >= 16) v += dpp_move<0x140>(v); // lane i <-> 15 - i within 16
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
