@@ -32,18 +32,22 @@ FP32_PEAK = 157.3e12
 METRIC = "RLT decoder tokens/sec (B seqs x T) on 1 MI355X; % of per-step roofline"
 
 
-def step_roofline_seconds(cfg, B: int, T: int) -> float:
+def step_roofline_seconds(cfg, B: int, T: int, memory_once: bool = False) -> float:
     """Ideal time of one run: memory projection + T steps, each at max(bytes / HBM peak,
     flops / MFMA peak) with the algorithmic bytes of every step (weights once, the window and
-    the memory prefix of every layer once, s read and written)."""
+    the memory prefix of every layer once, s read and written). With ``memory_once`` (only
+    meaningful for one memory shared by all layers) the shared prefix counts once per step
+    instead of once per layer: the floor if the layers' re-reads all hit a cache."""
     d, L, F, W, G = cfg.d, cfg.n_layers, cfg.ffn, cfg.window, cfg.n_groups
     es = 2 if cfg.dtype == "bf16" else 4
     peak = BF16_PEAK if cfg.dtype == "bf16" else FP32_PEAK
     p_step = 2 * d * d + L * (6 * d * d + 3 * d * F)
+    mem_reads = 1 if memory_once else L
     total = 0.0
     for t in range(1, T + 1):
         win = min(t, W)
-        by = es * (p_step + B * L * win * 2 * d + B * L * t * 2 * d) + B * d * (es + 8)
+        by = (es * (p_step + B * L * win * 2 * d + B * mem_reads * t * 2 * d)
+              + B * d * (es + 8))
         fl = 2 * B * p_step + 4 * B * L * d * (win + t)
         total += max(by / HBM_PEAK, fl / peak)
     mp_bytes = es * (B * T * d + G * B * T * 2 * d + 2 * G * d * d)
@@ -256,6 +260,11 @@ def main():
                           "peaks": "HBM 8.0 TB/s, bf16 MFMA 2.5 PFLOP/s"},
         "memproj_ms": round(prof["memproj"]["total_ms"] / args.steps, 2),
     }
+    if cfg.n_groups == 1 and cfg.n_layers > 1:
+        # one memory shared by every layer: also against the floor where it is read once a step
+        once = step_roofline_seconds(cfg, B, T, memory_once=True)
+        out["step_roofline"]["ideal_memory_once_s"] = round(once, 4)
+        out["step_roofline"]["frac_memory_once"] = round(once / (secs / args.steps), 4)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, params, args.cpu_seconds)

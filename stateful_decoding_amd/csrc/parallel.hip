@@ -196,8 +196,8 @@ struct ATok {
 template <class EP, bool TOK = false>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
                                                          const bf16* __restrict__ A, int R,
-                                                         const bf16* __restrict__ Wt, EP ep,
-                                                         ATok tok) {
+                                                         const bf16* __restrict__ Wt, int wks,
+                                                         EP ep, ATok tok) {
   constexpr int FM = 8, FN = 4, PER = 4;  // fragments each wave copies per k-step
   __shared__ __attribute__((aligned(16))) u32x4 sm[kBigStages][32][kWave];
   const int tiles_n = N / 256, nb = (int)gridDim.x;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(int N, int ksteps,
     const int f = wave + 8 * u;
     gstep[u] = 512;
     if (f >= 16) {
-      gp[u] = Wt + ((((int64_t)(tn * 16 + f - 16) * ksteps) << 6) + lane) * 8;
+      gp[u] = Wt + ((((int64_t)(tn * 16 + f - 16) * wks) << 6) + lane) * 8;
     } else if (TOK) {
       const int r = min(tm * 256 + f * 16 + (lane & 15), R - 1);
       const int b = r / tok.a_n, i = r - b * tok.a_n;
@@ -348,15 +348,43 @@ struct PGate : PerElement<PGate>, RowScale {
     const float ev = (float)e[((int64_t)bs * e_seq + i) * d + col];
     h[(int64_t)row * d + col] = sigmoidf_(v + b[col]) * ev;
   }
-  __device__ void op4(int row, int col, f32x4 v) const {
+  __device__ uint2 e4(int row, int col) const {
+    if (row >= R) return uint2{0u, 0u};
     const int bs = row / n, i = row - bs * n;
-    const uint2 eraw = *reinterpret_cast<const uint2*>(e + ((int64_t)bs * e_seq + i) * d + col);
+    return *reinterpret_cast<const uint2*>(e + ((int64_t)bs * e_seq + i) * d + col);
+  }
+  __device__ void store4(int row, int col, f32x4 v, uint2 eraw, f32x4 bias) const {
     const float ev[4] = {__uint_as_float(eraw.x << 16), __uint_as_float(eraw.x & 0xffff0000u),
                          __uint_as_float(eraw.y << 16), __uint_as_float(eraw.y & 0xffff0000u)};
     f32x4 r;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = sigmoidf_(v[k] + b[col + k]) * ev[k];
+    for (int k = 0; k < 4; ++k) r[k] = sigmoidf_(v[k] + bias[k]) * ev[k];
     *reinterpret_cast<f32x4*>(h + (int64_t)row * d + col) = r;
+  }
+  __device__ void op4(int row, int col, f32x4 v) const {
+    store4(row, col, v, e4(row, col), *reinterpret_cast<const f32x4*>(b + col));
+  }
+  // after k_gemm_big: every e_t value of the wave's tile is read before the first store (a
+  // wait for a load also waits for the stores issued before it)
+  template <int FM, int FN>
+  __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int) const {
+    f32x4 bias[FN];
+    uint2 ev[FM][FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) bias[fn] = *reinterpret_cast<const f32x4*>(b + col0 + 16 * fn);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) ev[fm][fn] = e4(row0 + 16 * fm, col0 + 16 * fn);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = row0 + 16 * fm;
+      if (row >= R) continue;
+      const float sc = scale(row);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        store4(row, col0 + 16 * fn, acc[fm][fn] * sc, ev[fm][fn], bias[fn]);
+    }
   }
 };
 
@@ -411,41 +439,71 @@ struct PResidual : PerElement<PResidual>, RowScale {
   bf16* hg = nullptr;
   const float* gnext = nullptr;
   float* ssq_out = nullptr;
+  // The old h of row group q + 1 (two fragment rows) is read before row group q is written: a
+  // wait for a load also waits for every store issued before it (one counter for both), so
+  // reading each fragment of h right after the previous one's stores would cost a memory round
+  // trip per fragment; this way the epilogue costs about one.
   template <int FM, int FN>
   __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int lane) const {
-    if (!hg) {
-      PerElement<PResidual>::tile_t<FM, FN>(acc, row0, col0, lane);
-      return;
-    }
+    static_assert(FM % 2 == 0, "row groups of two fragment rows");
+    constexpr int GR = 2, NG = FM / GR;
     f32x4 g[FN];
+    if (hg) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      g[fn] = *reinterpret_cast<const f32x4*>(gnext + col0 + 16 * fn);
+      for (int fn = 0; fn < FN; ++fn)
+        g[fn] = *reinterpret_cast<const f32x4*>(gnext + col0 + 16 * fn);
+    }
     const int slot = (col0 - 4 * (lane >> 4)) / 64;
+    f32x4 cur[GR][FN], nxt[GR][FN];
+    auto load = [&](int q, f32x4(&v)[GR][FN]) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int row = row0 + 16 * fm;
-      float ss = 0.f;
-      if (row < R) {
+      for (int i = 0; i < GR; ++i) {
+        const int row = row0 + 16 * (q * GR + i);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = col0 + 16 * fn;
-          f32x4* p = reinterpret_cast<f32x4*>(h + (int64_t)row * d + col);
-          const f32x4 r = *p + acc[fm][fn];
-          *p = r;
-          if (out) {
-            const int b = row / n, i = row - b * n;
-            *reinterpret_cast<f32x4*>(out + (int64_t)b * out_seq + (int64_t)i * d + col) = r;
+        for (int fn = 0; fn < FN; ++fn)
+          v[i][fn] = row < R ? *reinterpret_cast<const f32x4*>(h + (int64_t)row * d + col0 + 16 * fn)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    load(0, cur);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      if (q + 1 < NG) load(q + 1, nxt);
+#pragma unroll
+      for (int i = 0; i < GR; ++i) {
+        const int fm = q * GR + i, row = row0 + 16 * fm;
+        float ss = 0.f;
+        if (row < R) {
+          const float sc = scale(row);
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = col0 + 16 * fn;
+            const f32x4 r = cur[i][fn] + acc[fm][fn] * sc;
+            *reinterpret_cast<f32x4*>(h + (int64_t)row * d + col) = r;
+            if (out) {
+              const int b = row / n, t = row - b * n;
+              *reinterpret_cast<f32x4*>(out + (int64_t)b * out_seq + (int64_t)t * d + col) = r;
+            }
+            if (hg) {
+              *reinterpret_cast<uint2*>(hg + frag_off(row, col, d / 32)) = pack_bf16x4(r * g[fn]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ss += r[e] * r[e];
+            }
           }
-          *reinterpret_cast<uint2*>(hg + frag_off(row, col, d / 32)) = pack_bf16x4(r * g[fn]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ss += r[i] * r[i];
+        }
+        if (hg) {
+          // the four lanes holding this row (lane % 16 equal) cover the wave's 64 columns
+          ss += __shfl_xor(ss, 16, kWave);
+          ss += __shfl_xor(ss, 32, kWave);
+          if (row < R && lane < 16) ssq_out[(int64_t)row * (d / 64) + slot] = ss;
         }
       }
-      // the four lanes holding this row (lane % 16 equal) cover the wave's 64 columns
-      ss += __shfl_xor(ss, 16, kWave);
-      ss += __shfl_xor(ss, 32, kWave);
-      if (row < R && lane < 16) ssq_out[(int64_t)row * (d / 64) + slot] = ss;
+      if (q + 1 < NG) {
+#pragma unroll
+        for (int i = 0; i < GR; ++i)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) cur[i][fn] = nxt[i][fn];
+      }
     }
   }
   __device__ void op(int row, int col, float v) const {
@@ -618,9 +676,22 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
 }
 
 // ---- causal flash attention, all queries of a (sequence, head) block at once ----------------------
+// Transposed values keep each group of 32 keys in the order the P V product takes them: position
+// 8 g + 4 u + i holds key 16 u + 4 g + i (g, i < 4; u < 2), so the 8 keys a lane multiplies in one
+// k-step (4 g + [0, 4) of the first 16-key tile, then of the second) are adjacent.
+__device__ __forceinline__ int vt_key(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 // A workgroup takes QB = 64 QT consecutive queries of one (sequence, head); wave w owns the QT
-// 16-query tiles starting at q0 + 16 QT w. Key blocks of 64 are staged in LDS (K as rows, V
-// transposed) and each wave computes S^T = K Q^T with MFMA, every K fragment read from LDS
+// 16-query tiles starting at q0 + 16 QT w. Key blocks of 64 are staged in LDS: K in the MFMA's
+// fragment order (each 1 KB piece one operand fragment with lane l's 16 bytes at 16 l, so every K
+// fragment read is a linear 16-byte read per lane, which the LDS serves at full rate; a row-padded
+// tile read 16 rows x 16 bytes at a time runs at half of it), V transposed in padded rows. Each
+// wave computes S^T = K Q^T with MFMA, every K fragment read from LDS
 // serving its QT query tiles, so a lane holds the scores of one query (lane % 16 of a tile)
 // against keys 4 (lane / 16) + i of each 16-key tile. The softmax is online in fp32, against a
 // per-query reference maximum that moves only when a block's scores exceed it by more than 8
@@ -629,9 +700,10 @@ __global__ __launch_bounds__(kThreads) void k_norm_rows(const float* __restrict_
 // keys 4 g + [0, 4) of the first 16-key tile, then of the second, g = lane / 16), and V^T is
 // read from LDS in that same order, so P never moves between lanes.
 // Masks: the key j of query t is used when j <= t, and for the window also j > t - W.
-// VTG: the values come transposed from global memory (Vt = [B H][HD][vt_len], keys beyond n
-// zero up to vt_len, a multiple of 64), so staging them into LDS is a plain 16-byte copy;
-// otherwise V is [B H][keys][HD] and is transposed on its way into LDS with 2-byte stores.
+// VTG: the values come transposed from global memory (Vt = [B H][HD][vt_len], keys permuted
+// within groups of 32 as vt_key gives, zero from key n up to vt_len, a multiple of 64), so staging
+// them into LDS is a plain 16-byte copy; otherwise V is [B H][keys][HD] and is transposed (and
+// permuted) on its way into LDS with 2-byte stores.
 template <int HD, int QT, bool VTG>
 __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ Q,
                                                     const bf16* __restrict__ K,
@@ -641,12 +713,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
                                                     const bf16* __restrict__ Vt, int vt_len,
                                                     bf16* __restrict__ o) {
   constexpr int KB = 64, QB = 64 * QT, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
-  // two LDS buffers: block k + 1 is staged while block k is multiplied, one barrier per block
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][KB][HD + 8];
+  constexpr int FK = NT * KS;  // K fragments, (16-key tile j, 32-dim step s) at j KS + s
+  // two LDS buffers: block k + 1 is staged while block k is multiplied, one barrier per block.
+  // K fragment (j, s), lane l: key 16 j + l % 16, dims 32 s + 8 (l / 16). V^T stays in padded
+  // rows [HD][KB + 8] (V^T in fragment order measured slower: 35.6-36.2 against 27.8-28.1 ms of
+  // memory attention per pass), read 16 bytes at a time at the lane's permuted key positions.
+  __shared__ __attribute__((aligned(16))) u32x4 ks[2][FK][kWave];
   __shared__ __attribute__((aligned(16))) bf16 vt[2][HD][KB + 8];
-  // heavy blocks (late queries) first
-  const int qb = qblocks - 1 - (int)(blockIdx.x % qblocks);
-  const int bh = blockIdx.x / qblocks;
+  // Workgroups are numbered XCD-major (the i-th one dispatched to an XCD takes the i-th of that
+  // XCD's contiguous share), so the query blocks of one (sequence, head) run on one XCD and read
+  // its keys and values through that XCD's L2; within a (sequence, head), heavy blocks (late
+  // queries) first.
+  int blk = (int)blockIdx.x;
+  const int nblocks = (int)gridDim.x;
+  if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
+  const int qb = qblocks - 1 - blk % qblocks;
+  const int bh = blk / qblocks;
   const int b = bh / H, hh = bh - b * H;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4;
   const int q0 = qb * QB, qw = q0 + wave * 16 * QT;  // the wave's first query
@@ -677,24 +759,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
 
   const int kend = min(n, q0 + QB);                      // keys this block can use
   const int kbeg = W > 0 ? max(0, q0 - W + 1) / KB * KB : 0;
-  // staging: thread -> CH chunks of (key, 8 dims), consecutive threads on consecutive keys, so
-  // a wave's transposed V writes fill whole LDS rows without bank conflicts; the next block's
-  // chunks are loaded into registers while the current block is multiplied
+  // staging: thread -> CH 16-byte slots c = tid + 256 u; for K, slot c is lane c % 64 of fragment
+  // c / 64 (linear LDS stores); the transposed values come as (dim c / 8, positions 8 (c % 8) ..),
+  // plain values as (key c % 64, dims 8 (c / 64) ..), transposed on the way into LDS. The next
+  // block's slots are loaded into registers while the current block is multiplied.
   constexpr int CH = KB * HD / 8 / kThreads;
-  static_assert(CH >= 1 && KB * HD / 8 == CH * kThreads, "staging split");
+  static_assert(CH >= 1 && KB * HD / 8 == CH * kThreads && FK * kWave == CH * kThreads, "staging");
   u32x4 kr[CH], vr[CH];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int c = tid + u * kThreads;
+      const int c = tid + u * kThreads, f = c / kWave, l = c % kWave;
+      const int j = f / KS, sd = f - j * KS;
       // keys past kend are clamped to the last usable one: their scores are masked to -inf
       // and their weights are 0, so only finiteness matters
-      const int key = min(k0 + c % KB, kend - 1), dd = (c / KB) * 8;
-      kr[u] = ld16(Kb + (int64_t)key * HD + dd);
-      if (VTG)  // dim c / (KB / 8), keys k0 + 8 (c % (KB / 8)) .. + 7, all < vt_len
+      const int key = min(k0 + 16 * j + (l & 15), kend - 1);
+      kr[u] = ld16(Kb + (int64_t)key * HD + 32 * sd + 8 * (l >> 4));
+      if constexpr (VTG) {  // dim c / 8, positions k0 + 8 (c % 8) .. + 7, all < vt_len
         vr[u] = ld16(VTb + (int64_t)(c / (KB / 8)) * vt_len + k0 + 8 * (c % (KB / 8)));
-      else
-        vr[u] = ld16(Vb + (int64_t)key * HD + dd);
+      } else {
+        vr[u] = ld16(Vb + (int64_t)min(k0 + c % KB, kend - 1) * HD + (c / KB) * 8);
+      }
     }
   };
   // scores go through exp2: fold log2(e) into the scale
@@ -705,14 +790,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int c = tid + u * kThreads;
-      const int kk = c % KB, dd = (c / KB) * 8;
-      *reinterpret_cast<u32x4*>(&ks[buf][kk][dd]) = kr[u];
-      if (VTG) {
+      ks[buf][c / kWave][c % kWave] = kr[u];
+      if constexpr (VTG) {
         *reinterpret_cast<u32x4*>(&vt[buf][c / (KB / 8)][8 * (c % (KB / 8))]) = vr[u];
       } else {
+        const int kk = c % KB, dd = (c / KB) * 8;
         const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[u]);
+        const int kp = vt_pos(kk);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vt[buf][dd + i][kk] = v8[i];
+        for (int i = 0; i < 8; ++i) vt[buf][dd + i][kp] = v8[i];
       }
     }
     __syncthreads();
@@ -725,8 +811,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
       for (int t = 0; t < QT; ++t) st[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&ks[buf][16 * j + (lane & 15)][32 * s + 8 * g]));
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, ks[buf][j * KS + s][lane]);
 #pragma unroll
         for (int t = 0; t < QT; ++t)
           st[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][s].v, st[t][j], 0, 0, 0);
@@ -734,17 +819,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
     }
     // V^T fragments of this block, read now so that the LDS latency overlaps the softmax:
     // row 16 c + lane % 16 of V^T, the 8 keys of this lane's P order in k-step h (tile 2h keys
-    // 4g..4g+3, then tile 2h+1 keys 4g..4g+3)
+    // 4g..4g+3, then tile 2h+1 keys 4g..4g+3), adjacent in the permuted key order
     bf16x8 vf[VT][PK];
 #pragma unroll
     for (int c = 0; c < VT; ++c)
 #pragma unroll
-      for (int h = 0; h < PK; ++h) {
-        const bf16* vp = &vt[buf][16 * c + (lane & 15)][32 * h];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 + 4 * g);
-        vf[c][h] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      }
+      for (int h = 0; h < PK; ++h)
+        vf[c][h] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&vt[buf][16 * c + (lane & 15)][32 * h + 8 * g]));
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int qt0 = qw + 16 * t;  // first query of the tile
@@ -825,8 +907,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
 }
 
 // ---- values transposed for the prefix attention ----------------------------------------------------
-// vt[bh][dd][j] = v[bh][j][dd] for keys j < n, 0 for n <= j < vt_len (vt_len a multiple of 64). One
-// workgroup per (bh, 64-key tile): 64 x HD elements through LDS, 16-byte loads and stores.
+// vt[bh][dd][p] = v[bh][vt_key(p)][dd] for keys < n, 0 for n <= key < vt_len (vt_len a multiple of
+// 64; keys permuted within groups of 32 as the P V product takes them). One workgroup per (bh,
+// 64-key tile): 64 x HD elements through LDS, 16-byte loads and stores.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_transpose_v(const bf16* __restrict__ v,
                                                           int64_t bh_stride, int n, int vt_len,
@@ -847,7 +930,7 @@ __global__ __launch_bounds__(kThreads) void k_transpose_v(const bf16* __restrict
     const int dd = c / 8, j = 8 * (c % 8);
     bf16x8 o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = t[j + i][dd];
+    for (int i = 0; i < 8; ++i) o[i] = t[vt_key(j + i)][dd];
     st16(dst + (int64_t)dd * vt_len + j, __builtin_bit_cast(u32x4, o));
   }
 }
@@ -914,7 +997,7 @@ ParLayout par_layout(const Dims& D, int B, int64_t n) {
   p.v = take(R * d * 2);
   p.o = take(R16 * d * 2);
   p.act = take(R16 * D.F * 2);
-  p.vt = take((size_t)B * d * ((n + 63) / 64 * 64) * 2);  // values transposed, one group
+  p.vt = take((size_t)B * d * ((n + 63) / 64 * 64 + 64) * 2);  // values transposed, one group
   p.ssq = take(R * (d / 64 + 1) * 4);  // per-row partial sums of squares (64 columns each), 1/rms
   p.total = o;
   return p;
@@ -951,10 +1034,14 @@ template <class AL, class EP>
 static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const void* Wt,
                             const AL& al, const EP& ep, double out_bytes,
                             bool force_big = false) {
-  if constexpr (std::is_same<AL, PA>::value) {
+  constexpr bool kFrag = std::is_same<AL, PA>::value, kTok = std::is_same<AL, PTokens>::value;
+  if constexpr (kFrag || kTok) {
     // the 256 x 256 kernel when it has at least one workgroup per compute unit (always when
-    // force_big: epilogues that write the next norm's operand exist only in its layout)
-    if (N % 256 == 0 && wks == K / 32 &&
+    // force_big: epilogues that write the next norm's operand exist only in its layout);
+    // token rows (PTokens) are read by it directly when each row is exactly K wide
+    bool rows_ok = true;
+    if constexpr (kTok) rows_ok = al.d == K;
+    if (N % 256 == 0 && wks >= K / 32 && rows_ok &&
         (force_big || (int64_t)((R + 255) / 256) * (N / 256) >= 256)) {
       const int64_t blocks = (int64_t)((R + 255) / 256) * (N / 256);
       if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -962,9 +1049,16 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
       hipError_t e = c.arm(RLT_K_PAR_GEMM, 2.0 * ((double)R * K + (double)K * N) + out_bytes,
                            2.0 * R * N * K, x);
       if (e != hipSuccess) return e;
-      return launch(k_gemm_big<EP, false>, dim3((unsigned)blocks), dim3(kBigThreads), x, N,
-                    K / 32, al.a, R, static_cast<const bf16*>(Wt), ep, ATok{0, 1});
+      if constexpr (kTok)
+        return launch(k_gemm_big<EP, true>, dim3((unsigned)blocks), dim3(kBigThreads), x, N,
+                      K / 32, al.e, R, static_cast<const bf16*>(Wt), wks, ep,
+                      ATok{al.e_seq, al.n});
+      else
+        return launch(k_gemm_big<EP, false>, dim3((unsigned)blocks), dim3(kBigThreads), x, N,
+                      K / 32, al.a, R, static_cast<const bf16*>(Wt), wks, ep, ATok{0, 1});
     }
+  }
+  if constexpr (kFrag) {
     if (N % 128 == 0 && wks == K / 32) {
       const int64_t blocks = (int64_t)((R + 127) / 128) * (N / 128);
       if (K % 32 != 0 || blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -991,7 +1085,7 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
   constexpr int QT = 1;
   const int qblocks = (n + 64 * QT - 1) / (64 * QT);
   const int64_t blocks = (int64_t)B * H * qblocks;
-  const int vt_tiles = (n + 63) / 64;
+  const int vt_tiles = (n + 63) / 64 + 1;  // with the spare tile
   if (blocks > INT32_MAX || (int64_t)B * H * vt_tiles > INT32_MAX) return hipErrorInvalidValue;
   // keys per query summed over t = 0..n-1: min(t + 1, W) or t + 1
   double keys = 0;
@@ -1002,6 +1096,8 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
     keys = (double)n * (n + 1) / 2;
   }
   const double bhd = (double)B * H * HD;
+  // one spare (zero) tile per row: rows are then not a power-of-two multiple of 128 bytes apart,
+  // so the rows a block reads spread over the L2 channels
   const int vt_len = vt_tiles * 64;
   hipError_t e;
   if (vt && !vt_fresh) {  // values transposed first (timed as its own kind)
@@ -1106,7 +1202,7 @@ hipError_t launch_memproj_rows(const Dims& D, int B, const Packed& P, const MemB
   ep.R = (int)rows;
   return launch(k_gemm_big<PMemproj, true>, dim3((unsigned)blocks), dim3(kBigThreads), st, N,
                 D.d / 32, static_cast<const bf16*>(e), (int)rows,
-                static_cast<const bf16*>(P.wm_t), ep, ATok{e_seq, (int)n});
+                static_cast<const bf16*>(P.wm_t), D.d / 32, ep, ATok{e_seq, (int)n});
 }
 
 hipError_t launch_readout_rows(const Dims& D, int B, const HeadBufs& Hd, const float* s, void* a,
