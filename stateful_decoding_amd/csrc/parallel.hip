@@ -395,9 +395,11 @@ struct PHeads : PerElement<PHeads>, RowScale {
   bf16* k;
   bf16* v;
   int n, d, H, hd, R;
+  float qscale = 1.f;  // queries are stored times qscale (k_flash takes them in log2 units)
   __device__ void op(int row, int col, float x) const {
     const int b = row / n, i = row - b * n;
     bf16* dst = q;
+    if (col < d) x *= qscale;
     if (col >= d) {
       col -= d;
       dst = k;
@@ -413,6 +415,7 @@ struct PHeads : PerElement<PHeads>, RowScale {
   __device__ void op4(int row, int col, f32x4 x) const {
     const int b = row / n, i = row - b * n;
     bf16* dst = q;
+    if (col < d) x *= qscale;
     if (col >= d) {
       col -= d;
       dst = k;
@@ -693,9 +696,11 @@ __device__ __forceinline__ int vt_pos(int k) {
 // tile read 16 rows x 16 bytes at a time runs at half of it), V transposed in padded rows. Each
 // wave computes S^T = K Q^T with MFMA, every K fragment read from LDS
 // serving its QT query tiles, so a lane holds the scores of one query (lane % 16 of a tile)
-// against keys 4 (lane / 16) + i of each 16-key tile. The softmax is online in fp32, against a
-// per-query reference maximum that moves only when a block's scores exceed it by more than 8
-// in log2 units, and the weight sums are taken by the matrix cores (ones x P^T). For
+// against keys 4 (lane / 16) + i of each 16-key tile. The queries come multiplied by the softmax
+// scale and log2(e), so scores are in log2 units. The softmax is online in fp32, against a
+// per-query reference maximum that moves only when a block's scores exceed it by more than 8,
+// and the score product starts from minus that reference, so its results are the exponents
+// exp2 takes; the weight sums are taken by the matrix cores (ones x P^T). For
 // O^T = V^T P^T the MFMA's k index is taken in the order the lane already holds P (per 32 keys:
 // keys 4 g + [0, 4) of the first 16-key tile, then of the second, g = lane / 16), and V^T is
 // read from LDS in that same order, so P never moves between lanes.
@@ -709,9 +714,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
                                                     const bf16* __restrict__ K,
                                                     const bf16* __restrict__ V,
                                                     int64_t kv_bh_stride, int n, int H, int W,
-                                                    int qblocks, float scale,
-                                                    const bf16* __restrict__ Vt, int vt_len,
-                                                    bf16* __restrict__ o) {
+                                                    int qblocks, const bf16* __restrict__ Vt,
+                                                    int vt_len, bf16* __restrict__ o) {
   constexpr int KB = 64, QB = 64 * QT, KS = HD / 32, VT = HD / 16, NT = KB / 16, PK = KB / 32;
   constexpr int FK = NT * KS;  // K fragments, (16-key tile j, 32-dim step s) at j KS + s
   // two LDS buffers: block k + 1 is staged while block k is multiplied, one barrier per block.
@@ -742,6 +746,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
   f32x4 acc[QT][VT];
   float mref[QT];
   f32x4 lsum[QT];  // every entry: this lane's query's weight sum
+  f32x4 cinit[QT];  // every entry: -mb, the score product's initial value (mb below)
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     tq[t] = qw + 16 * t + (lane & 15);
@@ -752,6 +757,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
     for (int c = 0; c < VT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     mref[t] = -INFINITY;
     lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cinit[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8 ones;
 #pragma unroll
@@ -782,8 +788,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
       }
     }
   };
-  // scores go through exp2: fold log2(e) into the scale
-  const float c2 = scale * 1.4426950408889634f;
   if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg, buf = 0; k0 < kend; k0 += KB, buf ^= 1) {
     // buffer `buf` was last read two blocks ago, before the previous block's barrier
@@ -803,18 +807,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
     }
     __syncthreads();
     if (k0 + KB < kend) fetch(k0 + KB);
-    // S^T for the NT 16-key tiles of every query tile
+    // S^T for the NT 16-key tiles of every query tile, started at -mb: the queries carry the
+    // softmax scale times log2(e), so st = log2-unit score - mb, the exponent of the weight
     f32x4 st[QT][NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-#pragma unroll
-      for (int t = 0; t < QT; ++t) st[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, ks[buf][j * KS + s][lane]);
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          st[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][s].v, st[t][j], 0, 0, 0);
+          st[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][s].v,
+                                                             s == 0 ? cinit[t] : st[t][j], 0, 0, 0);
       }
     }
     // V^T fragments of this block, read now so that the LDS latency overlaps the softmax:
@@ -851,26 +855,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][j][i]);
       mx = max_xor16_32(mx);
-      // The weights are exp2(c2 s - mref) against a reference mref that only moves when some
-      // query's block maximum exceeds it by more than 8 (log2 units), so a weight is at most
-      // 2^8 and the accumulators are rescaled only on those blocks; the result is the same
-      // softmax (the reference cancels between numerator and denominator). A query with no
-      // key yet keeps mref = -inf and adds zero weights (exp2(-inf) = 0); every wave runs the
-      // same MFMAs, so no lane leaves the loop early.
-      const float mnew = mx * c2;
-      if (__ballot(mnew > mref[t] + 8.f) != 0) {
-        const float mr = fmaxf(mref[t], mnew);
+      // The weights are exp2(score - mref) (log2 units) against a reference mref that only moves
+      // when some query's block maximum exceeds it by more than 8, so a weight is at most 2^8 and
+      // the accumulators are rescaled only on those blocks; the result is the same softmax (the
+      // reference cancels between numerator and denominator). mb = mref, or 0 while a query has
+      // no key yet (mref = -inf: its weights are exp2(-inf) = 0, and its first usable block moves
+      // the reference). st holds score - mb; a block that moves a reference shifts st by the
+      // change. Every wave runs the same MFMAs, so no lane leaves the loop early.
+      const bool fresh = mref[t] == -INFINITY;
+      if (__ballot(fresh ? mx > -INFINITY : mx > 8.f) != 0) {
+        const float mb = fresh ? 0.f : mref[t];
+        const float mr = fmaxf(mref[t], mx + mb);
         const float alpha = mr == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mr);
 #pragma unroll
         for (int c = 0; c < VT; ++c) acc[t][c] *= alpha;
         lsum[t] *= alpha;
         mref[t] = mr;
+        const float mb_new = mr == -INFINITY ? 0.f : mr, shift = mb - mb_new;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) st[t][j] += shift;
+        cinit[t] = f32x4{-mb_new, -mb_new, -mb_new, -mb_new};
       }
-      const float mb = mref[t] == -INFINITY ? 0.f : mref[t];
       bf16x8 pb[PK];
 #pragma unroll
       for (int e = 0; e < 4 * NT; ++e)
-        pb[e / 8][e % 8] = (bf16)__builtin_amdgcn_exp2f(fmaf(st[t][e / 4][e % 4], c2, -mb));
+        pb[e / 8][e % 8] = (bf16)__builtin_amdgcn_exp2f(st[t][e / 4][e % 4]);
       // the row sums of the weights as they are multiplied (bf16), by the matrix cores: every
       // row of ones x P^T is the per-query sum
 #pragma unroll
@@ -1074,7 +1083,12 @@ static hipError_t gemm_rows(const ParCtx& c, int R, int N, int K, int wks, const
   return gemm_rows_t<2, 2>(c, R, N, K, wks, Wt, al, ep, out_bytes);
 }
 
-// W > 0: window attention (keys t-W+1..t of this layer); W = 0: memory prefix 0..t.
+// k_flash takes its queries times the softmax scale 1/sqrt(hd) and log2(e) (scores in log2
+// units); the projections that write them apply this factor before rounding to bf16.
+static float flash_qscale(int hd) { return 1.4426950408889634f / sqrtf((float)hd); }
+
+// W > 0: window attention (keys t-W+1..t of this layer); W = 0: memory prefix 0..t. q holds the
+// queries times flash_qscale(hd).
 template <int HD>
 static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const bf16* v,
                           int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
@@ -1113,11 +1127,9 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
     return e;
   if (vt)
     return launch(k_flash<HD, QT, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
-                  kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
-                  static_cast<const bf16*>(vt), vt_len, o);
+                  kv_bh_stride, n, H, W, qblocks, static_cast<const bf16*>(vt), vt_len, o);
   return launch(k_flash<HD, QT, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
-                kv_bh_stride, n, H, W, qblocks, 1.f / sqrtf((float)HD),
-                static_cast<const bf16*>(nullptr), 0, o);
+                kv_bh_stride, n, H, W, qblocks, static_cast<const bf16*>(nullptr), 0, o);
 }
 
 // vt (optional): workspace of B H hd ceil(n / 64) 64 elements for the values transposed first;
@@ -1251,6 +1263,7 @@ hipError_t launch_encode(const Dims& D, int B, int64_t n_, const Packed& P, cons
     if (norm_attn && (err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
     {
       PHeads ep{{}, {}, q, kk, vv, n, d, H, hd, R};
+      ep.qscale = flash_qscale(hd);
       if (!norm_attn && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
       if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
@@ -1333,6 +1346,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     if (norm_attn && (err = norm_rows(c, D, h, gam, R, a)) != hipSuccess) return err;
     {
       PHeads ep{{}, {}, q, kk, vv, n, d, H, hd, R};
+      ep.qscale = flash_qscale(hd);
       if (!norm_attn && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wq = static_cast<const bf16*>(P.wqkv_t) + (int64_t)l * 3 * d * d;
       if ((err = gemm_rows(c, R, 3 * d, d, d / 32, Wq, PA{a, d / 32, R}, ep, Rd * 6)) !=
@@ -1362,6 +1376,7 @@ hipError_t launch_parallel(const Dims& D, int B, const Packed& P, const StateBuf
     if (!fold && (err = norm_rows(c, D, h, gam + d, R, a)) != hipSuccess) return err;
     {
       PHeads ep{{}, {}, q, nullptr, nullptr, n, d, H, hd, R};
+      ep.qscale = flash_qscale(hd);
       if (fold && (err = row_scale(c, D, R, ssq, &ep)) != hipSuccess) return err;
       const bf16* Wc = static_cast<const bf16*>(P.wcq_t) + wdd;
       if ((err = gemm_rows(c, R, d, d, d / 32, Wc, PA{a, d / 32, R}, ep, Rd * 2)) !=
