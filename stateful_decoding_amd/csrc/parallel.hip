@@ -772,20 +772,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
   constexpr int CH = KB * HD / 8 / kThreads;
   static_assert(CH >= 1 && KB * HD / 8 == CH * kThreads && FK * kWave == CH * kThreads, "staging");
   u32x4 kr[CH], vr[CH];
+  // each thread's key row within a block, column offset and value offset (elements), added to
+  // block-uniform bases, so a block's loads cost one clamp and one multiply-add per K chunk
+  int krow[CH], kcol[CH], voff[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int c = tid + u * kThreads, f = c / kWave, l = c % kWave;
+    const int j = f / KS, sd = f - j * KS;
+    krow[u] = 16 * j + (l & 15);
+    kcol[u] = 32 * sd + 8 * (l >> 4);
+    if constexpr (VTG)  // dim c / 8, positions 8 (c % 8) .. + 7 of the block
+      voff[u] = (c / (KB / 8)) * vt_len + 8 * (c % (KB / 8));
+    else  // key c % 64, dims 8 (c / 64) .. + 7
+      voff[u] = (c % KB) * HD + (c / KB) * 8;
+  }
   auto fetch = [&](int k0) {
+    // keys past kend are clamped to the last usable one: their scores are masked to -inf and
+    // their weights are 0, so only finiteness matters; transposed-value positions stay below
+    // vt_len (zero past n)
+    const bf16* kblk = Kb + (int64_t)k0 * HD;
+    const int lim = kend - 1 - k0;
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int c = tid + u * kThreads, f = c / kWave, l = c % kWave;
-      const int j = f / KS, sd = f - j * KS;
-      // keys past kend are clamped to the last usable one: their scores are masked to -inf
-      // and their weights are 0, so only finiteness matters
-      const int key = min(k0 + 16 * j + (l & 15), kend - 1);
-      kr[u] = ld16(Kb + (int64_t)key * HD + 32 * sd + 8 * (l >> 4));
-      if constexpr (VTG) {  // dim c / 8, positions k0 + 8 (c % 8) .. + 7, all < vt_len
-        vr[u] = ld16(VTb + (int64_t)(c / (KB / 8)) * vt_len + k0 + 8 * (c % (KB / 8)));
-      } else {
-        vr[u] = ld16(Vb + (int64_t)min(k0 + c % KB, kend - 1) * HD + (c / KB) * 8);
-      }
+      kr[u] = ld16(kblk + (uint32_t)(min(krow[u], lim) * HD + kcol[u]));
+      if constexpr (VTG)
+        vr[u] = ld16(VTb + k0 + (uint32_t)voff[u]);
+      else
+        vr[u] = ld16(Vb + (int64_t)min(k0 + (tid + u * kThreads) % KB, kend - 1) * HD +
+                     ((tid + u * kThreads) / KB) * 8);
     }
   };
   if (kbeg < kend) fetch(kbeg);
