@@ -427,6 +427,53 @@ struct PHeads : PerElement<PHeads>, RowScale {
     const int hh = col / hd, dd = col - hh * hd;
     *reinterpret_cast<uint2*>(dst + (((int64_t)b * H + hh) * n + i) * hd + dd) = pack_bf16x4(x);
   }
+  // after k_gemm_big: the (sequence, token) split of each of the wave's FM rows and the
+  // (q / k / v, head, dim) split of each of its FN column groups are formed once, not per
+  // element (hd is a power of two)
+  template <int FM, int FN>
+  __device__ void tile_t(const f32x4 (&acc)[FM][FN], int row0, int col0, int) const {
+    const int hs = __builtin_ctz((unsigned)hd);
+    const int64_t head_sz = (int64_t)n << hs;  // elements of one (sequence, head) block
+    int sel[FN];  // 0 q, 1 k, 2 v
+    int64_t coff[FN];
+    float cs[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      int col = col0 + 16 * fn;
+      sel[fn] = 0;
+      cs[fn] = qscale;
+      if (col >= d) {
+        col -= d;
+        sel[fn] = 1;
+        cs[fn] = 1.f;
+        if (col >= d) {
+          col -= d;
+          sel[fn] = 2;
+        }
+      }
+      coff[fn] = (int64_t)(col >> hs) * head_sz + (col & (hd - 1));
+    }
+    int b = row0 / n, i = row0 - b * n;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm > 0) {  // the next fragment row is 16 rows further
+        i += 16;
+        if (i >= n) {
+          b += i / n;
+          i -= (i / n) * n;
+        }
+      }
+      const int row = row0 + 16 * fm;
+      if (row >= R) continue;
+      const float sc = scale(row);
+      const int64_t roff = (int64_t)b * H * head_sz + ((int64_t)i << hs);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        bf16* dst = sel[fn] == 0 ? q : sel[fn] == 1 ? k : v;
+        *reinterpret_cast<uint2*>(dst + roff + coff[fn]) = pack_bf16x4(acc[fm][fn] * (sc * cs[fn]));
+      }
+    }
+  }
 };
 
 // h += v (fp32, in place); at the last layer also s rows to out (row (b, i) at
@@ -747,6 +794,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
   float mref[QT];
   f32x4 lsum[QT];  // every entry: this lane's query's weight sum
   f32x4 cinit[QT];  // every entry: -mb, the score product's initial value (mb below)
+  float thr[QT];    // a block whose maximum exceeds this moves the reference (-inf until set)
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     tq[t] = qw + 16 * t + (lane & 15);
@@ -758,6 +806,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
     mref[t] = -INFINITY;
     lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     cinit[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    thr[t] = -INFINITY;
   }
   bf16x8 ones;
 #pragma unroll
@@ -868,17 +917,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][j][i]);
-      mx = max_xor16_32(mx);
       // The weights are exp2(score - mref) (log2 units) against a reference mref that only moves
       // when some query's block maximum exceeds it by more than 8, so a weight is at most 2^8 and
       // the accumulators are rescaled only on those blocks; the result is the same softmax (the
       // reference cancels between numerator and denominator). mb = mref, or 0 while a query has
       // no key yet (mref = -inf: its weights are exp2(-inf) = 0, and its first usable block moves
       // the reference). st holds score - mb; a block that moves a reference shifts st by the
-      // change. Every wave runs the same MFMAs, so no lane leaves the loop early.
-      const bool fresh = mref[t] == -INFINITY;
-      if (__ballot(fresh ? mx > -INFINITY : mx > 8.f) != 0) {
-        const float mb = fresh ? 0.f : mref[t];
+      // change. The four lanes of a query (lane % 16 equal) share its reference: the test uses
+      // each lane's own keys, and a block that moves some reference first takes each query's
+      // maximum over its four lanes. Every wave runs the same MFMAs, so no lane leaves the loop
+      // early.
+      if (__ballot(mx > thr[t]) != 0) {
+        mx = max_xor16_32(mx);
+        const float mb = mref[t] == -INFINITY ? 0.f : mref[t];
         const float mr = fmaxf(mref[t], mx + mb);
         const float alpha = mr == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mr);
 #pragma unroll
@@ -889,6 +940,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_flash(const bf16* __restrict__ 
 #pragma unroll
         for (int j = 0; j < NT; ++j) st[t][j] += shift;
         cinit[t] = f32x4{-mb_new, -mb_new, -mb_new, -mb_new};
+        thr[t] = mr == -INFINITY ? -INFINITY : 8.f;
       }
       bf16x8 pb[PK];
 #pragma unroll
