@@ -315,9 +315,9 @@ def bench_parallel(args, cfg, params, model, state, mem, e, traj, stream):
     mfma = dom["flops"] / BF16_PEAK > dom["bytes"] / HBM_PEAK
     rate = (dom["flops"] if mfma else dom["bytes"]) / (dom["total_ms"] / 1e3)
     peak = BF16_PEAK if mfma else HBM_PEAK
-    kern = {"par_gemm": "k_gemm_rows (all projections)", "par_cross_attn": "k_flash (memory prefix)",
-            "par_self_attn": "k_flash (window)", "par_other": "k_norm_rows / hand-off",
-            "memproj": "k_gemm_tokens (memory projection)"}[dom_name]
+    kern = {"par_gemm": "k_gemm_big (all projections)", "par_cross_attn": "k_flash (memory prefix)",
+            "par_self_attn": "k_flash (window)", "par_other": "k_norm_rows, k_row_rinv / hand-off",
+            "memproj": "k_gemm_big (memory projection)"}[dom_name]
     out = {
         "metric": "RLT token-parallel decoder pass at alpha = 0, tokens/sec (B seqs x T) on 1 "
                   "MI355X; % of the pass roofline",
