@@ -1159,10 +1159,14 @@ template <int HD>
 static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const bf16* v,
                           int64_t kv_bh_stride, int B, int n, int H, int W, bf16* o,
                           bf16* vt, bool vt_fresh) {
-  // one 16-query tile per wave: two (each K / V fragment read from LDS serving both) measured
-  // no faster at hd = 64 (41.6 against 41.3 ms of memory attention per pass) with half the
-  // resident waves, and do not fit in 256 registers at hd = 128
-  constexpr int QT = 1;
+  // 16-query tiles per wave: with the transposed values (memory prefix, W = 0) two at hd = 64,
+  // each K / V fragment read from LDS serving both (22.8-22.9 against 25.9-26.0 ms of memory
+  // attention per pass at 200 registers and half the resident waves; the VALU work per key
+  // block, its staging and addressing, is shared by twice the queries); one for the window,
+  // whose 128-query blocks would cover 1.5x the keys they use (3.2 against 2.6 ms), and at
+  // hd = 128, where two do not fit in 256 registers
+  constexpr int QTV = HD == 64 ? 2 : 1;
+  const int QT = vt ? QTV : 1;
   const int qblocks = (n + 64 * QT - 1) / (64 * QT);
   const int64_t blocks = (int64_t)B * H * qblocks;
   const int vt_tiles = (n + 63) / 64 + 1;  // with the spare tile
@@ -1192,9 +1196,9 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
                  x)) != hipSuccess)
     return e;
   if (vt)
-    return launch(k_flash<HD, QT, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+    return launch(k_flash<HD, QTV, true>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
                   kv_bh_stride, n, H, W, qblocks, static_cast<const bf16*>(vt), vt_len, o);
-  return launch(k_flash<HD, QT, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
+  return launch(k_flash<HD, 1, false>, dim3((unsigned)blocks), dim3(kThreads), x, q, k, v,
                 kv_bh_stride, n, H, W, qblocks, static_cast<const bf16*>(nullptr), 0, o);
 }
 
