@@ -1162,7 +1162,8 @@ static hipError_t flash_t(const ParCtx& c, const bf16* q, const bf16* k, const b
   // 16-query tiles per wave: with the transposed values (memory prefix, W = 0) two at hd = 64,
   // each K / V fragment read from LDS serving both (22.8-22.9 against 25.9-26.0 ms of memory
   // attention per pass at 200 registers and half the resident waves; the VALU work per key
-  // block, its staging and addressing, is shared by twice the queries); one for the window,
+  // block, its staging and addressing, is shared by twice the queries; four take 423 registers,
+  // one wave per SIMD: 46.3-46.8 ms); one for the window,
   // whose 128-query blocks would cover 1.5x the keys they use (3.2 against 2.6 ms), and at
   // hd = 128, where two do not fit in 256 registers
   constexpr int QTV = HD == 64 ? 2 : 1;
