@@ -24,7 +24,7 @@ namespace rlt {
 // Rows per lane slot loaded per batch, and the largest grid of an attention launch (0: one
 // workgroup per item).
 #ifndef RLT_ATTN_U
-#define RLT_ATTN_U 4
+#define RLT_ATTN_U 6
 #endif
 #ifndef RLT_ATTN_CAP
 #define RLT_ATTN_CAP 0
@@ -152,8 +152,8 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
     for (int u = 0; u < U; ++u) {
       const int row = base + u * RPB + first;
       const bool ok = row < n;
-      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
-      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      kr[u] = ok ? ld16_stream(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16_stream(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
     }
     step_batch<T, HD, U>(kr, vr, base, RPB, first, n, qv, m, l, acc);
   }

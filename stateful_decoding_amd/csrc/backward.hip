@@ -515,8 +515,8 @@ __device__ __forceinline__ void xattn_back_body(
     for (int u = 0; u < U; ++u) {
       const int row = base + u * RPB + first;
       const bool ok = row < ntok;
-      kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
-      vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      kr[u] = ok ? ld16_stream(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      vr[u] = ok ? ld16_stream(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
     }
     float sc[U], dp[U];
     float mb = S.m;
