@@ -70,7 +70,7 @@ def traffic_record(workload: str):
     rec = dict(line.split(": ", 1) for line in m.group(1).strip().splitlines())
     csrc = os.path.join(ROOT, "stateful_decoding_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("attention.hip", "internal.h"):
+    for name in ("attention.hip", "internal.h", "common.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     if rec.get("workload") != workload or rec.get("source_sha256_16") != h.hexdigest()[:16]:
