@@ -107,7 +107,7 @@ __device__ __forceinline__ void step_batch(const u32x4* kr, const u32x4* vr, int
 // sum 0) for k_attend_merge.
 // qssq != NULL: q[b] is unnormalised and is scaled by 1/sqrt(sum(qssq[b]) / d + eps), the
 // 1/rms of the residual stream whose 32-column sums of squares qssq[b] holds.
-template <typename T, int HD, int NW, int U>
+template <typename T, int HD, int NW, int U, bool NTL = true>
 __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __restrict__ K,
                                        const T* __restrict__ V, int64_t bh_stride,
                                        const int64_t* __restrict__ pos, int64_t t_uniform,
@@ -152,8 +152,13 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const T* __r
     for (int u = 0; u < U; ++u) {
       const int row = base + u * RPB + first;
       const bool ok = row < n;
-      kr[u] = ok ? ld16_stream(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
-      vr[u] = ok ? ld16_stream(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      if constexpr (NTL) {
+        kr[u] = ok ? ld16_stream(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+        vr[u] = ok ? ld16_stream(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      } else {
+        kr[u] = ok ? ld16(Kb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+        vr[u] = ok ? ld16(Vb + (int64_t)row * HD) : u32x4{0, 0, 0, 0};
+      }
     }
     step_batch<T, HD, U>(kr, vr, base, RPB, first, n, qv, m, l, acc);
   }
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
 // launch (LaunchClock).
 // Workgroup g takes the items g, g + gridDim.x, ... of the items = sequences x heads x parts
 // (one each unless the launch caps its grid).
-template <typename T, int HD, int NW, int U>
+template <typename T, int HD, int NW, int U, bool NTL>
 __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T* V,
                                              int64_t bh_stride, const int64_t* pos,
                                              int64_t t_uniform, int window, int H, float scale,
@@ -221,8 +226,8 @@ __device__ __forceinline__ void attend_timed(const float* q, const T* K, const T
   const LaunchClock lc{clk};
   lc.start();
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    attend<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts, part,
-                         qssq, eps, item);
+    attend<T, HD, NW, U, NTL>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
+                              part, qssq, eps, item);
     if (item + (int)gridDim.x < items) __syncthreads();  // LDS is reused by the next item
   }
   lc.stop();
@@ -232,16 +237,16 @@ __global__ __launch_bounds__(NW * kWave) void k_attend_window(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
     int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
     const float* qssq, float eps, int items, unsigned long long* clk) {
-  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, qssq, eps, items, clk);
+  attend_timed<T, HD, NW, U, true>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out,
+                                   parts, part, qssq, eps, items, clk);
 }
-template <typename T, int HD, int NW, int U>
+template <typename T, int HD, int NW, int U, bool NTL>
 __global__ __launch_bounds__(NW * kWave) void k_attend_memory(
     const float* q, const T* K, const T* V, int64_t bh_stride, const int64_t* pos,
     int64_t t_uniform, int window, int H, float scale, T* out, int parts, float* part,
     const float* qssq, float eps, int items, unsigned long long* clk) {
-  attend_timed<T, HD, NW, U>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out, parts,
-                             part, qssq, eps, items, clk);
+  attend_timed<T, HD, NW, U, NTL>(q, K, V, bh_stride, pos, t_uniform, window, H, scale, out,
+                                  parts, part, qssq, eps, items, clk);
 }
 
 template <typename T>
@@ -256,7 +261,7 @@ template <typename T, int HD, bool MEMORY>
 static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64_t bh_stride,
                            const int64_t* pos, int64_t t_uniform, int window, int H, T* out,
                            int parts, float* part, const float* qssq, float eps,
-                           const Exec& st) {
+                           const Exec& st, bool stream = true) {
   const float scale = 1.f / sqrtf((float)HD);
   const int64_t items = (int64_t)BH * parts;
   if (parts < 1 || parts > kMaxSplits || items > INT32_MAX) return hipErrorInvalidValue;
@@ -264,7 +269,9 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
   const int nw = items >= 1024 ? 4 : items >= 512 ? 8 : 16;
   hipError_t e = hipSuccess;
 #define RLT_ATTEND(NW)                                                                     \
-  e = launch(MEMORY ? k_attend_memory<T, HD, NW, kAttnU> : k_attend_window<T, HD, NW, kAttnU>, \
+  e = launch(!MEMORY ? k_attend_window<T, HD, NW, kAttnU>                                  \
+             : stream ? k_attend_memory<T, HD, NW, kAttnU, true>                           \
+                      : k_attend_memory<T, HD, NW, kAttnU, false>,                         \
              dim3((unsigned)blocks), dim3(NW * kWave), st, q, K, V, bh_stride, pos, t_uniform, \
              window, H, scale, out, parts, part, qssq, eps, (int)items, st.clk)
   if (nw == 4) RLT_ATTEND(4);
@@ -275,6 +282,18 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
   const int64_t threads = (int64_t)BH * HD;
   return launch(k_attend_merge<T, HD>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
                 dim3(kThreads), Exec(st.st), (const float*)part, parts, BH, H, out);
+}
+
+bool memory_streams(const Dims& D, int Bt, int64_t t_max) {
+  // Layers that share one memory (G = 1) read the same prefix once per layer and token: while
+  // the whole batch's prefix fits in half of the 256 MB memory-side cache, ordinary loads let
+  // the later layers find it there. Otherwise (a memory per layer, or a longer prefix) each
+  // row is read once before hundreds of megabytes of others, and non-temporal loads keep the
+  // projections' weights cached instead. Measured: the 50M-scale batch of 64 (128 MiB of
+  // memory at 1024 tokens) 281 -> 273 ms per run; the long-context batch of 16 (403 MB)
+  // 7.61 s with ordinary loads throughout against 7.38 s non-temporal.
+  const double bytes = (double)Bt * (double)(t_max + 1) * 2.0 * D.d * (double)D.es;
+  return !(D.G == 1 && bytes <= (double)(128 << 20));
 }
 
 int64_t attn_blocks(int64_t items) {
@@ -310,7 +329,8 @@ static hipError_t cross_t(const Dims& D, int B, int l, const StateBufs& S, const
   return attend_t<T, HD, true>(B * D.H, S.qc, elem<T>(M.k, grp), elem<T>(M.v, grp),
                                M.capacity * HD, S.pos, S.t_uniform, 0, D.H,
                                static_cast<T*>(S.o), cross_splits(D, B, S.t_max), S.part,
-                               q_unnormalised ? S.ssq : nullptr, D.eps, st);
+                               q_unnormalised ? S.ssq : nullptr, D.eps, st,
+                               memory_streams(D, M.Bt, S.t_max));
 }
 
 #define RLT_HD_DISPATCH(fn, ...)                                              \

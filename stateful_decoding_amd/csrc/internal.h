@@ -297,6 +297,9 @@ hipError_t attn_self(const Dims& D, int B, int l, const StateBufs& S, const Exec
 // q_unnormalised: S.qc holds (h1 * g1) W_cq and each row's 1/rms(h1) comes from S.ssq.
 hipError_t attn_cross(const Dims& D, int B, int l, const StateBufs& S, const MemBufs& M,
                       const Exec& st, bool q_unnormalised = false);
+// Whether the memory attention loads its rows with the non-temporal policy (false: ordinary
+// loads) for a memory of Bt sequences read up to position t_max.
+bool memory_streams(const Dims& D, int Bt, int64_t t_max);
 // Parts the memory attention of B rows splits each prefix into when the largest row position is
 // t_max (1: one workgroup per sequence and head, no merge launch). The timed main launch has
 // B * H * parts workgroups.
