@@ -484,7 +484,13 @@ static hipError_t run_proj(int M, int N, int K, const void* Wt, const AL& al, co
   constexpr int kMaxNW = FM * FN <= 2 ? 16 : 8;  // 1024-thread blocks only for the small tile
   int nw = 4;
   while (nw < kMaxNW && (ksteps + nw - 1) / nw > U) nw *= 2;
-  if (tiles < 128 && ksteps >= 32) nw = kMaxNW;
+  // Few tiles: the most waves, so that each compute unit has more loads in flight. Below 128
+  // rows the batch runs as one row group and the launch has the chip to itself, so this pays
+  // from 256 tiles and 16 k-steps down (one box: long-context batch of 16 7.39 -> 6.96 s per
+  // run, 50M-scale batch of 64 273 -> 264 ms); at 128 rows per group the other group's
+  // attention shares the compute units, and the same rule cost the 140M-scale run 2.4%.
+  const bool few = M < 128 ? tiles < 256 && ksteps >= 16 : tiles < 128 && ksteps >= 32;
+  if (few) nw = kMaxNW;
   const T* W = static_cast<const T*>(Wt);
   if (nw == 4) launch_proj<T, FM, FN, 4>(tiles, N, K, W, al, ep, st);
   else if (nw == 8) launch_proj<T, FM, FN, 8>(tiles, N, K, W, al, ep, st);
