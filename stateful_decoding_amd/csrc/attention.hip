@@ -266,7 +266,13 @@ static hipError_t attend_t(int BH, const float* q, const T* K, const T* V, int64
   const int64_t items = (int64_t)BH * parts;
   if (parts < 1 || parts > kMaxSplits || items > INT32_MAX) return hipErrorInvalidValue;
   const int64_t blocks = attn_blocks(items);
-  const int nw = items >= 1024 ? 4 : items >= 512 ? 8 : 16;
+  // Waves per workgroup from the number of items (sequence-head pairs x parts): few waves per
+  // workgroup stream best once there are many workgroups. One box, against the earlier 4 / 8 /
+  // 16 waves from 1024 / 512 / fewer items: 50M-scale batch of 64 (512 pairs) 263.5 -> 255.3 ms
+  // per run and 48-layer batch of 32 (512 pairs) 5.24 -> 5.04 s over its first 1024 tokens with
+  // 4 waves (16 waves: 317.7 ms, 5.54 s); long-context batch of 16 (192 pairs) 6.96 -> 6.71 s
+  // with 8 waves (4 waves: 7.31 s).
+  const int nw = items >= 512 ? 4 : items >= 128 ? 8 : 16;
   hipError_t e = hipSuccess;
 #define RLT_ATTEND(NW)                                                                     \
   e = launch(!MEMORY ? k_attend_window<T, HD, NW, kAttnU>                                  \
